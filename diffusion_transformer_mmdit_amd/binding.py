@@ -1,0 +1,356 @@
+"""Thin ctypes binding of libmmdit.so (C ABI in include/mmdit.h).
+
+Functions carry the C names and only marshal arguments: torch tensors become
+device pointers, the current torch stream becomes the hipStream_t, non-zero
+statuses become MMDiTError. Every computation happens in the library's HIP
+kernels. There is no fallback: if libmmdit.so has not been built, lib() raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmmdit.so")
+_lib = None
+
+F32, BF16 = 0, 1
+W_DENSE, W_Q4G64, W_Q8G64 = 0, 1, 2
+PC_GEMM, PC_ATTN, PC_LN, PC_QKNORM, PC_GEMV = 1, 2, 3, 4, 5
+
+
+class MMDiTError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().mmdit_last_error().decode(errors="replace")
+        st = lib().mmdit_status_str(status).decode()
+        super().__init__(f"{where}: status {status} ({st}): {msg}")
+
+
+# ------------------------------------------------------------------ structs --
+class mmdit_dims(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("hidden", C.c_int32), ("heads", C.c_int32),
+                ("head_dim", C.c_int32), ("mlp_hidden", C.c_int32), ("txt_len", C.c_int32),
+                ("img_len", C.c_int32), ("axes_dim", C.c_int32 * 3), ("theta", C.c_double),
+                ("ln_eps", C.c_float), ("rms_eps", C.c_float), ("act_dtype", C.c_int32)]
+
+
+class mmdit_linear(C.Structure):
+    _fields_ = [("w", C.c_void_p), ("scales", C.c_void_p), ("bias", C.c_void_p),
+                ("fmt", C.c_int32), ("n_out", C.c_int32), ("k_in", C.c_int32)]
+
+
+class mmdit_stream_w(C.Structure):
+    _fields_ = [("mod", mmdit_linear), ("qkv", mmdit_linear), ("proj", mmdit_linear),
+                ("fc1", mmdit_linear), ("fc2", mmdit_linear), ("q_norm", C.c_void_p),
+                ("k_norm", C.c_void_p)]
+
+
+class mmdit_double_w(C.Structure):
+    _fields_ = [("img", mmdit_stream_w), ("txt", mmdit_stream_w)]
+
+
+class mmdit_single_w(C.Structure):
+    _fields_ = [("mod", mmdit_linear), ("lin1", mmdit_linear), ("lin2", mmdit_linear),
+                ("q_norm", C.c_void_p), ("k_norm", C.c_void_p)]
+
+
+class mmdit_config(C.Structure):
+    _fields_ = [("dims", mmdit_dims), ("n_double", C.c_int32), ("n_single", C.c_int32),
+                ("in_ch", C.c_int32), ("txt_in_dim", C.c_int32), ("vec_in_dim", C.c_int32),
+                ("temb_dim", C.c_int32)]
+
+
+class mmdit_model_w(C.Structure):
+    _fields_ = [("img_in", mmdit_linear), ("txt_in", mmdit_linear), ("time_in0", mmdit_linear),
+                ("time_in1", mmdit_linear), ("vec_in0", mmdit_linear), ("vec_in1", mmdit_linear),
+                ("final_mod", mmdit_linear), ("final_lin", mmdit_linear),
+                ("dbl", C.POINTER(mmdit_double_w)), ("sgl", C.POINTER(mmdit_single_w))]
+
+
+# Every function the header declares, with its ctypes signature.
+_P = C.c_void_p
+_SIGS = {
+    "mmdit_double_block_workspace": (C.c_int, [C.POINTER(mmdit_dims), C.POINTER(C.c_size_t)]),
+    "mmdit_single_block_workspace": (C.c_int, [C.POINTER(mmdit_dims), C.POINTER(C.c_size_t)]),
+    "mmdit_step_workspace": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(C.c_size_t)]),
+    "mmdit_double_block_fwd": (C.c_int, [C.POINTER(mmdit_dims), C.POINTER(mmdit_double_w), _P, _P, _P, _P,
+                                         _P, _P, _P, C.c_size_t, _P]),
+    "mmdit_single_block_fwd": (C.c_int, [C.POINTER(mmdit_dims), C.POINTER(mmdit_single_w), _P, _P, _P, _P,
+                                         _P, C.c_size_t, _P]),
+    "mmdit_step": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(mmdit_model_w), _P, _P, _P, _P, _P,
+                             C.c_double, C.c_double, _P, C.c_size_t, _P]),
+    "mmdit_schedule": (C.c_int, [C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double, C.c_int32, _P]),
+    "mmdit_make_ids": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P]),
+    "mmdit_pack_latents": (C.c_int, [_P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P]),
+    "mmdit_unpack_latents": (C.c_int, [_P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P]),
+    "mmdit_rope_table": (C.c_int, [_P, C.c_int32, _P, C.c_double, _P, _P]),
+    "mmdit_quantise": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P]),
+    "mmdit_profile_begin": (C.c_int, [C.c_int32, C.c_int32]),
+    "mmdit_profile_end": (C.c_int, [C.POINTER(C.c_double), C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
+    "mmdit_status_str": (C.c_char_p, [C.c_int32]),
+    "mmdit_last_error": (C.c_char_p, []),
+    "mmdit_version": (C.c_char_p, []),
+}
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libmmdit.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                              "`python -m diffusion_transformer_mmdit_amd.build`")
+        L = C.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MMDiTError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# ------------------------------------------------------------------ weights --
+def _dt(dtype: int):
+    import torch
+    return torch.bfloat16 if dtype == BF16 else torch.float32
+
+
+class Linear:
+    """Device tensors of one linear layer (keeps them alive)."""
+
+    def __init__(self, w, bias=None, scales=None, fmt=W_DENSE, n_out=None, k_in=None):
+        self.w, self.bias, self.scales, self.fmt = w, bias, scales, fmt
+        self.n_out = int(n_out if n_out is not None else w.shape[0])
+        self.k_in = int(k_in if k_in is not None else w.shape[1])
+
+    def c(self) -> mmdit_linear:
+        return mmdit_linear(_ptr(self.w), _ptr(self.scales), _ptr(self.bias), self.fmt, self.n_out, self.k_in)
+
+    @staticmethod
+    def from_numpy(w: np.ndarray, b: Optional[np.ndarray], dtype: int, device, bits: int = 0) -> "Linear":
+        import torch
+        bt = None if b is None else torch.from_numpy(np.ascontiguousarray(b)).to(device).to(_dt(dtype))
+        if bits == 0:
+            wt = torch.from_numpy(np.ascontiguousarray(w)).to(device).to(_dt(dtype))
+            return Linear(wt, bt)
+        packed, scales = mmdit_quantise(w, bits)
+        st = torch.from_numpy(scales.view(np.int16)).to(device).view(torch.bfloat16)
+        pt = torch.from_numpy(packed).to(device)
+        return Linear(pt, bt, st, W_Q4G64 if bits == 4 else W_Q8G64, w.shape[0], w.shape[1])
+
+
+def _vec(a, dtype, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device).to(_dt(dtype))
+
+
+class StreamW:
+    def __init__(self, d: Dict[str, np.ndarray], dtype: int, device, quant: Optional[Dict[str, int]] = None):
+        q = quant or {}
+        self.mod = Linear.from_numpy(d["mod_w"], d["mod_b"], dtype, device)
+        self.qkv = Linear.from_numpy(d["qkv_w"], d["qkv_b"], dtype, device, q.get("qkv", 0))
+        self.proj = Linear.from_numpy(d["proj_w"], d["proj_b"], dtype, device, q.get("proj", 0))
+        self.fc1 = Linear.from_numpy(d["fc1_w"], d["fc1_b"], dtype, device, q.get("fc1", 0))
+        self.fc2 = Linear.from_numpy(d["fc2_w"], d["fc2_b"], dtype, device, q.get("fc2", 0))
+        self.q_norm = _vec(d["q_norm"], dtype, device)
+        self.k_norm = _vec(d["k_norm"], dtype, device)
+
+    def c(self) -> mmdit_stream_w:
+        return mmdit_stream_w(self.mod.c(), self.qkv.c(), self.proj.c(), self.fc1.c(), self.fc2.c(),
+                              _ptr(self.q_norm), _ptr(self.k_norm))
+
+
+class DoubleW:
+    def __init__(self, d, dtype: int, device, quant=None):
+        self.img = StreamW(d["img"], dtype, device, quant)
+        self.txt = StreamW(d["txt"], dtype, device, quant)
+
+    def c(self) -> mmdit_double_w:
+        return mmdit_double_w(self.img.c(), self.txt.c())
+
+
+class SingleW:
+    def __init__(self, d, dtype: int, device, quant=None):
+        q = quant or {}
+        self.mod = Linear.from_numpy(d["mod_w"], d["mod_b"], dtype, device)
+        self.lin1 = Linear.from_numpy(d["lin1_w"], d["lin1_b"], dtype, device, q.get("lin1", 0))
+        self.lin2 = Linear.from_numpy(d["lin2_w"], d["lin2_b"], dtype, device, q.get("lin2", 0))
+        self.q_norm = _vec(d["q_norm"], dtype, device)
+        self.k_norm = _vec(d["k_norm"], dtype, device)
+
+    def c(self) -> mmdit_single_w:
+        return mmdit_single_w(self.mod.c(), self.lin1.c(), self.lin2.c(), _ptr(self.q_norm), _ptr(self.k_norm))
+
+
+# Quantisation policy: the layers writing into the residual stream keep 8
+# bits, the inner projections 4 bits (stable-diffusion.rs README).
+QUANT_POLICY = {"qkv": 4, "fc1": 4, "lin1": 4, "proj": 8, "fc2": 8, "lin2": 8}
+
+
+class ModelW:
+    """Whole-model weights: global layers plus lists of block weights."""
+
+    def __init__(self, g: Dict[str, np.ndarray], dbl: Sequence, sgl: Sequence, dtype: int, device):
+        L = lambda n: Linear.from_numpy(g[n + "_w"], g[n + "_b"], dtype, device)  # noqa: E731
+        self.img_in, self.txt_in = L("img_in"), L("txt_in")
+        self.time_in0, self.time_in1 = L("time_in0"), L("time_in1")
+        self.vec_in0, self.vec_in1 = L("vec_in0"), L("vec_in1")
+        self.final_mod = L("final_mod")
+        self.final_lin = Linear.from_numpy(g["final_w"], g["final_b"], dtype, device)
+        self.dbl: List = list(dbl)
+        self.sgl: List = list(sgl)
+
+    def c(self) -> mmdit_model_w:
+        self._dbl_arr = (mmdit_double_w * max(1, len(self.dbl)))(*[d.c() for d in self.dbl])
+        self._sgl_arr = (mmdit_single_w * max(1, len(self.sgl)))(*[s.c() for s in self.sgl])
+        return mmdit_model_w(self.img_in.c(), self.txt_in.c(), self.time_in0.c(), self.time_in1.c(),
+                             self.vec_in0.c(), self.vec_in1.c(), self.final_mod.c(), self.final_lin.c(),
+                             C.cast(self._dbl_arr, C.POINTER(mmdit_double_w)),
+                             C.cast(self._sgl_arr, C.POINTER(mmdit_single_w)))
+
+
+def make_dims(s, dtype: Optional[int] = None) -> mmdit_dims:
+    """mmdit_dims from an inputs.Shape."""
+    d = mmdit_dims()
+    d.batch, d.hidden, d.heads, d.head_dim = s.batch, s.hidden, s.heads, s.head_dim
+    d.mlp_hidden, d.txt_len, d.img_len = s.mlp_hidden, s.txt_len, s.img_len
+    d.axes_dim = (C.c_int32 * 3)(*s.axes_dim)
+    d.theta, d.ln_eps, d.rms_eps = s.theta, 1e-6, 1e-6
+    d.act_dtype = dtype if dtype is not None else (BF16 if s.dtype == "bf16" else F32)
+    return d
+
+
+def make_config(s, dtype: Optional[int] = None) -> mmdit_config:
+    c = mmdit_config()
+    c.dims = make_dims(s, dtype)
+    c.n_double, c.n_single = s.n_double, s.n_single
+    c.in_ch, c.txt_in_dim, c.vec_in_dim, c.temb_dim = s.in_ch, s.txt_in_dim, s.vec_in_dim, s.temb_dim
+    return c
+
+
+# ------------------------------------------------------------------ entry points --
+def mmdit_double_block_workspace(dims: mmdit_dims) -> int:
+    n = C.c_size_t()
+    _check(lib().mmdit_double_block_workspace(C.byref(dims), C.byref(n)), "mmdit_double_block_workspace")
+    return n.value
+
+
+def mmdit_single_block_workspace(dims: mmdit_dims) -> int:
+    n = C.c_size_t()
+    _check(lib().mmdit_single_block_workspace(C.byref(dims), C.byref(n)), "mmdit_single_block_workspace")
+    return n.value
+
+
+def mmdit_step_workspace(cfg: mmdit_config) -> int:
+    n = C.c_size_t()
+    _check(lib().mmdit_step_workspace(C.byref(cfg), C.byref(n)), "mmdit_step_workspace")
+    return n.value
+
+
+def mmdit_double_block_fwd(dims, w: mmdit_double_w, img_in, txt_in, img_out, txt_out, vec, ids, ws,
+                           stream=None):
+    _check(lib().mmdit_double_block_fwd(C.byref(dims), C.byref(w), _ptr(img_in), _ptr(txt_in), _ptr(img_out),
+                                        _ptr(txt_out), _ptr(vec), _ptr(ids), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)),
+           "mmdit_double_block_fwd")
+
+
+def mmdit_single_block_fwd(dims, w: mmdit_single_w, x_in, x_out, vec, ids, ws, stream=None):
+    _check(lib().mmdit_single_block_fwd(C.byref(dims), C.byref(w), _ptr(x_in), _ptr(x_out), _ptr(vec),
+                                        _ptr(ids), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "mmdit_single_block_fwd")
+
+
+def mmdit_step(cfg, w: mmdit_model_w, x_packed, v_out, txt_emb, y, ids, sigma: float, sigma_next: float, ws,
+               stream=None):
+    _check(lib().mmdit_step(C.byref(cfg), C.byref(w), _ptr(x_packed), _ptr(v_out), _ptr(txt_emb), _ptr(y),
+                            _ptr(ids), float(sigma), float(sigma_next), _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream)),
+           "mmdit_step")
+
+
+def mmdit_schedule(n_steps: int, img_len: int, base_shift=0.5, max_shift=1.15, sigma_terminal=0.0,
+                   shift=True) -> np.ndarray:
+    out = np.zeros(n_steps + 1, dtype=np.float64)
+    _check(lib().mmdit_schedule(n_steps, img_len, base_shift, max_shift, sigma_terminal, int(shift),
+                                out.ctypes.data_as(C.c_void_p)), "mmdit_schedule")
+    return out
+
+
+def mmdit_make_ids(grid_h: int, grid_w: int, txt_len: int, frame: int = 0) -> np.ndarray:
+    out = np.zeros((txt_len + grid_h * grid_w, 3), dtype=np.int32)
+    _check(lib().mmdit_make_ids(grid_h, grid_w, txt_len, frame, out.ctypes.data_as(C.c_void_p)), "mmdit_make_ids")
+    return out
+
+
+def mmdit_pack_latents(z, x, stream=None):
+    B, Cc, H, W = z.shape
+    _check(lib().mmdit_pack_latents(_ptr(z), _ptr(x), B, Cc, H, W, z.element_size(), _stream(stream)),
+           "mmdit_pack_latents")
+
+
+def mmdit_unpack_latents(x, z, stream=None):
+    B, Cc, H, W = z.shape
+    _check(lib().mmdit_unpack_latents(_ptr(x), _ptr(z), B, Cc, H, W, z.element_size(), _stream(stream)),
+           "mmdit_unpack_latents")
+
+
+def mmdit_rope_table(ids, axes_dim, theta, table, stream=None):
+    ax = np.ascontiguousarray(np.asarray(axes_dim, dtype=np.int32))
+    _check(lib().mmdit_rope_table(_ptr(ids), ids.shape[0], ax.ctypes.data_as(C.c_void_p), float(theta),
+                                  _ptr(table), _stream(stream)), "mmdit_rope_table")
+
+
+def mmdit_quantise(w: np.ndarray, bits: int):
+    """Returns (packed uint8/int8 codes, scales as uint16 bf16 bits)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    packed = np.zeros((n, k // 2) if bits == 4 else (n, k), dtype=np.uint8 if bits == 4 else np.int8)
+    scales = np.zeros((n, k // 64), dtype=np.uint16)
+    _check(lib().mmdit_quantise(w.ctypes.data_as(C.c_void_p), n, k, bits, packed.ctypes.data_as(C.c_void_p),
+                                scales.ctypes.data_as(C.c_void_p)), "mmdit_quantise")
+    return packed, scales
+
+
+def mmdit_profile_begin(kernel_class: int, max_launches: int):
+    _check(lib().mmdit_profile_begin(kernel_class, max_launches), "mmdit_profile_begin")
+
+
+def mmdit_profile_end():
+    ms, n, work = C.c_double(), C.c_int32(), C.c_double()
+    _check(lib().mmdit_profile_end(C.byref(ms), C.byref(n), C.byref(work)), "mmdit_profile_end")
+    return ms.value, n.value, work.value
+
+
+def mmdit_status_str(status: int) -> str:
+    return lib().mmdit_status_str(status).decode()
+
+
+def mmdit_last_error() -> str:
+    return lib().mmdit_last_error().decode()
+
+
+def mmdit_version() -> str:
+    return lib().mmdit_version().decode()

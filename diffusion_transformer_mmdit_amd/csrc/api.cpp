@@ -1,0 +1,722 @@
+// C ABI of the MMDiT denoising step: argument validation, workspace layout
+// and the order of kernel launches for the dual-stream block, the
+// single-stream block and the whole step. All arithmetic runs in the HIP
+// kernels (k_*.hip); this file only checks, carves buffers and enqueues.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/mmdit.h"
+#include "kernels.h"
+
+using namespace mmdit;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(MMDIT_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ------------------------------------------------------------------ profiling --
+struct Prof {
+  std::mutex mu;
+  bool active = false;
+  int cls = 0;
+  int cap = 0;
+  int used = 0;
+  double work = 0;
+  std::vector<hipEvent_t> ev;
+};
+Prof g_prof;
+
+enum { PC_GEMM = 1, PC_ATTN = 2, PC_LN = 3, PC_QKNORM = 4, PC_GEMV = 5 };
+
+struct ProfScope {
+  hipEvent_t stop = nullptr;
+  hipStream_t s;
+  ProfScope(int cls, double work, hipStream_t st) : s(st) {
+    if (!g_prof.active || g_prof.cls != cls || g_prof.used >= g_prof.cap) return;
+    hipEvent_t start = g_prof.ev[2 * g_prof.used];
+    stop = g_prof.ev[2 * g_prof.used + 1];
+    g_prof.used++;
+    g_prof.work += work;
+    (void)hipEventRecord(start, s);
+  }
+  ~ProfScope() {
+    if (stop) (void)hipEventRecord(stop, s);
+  }
+};
+
+// ------------------------------------------------------------------ checks --
+struct Geo {
+  int B, h, H, m, Lt, Li, L, Lpad;
+  bool bf16;
+  int esz;
+};
+
+int check_dims(const mmdit_dims* d, Geo& g) {
+  if (!d) return fail(MMDIT_ERR_NULL, "dims is NULL");
+  if (d->act_dtype != MMDIT_F32 && d->act_dtype != MMDIT_BF16)
+    return fail(MMDIT_ERR_DTYPE, "act_dtype %d is not MMDIT_F32 or MMDIT_BF16", d->act_dtype);
+  if (d->head_dim != 128) return fail(MMDIT_ERR_UNSUPPORTED, "head_dim %d: only 128 is implemented", d->head_dim);
+  if (d->batch < 1 || d->heads < 1) return fail(MMDIT_ERR_SHAPE, "batch and heads must be >= 1");
+  if ((int64_t)d->heads * 128 != d->hidden) return fail(MMDIT_ERR_SHAPE, "hidden %d != heads*head_dim", d->hidden);
+  if (d->hidden % 256 != 0 || d->hidden > 4096)
+    return fail(MMDIT_ERR_SHAPE, "hidden %d must be a multiple of 256 and at most 4096", d->hidden);
+  if (d->mlp_hidden < 64 || d->mlp_hidden % 64 != 0) return fail(MMDIT_ERR_SHAPE, "mlp_hidden %d must be a positive multiple of 64", d->mlp_hidden);
+  if (d->txt_len < 0 || d->img_len < 1) return fail(MMDIT_ERR_SHAPE, "need txt_len >= 0 and img_len >= 1");
+  int sum = 0;
+  for (int a = 0; a < 3; ++a) {
+    if (d->axes_dim[a] < 0 || d->axes_dim[a] % 2) return fail(MMDIT_ERR_SHAPE, "axes_dim[%d] must be even and >= 0", a);
+    sum += d->axes_dim[a];
+  }
+  if (sum != d->head_dim) return fail(MMDIT_ERR_SHAPE, "axes_dim sum %d != head_dim", sum);
+  if (!(d->theta > 0) || !(d->ln_eps > 0) || !(d->rms_eps > 0)) return fail(MMDIT_ERR_SHAPE, "theta and eps must be > 0");
+  g.B = d->batch; g.h = d->hidden; g.H = d->heads; g.m = d->mlp_hidden;
+  g.Lt = d->txt_len; g.Li = d->img_len; g.L = g.Lt + g.Li;
+  g.Lpad = (g.L + 127) / 128 * 128;
+  g.bf16 = d->act_dtype == MMDIT_BF16;
+  g.esz = g.bf16 ? 2 : 4;
+  const int64_t widest = 3 * (int64_t)g.h + g.m;
+  if ((int64_t)g.B * g.Lpad * widest >= (int64_t(1) << 31) || (int64_t)g.B * g.H * g.Lpad * 128 >= (int64_t(1) << 31))
+    return fail(MMDIT_ERR_SHAPE, "batch * tokens too large for 32-bit row indexing");
+  return MMDIT_OK;
+}
+
+// GEMM linear: dense (any K for f32; K % 64 for bf16) or quantised (bf16 only).
+int check_linear(const mmdit_linear& l, int n, int k, const Geo& g, const char* name) {
+  if (!l.w) return fail(MMDIT_ERR_NULL, "%s.w is NULL", name);
+  if (l.n_out != n || l.k_in != k) return fail(MMDIT_ERR_SHAPE, "%s is [%d, %d], expected [%d, %d]", name, l.n_out, l.k_in, n, k);
+  if (l.fmt == MMDIT_W_DENSE) {
+    if (g.bf16 && k % 64) return fail(MMDIT_ERR_SHAPE, "%s: k_in %d must be a multiple of 64 for bf16", name, k);
+    return MMDIT_OK;
+  }
+  if (l.fmt != MMDIT_W_Q4G64 && l.fmt != MMDIT_W_Q8G64) return fail(MMDIT_ERR_DTYPE, "%s: unknown weight format %d", name, l.fmt);
+  if (!g.bf16) return fail(MMDIT_ERR_DTYPE, "%s: quantised weights need bf16 activations", name);
+  if (k % 64) return fail(MMDIT_ERR_SHAPE, "%s: quantised k_in %d must be a multiple of 64", name, k);
+  if (!l.scales) return fail(MMDIT_ERR_NULL, "%s.scales is NULL", name);
+  return MMDIT_OK;
+}
+
+// GEMV linear (modulation, conditioning MLPs): dense, K % 8, K <= 4096.
+int check_gemv(const mmdit_linear& l, int n, int k, const char* name) {
+  if (!l.w) return fail(MMDIT_ERR_NULL, "%s.w is NULL", name);
+  if (l.n_out != n || l.k_in != k) return fail(MMDIT_ERR_SHAPE, "%s is [%d, %d], expected [%d, %d]", name, l.n_out, l.k_in, n, k);
+  if (l.fmt != MMDIT_W_DENSE) return fail(MMDIT_ERR_DTYPE, "%s must be dense", name);
+  if (k % 8 || k > 4096) return fail(MMDIT_ERR_SHAPE, "%s: k_in %d must be a multiple of 8 and <= 4096", name, k);
+  return MMDIT_OK;
+}
+
+int check_stream(const mmdit_stream_w& s, const Geo& g, const char* name) {
+  char nm[64];
+  int r;
+  snprintf(nm, sizeof nm, "%s.mod", name);
+  if ((r = check_gemv(s.mod, 6 * g.h, g.h, nm))) return r;
+  snprintf(nm, sizeof nm, "%s.qkv", name);
+  if ((r = check_linear(s.qkv, 3 * g.h, g.h, g, nm))) return r;
+  snprintf(nm, sizeof nm, "%s.proj", name);
+  if ((r = check_linear(s.proj, g.h, g.h, g, nm))) return r;
+  snprintf(nm, sizeof nm, "%s.fc1", name);
+  if ((r = check_linear(s.fc1, g.m, g.h, g, nm))) return r;
+  snprintf(nm, sizeof nm, "%s.fc2", name);
+  if ((r = check_linear(s.fc2, g.h, g.m, g, nm))) return r;
+  if (!s.q_norm || !s.k_norm) return fail(MMDIT_ERR_NULL, "%s q_norm/k_norm is NULL", name);
+  return MMDIT_OK;
+}
+
+int check_single(const mmdit_single_w& s, const Geo& g) {
+  int r;
+  if ((r = check_gemv(s.mod, 3 * g.h, g.h, "single.mod"))) return r;
+  if ((r = check_linear(s.lin1, 3 * g.h + g.m, g.h, g, "single.lin1"))) return r;
+  if ((r = check_linear(s.lin2, g.h, g.h + g.m, g, "single.lin2"))) return r;
+  if (!s.q_norm || !s.k_norm) return fail(MMDIT_ERR_NULL, "single q_norm/k_norm is NULL");
+  return MMDIT_OK;
+}
+
+// ---------------------------------------------------------------- workspace --
+// Block scratch (activation dtype unless noted):
+//   xn [rows, h], qkv [rows, 3h], Q/K/V [B, H, Lpad, 128],
+//   o   [rows, h] (dual) or cat [rows, h + m] (single), mlp [rows, m] (dual).
+struct BlockWs {
+  size_t xn, qkv, q, k, v, o, mlp, total;
+};
+
+BlockWs plan_block(const Geo& g, size_t base) {
+  BlockWs w;
+  const size_t rows = (size_t)g.B * g.L;
+  const size_t qkvh = (size_t)g.B * g.H * g.Lpad * 128;
+  size_t at = base;
+  w.xn = at; at = align_up(at + rows * g.h * g.esz);
+  w.qkv = at; at = align_up(at + rows * 3 * g.h * g.esz);
+  w.q = at; at = align_up(at + qkvh * g.esz);
+  w.k = at; at = align_up(at + qkvh * g.esz);
+  w.v = at; at = align_up(at + qkvh * g.esz);
+  w.o = at; at = align_up(at + rows * (size_t)(g.h + g.m) * g.esz);
+  w.mlp = at; at = align_up(at + rows * g.m * g.esz);
+  w.total = at;
+  return w;
+}
+
+// Block-call workspace: RoPE table [L, 64, 2] f32, modulation f32, scratch.
+struct BlockCallWs {
+  size_t table, mod;
+  BlockWs blk;
+};
+
+BlockCallWs plan_block_call(const Geo& g, int mod_width) {
+  BlockCallWs w;
+  size_t at = 0;
+  w.table = at; at = align_up(at + (size_t)g.L * 64 * 2 * 4);
+  w.mod = at; at = align_up(at + (size_t)g.B * mod_width * 4);
+  w.blk = plan_block(g, at);
+  return w;
+}
+
+// Step workspace.
+struct StepWs {
+  size_t x, vec, temb, hid, mods, table, xin;
+  BlockWs blk;
+  size_t mod_dual, mod_single, mod_final;  // offsets inside mods (floats)
+};
+
+StepWs plan_step(const mmdit_config* c, const Geo& g) {
+  StepWs w;
+  size_t at = 0;
+  const size_t B = g.B;
+  w.x = at; at = align_up(at + B * g.L * g.h * 4);
+  w.vec = at; at = align_up(at + B * g.h * 4);
+  w.temb = at; at = align_up(at + B * c->temb_dim * 4);
+  w.hid = at; at = align_up(at + B * g.h * 4);
+  w.mod_dual = 0;
+  w.mod_single = (size_t)c->n_double * 2 * B * 6 * g.h;
+  w.mod_final = w.mod_single + (size_t)c->n_single * B * 3 * g.h;
+  w.mods = at; at = align_up(at + (w.mod_final + B * 2 * g.h) * 4);
+  w.table = at; at = align_up(at + (size_t)g.L * 64 * 2 * 4);
+  w.xin = at; at = align_up(at + B * g.Li * c->in_ch * g.esz);
+  w.blk = plan_block(g, at);
+  return w;
+}
+
+// --------------------------------------------------------------- launches --
+struct Ctx {
+  hipStream_t s;
+  Geo g;
+  float ln_eps, rms_eps;
+};
+
+char* ptr(void* base, size_t off) { return reinterpret_cast<char*>(base) + off; }
+
+int gemm(const Ctx& c, GemmProblem* p, int np, int epi) {
+  double flops = 0;
+  for (int i = 0; i < np; ++i) flops += 2.0 * p[i].M * (double)p[i].N * p[i].K;
+  ProfScope ps(PC_GEMM, flops, c.s);
+  HIP_TRY(c.g.bf16 ? launch_gemm_bf16(p, np, epi, c.s) : launch_gemm_f32(p, np, epi, c.s));
+  return MMDIT_OK;
+}
+
+int gemv(const Ctx& c, const mmdit_linear& l, const void* x, bool x_f32, int x_bstride, float* y,
+         int y_bstride, bool silu, bool accumulate) {
+  GemvArgs a;
+  a.W = l.w; a.bias = l.bias; a.x = x; a.y = y;
+  a.N = l.n_out; a.K = l.k_in; a.B = c.g.B;
+  a.x_bstride = x_bstride; a.y_bstride = y_bstride;
+  a.silu_in = silu; a.accumulate = accumulate;
+  ProfScope ps(PC_GEMV, (double)l.n_out * l.k_in * c.g.esz, c.s);
+  HIP_TRY(launch_gemv(a, c.g.bf16, x_f32 || !c.g.bf16, c.s));
+  return MMDIT_OK;
+}
+
+// A block operates on up to two parts: the text rows and the image rows.
+// Part p has len tokens per batch; its rows in the contiguous scratch buffers
+// start at row0 (row = row0 + b * len + t_local); its residual rows are x_in /
+// x_out (activation dtype, or f32 when res_f32).
+struct Part {
+  int len;
+  int64_t row0;
+  RowSeg x_in, x_out;
+  const float* mod;
+};
+
+RowSeg rows_of(void* buf, int64_t row0, int len, int ld, int esz) {
+  RowSeg r;
+  r.base = ptr(buf, (size_t)row0 * ld * esz);
+  r.batch_stride = (int64_t)len * ld;
+  r.rows_per_batch = len > 0 ? len : 1;
+  r.ld = ld;
+  return r;
+}
+
+int run_ln(const Ctx& c, const Part* parts, int np, int mod_bstride, int shift_off, int scale_off,
+           bool res_f32, void* y) {
+  const Geo& g = c.g;
+  LnArgs a{};
+  int rows = 0;
+  for (int p = 0; p < 2; ++p) {
+    if (p < np) {
+      a.seg[p] = parts[p].x_in;
+      a.seg_rows[p] = g.B * parts[p].len;
+      a.mod[p] = parts[p].mod;
+    } else {
+      a.seg[p] = parts[0].x_in;
+      a.seg_rows[p] = 0;
+      a.mod[p] = parts[0].mod;
+    }
+    rows += a.seg_rows[p];
+  }
+  a.mod_bstride = mod_bstride; a.shift_off = shift_off; a.scale_off = scale_off;
+  a.y = y; a.h = g.h; a.eps = c.ln_eps;
+  if (rows == 0) return MMDIT_OK;
+  ProfScope ps(PC_LN, (double)rows * g.h * ((res_f32 ? 4 : g.esz) + g.esz), c.s);
+  HIP_TRY(launch_adaln_ln(a, rows, res_f32 || !g.bf16, g.bf16, c.s));
+  return MMDIT_OK;
+}
+
+int run_qk_attn(const Ctx& c, const Part* parts, int np, void* qkv, const void* const qn[2],
+                const void* const kn[2], const float* table, const BlockWs& w, void* ws, void* obuf, int o_ld) {
+  const Geo& g = c.g;
+  QkNormArgs q{};
+  AttnArgs at{};
+  for (int p = 0; p < 2; ++p) {
+    const int pp = p < np ? p : 0;
+    q.seg[p] = rows_of(qkv, parts[pp].row0, parts[pp].len, 3 * g.h, g.esz);
+    q.qn[p] = qn[pp];
+    q.kn[p] = kn[pp];
+    at.out[p] = rows_of(obuf, parts[pp].row0, parts[pp].len, o_ld, g.esz);
+  }
+  q.seg_len0 = np == 2 ? parts[0].len : g.L;
+  q.table = table;
+  q.Q = ptr(ws, w.q); q.K = ptr(ws, w.k); q.V = ptr(ws, w.v);
+  q.B = g.B; q.H = g.H; q.L = g.L; q.Lpad = g.Lpad; q.eps = c.rms_eps;
+  {
+    ProfScope ps(PC_QKNORM, (double)g.B * g.L * 3 * g.h * g.esz * 2, c.s);
+    HIP_TRY(launch_qk_norm_rope(q, g.bf16, g.bf16, c.s));
+  }
+  at.Q = q.Q; at.K = q.K; at.V = q.V;
+  at.seg_len0 = q.seg_len0;
+  at.B = g.B; at.H = g.H; at.L = g.L; at.Lpad = g.Lpad;
+  at.scale = 1.0f / sqrtf(128.0f);
+  {
+    ProfScope ps(PC_ATTN, 4.0 * g.B * g.H * (double)g.L * g.L * 128, c.s);
+    HIP_TRY(g.bf16 ? launch_attention_bf16(at, c.s) : launch_attention_f32(at, c.s));
+  }
+  return MMDIT_OK;
+}
+
+GemmProblem base_problem(const mmdit_linear& l) {
+  GemmProblem p{};
+  p.W = l.w; p.scales = l.scales; p.bias = l.bias; p.fmt = l.fmt;
+  p.N = l.n_out; p.K = l.k_in;
+  return p;
+}
+
+// Dual-stream block; parts[0] text, parts[1] image; sw[p] the stream weights.
+int run_double(const Ctx& c, const mmdit_stream_w* const sw[2], const Part* parts, bool res_f32,
+               const float* table, void* ws, const BlockWs& w) {
+  const Geo& g = c.g;
+  const int h = g.h, m = g.m;
+  int r;
+  void* xn = ptr(ws, w.xn);
+  void* qkv = ptr(ws, w.qkv);
+  void* o = ptr(ws, w.o);
+  void* mlp = ptr(ws, w.mlp);
+  // adaLN LayerNorm 1
+  if ((r = run_ln(c, parts, 2, 6 * h, 0, h, res_f32, xn))) return r;
+  // QKV projection (both streams, one launch)
+  GemmProblem gp[2];
+  for (int p = 0; p < 2; ++p) {
+    gp[p] = base_problem(sw[p]->qkv);
+    gp[p].A = ptr(xn, (size_t)parts[p].row0 * h * g.esz); gp[p].lda = h;
+    gp[p].M = g.B * parts[p].len;
+    gp[p].out = ptr(qkv, (size_t)parts[p].row0 * 3 * h * g.esz); gp[p].ldo = 3 * h;
+  }
+  if ((r = gemm(c, gp, 2, EPI_STORE))) return r;
+  // QK RMSNorm + RoPE, joint attention
+  const void* qn[2] = {sw[0]->q_norm, sw[1]->q_norm};
+  const void* kn[2] = {sw[0]->k_norm, sw[1]->k_norm};
+  if ((r = run_qk_attn(c, parts, 2, qkv, qn, kn, table, w, ws, o, h))) return r;
+  // out-projection, x += gate1 * (.)
+  for (int p = 0; p < 2; ++p) {
+    gp[p] = base_problem(sw[p]->proj);
+    gp[p].A = ptr(o, (size_t)parts[p].row0 * h * g.esz); gp[p].lda = h;
+    gp[p].M = g.B * parts[p].len;
+    gp[p].res_in = parts[p].x_in; gp[p].res_out = parts[p].x_out; gp[p].res_f32 = res_f32;
+    gp[p].gate = parts[p].mod + 2 * h; gp[p].gate_bstride = 6 * h;
+  }
+  if ((r = gemm(c, gp, 2, EPI_GATE_RES))) return r;
+  // adaLN LayerNorm 2 on the updated residual
+  Part p2[2] = {parts[0], parts[1]};
+  for (int p = 0; p < 2; ++p) p2[p].x_in = parts[p].x_out;
+  if ((r = run_ln(c, p2, 2, 6 * h, 3 * h, 4 * h, res_f32, xn))) return r;
+  // fc1 + GELU
+  for (int p = 0; p < 2; ++p) {
+    gp[p] = base_problem(sw[p]->fc1);
+    gp[p].A = ptr(xn, (size_t)parts[p].row0 * h * g.esz); gp[p].lda = h;
+    gp[p].M = g.B * parts[p].len;
+    gp[p].out = ptr(mlp, (size_t)parts[p].row0 * m * g.esz); gp[p].ldo = m;
+  }
+  if ((r = gemm(c, gp, 2, EPI_GELU))) return r;
+  // fc2, x += gate2 * (.)
+  for (int p = 0; p < 2; ++p) {
+    gp[p] = base_problem(sw[p]->fc2);
+    gp[p].A = ptr(mlp, (size_t)parts[p].row0 * m * g.esz); gp[p].lda = m;
+    gp[p].M = g.B * parts[p].len;
+    gp[p].res_in = parts[p].x_out; gp[p].res_out = parts[p].x_out; gp[p].res_f32 = res_f32;
+    gp[p].gate = parts[p].mod + 5 * h; gp[p].gate_bstride = 6 * h;
+  }
+  return gemm(c, gp, 2, EPI_GATE_RES);
+}
+
+// Single-stream block over np parts sharing the weights.
+int run_single(const Ctx& c, const mmdit_single_w& sw, const Part* parts, int np, bool res_f32,
+               const float* table, void* ws, const BlockWs& w) {
+  const Geo& g = c.g;
+  const int h = g.h, m = g.m;
+  int r;
+  void* xn = ptr(ws, w.xn);
+  void* qkv = ptr(ws, w.qkv);
+  void* cat = ptr(ws, w.o);
+  if ((r = run_ln(c, parts, np, 3 * h, 0, h, res_f32, xn))) return r;
+  GemmProblem gp[2];
+  for (int p = 0; p < np; ++p) {
+    gp[p] = base_problem(sw.lin1);
+    gp[p].A = ptr(xn, (size_t)parts[p].row0 * h * g.esz); gp[p].lda = h;
+    gp[p].M = g.B * parts[p].len;
+    gp[p].out = ptr(qkv, (size_t)parts[p].row0 * 3 * h * g.esz); gp[p].ldo = 3 * h;
+    gp[p].split_n = 3 * h;
+    gp[p].out2 = ptr(cat, ((size_t)parts[p].row0 * (h + m) + h) * g.esz); gp[p].ldo2 = h + m;
+  }
+  if ((r = gemm(c, gp, np, EPI_SPLIT))) return r;
+  const void* qn[2] = {sw.q_norm, sw.q_norm};
+  const void* kn[2] = {sw.k_norm, sw.k_norm};
+  if ((r = run_qk_attn(c, parts, np, qkv, qn, kn, table, w, ws, cat, h + m))) return r;
+  for (int p = 0; p < np; ++p) {
+    gp[p] = base_problem(sw.lin2);
+    gp[p].A = ptr(cat, (size_t)parts[p].row0 * (h + m) * g.esz); gp[p].lda = h + m;
+    gp[p].M = g.B * parts[p].len;
+    gp[p].res_in = parts[p].x_in; gp[p].res_out = parts[p].x_out; gp[p].res_f32 = res_f32;
+    gp[p].gate = parts[p].mod + 2 * h; gp[p].gate_bstride = 3 * h;
+  }
+  return gemm(c, gp, np, EPI_GATE_RES);
+}
+
+int rope(const Ctx& c, const mmdit_dims* d, const int32_t* ids, float* table) {
+  HIP_TRY(launch_rope_table(ids, c.g.L, d->axes_dim[0], d->axes_dim[1], d->axes_dim[2], d->theta, table, c.s));
+  return MMDIT_OK;
+}
+
+}  // namespace
+
+// ===================================================================== C ABI ==
+extern "C" {
+
+int mmdit_double_block_workspace(const mmdit_dims* dims, size_t* bytes) {
+  Geo g;
+  int r;
+  if (!bytes) return fail(MMDIT_ERR_NULL, "bytes is NULL");
+  if ((r = check_dims(dims, g))) return r;
+  *bytes = plan_block_call(g, 2 * 6 * g.h).blk.total;
+  return MMDIT_OK;
+}
+
+int mmdit_single_block_workspace(const mmdit_dims* dims, size_t* bytes) {
+  Geo g;
+  int r;
+  if (!bytes) return fail(MMDIT_ERR_NULL, "bytes is NULL");
+  if ((r = check_dims(dims, g))) return r;
+  *bytes = plan_block_call(g, 3 * g.h).blk.total;
+  return MMDIT_OK;
+}
+
+int mmdit_double_block_fwd(const mmdit_dims* dims, const mmdit_double_w* w, const void* img_in,
+                           const void* txt_in, void* img_out, void* txt_out, const void* vec,
+                           const int32_t* ids, void* ws, size_t ws_bytes, void* hip_stream) {
+  Geo g;
+  int r;
+  if ((r = check_dims(dims, g))) return r;
+  if (!w || !img_in || !img_out || !vec || !ids) return fail(MMDIT_ERR_NULL, "NULL weights, image, vec or ids");
+  if (g.Lt > 0 && (!txt_in || !txt_out)) return fail(MMDIT_ERR_NULL, "NULL text buffers with txt_len > 0");
+  if ((r = check_stream(w->txt, g, "txt"))) return r;
+  if ((r = check_stream(w->img, g, "img"))) return r;
+  const BlockCallWs lay = plan_block_call(g, 2 * 6 * g.h);
+  if (!ws || ws_bytes < lay.blk.total)
+    return fail(MMDIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, lay.blk.total);
+  Ctx c{(hipStream_t)hip_stream, g, dims->ln_eps, dims->rms_eps};
+  float* table = (float*)ptr(ws, lay.table);
+  float* mod = (float*)ptr(ws, lay.mod);
+  float* mod_txt = mod;
+  float* mod_img = mod + (size_t)g.B * 6 * g.h;
+  if ((r = rope(c, dims, ids, table))) return r;
+  if ((r = gemv(c, w->txt.mod, vec, false, g.h, mod_txt, 6 * g.h, true, false))) return r;
+  if ((r = gemv(c, w->img.mod, vec, false, g.h, mod_img, 6 * g.h, true, false))) return r;
+  Part parts[2];
+  void* tin = const_cast<void*>(txt_in ? txt_in : img_in);
+  void* tout = txt_out ? txt_out : img_out;
+  parts[0] = {g.Lt, 0, rows_of(tin, 0, g.Lt, g.h, g.esz), rows_of(tout, 0, g.Lt, g.h, g.esz), mod_txt};
+  parts[1] = {g.Li, (int64_t)g.B * g.Lt, rows_of(const_cast<void*>(img_in), 0, g.Li, g.h, g.esz),
+              rows_of(img_out, 0, g.Li, g.h, g.esz), mod_img};
+  const mmdit_stream_w* sw[2] = {&w->txt, &w->img};
+  return run_double(c, sw, parts, false, table, ws, lay.blk);
+}
+
+int mmdit_single_block_fwd(const mmdit_dims* dims, const mmdit_single_w* w, const void* x_in,
+                           void* x_out, const void* vec, const int32_t* ids, void* ws,
+                           size_t ws_bytes, void* hip_stream) {
+  Geo g;
+  int r;
+  if ((r = check_dims(dims, g))) return r;
+  if (!w || !x_in || !x_out || !vec || !ids) return fail(MMDIT_ERR_NULL, "NULL weights, x, vec or ids");
+  if ((r = check_single(*w, g))) return r;
+  const BlockCallWs lay = plan_block_call(g, 3 * g.h);
+  if (!ws || ws_bytes < lay.blk.total)
+    return fail(MMDIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, lay.blk.total);
+  Ctx c{(hipStream_t)hip_stream, g, dims->ln_eps, dims->rms_eps};
+  float* table = (float*)ptr(ws, lay.table);
+  float* mod = (float*)ptr(ws, lay.mod);
+  if ((r = rope(c, dims, ids, table))) return r;
+  if ((r = gemv(c, w->mod, vec, false, g.h, mod, 3 * g.h, true, false))) return r;
+  Part part = {g.L, 0, rows_of(const_cast<void*>(x_in), 0, g.L, g.h, g.esz), rows_of(x_out, 0, g.L, g.h, g.esz), mod};
+  return run_single(c, *w, &part, 1, false, table, ws, lay.blk);
+}
+
+static int check_config(const mmdit_config* cfg, Geo& g) {
+  if (!cfg) return fail(MMDIT_ERR_NULL, "config is NULL");
+  int r;
+  if ((r = check_dims(&cfg->dims, g))) return r;
+  if (cfg->n_double < 0 || cfg->n_single < 0) return fail(MMDIT_ERR_SHAPE, "negative block count");
+  if (cfg->in_ch < 64 || cfg->in_ch % 64) return fail(MMDIT_ERR_SHAPE, "in_ch %d must be a positive multiple of 64", cfg->in_ch);
+  if (cfg->txt_in_dim < 64 || cfg->txt_in_dim % 64) return fail(MMDIT_ERR_SHAPE, "txt_in_dim must be a positive multiple of 64");
+  if (cfg->vec_in_dim < 8 || cfg->vec_in_dim % 8 || cfg->vec_in_dim > 4096) return fail(MMDIT_ERR_SHAPE, "vec_in_dim must be a multiple of 8 in [8, 4096]");
+  if (cfg->temb_dim < 8 || cfg->temb_dim % 8 || cfg->temb_dim > 4096) return fail(MMDIT_ERR_SHAPE, "temb_dim must be a multiple of 8 in [8, 4096]");
+  return MMDIT_OK;
+}
+
+int mmdit_step_workspace(const mmdit_config* cfg, size_t* bytes) {
+  Geo g;
+  int r;
+  if (!bytes) return fail(MMDIT_ERR_NULL, "bytes is NULL");
+  if ((r = check_config(cfg, g))) return r;
+  *bytes = plan_step(cfg, g).blk.total;
+  return MMDIT_OK;
+}
+
+int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, void* v_out,
+               const void* txt_emb, const void* y, const int32_t* ids, double sigma,
+               double sigma_next, void* ws, size_t ws_bytes, void* hip_stream) {
+  Geo g;
+  int r;
+  if ((r = check_config(cfg, g))) return r;
+  if (!w || !x_packed || !y || !ids) return fail(MMDIT_ERR_NULL, "NULL weights, latent, y or ids");
+  if (g.Lt > 0 && !txt_emb) return fail(MMDIT_ERR_NULL, "txt_emb is NULL with txt_len > 0");
+  if ((cfg->n_double > 0 && !w->dbl) || (cfg->n_single > 0 && !w->sgl)) return fail(MMDIT_ERR_NULL, "block weight arrays are NULL");
+  if (!std::isfinite(sigma) || !std::isfinite(sigma_next)) return fail(MMDIT_ERR_SHAPE, "sigma values must be finite");
+  const int h = g.h;
+  if ((r = check_linear(w->img_in, h, cfg->in_ch, g, "img_in"))) return r;
+  if ((r = check_linear(w->txt_in, h, cfg->txt_in_dim, g, "txt_in"))) return r;
+  if ((r = check_gemv(w->time_in0, h, cfg->temb_dim, "time_in0"))) return r;
+  if ((r = check_gemv(w->time_in1, h, h, "time_in1"))) return r;
+  if ((r = check_gemv(w->vec_in0, h, cfg->vec_in_dim, "vec_in0"))) return r;
+  if ((r = check_gemv(w->vec_in1, h, h, "vec_in1"))) return r;
+  if ((r = check_gemv(w->final_mod, 2 * h, h, "final_mod"))) return r;
+  if ((r = check_linear(w->final_lin, cfg->in_ch, h, g, "final_lin"))) return r;
+  for (int i = 0; i < cfg->n_double; ++i) {
+    char nm[32];
+    snprintf(nm, sizeof nm, "dbl[%d].txt", i);
+    if ((r = check_stream(w->dbl[i].txt, g, nm))) return r;
+    snprintf(nm, sizeof nm, "dbl[%d].img", i);
+    if ((r = check_stream(w->dbl[i].img, g, nm))) return r;
+  }
+  for (int i = 0; i < cfg->n_single; ++i)
+    if ((r = check_single(w->sgl[i], g))) return fail(r, "sgl[%d]: %s", i, g_err.c_str());
+  const StepWs lay = plan_step(cfg, g);
+  if (!ws || ws_bytes < lay.blk.total)
+    return fail(MMDIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, lay.blk.total);
+
+  Ctx c{(hipStream_t)hip_stream, g, cfg->dims.ln_eps, cfg->dims.rms_eps};
+  const int B = g.B;
+  float* x = (float*)ptr(ws, lay.x);  // residual: [B*Lt text rows; B*Li image rows] f32
+  float* vec = (float*)ptr(ws, lay.vec);
+  float* temb = (float*)ptr(ws, lay.temb);
+  float* hid = (float*)ptr(ws, lay.hid);
+  float* mods = (float*)ptr(ws, lay.mods);
+  float* table = (float*)ptr(ws, lay.table);
+
+  // conditioning vector: L1(SiLU(L0(temb))) + V1(SiLU(V0(y)))
+  HIP_TRY(launch_timestep_embedding(temb, B, cfg->temb_dim, sigma, c.s));
+  if ((r = gemv(c, w->time_in0, temb, true, cfg->temb_dim, hid, h, false, false))) return r;
+  if ((r = gemv(c, w->time_in1, hid, true, h, vec, h, true, false))) return r;
+  if ((r = gemv(c, w->vec_in0, y, false, cfg->vec_in_dim, hid, h, false, false))) return r;
+  if ((r = gemv(c, w->vec_in1, hid, true, h, vec, h, true, true))) return r;
+  // every block's modulation up front
+  for (int i = 0; i < cfg->n_double; ++i) {
+    float* md = mods + lay.mod_dual + (size_t)i * 2 * B * 6 * h;
+    if ((r = gemv(c, w->dbl[i].txt.mod, vec, true, h, md, 6 * h, true, false))) return r;
+    if ((r = gemv(c, w->dbl[i].img.mod, vec, true, h, md + (size_t)B * 6 * h, 6 * h, true, false))) return r;
+  }
+  for (int i = 0; i < cfg->n_single; ++i) {
+    float* ms = mods + lay.mod_single + (size_t)i * B * 3 * h;
+    if ((r = gemv(c, w->sgl[i].mod, vec, true, h, ms, 3 * h, true, false))) return r;
+  }
+  float* mf = mods + lay.mod_final;
+  if ((r = gemv(c, w->final_mod, vec, true, h, mf, 2 * h, true, false))) return r;
+  if ((r = rope(c, &cfg->dims, ids, table))) return r;
+
+  // input projections into the f32 residual
+  const void* xa = x_packed;
+  if (g.bf16) {
+    HIP_TRY(launch_convert(x_packed, true, ptr(ws, lay.xin), false, (int64_t)B * g.Li * cfg->in_ch, c.s));
+    xa = ptr(ws, lay.xin);
+  }
+  GemmProblem gp[2];
+  int np = 0;
+  gp[np] = base_problem(w->img_in);
+  gp[np].A = xa; gp[np].lda = cfg->in_ch; gp[np].M = B * g.Li;
+  gp[np].out = x + (size_t)B * g.Lt * h; gp[np].ldo = h; gp[np].out_f32 = true;
+  ++np;
+  if (g.Lt > 0) {
+    gp[np] = base_problem(w->txt_in);
+    gp[np].A = txt_emb; gp[np].lda = cfg->txt_in_dim; gp[np].M = B * g.Lt;
+    gp[np].out = x; gp[np].ldo = h; gp[np].out_f32 = true;
+    ++np;
+  }
+  // the two projections have different K: one launch each
+  for (int i = 0; i < np; ++i)
+    if ((r = gemm(c, &gp[i], 1, EPI_STORE))) return r;
+
+  Part parts[2];
+  parts[0] = {g.Lt, 0, rows_of(x, 0, g.Lt, h, 4), rows_of(x, 0, g.Lt, h, 4), nullptr};
+  parts[1] = {g.Li, (int64_t)B * g.Lt, rows_of(x, (int64_t)B * g.Lt, g.Li, h, 4),
+              rows_of(x, (int64_t)B * g.Lt, g.Li, h, 4), nullptr};
+  for (int i = 0; i < cfg->n_double; ++i) {
+    float* md = mods + lay.mod_dual + (size_t)i * 2 * B * 6 * h;
+    parts[0].mod = md;
+    parts[1].mod = md + (size_t)B * 6 * h;
+    const mmdit_stream_w* sw[2] = {&w->dbl[i].txt, &w->dbl[i].img};
+    if ((r = run_double(c, sw, parts, true, table, ws, lay.blk))) return r;
+  }
+  for (int i = 0; i < cfg->n_single; ++i) {
+    float* ms = mods + lay.mod_single + (size_t)i * B * 3 * h;
+    parts[0].mod = ms;
+    parts[1].mod = ms;
+    if (g.Lt > 0) {
+      if ((r = run_single(c, w->sgl[i], parts, 2, true, table, ws, lay.blk))) return r;
+    } else {
+      if ((r = run_single(c, w->sgl[i], &parts[1], 1, true, table, ws, lay.blk))) return r;
+    }
+  }
+  // final layer on the image rows, Euler update fused into the epilogue
+  Part fin = parts[1];
+  fin.mod = mf;
+  void* xn = ptr(ws, lay.blk.xn);
+  if ((r = run_ln(c, &fin, 1, 2 * h, 0, h, true, xn))) return r;
+  GemmProblem f = base_problem(w->final_lin);
+  f.A = xn; f.lda = h; f.M = B * g.Li;
+  f.res_out = rows_of(x_packed, 0, g.Li, cfg->in_ch, 4);
+  f.res_in = f.res_out;
+  f.dsigma = (float)(sigma_next - sigma);
+  f.v_out = (float*)v_out;
+  return gemm(c, &f, 1, EPI_EULER);
+}
+
+int mmdit_pack_latents(const void* z, void* x, int32_t B, int32_t C, int32_t H, int32_t W,
+                       int32_t elem_bytes, void* hip_stream) {
+  if (!z || !x) return fail(MMDIT_ERR_NULL, "NULL buffer");
+  if (B < 1 || C < 1 || H < 2 || W < 2 || H % 2 || W % 2) return fail(MMDIT_ERR_SHAPE, "need B, C >= 1 and even H, W >= 2");
+  if (elem_bytes != 2 && elem_bytes != 4) return fail(MMDIT_ERR_DTYPE, "elem_bytes must be 2 or 4");
+  HIP_TRY(launch_pack(z, x, B, C, H, W, elem_bytes, false, (hipStream_t)hip_stream));
+  return MMDIT_OK;
+}
+
+int mmdit_unpack_latents(const void* x, void* z, int32_t B, int32_t C, int32_t H, int32_t W,
+                         int32_t elem_bytes, void* hip_stream) {
+  if (!z || !x) return fail(MMDIT_ERR_NULL, "NULL buffer");
+  if (B < 1 || C < 1 || H < 2 || W < 2 || H % 2 || W % 2) return fail(MMDIT_ERR_SHAPE, "need B, C >= 1 and even H, W >= 2");
+  if (elem_bytes != 2 && elem_bytes != 4) return fail(MMDIT_ERR_DTYPE, "elem_bytes must be 2 or 4");
+  HIP_TRY(launch_pack(x, z, B, C, H, W, elem_bytes, true, (hipStream_t)hip_stream));
+  return MMDIT_OK;
+}
+
+int mmdit_rope_table(const int32_t* ids, int32_t L, const int32_t* axes_dim, double theta,
+                     float* table, void* hip_stream) {
+  if (!ids || !axes_dim || !table) return fail(MMDIT_ERR_NULL, "NULL buffer");
+  if (L < 0) return fail(MMDIT_ERR_SHAPE, "L < 0");
+  for (int a = 0; a < 3; ++a)
+    if (axes_dim[a] < 0 || axes_dim[a] % 2) return fail(MMDIT_ERR_SHAPE, "axes must be even");
+  if (!(theta > 0)) return fail(MMDIT_ERR_SHAPE, "theta must be > 0");
+  HIP_TRY(launch_rope_table(ids, L, axes_dim[0], axes_dim[1], axes_dim[2], theta, table, (hipStream_t)hip_stream));
+  return MMDIT_OK;
+}
+
+int mmdit_profile_begin(int32_t kernel_class, int32_t max_launches) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (kernel_class < PC_GEMM || kernel_class > PC_GEMV) return fail(MMDIT_ERR_SHAPE, "unknown kernel class %d", kernel_class);
+  if (max_launches < 1 || max_launches > 1 << 20) return fail(MMDIT_ERR_SHAPE, "max_launches out of range");
+  if (g_prof.active) return fail(MMDIT_ERR_UNSUPPORTED, "profiling already active");
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
+  for (auto& e : g_prof.ev) HIP_TRY(hipEventCreate(&e));
+  g_prof.cls = kernel_class;
+  g_prof.cap = max_launches;
+  g_prof.used = 0;
+  g_prof.work = 0;
+  g_prof.active = true;
+  return MMDIT_OK;
+}
+
+int mmdit_profile_end(double* total_ms, int32_t* launches, double* work) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (!g_prof.active) return fail(MMDIT_ERR_UNSUPPORTED, "profiling not active");
+  g_prof.active = false;
+  double tot = 0;
+  for (int i = 0; i < g_prof.used; ++i) {
+    HIP_TRY(hipEventSynchronize(g_prof.ev[2 * i + 1]));
+    float ms = 0;
+    HIP_TRY(hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]));
+    tot += ms;
+  }
+  if (total_ms) *total_ms = tot;
+  if (launches) *launches = g_prof.used;
+  if (work) *work = g_prof.work;
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+  return MMDIT_OK;
+}
+
+const char* mmdit_status_str(int32_t status) {
+  switch (status) {
+    case MMDIT_OK: return "ok";
+    case MMDIT_ERR_NULL: return "null pointer";
+    case MMDIT_ERR_SHAPE: return "invalid shape";
+    case MMDIT_ERR_DTYPE: return "invalid dtype or weight format";
+    case MMDIT_ERR_WORKSPACE: return "workspace too small";
+    case MMDIT_ERR_UNSUPPORTED: return "unsupported";
+    case MMDIT_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* mmdit_last_error(void) { return g_err.c_str(); }
+
+const char* mmdit_version(void) { return "mmdit 0.1 gfx950"; }
+
+}  // extern "C"

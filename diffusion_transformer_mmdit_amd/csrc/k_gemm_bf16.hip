@@ -1,0 +1,250 @@
+// bf16 GEMM C = A W^T on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16),
+// float32 accumulation, fused epilogues. Used for every projection of the
+// block: QKV / linear1, attention out-projection, MLP fc1 / fc2, linear2,
+// the input projections and the final layer.
+//
+// Weights may be dense bf16 or group-quantised (4-bit or 8-bit codes, one
+// bf16 scale per 64 consecutive k). Quantised weights are dequantised one
+// K-tile at a time while being staged into LDS, so the MFMA loop is the same
+// for every format (stable-diffusion.rs README: weights held as packed bits
+// and dequantised inside the matmul a tile at a time).
+//
+// Structure: BM x BN block tile, K-tile 64, 4 wavefronts in a WM x WN grid,
+// LDS double buffer with one barrier per K-tile; global loads for tile k+1
+// are issued before the MFMAs of tile k. LDS rows are padded to 72 elements
+// (144 bytes) so the 16-byte fragment reads of 8 consecutive rows hit
+// distinct banks.
+#include "gemm_common.h"
+
+namespace mmdit {
+
+constexpr int kBK = 64;
+constexpr int kLDK = kBK + 8;
+
+// Dequantise 16 int8 codes (one 16-byte load) times scale into two bf16x8.
+__device__ __forceinline__ void deq8(const u32x4& w, float s, bf16x8& lo, bf16x8& hi) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = w[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float f = (float)(int8_t)(x >> (8 * j)) * s;
+      if (i < 2) lo[i * 4 + j] = (bf16)f;
+      else hi[(i - 2) * 4 + j] = (bf16)f;
+    }
+  }
+}
+
+// Dequantise 32 int4 codes (one 16-byte load; even k in the low nibble).
+__device__ __forceinline__ void deq4(const u32x4& w, float s, bf16x8 out[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = w[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = ((int)(x << (28 - 4 * j))) >> 28;
+      out[i][j] = (bf16)((float)q * s);
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int FMT>
+__global__ __launch_bounds__(256) void k_gemm_bf16(GemmBatch gb) {
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int A_CH = BM * 8 / 256;                                  // 16-byte A chunks per thread
+  constexpr int B_CH = FMT == 0 ? BN * 8 / 256 : (FMT == 2 ? BN * 4 / 256 : BN * 2 / 256);
+  static_assert(WM * WN == 4, "4 wavefronts");
+  static_assert(B_CH >= 1, "tile too small for this weight format");
+  __shared__ bf16 As[2][BM * kLDK];
+  __shared__ bf16 Bs[2][BN * kLDK];
+
+  int prob, tm, tn;
+  tile_of(gb, prob, tm, tn);
+  const GemmProblem& P = gb.p[prob];
+  const int M = P.M, N = P.N, K = P.K;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm0 = (wave / WN) * TM, wn0 = (wave % WN) * TN;
+  const bf16* A = reinterpret_cast<const bf16*>(P.A);
+
+  bf16x8 ra[A_CH];
+  u32x4 rb[B_CH];
+  float rs[B_CH];
+
+  auto load_tile = [&](int kt) {
+    const int k0 = kt * kBK;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + i * 256;
+      const int row = c >> 3, kc = c & 7;
+      const int gm = m0 + row;
+      ra[i] = gm < M ? *reinterpret_cast<const bf16x8*>(A + (int64_t)gm * P.lda + k0 + kc * 8) : (bf16x8){};
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = tid + i * 256;
+      if constexpr (FMT == 0) {
+        const int row = c >> 3, kc = c & 7;
+        const int gn = n0 + row;
+        rb[i] = gn < N ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16*>(P.W) + (int64_t)gn * K + k0 + kc * 8)
+                       : (u32x4){0, 0, 0, 0};
+      } else if constexpr (FMT == 2) {
+        const int row = c >> 2, part = c & 3;
+        const int gn = n0 + row;
+        if (gn < N) {
+          rb[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const int8_t*>(P.W) + (int64_t)gn * K + k0 + part * 16);
+          rs[i] = (float)reinterpret_cast<const bf16*>(P.scales)[(int64_t)gn * (K / 64) + kt];
+        } else {
+          rb[i] = (u32x4){0, 0, 0, 0};
+          rs[i] = 0.f;
+        }
+      } else {
+        const int row = c >> 1, part = c & 1;
+        const int gn = n0 + row;
+        if (gn < N) {
+          rb[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(P.W) + (int64_t)gn * (K / 2) + k0 / 2 + part * 16);
+          rs[i] = (float)reinterpret_cast<const bf16*>(P.scales)[(int64_t)gn * (K / 64) + kt];
+        } else {
+          rb[i] = (u32x4){0, 0, 0, 0};
+          rs[i] = 0.f;
+        }
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + i * 256;
+      *reinterpret_cast<bf16x8*>(&As[buf][(c >> 3) * kLDK + (c & 7) * 8]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = tid + i * 256;
+      if constexpr (FMT == 0) {
+        *reinterpret_cast<u32x4*>(&Bs[buf][(c >> 3) * kLDK + (c & 7) * 8]) = rb[i];
+      } else if constexpr (FMT == 2) {
+        bf16x8 lo, hi;
+        deq8(rb[i], rs[i], lo, hi);
+        bf16* d = &Bs[buf][(c >> 2) * kLDK + (c & 3) * 16];
+        *reinterpret_cast<bf16x8*>(d) = lo;
+        *reinterpret_cast<bf16x8*>(d + 8) = hi;
+      } else {
+        bf16x8 o[4];
+        deq4(rb[i], rs[i], o);
+        bf16* d = &Bs[buf][(c >> 1) * kLDK + (c & 1) * 32];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(d + 8 * j) = o[j];
+      }
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16){};
+
+  const int nk = K / kBK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_tile(kt + 1);
+    const bf16* as = As[cur];
+    const bf16* bs = Bs[cur];
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      bf16x8 af[FM], bfr[FN];
+      const int koff = kk * 16 + (lane >> 5) * 8;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(&as[(wm0 + i * 32 + (lane & 31)) * kLDK + koff]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&bs[(wn0 + j * 32 + (lane & 31)) * kLDK + koff]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // acc[i][j][r] holds C[m0 + wm0 + 32i + 8(r/4) + 4(lane/32) + r%4][n0 + wn0 + 32j + lane%32]
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn0 + j * 32 + (lane & 31);
+      if (n >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m < M) gemm_epilogue<EPI, bf16, false>(P, m, n, acc[i][j][r]);
+      }
+    }
+}
+
+// ------------------------------------------------------------------ launch --
+template <int BM, int BN, int WM, int WN, int EPI, int FMT>
+static hipError_t launch_cfg(const GemmProblem* p, int nprob, hipStream_t s) {
+  GemmBatch gb{};
+  int total = 0;
+  gb.tile_start[0] = 0;
+  for (int i = 0; i < 2; ++i) {
+    if (i < nprob) {
+      gb.p[i] = p[i];
+      gb.tiles_m[i] = (p[i].M + BM - 1) / BM;
+      gb.tiles_n[i] = (p[i].N + BN - 1) / BN;
+      total += gb.tiles_m[i] * gb.tiles_n[i];
+    } else {
+      gb.tiles_m[i] = 1;
+      gb.tiles_n[i] = 1;
+    }
+    gb.tile_start[i + 1] = total;
+  }
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI, FMT>), dim3(total), dim3(256), 0, s, gb);
+  return hipGetLastError();
+}
+
+template <int EPI, int FMT>
+static hipError_t launch_epi_fmt(const GemmProblem* p, int nprob, hipStream_t s) {
+  int64_t tiles256 = 0;
+  int maxN = 0;
+  for (int i = 0; i < nprob; ++i) {
+    tiles256 += (int64_t)((p[i].M + 255) / 256) * ((p[i].N + 255) / 256);
+    if (p[i].N > maxN) maxN = p[i].N;
+  }
+  if constexpr (FMT == 0) {
+    if (maxN <= 64) return launch_cfg<64, 64, 2, 2, EPI, FMT>(p, nprob, s);
+  }
+  if (tiles256 >= 256) return launch_cfg<256, 256, 2, 2, EPI, FMT>(p, nprob, s);
+  return launch_cfg<128, 128, 2, 2, EPI, FMT>(p, nprob, s);
+}
+
+template <int EPI>
+static hipError_t launch_epi(const GemmProblem* p, int nprob, hipStream_t s) {
+  switch (p[0].fmt) {
+    case 0: return launch_epi_fmt<EPI, 0>(p, nprob, s);
+    case 1: return launch_epi_fmt<EPI, 1>(p, nprob, s);
+    default: return launch_epi_fmt<EPI, 2>(p, nprob, s);
+  }
+}
+
+hipError_t launch_gemm_bf16(const GemmProblem* p, int nprob, int epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: return launch_epi<EPI_STORE>(p, nprob, s);
+    case EPI_GELU: return launch_epi<EPI_GELU>(p, nprob, s);
+    case EPI_GATE_RES: return launch_epi<EPI_GATE_RES>(p, nprob, s);
+    case EPI_SPLIT: return launch_epi<EPI_SPLIT>(p, nprob, s);
+    default: return launch_epi_fmt<EPI_EULER, 0>(p, nprob, s);
+  }
+}
+
+}  // namespace mmdit

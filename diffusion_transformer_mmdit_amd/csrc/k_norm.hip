@@ -1,0 +1,405 @@
+// Memory-bound kernels of the MMDiT block: adaLN modulated LayerNorm, fused
+// QK RMSNorm + 3D RoPE (writing the attention layout), the RoPE table, the
+// modulation / conditioning GEMV, the timestep embedding, latent packing.
+//
+// mflux-rs, "FLUX.1 MMDiT Architecture": dual-stream and single-stream
+// blocks; card "3D RoPE Coordinates": rotary axes [16, 56, 56] over the head
+// dimension 128. stable-diffusion.rs README: the fused layer_norm and
+// rms_norm kernels it relies on.
+#include "common.h"
+#include "kernels.h"
+
+namespace mmdit {
+
+__device__ __forceinline__ const char* seg_row(const RowSeg& s, int local, int esize) {
+  int b = local / s.rows_per_batch;
+  int t = local - b * s.rows_per_batch;
+  return reinterpret_cast<const char*>(s.base) +
+         ((int64_t)b * s.batch_stride + (int64_t)t * s.ld) * esize;
+}
+
+// ------------------------------------------------------------------ adaLN-LN --
+// One wavefront per row; each lane holds h/64 values in 4-wide chunks.
+constexpr int kLnMaxChunks = 16;  // h <= 4096
+
+template <typename TX, typename TY>
+__global__ __launch_bounds__(256) void k_adaln_ln(LnArgs a, int rows) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int s = r < a.seg_rows[0] ? 0 : 1;
+  const int local = s == 0 ? r : r - a.seg_rows[0];
+  const TX* x = reinterpret_cast<const TX*>(seg_row(a.seg[s], local, sizeof(TX)));
+  const int b = local / a.seg[s].rows_per_batch;
+  const float* mod = a.mod[s] + (int64_t)b * a.mod_bstride;
+  const float* shift = mod + a.shift_off;
+  const float* scale = mod + a.scale_off;
+  const int nc = a.h >> 8;  // chunks of 4 per lane
+  float v[kLnMaxChunks][4];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kLnMaxChunks; ++i) {
+    if (i < nc) {
+      load4(x + (i * 64 + lane) * 4, v[i]);
+      sum += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+    }
+  }
+  const float inv_h = 1.0f / (float)a.h;
+  const float mean = wave_sum(sum) * inv_h;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < kLnMaxChunks; ++i) {
+    if (i < nc) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float d = v[i][j] - mean;
+        sq += d * d;
+      }
+    }
+  }
+  const float var = wave_sum(sq) * inv_h;
+  const float rstd = 1.0f / sqrtf(var + a.eps);
+  TY* y = reinterpret_cast<TY*>(a.y) + (int64_t)r * a.h;
+#pragma unroll
+  for (int i = 0; i < kLnMaxChunks; ++i) {
+    if (i < nc) {
+      const int c = (i * 64 + lane) * 4;
+      float sh[4], sc[4], o[4];
+      load4(shift + c, sh);
+      load4(scale + c, sc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = (1.0f + sc[j]) * ((v[i][j] - mean) * rstd) + sh[j];
+      store4(y + c, o);
+    }
+  }
+}
+
+hipError_t launch_adaln_ln(const LnArgs& a, int rows, bool x_f32, bool y_bf16, hipStream_t s) {
+  dim3 grid((rows + 3) / 4), block(256);
+  if (x_f32 && y_bf16)
+    hipLaunchKernelGGL((k_adaln_ln<float, bf16>), grid, block, 0, s, a, rows);
+  else if (x_f32)
+    hipLaunchKernelGGL((k_adaln_ln<float, float>), grid, block, 0, s, a, rows);
+  else if (y_bf16)
+    hipLaunchKernelGGL((k_adaln_ln<bf16, bf16>), grid, block, 0, s, a, rows);
+  else
+    hipLaunchKernelGGL((k_adaln_ln<bf16, float>), grid, block, 0, s, a, rows);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------- QK RMSNorm + RoPE --
+// Block (64-token tile, head, batch), 256 threads. q and k: 16 lanes per
+// token, 8 dims per lane; RMS over the 128 dims of the head, times the
+// per-stream scale g, then rotation of the adjacent pairs (2j, 2j+1) by the
+// table's angle. V is copied, transposed to [d, token] for the MFMA path.
+constexpr int kQkTile = 64;
+constexpr int kVPad = 130;  // LDS row stride (elements) of the V transpose tile
+
+template <typename T>
+__device__ __forceinline__ void qk_rows(const QkNormArgs& a, int b, int hh, int t0, int col_off,
+                                        int which, T* dst) {
+  const int tid = threadIdx.x;
+  const int part = tid & 15;
+  const int d0 = part * 8;
+  for (int p = 0; p < kQkTile / 16; ++p) {
+    const int t = t0 + p * 16 + (tid >> 4);
+    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const bool valid = t < a.L;
+    if (valid) {
+      const int s = t < a.seg_len0 ? 0 : 1;
+      const int local = (s == 0 ? t : t - a.seg_len0) + b * (s == 0 ? a.seg_len0 : a.L - a.seg_len0);
+      const T* src = reinterpret_cast<const T*>(seg_row(a.seg[s], local, sizeof(T)));
+      load8(src + col_off + hh * 128 + d0, x);
+      load8(reinterpret_cast<const T*>(which == 0 ? a.qn[s] : a.kn[s]) + d0, g);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+    ss = group_sum<16>(ss);
+    const float rstd = 1.0f / sqrtf(ss * (1.0f / 128.0f) + a.eps);
+    float y[8];
+    if (valid) {
+      const float* tb = a.table + ((int64_t)t * 64 + (d0 >> 1)) * 2;
+      f32x4 cs0 = *reinterpret_cast<const f32x4*>(tb);
+      f32x4 cs1 = *reinterpret_cast<const f32x4*>(tb + 4);
+      float cs[8] = {cs0[0], cs0[1], cs0[2], cs0[3], cs1[0], cs1[1], cs1[2], cs1[3]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float y0 = x[2 * j] * rstd * g[2 * j];
+        const float y1 = x[2 * j + 1] * rstd * g[2 * j + 1];
+        const float c = cs[2 * j], sn = cs[2 * j + 1];
+        y[2 * j] = c * y0 - sn * y1;
+        y[2 * j + 1] = sn * y0 + c * y1;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = 0.f;
+    }
+    if (t < a.Lpad) store8(dst + (int64_t)t * 128 + d0, y);
+  }
+}
+
+template <typename T, bool VT>
+__global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
+  const int t0 = blockIdx.x * kQkTile;
+  const int hh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int h = a.H * 128;
+  const int64_t head_off = ((int64_t)b * a.H + hh) * (int64_t)a.Lpad * 128;
+  qk_rows<T>(a, b, hh, t0, 0, 0, reinterpret_cast<T*>(a.Q) + head_off);
+  qk_rows<T>(a, b, hh, t0, h, 1, reinterpret_cast<T*>(a.K) + head_off);
+
+  const int tid = threadIdx.x;
+  const int part = tid & 15;
+  const int d0 = part * 8;
+  if constexpr (!VT) {
+    T* V = reinterpret_cast<T*>(a.V) + head_off;
+    for (int p = 0; p < kQkTile / 16; ++p) {
+      const int t = t0 + p * 16 + (tid >> 4);
+      float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (t < a.L) {
+        const int s = t < a.seg_len0 ? 0 : 1;
+        const int local = (s == 0 ? t : t - a.seg_len0) + b * (s == 0 ? a.seg_len0 : a.L - a.seg_len0);
+        load8(reinterpret_cast<const T*>(seg_row(a.seg[s], local, sizeof(T))) + 2 * h + hh * 128 + d0, x);
+      }
+      if (t < a.Lpad) store8(V + (int64_t)t * 128 + d0, x);
+    }
+  } else {
+    __shared__ bf16 vs[kQkTile * kVPad];
+    for (int p = 0; p < kQkTile / 16; ++p) {
+      const int tl = p * 16 + (tid >> 4);
+      const int t = t0 + tl;
+      bf16x8 v = {};
+      if (t < a.L) {
+        const int s = t < a.seg_len0 ? 0 : 1;
+        const int local = (s == 0 ? t : t - a.seg_len0) + b * (s == 0 ? a.seg_len0 : a.L - a.seg_len0);
+        v = *reinterpret_cast<const bf16x8*>(
+            reinterpret_cast<const bf16*>(seg_row(a.seg[s], local, 2)) + 2 * h + hh * 128 + d0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vs[tl * kVPad + d0 + i] = v[i];
+    }
+    __syncthreads();
+    // Vt[b, hh, d, t0 .. t0+63]: 128 rows of 64 tokens, 8 tokens per thread
+    bf16* Vt = reinterpret_cast<bf16*>(a.V) + head_off;
+    for (int c = tid; c < 128 * (kQkTile / 8); c += 256) {
+      const int d = c >> 3;
+      const int tc = (c & 7) * 8;
+      if (t0 + tc < a.Lpad) {
+        bf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = vs[(tc + i) * kVPad + d];
+        *reinterpret_cast<bf16x8*>(Vt + (int64_t)d * a.Lpad + t0 + tc) = o;
+      }
+    }
+  }
+}
+
+hipError_t launch_qk_norm_rope(const QkNormArgs& a, bool bf16_act, bool v_trans, hipStream_t s) {
+  dim3 grid((a.Lpad + kQkTile - 1) / kQkTile, a.H, a.B), block(256);
+  if (bf16_act && v_trans)
+    hipLaunchKernelGGL((k_qk_norm_rope<bf16, true>), grid, block, 0, s, a);
+  else if (bf16_act)
+    hipLaunchKernelGGL((k_qk_norm_rope<bf16, false>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((k_qk_norm_rope<float, false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- RoPE table --
+// table[t, p] = (cos, sin)(ids[t, axis] * theta^(-2j / d_axis)) in float64,
+// pairs p ordered axis 0, axis 1, axis 2.
+__global__ void k_rope_table(const int32_t* ids, int L, int a0, int a1, int a2, double theta,
+                             float* table) {
+  const int np = (a0 + a1 + a2) / 2;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)L * np) return;
+  const int t = (int)(i / np);
+  const int p = (int)(i - (int64_t)t * np);
+  int axis, j, da;
+  if (p < a0 / 2) { axis = 0; j = p; da = a0; }
+  else if (p < (a0 + a1) / 2) { axis = 1; j = p - a0 / 2; da = a1; }
+  else { axis = 2; j = p - (a0 + a1) / 2; da = a2; }
+  const double omega = pow(theta, -2.0 * (double)j / (double)da);
+  const double ang = (double)ids[t * 3 + axis] * omega;
+  table[i * 2] = (float)cos(ang);
+  table[i * 2 + 1] = (float)sin(ang);
+}
+
+hipError_t launch_rope_table(const int32_t* ids, int L, int a0, int a1, int a2, double theta,
+                             float* table, hipStream_t s) {
+  const int64_t n = (int64_t)L * ((a0 + a1 + a2) / 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ids, L, a0,
+                     a1, a2, theta, table);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------- GEMV --
+// y[b, n] (+)= bias[n] + sum_k W[n, k] f(x[b, k]). The input vector(s) are
+// staged in LDS as float32 (after SiLU); each wavefront reduces two weight
+// rows at a time with 16-byte loads along K. Up to 4 batch rows per launch.
+constexpr int kGemvRowsPerWave = 2;
+constexpr int kGemvMaxB = 4;
+
+template <typename TW, typename TX>
+__global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
+  extern __shared__ float xs[];  // [B, K]
+  const int K = a.K;
+  for (int i = threadIdx.x; i < a.B * K; i += 256) {
+    const int bb = i / K, k = i - bb * K;
+    float v = to_f32(reinterpret_cast<const TX*>(a.x)[(int64_t)bb * a.x_bstride + k]);
+    xs[i] = a.silu_in ? silu_f<true>(v) : v;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n0 = (blockIdx.x * 4 + wave) * kGemvRowsPerWave;
+  constexpr int VEC = 16 / sizeof(TW);
+  const int nchunk = K / VEC;
+  const TW* W = reinterpret_cast<const TW*>(a.W);
+  float acc[kGemvRowsPerWave][kGemvMaxB];
+#pragma unroll
+  for (int r = 0; r < kGemvRowsPerWave; ++r)
+#pragma unroll
+    for (int bb = 0; bb < kGemvMaxB; ++bb) acc[r][bb] = 0.f;
+  for (int c = lane; c < nchunk; c += 64) {
+    float w[kGemvRowsPerWave][VEC];
+#pragma unroll
+    for (int r = 0; r < kGemvRowsPerWave; ++r) {
+      const int n = n0 + r;
+      if (n < a.N) {
+        if constexpr (VEC == 8) load8(W + (int64_t)n * K + c * VEC, w[r]);
+        else load4(W + (int64_t)n * K + c * VEC, w[r]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) w[r][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int bb = 0; bb < kGemvMaxB; ++bb) {
+      if (bb < a.B) {
+        const float* xv = xs + bb * K + c * VEC;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float xi = xv[i];
+#pragma unroll
+          for (int r = 0; r < kGemvRowsPerWave; ++r) acc[r][bb] += w[r][i] * xi;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kGemvRowsPerWave; ++r) {
+#pragma unroll
+    for (int bb = 0; bb < kGemvMaxB; ++bb) {
+      const float v = wave_sum(acc[r][bb]);
+      const int n = n0 + r;
+      if (lane == 0 && bb < a.B && n < a.N) {
+        float o = v + (a.bias ? to_f32(reinterpret_cast<const TW*>(a.bias)[n]) : 0.f);
+        float* dst = a.y + (int64_t)bb * a.y_bstride + n;
+        *dst = a.accumulate ? *dst + o : o;
+      }
+    }
+  }
+}
+
+hipError_t launch_gemv(const GemvArgs& a0, bool w_bf16, bool x_f32, hipStream_t s) {
+  for (int b0 = 0; b0 < a0.B; b0 += kGemvMaxB) {
+    GemvArgs a = a0;
+    a.B = a0.B - b0 < kGemvMaxB ? a0.B - b0 : kGemvMaxB;
+    a.x = reinterpret_cast<const char*>(a0.x) + (int64_t)b0 * a0.x_bstride * (x_f32 ? 4 : (w_bf16 ? 2 : 4));
+    a.y = a0.y + (int64_t)b0 * a0.y_bstride;
+    const int rows_per_block = 4 * kGemvRowsPerWave;
+    dim3 grid((a.N + rows_per_block - 1) / rows_per_block), block(256);
+    const size_t lds = (size_t)a.B * a.K * sizeof(float);
+    if (w_bf16 && x_f32)
+      hipLaunchKernelGGL((k_gemv<bf16, float>), grid, block, lds, s, a);
+    else if (w_bf16)
+      hipLaunchKernelGGL((k_gemv<bf16, bf16>), grid, block, lds, s, a);
+    else
+      hipLaunchKernelGGL((k_gemv<float, float>), grid, block, lds, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ------------------------------------------------------- timestep embedding --
+// tau = 1000 sigma; f_i = exp(-ln(10000) i / half); [cos(tau f) | sin(tau f)],
+// evaluated in float64.
+__global__ void k_temb(float* out, int B, int dim, double sigma) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * dim) return;
+  const int half = dim / 2;
+  const int j = i % dim;
+  const int k = j < half ? j : j - half;
+  const double f = exp(-log(10000.0) * (double)k / (double)half);
+  const double ang = 1000.0 * sigma * f;
+  out[i] = (float)(j < half ? cos(ang) : sin(ang));
+}
+
+hipError_t launch_timestep_embedding(float* out, int B, int dim, double sigma, hipStream_t s) {
+  hipLaunchKernelGGL(k_temb, dim3((B * dim + 255) / 256), dim3(256), 0, s, out, B, dim, sigma);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ packing --
+// x[b, hp*Wp + wp, c*4 + ph*2 + pw] = z[b, c, 2hp + ph, 2wp + pw], raw bits.
+template <typename U>
+__global__ void k_pack(const U* src, U* dst, int B, int C, int H, int W, bool unpack) {
+  const int64_t n = (int64_t)B * C * H * W;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  // i enumerates the packed layout [B, Hp*Wp, 4C]
+  const int Hp = H / 2, Wp = W / 2, C4 = 4 * C;
+  const int64_t per_b = (int64_t)Hp * Wp * C4;
+  const int b = (int)(i / per_b);
+  const int64_t rem = i - b * per_b;
+  const int tok = (int)(rem / C4);
+  const int ch = (int)(rem - (int64_t)tok * C4);
+  const int hp = tok / Wp, wp = tok - (tok / Wp) * Wp;
+  const int c = ch >> 2, ph = (ch >> 1) & 1, pw = ch & 1;
+  const int64_t zi = (((int64_t)b * C + c) * H + (2 * hp + ph)) * W + (2 * wp + pw);
+  if (unpack) dst[zi] = src[i];
+  else dst[i] = src[zi];
+}
+
+hipError_t launch_pack(const void* src, void* dst, int B, int C, int H, int W, int elem_bytes,
+                       bool unpack, hipStream_t s) {
+  const int64_t n = (int64_t)B * C * H * W;
+  if (n == 0) return hipSuccess;
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(k_pack<uint16_t>, grid, block, 0, s, (const uint16_t*)src, (uint16_t*)dst,
+                       B, C, H, W, unpack);
+  else
+    hipLaunchKernelGGL(k_pack<uint32_t>, grid, block, 0, s, (const uint32_t*)src, (uint32_t*)dst,
+                       B, C, H, W, unpack);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ convert --
+template <typename TS, typename TD>
+__global__ void k_convert(const TS* src, TD* dst, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = from_f32<TD>(to_f32(src[i]));
+}
+
+hipError_t launch_convert(const void* src, bool src_f32, void* dst, bool dst_f32, int64_t n,
+                          hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (src_f32 && dst_f32)
+    hipLaunchKernelGGL((k_convert<float, float>), grid, block, 0, s, (const float*)src, (float*)dst, n);
+  else if (src_f32)
+    hipLaunchKernelGGL((k_convert<float, bf16>), grid, block, 0, s, (const float*)src, (bf16*)dst, n);
+  else if (dst_f32)
+    hipLaunchKernelGGL((k_convert<bf16, float>), grid, block, 0, s, (const bf16*)src, (float*)dst, n);
+  else
+    hipLaunchKernelGGL((k_convert<bf16, bf16>), grid, block, 0, s, (const bf16*)src, (bf16*)dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace mmdit

@@ -1,0 +1,141 @@
+// Launchers of the gfx950 kernels (host side). Each returns the hipError_t
+// of its launch. Sizes are validated by the callers in api.cpp before any
+// launch; the launchers themselves assume valid arguments.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mmdit {
+
+// A set of activation rows split in up to two segments (text rows, then
+// image rows). Row r of segment s belongs to batch r / rows_per_batch and
+// sits at base + (r / rows_per_batch) * batch_stride + (r % rows_per_batch) * ld
+// (strides in elements).
+struct RowSeg {
+  void* base;
+  int64_t batch_stride;
+  int32_t rows_per_batch;
+  int32_t ld;
+};
+
+// ---- adaLN modulated LayerNorm -------------------------------------------
+// y[r, :] = (1 + scale_b) * LN(x[r, :]) + shift_b for r in [0, rows) where the
+// first seg_rows[0] rows come from seg[0] and the rest from seg[1]; y is
+// contiguous [rows, h]. shift/scale for row r of segment s:
+// mod[s] + b * mod_bstride + shift_off / scale_off.
+struct LnArgs {
+  RowSeg seg[2];
+  int32_t seg_rows[2];
+  const float* mod[2];
+  int32_t mod_bstride;
+  int32_t shift_off, scale_off;
+  void* y;
+  int32_t h;
+  float eps;
+};
+// x_f32: residual rows are float32 (else the activation type);
+// y_bf16: output bf16 (else float32).
+hipError_t launch_adaln_ln(const LnArgs& a, int rows, bool x_f32, bool y_bf16, hipStream_t s);
+
+// ---- QK RMSNorm + RoPE + attention layout ------------------------------------
+// Token t of batch b reads q|k|v from row (b, t) of seg[0] when t < seg_len0,
+// else row (b, t - seg_len0) of seg[1] (q at col 0, k at h, v at 2h).
+// Writes Q, K [B, H, Lpad, d] and V either [B, H, d, Lpad] (v_trans, bf16
+// MFMA path) or [B, H, Lpad, d]; positions t in [L, Lpad) are zero-filled.
+struct QkNormArgs {
+  RowSeg seg[2];
+  int32_t seg_len0;  // tokens in segment 0 per batch
+  const void* qn[2];
+  const void* kn[2];
+  const float* table;  // [L, 64, 2] cos, sin
+  void* Q;
+  void* K;
+  void* V;
+  int32_t B, H, L, Lpad;
+  float eps;
+};
+hipError_t launch_qk_norm_rope(const QkNormArgs& a, bool bf16, bool v_trans, hipStream_t s);
+
+// ---- RoPE table -------------------------------------------------------------
+hipError_t launch_rope_table(const int32_t* ids, int L, int a0, int a1, int a2, double theta,
+                             float* table, hipStream_t s);
+
+// ---- GEMV: y[b, n] (+)= bias[n] + sum_k W[n, k] f(x[b, k]) --------------------
+// W dense [N, K] in w_bf16 ? bf16 : float; x [B, K] float32 or activation
+// dtype; f = SiLU when silu_in; y [B, N] float32 (accumulate adds to y).
+struct GemvArgs {
+  const void* W;
+  const void* bias;
+  const void* x;
+  float* y;
+  int32_t N, K, B;
+  int32_t x_bstride, y_bstride;
+  bool silu_in, accumulate;
+};
+hipError_t launch_gemv(const GemvArgs& a, bool w_bf16, bool x_f32, hipStream_t s);
+
+// ---- sinusoidal timestep embedding: t[b, i], tau = 1000 * sigma ---------------
+hipError_t launch_timestep_embedding(float* out, int B, int dim, double sigma, hipStream_t s);
+
+// ---- latent packing ---------------------------------------------------------
+hipError_t launch_pack(const void* src, void* dst, int B, int C, int H, int W, int elem_bytes,
+                       bool unpack, hipStream_t s);
+
+// ---- elementwise cast/copy: dst[i] = src[i] (float <-> activation type) --------
+hipError_t launch_convert(const void* src, bool src_f32, void* dst, bool dst_f32, int64_t n,
+                          hipStream_t s);
+
+// ---- GEMM: C = A W^T with a fused epilogue ---------------------------------------
+enum Epi : int {
+  EPI_STORE = 0,     // out = acc + bias                      (activation type or f32)
+  EPI_GELU = 1,      // out = GELU(acc + bias)
+  EPI_GATE_RES = 2,  // res_out = res_in + gate[b, n] * (acc + bias)
+  EPI_SPLIT = 3,     // n < split_n: out = acc + bias; else out2[n - split_n] = GELU(acc + bias)
+  EPI_EULER = 4,     // x[r, n] += dsigma * (acc + bias); v_out (if set) = acc + bias  (f32)
+};
+
+struct GemmProblem {
+  const void* A;  // [M, K] activation type, row stride lda
+  int64_t lda;
+  const void* W;  // weights per fmt
+  const void* scales;
+  const void* bias;
+  int32_t fmt;  // 0 dense, 1 q4g64, 2 q8g64
+  int32_t M, N, K;
+  // outputs
+  void* out;  // EPI_STORE/GELU/SPLIT: rows contiguous, stride ldo
+  int64_t ldo;
+  bool out_f32;
+  void* out2;  // EPI_SPLIT: GELU part
+  int64_t ldo2;
+  int32_t split_n;
+  RowSeg res_in, res_out;  // EPI_GATE_RES / EPI_EULER (res_out = x); single segment
+  bool res_f32;
+  const float* gate;  // [B, gate_bstride] at column offset already applied
+  int32_t gate_bstride;
+  float dsigma;
+  float* v_out;  // EPI_EULER, contiguous [M, N], may be null
+};
+
+// Up to two problems with the same epilogue in one launch (text and image
+// streams of a dual block). bf16 operands, MFMA.
+hipError_t launch_gemm_bf16(const GemmProblem* p, int nprob, int epi, hipStream_t s);
+// float32 operands and accumulation (VALU), dense weights only.
+hipError_t launch_gemm_f32(const GemmProblem* p, int nprob, int epi, hipStream_t s);
+
+// ---- joint attention ------------------------------------------------------------
+// O rows: token t of batch b goes to seg[0] row (b, t) if t < seg_len0 else
+// seg[1] row (b, t - seg_len0), at column offset head * d.
+struct AttnArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  RowSeg out[2];
+  int32_t seg_len0;
+  int32_t B, H, L, Lpad;
+  float scale;  // 1/sqrt(d)
+};
+hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t s);
+
+}  // namespace mmdit

@@ -1,0 +1,231 @@
+/*
+ * mmdit.h - C ABI of the MI355X (gfx950) FLUX-style MMDiT denoising step.
+ *
+ * The library computes the denoising step of a multimodal diffusion
+ * transformer: dual-stream blocks (separate text and image weights, joint
+ * attention), single-stream blocks over the concatenated [text; image]
+ * sequence, the conditioning vector and the flow-matching Euler update.
+ * Sources: mflux-rs "Native Apple Silicon FLUX.1 in Safe Rust", section
+ * "FLUX.1 MMDiT Architecture" (cards Dual-Stream MMDiT, Single-Stream Blocks,
+ * 3D RoPE Coordinates, Flow-Matching Euler) and its patch-packing calculator;
+ * the mistral.rs FLUX.1-schnell article, section on FluxStepper and its
+ * sampling parameters; the stable-diffusion.rs README on quantised weights
+ * dequantised inside the matmul.
+ *
+ * Conventions for every entry point:
+ *  - Memory. The caller owns every buffer. Pointers documented as "device"
+ *    are HIP device allocations on the current device; "host" pointers are
+ *    ordinary CPU memory. The library never allocates or frees device memory
+ *    and keeps no device state between calls. Weight structs hold borrowed
+ *    device pointers.
+ *  - Streams. Device work is enqueued on `hip_stream` (a hipStream_t passed
+ *    as void*, NULL = the null stream) and the call returns without waiting.
+ *    Faults inside kernels surface at the caller's next synchronisation.
+ *  - Errors. Every function returns an mmdit_status. Argument, shape, format
+ *    and workspace checks all run before the first launch, so on an error no
+ *    kernel has been enqueued and no output has been written.
+ *    mmdit_last_error() returns a per-thread text describing the last error.
+ *  - Layouts. Matrices are row-major. Activations are [B, tokens, width].
+ *    Joint sequences put the text tokens first, then the image tokens.
+ *  - Re-entrancy. Calls on distinct streams with distinct workspaces may run
+ *    concurrently.
+ */
+#ifndef MMDIT_H
+#define MMDIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MMDIT_OK = 0,
+  MMDIT_ERR_NULL = 1,        /* a required pointer is NULL */
+  MMDIT_ERR_SHAPE = 2,       /* sizes inconsistent or out of the supported range */
+  MMDIT_ERR_DTYPE = 3,       /* dtype / weight format not valid for this call */
+  MMDIT_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
+  MMDIT_ERR_UNSUPPORTED = 5, /* valid request this build does not implement */
+  MMDIT_ERR_HIP = 6          /* a HIP runtime call failed (detail in mmdit_last_error) */
+} mmdit_status;
+
+typedef enum { MMDIT_F32 = 0, MMDIT_BF16 = 1 } mmdit_dtype;
+
+/* Weight storage of one linear layer y = x W^T + b.
+ * DENSE: W [n_out, k_in] in the activation dtype.
+ * Q4G64: symmetric 4-bit codes in -7..7, two's complement nibbles, two per
+ *        byte with the even k in the low nibble: uint8 [n_out, k_in/2];
+ *        scales bf16 [n_out, k_in/64], one per group of 64 consecutive k.
+ * Q8G64: symmetric 8-bit codes in -127..127: int8 [n_out, k_in]; scales as Q4G64.
+ * The dequantised weight is code * scale. Quantised formats need bf16
+ * activations and k_in % 64 == 0. (stable-diffusion.rs README: weights held
+ * quantised at rest and dequantised inside the matmul a tile at a time.) */
+typedef enum { MMDIT_W_DENSE = 0, MMDIT_W_Q4G64 = 1, MMDIT_W_Q8G64 = 2 } mmdit_wfmt;
+
+typedef struct {
+  int32_t batch;       /* B >= 1 */
+  int32_t hidden;      /* h = heads * head_dim, a multiple of 256 */
+  int32_t heads;       /* H >= 1 */
+  int32_t head_dim;    /* d; must be 128 */
+  int32_t mlp_hidden;  /* m, a multiple of 64 */
+  int32_t txt_len;     /* Lt >= 0 text tokens */
+  int32_t img_len;     /* Li >= 1 image tokens */
+  int32_t axes_dim[3]; /* RoPE axes (frame, row, col), each even, summing to head_dim */
+  double theta;        /* RoPE base (10000) */
+  float ln_eps;        /* LayerNorm epsilon (1e-6) */
+  float rms_eps;       /* QK RMSNorm epsilon (1e-6) */
+  int32_t act_dtype;   /* mmdit_dtype of activations, dense weights, biases, norm scales */
+} mmdit_dims;
+
+typedef struct {
+  const void* w;       /* device; layout per mmdit_wfmt */
+  const void* scales;  /* device bf16 [n_out, k_in/64] for Q4G64/Q8G64, else NULL */
+  const void* bias;    /* device [n_out] in the activation dtype, or NULL for no bias */
+  int32_t fmt;         /* mmdit_wfmt */
+  int32_t n_out;
+  int32_t k_in;
+} mmdit_linear;
+
+/* One stream (text or image) of a dual-stream block.
+ * mod: h -> 6h, output split (shift1, scale1, gate1, shift2, scale2, gate2).
+ * qkv: h -> 3h, output columns [q | k | v], each head-major (head, dim).
+ * proj: h -> h.  fc1: h -> m (GELU-tanh).  fc2: m -> h.
+ * q_norm, k_norm: device RMSNorm scales [head_dim], shared by all heads. */
+typedef struct {
+  mmdit_linear mod, qkv, proj, fc1, fc2;
+  const void* q_norm;
+  const void* k_norm;
+} mmdit_stream_w;
+
+typedef struct {
+  mmdit_stream_w img, txt;
+} mmdit_double_w;
+
+/* Single-stream block. mod: h -> 3h split (shift, scale, gate).
+ * lin1: h -> 3h + m with columns [q | k | v | mlp].
+ * lin2: h + m -> h, input columns [attention | GELU(mlp)]. */
+typedef struct {
+  mmdit_linear mod, lin1, lin2;
+  const void* q_norm;
+  const void* k_norm;
+} mmdit_single_w;
+
+typedef struct {
+  mmdit_dims dims;
+  int32_t n_double;    /* dual-stream blocks (19 for FLUX.1) */
+  int32_t n_single;    /* single-stream blocks (38 for FLUX.1) */
+  int32_t in_ch;       /* packed latent channels (64 = 16 channels x 2x2), a multiple of 64 */
+  int32_t txt_in_dim;  /* text embedding width (4096 for T5), a multiple of 64 */
+  int32_t vec_in_dim;  /* pooled text vector width (768) */
+  int32_t temb_dim;    /* sinusoidal timestep embedding width (256), even */
+} mmdit_config;
+
+/* Whole-model weights. img_in: in_ch -> h. txt_in: txt_in_dim -> h.
+ * time_in0: temb_dim -> h, time_in1: h -> h. vec_in0: vec_in_dim -> h,
+ * vec_in1: h -> h. final_mod: h -> 2h split (shift, scale). final_lin: h -> in_ch.
+ * dbl / sgl: HOST arrays of n_double / n_single block weight structs. */
+typedef struct {
+  mmdit_linear img_in, txt_in, time_in0, time_in1, vec_in0, vec_in1, final_mod, final_lin;
+  const mmdit_double_w* dbl;
+  const mmdit_single_w* sgl;
+} mmdit_model_w;
+
+/* Workspace sizes in bytes (host-only; no device work). */
+int mmdit_double_block_workspace(const mmdit_dims* dims, size_t* bytes);
+int mmdit_single_block_workspace(const mmdit_dims* dims, size_t* bytes);
+int mmdit_step_workspace(const mmdit_config* cfg, size_t* bytes);
+
+/* Dual-stream block forward (mflux-rs, card "Dual-Stream MMDiT").
+ * img_in [B, Li, h], txt_in [B, Lt, h]: device, activation dtype.
+ * img_out, txt_out: same shapes; each may alias its input.
+ * vec [B, h]: device, activation dtype; modulation = W_mod SiLU(vec) + b.
+ * ids [Lt + Li, 3]: device int32 position ids (frame, row, col), text first,
+ *   shared by the batch; RoPE angles are ids[:, a] * theta^(-2j/axes_dim[a]).
+ * ws: device workspace of at least mmdit_double_block_workspace() bytes.
+ * The residual stream is kept in the activation dtype. */
+int mmdit_double_block_fwd(const mmdit_dims* dims, const mmdit_double_w* w,
+                           const void* img_in, const void* txt_in, void* img_out, void* txt_out,
+                           const void* vec, const int32_t* ids,
+                           void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Single-stream block forward (mflux-rs, card "Single-Stream Blocks").
+ * x_in, x_out [B, Lt + Li, h]: device, activation dtype, text rows first;
+ * x_out may alias x_in. vec, ids and ws as for the dual block. */
+int mmdit_single_block_fwd(const mmdit_dims* dims, const mmdit_single_w* w,
+                           const void* x_in, void* x_out, const void* vec, const int32_t* ids,
+                           void* ws, size_t ws_bytes, void* hip_stream);
+
+/* One denoising step (mflux-rs architecture cards and "Flow-Matching Euler").
+ * x_packed [B, Li, in_ch]: device float32 packed latent, updated in place to
+ *   x + (sigma_next - sigma) * v.
+ * v_out [B, Li, in_ch]: device float32 velocity, or NULL.
+ * txt_emb [B, Lt, txt_in_dim], y [B, vec_in_dim]: device, activation dtype.
+ * ids as for the blocks. sigma, sigma_next: the schedule pair of this step;
+ * the timestep embedding uses 1000 * sigma.
+ * Inside the step the residual stream is float32 whatever the activation dtype. */
+int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w,
+               void* x_packed, void* v_out, const void* txt_emb, const void* y,
+               const int32_t* ids, double sigma, double sigma_next,
+               void* ws, size_t ws_bytes, void* hip_stream);
+
+/* ---- helpers ---------------------------------------------------------- */
+
+/* Host. sigmas[0..n_steps] of the shifted flow-matching schedule: t_i = 1 - i/n,
+ * mu = base + (max - base) * (img_len - 256) / (4096 - 256) when shift != 0 else 0,
+ * sigma_i = e^mu / (e^mu + 1/t_i - 1), sigma_n = 0. With sigma_terminal > 0 and
+ * n_steps >= 2 the non-zero sigmas are stretched so the last equals
+ * sigma_terminal. (mistral.rs article, FluxStepper shift 0.5 / 1.15; mflux-rs
+ * card "Flow-Matching Euler", sigma_terminal 0.02.) */
+int mmdit_schedule(int32_t n_steps, int32_t img_len, double base_shift, double max_shift,
+                   double sigma_terminal, int32_t shift, double* sigmas);
+
+/* Host. ids [txt_len + grid_h*grid_w, 3] int32: text rows (0,0,0); image
+ * token r*grid_w + c gets (frame, r, c). (mflux-rs RoPE visualiser: axis 0
+ * frame, axis 1 row, axis 2 column.) */
+int mmdit_make_ids(int32_t grid_h, int32_t grid_w, int32_t txt_len, int32_t frame, int32_t* ids);
+
+/* Device, async. Bit-exact 2x2 patch packing of z [B, C, H, W] into
+ * x [B, (H/2)(W/2), 4C] with x[b, hp*(W/2)+wp, c*4+ph*2+pw] = z[b, c, 2hp+ph, 2wp+pw],
+ * and its inverse. elem_bytes is 2 or 4; values are moved as raw bits.
+ * (mflux-rs patch packing calculator; telemetry: bit-exact bijection.) */
+int mmdit_pack_latents(const void* z, void* x, int32_t B, int32_t C, int32_t H, int32_t W,
+                       int32_t elem_bytes, void* hip_stream);
+int mmdit_unpack_latents(const void* x, void* z, int32_t B, int32_t C, int32_t H, int32_t W,
+                         int32_t elem_bytes, void* hip_stream);
+
+/* Device, async. RoPE table [L, sum(axes)/2, 2] float32 (cos, sin) for ids
+ * [L, 3], angles evaluated in float64; the blocks build the same table. */
+int mmdit_rope_table(const int32_t* ids, int32_t L, const int32_t* axes_dim, double theta,
+                     float* table, void* hip_stream);
+
+/* Host. Symmetric group quantiser for w [n_out, k_in] float32 (host),
+ * k_in % 64 == 0, bits 4 or 8: per row and group of 64 k,
+ * s = smallest bf16 >= max|w| / qmax (qmax 7 or 127), q = round-half-even(w / s),
+ * all-zero group -> s = 0, q = 0. packed: host, n_out*k_in/2 bytes (4-bit,
+ * even k in the low nibble) or n_out*k_in bytes (8-bit); scales_bf16: host
+ * [n_out, k_in/64]. */
+int mmdit_quantise(const float* w, int32_t n_out, int32_t k_in, int32_t bits,
+                   void* packed, uint16_t* scales_bf16);
+
+/* Kernel timing for benchmarks. While enabled, each launch of the selected
+ * kernel class is bracketed by HIP events recorded on the launch stream.
+ * classes: 1 = bf16 GEMMs (all projections), 2 = joint attention,
+ * 3 = adaLN LayerNorm, 4 = QK RMSNorm + RoPE, 5 = modulation GEMV.
+ * mmdit_profile_begin creates up to max_launches event pairs (host call, no
+ * device allocation). mmdit_profile_end waits for the recorded events and
+ * returns the summed kernel time, the launch count and the summed algorithmic
+ * FLOPs (classes 1, 2) or bytes (classes 3-5) of those launches. */
+int mmdit_profile_begin(int32_t kernel_class, int32_t max_launches);
+int mmdit_profile_end(double* total_ms, int32_t* launches, double* work);
+
+const char* mmdit_status_str(int32_t status);
+const char* mmdit_last_error(void);
+/* Library version string, e.g. "mmdit 0.1 gfx950". */
+const char* mmdit_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MMDIT_H */

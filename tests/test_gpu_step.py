@@ -1,0 +1,151 @@
+"""GPU parity of the denoising step (mmdit_step) and of the packing / RoPE
+helpers against the CPU oracle."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from diffusion_transformer_mmdit_amd import binding as bd
+from diffusion_transformer_mmdit_amd import inputs as I
+from tests.gpu_util import assert_parity, down, dtype_code, rel_l2, sync, torch, up, up_i32, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------- helpers ------
+def test_pack_unpack_bit_exact():
+    t = torch()
+    rng = np.random.default_rng(3)
+    for nbytes, npdt, tdt in ((4, np.uint32, t.int32), (2, np.uint16, t.int16)):
+        z = rng.integers(0, 2 ** (8 * nbytes), size=(2, 16, 128, 96), dtype=np.uint64).astype(npdt)
+        zd = t.from_numpy(z.view(np.int32 if nbytes == 4 else np.int16)).cuda()
+        xd = t.empty((2, 64 * 48, 64), dtype=tdt, device="cuda")
+        print(f"pack elem_bytes={nbytes}", flush=True)
+        bd.mmdit_pack_latents(zd, xd)
+        back = t.empty_like(zd)
+        bd.mmdit_unpack_latents(xd, back)
+        sync()
+        X = xd.cpu().numpy().view(npdt)
+        assert np.array_equal(X, oracle.pack_latents(z))
+        assert np.array_equal(back.cpu().numpy().view(npdt), z)
+
+
+def test_rope_table_matches_oracle():
+    t = torch()
+    ids = oracle.make_ids(64, 64, 512, frame=3)
+    ids[:512, 1] = np.arange(512)
+    tab = t.empty((ids.shape[0], 64, 2), dtype=t.float32, device="cuda")
+    bd.mmdit_rope_table(up_i32(ids), (16, 56, 56), 10000.0, tab)
+    sync()
+    cos, sin = oracle.rope_table(ids)
+    got = tab.cpu().numpy()
+    err = max(np.abs(got[..., 0] - cos).max(), np.abs(got[..., 1] - sin).max())
+    print(f"rope table max abs err {err:.2e}, exact {np.mean(got[..., 0] == cos):.4f}", flush=True)
+    assert err <= 2e-6
+
+
+# ---------------------------------------------------------------- step -------
+def model_numpy(s: I.Shape):
+    g = I.global_weights(s)
+    dbl = [I.double_block_weights(s, i) for i in range(s.n_double)]
+    sgl = [I.single_block_weights(s, i) for i in range(s.n_single)]
+    return g, dbl, sgl
+
+
+def run_step(s: I.Shape, g, dbl, sgl, inp, sig_i: int, n_steps: int = 4, quant=None, repeat: int = 1):
+    t = torch()
+    dt = dtype_code(s.dtype)
+    cfg = bd.make_config(s)
+    M = bd.ModelW(g, [bd.DoubleW(d, dt, "cuda", quant) for d in dbl],
+                  [bd.SingleW(w, dt, "cuda", quant) for w in sgl], dt, "cuda")
+    mc = M.c()
+    z = t.from_numpy(inp["z"]).cuda()
+    X = t.empty((s.batch, s.img_len, s.in_ch), dtype=t.float32, device="cuda")
+    bd.mmdit_pack_latents(z, X)
+    ids = up_i32(bd.mmdit_make_ids(s.grid_h, s.grid_w, s.txt_len))
+    sig = bd.mmdit_schedule(n_steps, s.img_len)
+    T = up(inp["T"], s.dtype)
+    y = up(inp["y"], s.dtype)
+    v = t.empty_like(X)
+    ws = workspace(bd.mmdit_step_workspace(cfg))
+    outs = []
+    for _ in range(repeat):
+        Xr = X.clone()
+        print(f"step B={s.batch} h={s.hidden} {s.n_double}+{s.n_single} blocks L={s.seq_len} {s.dtype} "
+              f"sigma {sig[sig_i]:.4f}->{sig[sig_i + 1]:.4f}", flush=True)
+        bd.mmdit_step(cfg, mc, Xr, v, T, y, ids, sig[sig_i], sig[sig_i + 1], ws)
+        sync()
+        outs.append((down(Xr), down(v)))
+    return outs if repeat > 1 else outs[0]
+
+
+def oracle_step(s: I.Shape, g, dbl, sgl, inp, sig_i: int, n_steps: int = 4):
+    X = oracle.pack_latents(inp["z"])
+    ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
+    sig = oracle.schedule(n_steps, s.img_len)
+    return oracle.step(g, dbl, sgl, X, inp["T"], inp["y"], ids, sig[sig_i], sig[sig_i + 1], s.heads,
+                       s.axes_dim, s.theta)
+
+
+TINY_F32 = I.Shape(hidden=256, heads=2, mlp_hidden=512, txt_len=16, grid_h=8, grid_w=8, dtype="f32",
+                   cfg_id=41, n_double=2, n_single=2, txt_in_dim=256, vec_in_dim=256)
+
+
+@pytest.mark.parametrize("sig_i", [0, 3])
+def test_step_f32_tiny(sig_i):
+    s = TINY_F32
+    g, dbl, sgl = model_numpy(s)
+    inp = I.step_inputs(s)
+    Xg, vg = run_step(s, g, dbl, sgl, inp, sig_i)
+    Xr, vr = oracle_step(s, g, dbl, sgl, inp, sig_i)
+    assert_parity(vg, vr, "f32", "step v")
+    assert_parity(Xg, Xr, "f32", "step x_next")
+
+
+def test_step_f32_batch2_no_text():
+    s = dataclasses.replace(TINY_F32, batch=2, txt_len=0, grid_h=6, grid_w=10, cfg_id=42)
+    g, dbl, sgl = model_numpy(s)
+    inp = I.step_inputs(s)
+    Xg, vg = run_step(s, g, dbl, sgl, inp, 1)
+    Xr, vr = oracle_step(s, g, dbl, sgl, inp, 1)
+    assert_parity(vg, vr, "f32", "step v (B=2, Lt=0)")
+
+
+def test_step_f32_batch2_ragged():
+    s = dataclasses.replace(TINY_F32, batch=2, txt_len=21, grid_h=5, grid_w=9, cfg_id=43)
+    g, dbl, sgl = model_numpy(s)
+    inp = I.step_inputs(s)
+    _, vg = run_step(s, g, dbl, sgl, inp, 2)
+    _, vr = oracle_step(s, g, dbl, sgl, inp, 2)
+    assert_parity(vg, vr, "f32", "step v (B=2 ragged)")
+
+
+def test_step_bf16_full_tokens_two_plus_two_blocks():
+    # 1024^2 workload (4096 image + 512 text tokens, h 3072) at depth 2 + 2
+    s = dataclasses.replace(I.CFG4, n_double=2, n_single=2)
+    g, dbl, sgl = model_numpy(s)
+    inp = I.step_inputs(s)
+    Xg, vg = run_step(s, g, dbl, sgl, inp, 0)
+    Xr, vr = oracle_step(s, g, dbl, sgl, inp, 0)
+    assert_parity(vg, vr, "bf16", "bf16 step v")
+    assert_parity(Xg, Xr, "bf16", "bf16 step x_next")
+
+
+def test_step_quantised_full_tokens_one_plus_one_blocks():
+    s = dataclasses.replace(I.CFG5, n_double=1, n_single=1)
+    g, dbl, sgl = model_numpy(s)
+    inp = I.step_inputs(s)
+    _, vg = run_step(s, g, dbl, sgl, inp, 1, quant=bd.QUANT_POLICY)
+    from tests.test_gpu_blocks import dequantised
+    _, vr = oracle_step(s, g, [dequantised(d, bd.QUANT_POLICY) for d in dbl],
+                        [dequantised(w, bd.QUANT_POLICY) for w in sgl], inp, 1)
+    assert_parity(vg, vr, "bf16", "quantised step v")
+
+
+def test_step_is_deterministic():
+    s = dataclasses.replace(I.CFG4, n_double=1, n_single=1, txt_len=128, grid_h=32, grid_w=32, cfg_id=44)
+    g, dbl, sgl = model_numpy(s)
+    inp = I.step_inputs(s)
+    (x1, v1), (x2, v2) = run_step(s, g, dbl, sgl, inp, 0, repeat=2)
+    assert np.array_equal(v1, v2) and np.array_equal(x1, x2)
