@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the FLUX-style MMDiT denoising step on one MI355X.
+
+Workload: one denoising step at 1024x1024 (64x64 patch grid = 4096 image
+tokens, 512 text tokens, joint sequence 4608), 19 dual-stream + 38
+single-stream blocks, hidden 3072, 24 heads x 128, MLP 12288, bf16 operands
+with float32 accumulation, batch 1, random-init weights drawn on the GPU.
+A step = conditioning vector, all modulations, input projections, the 57
+blocks, the final layer and the fused Euler update (mmdit_step).
+
+Prints ONE JSON line. `value` is the step latency in ms (lower is better).
+Extra fields: HIP-graph replay latency, block TFLOP/s for one dual and one
+single block at 4608 tokens, the quantised-weight step latency, the roofline
+of the dominant GEMM kernel (timed with HIP events on the library's stream)
+and the CPU oracle on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "MMDiT step latency (ms) + block TFLOP/s at 1024² (4096 img+512 txt tok), bf16"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def block_flops(s):
+    """Algorithmic FLOPs of one dual (== single) block at s: projections
+    2 L sum(K N) + attention 4 H L^2 d."""
+    h, m, L, H = s.hidden, s.mlp_hidden, s.seq_len, s.heads
+    kn_dual = h * 3 * h + h * h + h * m + m * h
+    kn_single = h * (3 * h + m) + (h + m) * h
+    assert kn_dual == kn_single
+    return 2.0 * L * kn_dual + 4.0 * H * L * L * s.head_dim
+
+
+def step_flops(s):
+    h = s.hidden
+    Li, Lt = s.img_len, s.txt_len
+    blocks = (s.n_double + s.n_single) * block_flops(s)
+    io = 2.0 * Li * s.in_ch * h + 2.0 * Lt * s.txt_in_dim * h + 2.0 * Li * h * s.in_ch
+    return blocks + io
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(s):
+    """The oracle on the host cores: one dual and one single block at the
+    full 4608-token size (config-3 weights), scaled to 19 + 38 blocks."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    from diffusion_transformer_mmdit_amd import inputs as I
+    import dataclasses
+    sb = dataclasses.replace(I.CFG3, txt_len=s.txt_len, grid_h=s.grid_h, grid_w=s.grid_w)
+    x = I.block_inputs(sb)
+    ids = oracle.make_ids(sb.grid_h, sb.grid_w, sb.txt_len)
+    wd = I.double_block_weights(sb, 0)
+    t0 = time.perf_counter()
+    oracle.double_block(wd, x["x_img"], x["x_txt"], x["vec"], ids, sb.heads)
+    t_dual = time.perf_counter() - t0
+    del wd
+    ws = I.single_block_weights(sb, 0)
+    t0 = time.perf_counter()
+    oracle.single_block(ws, x["x"], x["vec"], ids, sb.heads)
+    t_single = time.perf_counter() - t0
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    est_ms = 1e3 * (s.n_double * t_dual + s.n_single * t_single)
+    return {"value": round(est_ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
+            "sample": (f"numpy float32 oracle, 1 dual block ({t_dual:.2f} s) + 1 single block ({t_single:.2f} s) "
+                       f"at 4608 tokens, scaled to {s.n_double}+{s.n_single} blocks; BLAS "
+                       f"{info[0].get('internal_api', '?') if info else '?'}, affinity "
+                       f"{len(os.sched_getaffinity(0))} cores")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=12)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip block, graph and quantised timings")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from diffusion_transformer_mmdit_amd import binding as bd
+    from diffusion_transformer_mmdit_amd import inputs as I
+    from diffusion_transformer_mmdit_amd import random_init as RI
+
+    bd.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = I.CFG4
+    log(f"building random-init model: {s.n_double}+{s.n_single} blocks, h {s.hidden}, bf16")
+    t0 = time.perf_counter()
+    M = RI.model(s, seed=42, device=dev)
+    mc = M.c()
+    cfg = bd.make_config(s)
+    torch.cuda.synchronize()
+    log(f"  weights ready in {time.perf_counter() - t0:.1f} s")
+
+    inp_z = I.box_muller(s.batch * 16 * 4 * s.grid_h * s.grid_w).reshape(s.batch, 16, 2 * s.grid_h, 2 * s.grid_w)
+    z = torch.from_numpy(inp_z).to(dev)
+    X = torch.empty((s.batch, s.img_len, s.in_ch), dtype=torch.float32, device=dev)
+    bd.mmdit_pack_latents(z, X)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    T = torch.randn((s.batch, s.txt_len, s.txt_in_dim), generator=g, device=dev).to(torch.bfloat16)
+    y = torch.randn((s.batch, s.vec_in_dim), generator=g, device=dev).to(torch.bfloat16)
+    ids = torch.from_numpy(bd.mmdit_make_ids(s.grid_h, s.grid_w, s.txt_len)).to(dev)
+    sig = bd.mmdit_schedule(4, s.img_len)
+    v = torch.empty_like(X)
+    ws = torch.empty(bd.mmdit_step_workspace(cfg), dtype=torch.uint8, device=dev)
+
+    def step(i, model_c=mc, xx=X):
+        j = i % 4
+        bd.mmdit_step(cfg, model_c, xx, v, T, y, ids, sig[j], sig[j + 1], ws)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e3 / n
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms = timed(step, a.steps)
+    log(f"step: {ms:.2f} ms")
+    flops = step_flops(s)
+
+    # roofline of the dominant kernels, timed with HIP events around each launch
+    prof = {}
+    for name, cls in (("gemm_lin1", bd.PC_GEMM_LIN1), ("gemm_all", bd.PC_GEMM), ("attention", bd.PC_ATTN)):
+        bd.mmdit_profile_begin(cls, 400 * max(1, a.steps))
+        for i in range(a.steps):
+            step(i)
+        tot_ms, n, work = bd.mmdit_profile_end()
+        prof[name] = dict(ms_total=tot_ms, launches=n, flops=work,
+                          avg_us=1e3 * tot_ms / max(n, 1), tflops=work / max(tot_ms, 1e-9) / 1e9)
+        log(f"{name}: {n} launches, avg {prof[name]['avg_us']:.1f} us, {prof[name]['tflops']:.1f} TFLOP/s")
+    dom = "gemm_lin1"
+    p = prof[dom]
+    roofline = {"bound": "mfma", "kernel": "k_gemm_bf16 256x256 split epilogue (single-block linear1, "
+                "M 4608 N 21504 K 3072)", "achieved": round(p["tflops"], 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(p["avg_us"], 2), "flops_per_launch": p["flops"] / max(p["launches"], 1)}
+
+    out = {"metric": METRIC, "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": a.steps,
+           "warmup": a.warmup, "ms_per_step": round(ms, 3), "higher_is_better": False, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random-init weights and inputs)",
+           "config": {"workload": "FLUX-style MMDiT denoising step at 1024x1024: 19 dual + 38 single blocks, "
+                                  "hidden 3072, 24x128 heads, MLP 12288, 4096 image + 512 text tokens, batch 1",
+                      "global_batch": 1, "seq_len": s.seq_len, "image_tokens": s.img_len, "text_tokens": s.txt_len,
+                      "parallelism": "single GPU"},
+           "step_tflops": round(flops / ms / 1e9, 1),
+           "step_frac_of_bf16_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+           "roofline": roofline,
+           "kernels": {k: {"avg_us": round(v_["avg_us"], 2), "tflops": round(v_["tflops"], 1),
+                           "launches_per_step": v_["launches"] // max(a.steps, 1)} for k, v_ in prof.items()}}
+
+    if not a.no_extras:
+        # HIP graphs: one captured graph per schedule position (sigma differs)
+        graphs = []
+        try:
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            for j in range(4):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=cap):
+                    step(j)
+                graphs.append(gr)
+            torch.cuda.synchronize()
+            for i in range(4):
+                graphs[i % 4].replay()
+            gms = timed(lambda i: graphs[i % 4].replay(), a.steps)
+            out["graph_ms_per_step"] = round(gms, 3)
+            log(f"graph step: {gms:.2f} ms")
+        except Exception as e:  # report, do not hide the main number
+            out["graph_ms_per_step"] = None
+            out["graph_error"] = str(e)[:200]
+        del graphs
+
+        # block TFLOP/s at 4608 tokens, two weight sets alternating
+        s3 = I.CFG3
+        dims = bd.make_dims(s3)
+        dbl = [RI.double_block(s3, 100 + i, dev) for i in range(2)]
+        sgl = [RI.single_block(s3, 200 + i, dev) for i in range(2)]
+        dblc = [d.c() for d in dbl]
+        sglc = [x.c() for x in sgl]
+        img = torch.randn((1, s3.img_len, s3.hidden), generator=g, device=dev).to(torch.bfloat16)
+        txt = torch.randn((1, s3.txt_len, s3.hidden), generator=g, device=dev).to(torch.bfloat16)
+        xj = torch.randn((1, s3.seq_len, s3.hidden), generator=g, device=dev).to(torch.bfloat16)
+        vec = torch.randn((1, s3.hidden), generator=g, device=dev).to(torch.bfloat16)
+        ids3 = torch.from_numpy(bd.mmdit_make_ids(s3.grid_h, s3.grid_w, s3.txt_len)).to(dev)
+        wsb = torch.empty(max(bd.mmdit_double_block_workspace(dims), bd.mmdit_single_block_workspace(dims)),
+                          dtype=torch.uint8, device=dev)
+        io, to = torch.empty_like(img), torch.empty_like(txt)
+        xo = torch.empty_like(xj)
+        fd = lambda i: bd.mmdit_double_block_fwd(dims, dblc[i % 2], img, txt, io, to, vec, ids3, wsb)  # noqa
+        fs = lambda i: bd.mmdit_single_block_fwd(dims, sglc[i % 2], xj, xo, vec, ids3, wsb)  # noqa
+        for i in range(4):
+            fd(i)
+            fs(i)
+        nb = max(2 * a.steps, 8)
+        dms = timed(fd, nb)
+        sms = timed(fs, nb)
+        bf = block_flops(s3)
+        out["block"] = {"dual_ms": round(dms, 4), "single_ms": round(sms, 4),
+                        "dual_tflops": round(bf / dms / 1e9, 1), "single_tflops": round(bf / sms / 1e9, 1),
+                        "dual_block_fwd_per_s": round(1e3 / dms, 1), "single_block_fwd_per_s": round(1e3 / sms, 1),
+                        "flops_per_block": bf}
+        log(f"blocks: dual {dms:.3f} ms ({bf / dms / 1e9:.0f} TFLOP/s), single {sms:.3f} ms "
+            f"({bf / sms / 1e9:.0f} TFLOP/s)")
+        del dbl, sgl, dblc, sglc
+
+        # quantised-weight step (4-bit inner projections, 8-bit residual-writing layers)
+        Mq = RI.model(I.CFG5, seed=43, device=dev, quant=bd.QUANT_POLICY)
+        mqc = Mq.c()
+        Xq = X.clone()
+        for i in range(a.warmup):
+            step(i, mqc, Xq)
+        qms = timed(lambda i: step(i, mqc, Xq), a.steps)
+        out["quantised_ms_per_step"] = round(qms, 3)
+        log(f"quantised step: {qms:.2f} ms")
+        del Mq, mqc
+
+    if not a.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(s)
+        log(f"  {out['cpu_baseline']}")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,7 +18,7 @@ _lib = None
 
 F32, BF16 = 0, 1
 W_DENSE, W_Q4G64, W_Q8G64 = 0, 1, 2
-PC_GEMM, PC_ATTN, PC_LN, PC_QKNORM, PC_GEMV = 1, 2, 3, 4, 5
+PC_GEMM, PC_ATTN, PC_LN, PC_QKNORM, PC_GEMV, PC_GEMM_LIN1, PC_GEMM_RES = 1, 2, 3, 4, 5, 6, 7
 
 
 class MMDiTError(RuntimeError):
@@ -167,15 +167,18 @@ def _vec(a, dtype, device):
 
 
 class StreamW:
-    def __init__(self, d: Dict[str, np.ndarray], dtype: int, device, quant: Optional[Dict[str, int]] = None):
+    """One stream of a dual block: Linear objects plus RMSNorm scale tensors."""
+
+    def __init__(self, mod, qkv, proj, fc1, fc2, q_norm, k_norm):
+        self.mod, self.qkv, self.proj, self.fc1, self.fc2 = mod, qkv, proj, fc1, fc2
+        self.q_norm, self.k_norm = q_norm, k_norm
+
+    @classmethod
+    def from_numpy(cls, d: Dict[str, np.ndarray], dtype: int, device, quant: Optional[Dict[str, int]] = None):
         q = quant or {}
-        self.mod = Linear.from_numpy(d["mod_w"], d["mod_b"], dtype, device)
-        self.qkv = Linear.from_numpy(d["qkv_w"], d["qkv_b"], dtype, device, q.get("qkv", 0))
-        self.proj = Linear.from_numpy(d["proj_w"], d["proj_b"], dtype, device, q.get("proj", 0))
-        self.fc1 = Linear.from_numpy(d["fc1_w"], d["fc1_b"], dtype, device, q.get("fc1", 0))
-        self.fc2 = Linear.from_numpy(d["fc2_w"], d["fc2_b"], dtype, device, q.get("fc2", 0))
-        self.q_norm = _vec(d["q_norm"], dtype, device)
-        self.k_norm = _vec(d["k_norm"], dtype, device)
+        lin = lambda n: Linear.from_numpy(d[n + "_w"], d[n + "_b"], dtype, device, q.get(n, 0))  # noqa: E731
+        return cls(Linear.from_numpy(d["mod_w"], d["mod_b"], dtype, device), lin("qkv"), lin("proj"), lin("fc1"),
+                   lin("fc2"), _vec(d["q_norm"], dtype, device), _vec(d["k_norm"], dtype, device))
 
     def c(self) -> mmdit_stream_w:
         return mmdit_stream_w(self.mod.c(), self.qkv.c(), self.proj.c(), self.fc1.c(), self.fc2.c(),
@@ -183,22 +186,27 @@ class StreamW:
 
 
 class DoubleW:
-    def __init__(self, d, dtype: int, device, quant=None):
-        self.img = StreamW(d["img"], dtype, device, quant)
-        self.txt = StreamW(d["txt"], dtype, device, quant)
+    def __init__(self, d, dtype: int = None, device=None, quant=None, img=None, txt=None):
+        if d is not None:
+            img = StreamW.from_numpy(d["img"], dtype, device, quant)
+            txt = StreamW.from_numpy(d["txt"], dtype, device, quant)
+        self.img, self.txt = img, txt
 
     def c(self) -> mmdit_double_w:
         return mmdit_double_w(self.img.c(), self.txt.c())
 
 
 class SingleW:
-    def __init__(self, d, dtype: int, device, quant=None):
-        q = quant or {}
-        self.mod = Linear.from_numpy(d["mod_w"], d["mod_b"], dtype, device)
-        self.lin1 = Linear.from_numpy(d["lin1_w"], d["lin1_b"], dtype, device, q.get("lin1", 0))
-        self.lin2 = Linear.from_numpy(d["lin2_w"], d["lin2_b"], dtype, device, q.get("lin2", 0))
-        self.q_norm = _vec(d["q_norm"], dtype, device)
-        self.k_norm = _vec(d["k_norm"], dtype, device)
+    def __init__(self, d, dtype: int = None, device=None, quant=None, mod=None, lin1=None, lin2=None,
+                 q_norm=None, k_norm=None):
+        if d is not None:
+            q = quant or {}
+            mod = Linear.from_numpy(d["mod_w"], d["mod_b"], dtype, device)
+            lin1 = Linear.from_numpy(d["lin1_w"], d["lin1_b"], dtype, device, q.get("lin1", 0))
+            lin2 = Linear.from_numpy(d["lin2_w"], d["lin2_b"], dtype, device, q.get("lin2", 0))
+            q_norm = _vec(d["q_norm"], dtype, device)
+            k_norm = _vec(d["k_norm"], dtype, device)
+        self.mod, self.lin1, self.lin2, self.q_norm, self.k_norm = mod, lin1, lin2, q_norm, k_norm
 
     def c(self) -> mmdit_single_w:
         return mmdit_single_w(self.mod.c(), self.lin1.c(), self.lin2.c(), _ptr(self.q_norm), _ptr(self.k_norm))
@@ -208,25 +216,27 @@ class SingleW:
 # bits, the inner projections 4 bits (stable-diffusion.rs README).
 QUANT_POLICY = {"qkv": 4, "fc1": 4, "lin1": 4, "proj": 8, "fc2": 8, "lin2": 8}
 
+GLOBAL_LINEARS = ("img_in", "txt_in", "time_in0", "time_in1", "vec_in0", "vec_in1", "final_mod", "final_lin")
+
 
 class ModelW:
-    """Whole-model weights: global layers plus lists of block weights."""
+    """Whole-model weights: global Linear objects plus lists of block weights."""
 
-    def __init__(self, g: Dict[str, np.ndarray], dbl: Sequence, sgl: Sequence, dtype: int, device):
-        L = lambda n: Linear.from_numpy(g[n + "_w"], g[n + "_b"], dtype, device)  # noqa: E731
-        self.img_in, self.txt_in = L("img_in"), L("txt_in")
-        self.time_in0, self.time_in1 = L("time_in0"), L("time_in1")
-        self.vec_in0, self.vec_in1 = L("vec_in0"), L("vec_in1")
-        self.final_mod = L("final_mod")
-        self.final_lin = Linear.from_numpy(g["final_w"], g["final_b"], dtype, device)
+    def __init__(self, g: Optional[Dict[str, np.ndarray]], dbl: Sequence, sgl: Sequence, dtype: int = None,
+                 device=None, linears: Optional[Dict[str, Linear]] = None):
+        if g is not None:
+            names = {n: n for n in GLOBAL_LINEARS}
+            names["final_lin"] = "final"
+            linears = {n: Linear.from_numpy(g[k + "_w"], g[k + "_b"], dtype, device) for n, k in names.items()}
+        for n in GLOBAL_LINEARS:
+            setattr(self, n, linears[n])
         self.dbl: List = list(dbl)
         self.sgl: List = list(sgl)
 
     def c(self) -> mmdit_model_w:
         self._dbl_arr = (mmdit_double_w * max(1, len(self.dbl)))(*[d.c() for d in self.dbl])
         self._sgl_arr = (mmdit_single_w * max(1, len(self.sgl)))(*[s.c() for s in self.sgl])
-        return mmdit_model_w(self.img_in.c(), self.txt_in.c(), self.time_in0.c(), self.time_in1.c(),
-                             self.vec_in0.c(), self.vec_in1.c(), self.final_mod.c(), self.final_lin.c(),
+        return mmdit_model_w(*[getattr(self, n).c() for n in GLOBAL_LINEARS],
                              C.cast(self._dbl_arr, C.POINTER(mmdit_double_w)),
                              C.cast(self._sgl_arr, C.POINTER(mmdit_single_w)))
 

@@ -25,7 +25,8 @@ LIB = os.path.join(PKG, "libmmdit.so")
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-pragma-unroll-threshold=1000000"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           "-Wno-pass-failed", "-I", os.path.join(ROOT, "include")]
 

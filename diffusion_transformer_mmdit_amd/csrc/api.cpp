@@ -50,13 +50,14 @@ struct Prof {
 };
 Prof g_prof;
 
-enum { PC_GEMM = 1, PC_ATTN = 2, PC_LN = 3, PC_QKNORM = 4, PC_GEMV = 5 };
+enum { PC_GEMM = 1, PC_ATTN = 2, PC_LN = 3, PC_QKNORM = 4, PC_GEMV = 5, PC_GEMM_LIN1 = 6, PC_GEMM_RES = 7 };
 
 struct ProfScope {
   hipEvent_t stop = nullptr;
   hipStream_t s;
-  ProfScope(int cls, double work, hipStream_t st) : s(st) {
-    if (!g_prof.active || g_prof.cls != cls || g_prof.used >= g_prof.cap) return;
+  // records when the active class is `cls` or `cls2`
+  ProfScope(int cls, double work, hipStream_t st, int cls2 = -1) : s(st) {
+    if (!g_prof.active || (g_prof.cls != cls && g_prof.cls != cls2) || g_prof.used >= g_prof.cap) return;
     hipEvent_t start = g_prof.ev[2 * g_prof.used];
     stop = g_prof.ev[2 * g_prof.used + 1];
     g_prof.used++;
@@ -230,8 +231,10 @@ char* ptr(void* base, size_t off) { return reinterpret_cast<char*>(base) + off; 
 int gemm(const Ctx& c, GemmProblem* p, int np, int epi) {
   double flops = 0;
   for (int i = 0; i < np; ++i) flops += 2.0 * p[i].M * (double)p[i].N * p[i].K;
-  ProfScope ps(PC_GEMM, flops, c.s);
-  HIP_TRY(c.g.bf16 ? launch_gemm_bf16(p, np, epi, c.s) : launch_gemm_f32(p, np, epi, c.s));
+  ProfScope ps(PC_GEMM, flops, c.s, epi == EPI_SPLIT ? PC_GEMM_LIN1 : (epi == EPI_GATE_RES ? PC_GEMM_RES : -1));
+  if (!c.g.bf16) HIP_TRY(launch_gemm_f32(p, np, epi, c.s));
+  else if (gemm_dma_eligible(p, np, epi)) HIP_TRY(launch_gemm_dma(p, np, epi, c.s));
+  else HIP_TRY(launch_gemm_bf16(p, np, epi, c.s));
   return MMDIT_OK;
 }
 
@@ -669,7 +672,7 @@ int mmdit_rope_table(const int32_t* ids, int32_t L, const int32_t* axes_dim, dou
 
 int mmdit_profile_begin(int32_t kernel_class, int32_t max_launches) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
-  if (kernel_class < PC_GEMM || kernel_class > PC_GEMV) return fail(MMDIT_ERR_SHAPE, "unknown kernel class %d", kernel_class);
+  if (kernel_class < PC_GEMM || kernel_class > PC_GEMM_RES) return fail(MMDIT_ERR_SHAPE, "unknown kernel class %d", kernel_class);
   if (max_launches < 1 || max_launches > 1 << 20) return fail(MMDIT_ERR_SHAPE, "max_launches out of range");
   if (g_prof.active) return fail(MMDIT_ERR_UNSUPPORTED, "profiling already active");
   for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);

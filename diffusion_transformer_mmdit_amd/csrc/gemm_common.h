@@ -52,6 +52,136 @@ __device__ __forceinline__ void gemm_epilogue(const GemmProblem& P, int m, int n
   }
 }
 
+// GELU-tanh for the bf16 kernels: exp2 and reciprocal on the hardware
+// transcendental units (results are rounded to bf16 afterwards).
+__device__ __forceinline__ float gelu_fast(float x) {
+  const float k0 = 0.7978845608028654f, k1 = 0.044715f;
+  const float u = k0 * x * fmaf(k1, x * x, 1.0f);
+  const float e = __builtin_amdgcn_exp2f(u * 2.8853900817779268f);  // exp(2u)
+  const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  return 0.5f * x * (1.0f + t);
+}
+
+// Epilogue of one 32x32 MFMA accumulator block held by a lane: 16 rows
+// row(r) = mb + 8 (r / 4) + r % 4 of column n. Column constants (bias, gate)
+// come in precomputed. `fast` is true when every row of the block tile lies
+// in one batch and the residual rows are contiguous (rows_per_batch >= M);
+// otherwise each element takes the generic path. For EPI_SPLIT, `split_side`
+// is 0 (all columns of the tile before split_n), 1 (all after) or 2 (mixed).
+// GENERAL = false compiles out the per-element fallbacks (the caller
+// guarantees fast == true and split_side != 2).
+template <int EPI, bool GENERAL>
+__device__ __forceinline__ void epi_block_bf16(const GemmProblem& P, int mb, int n, const f32x16& acc,
+                                               float bias, float gate, bool fast, int split_side) {
+  const int M = P.M;
+  if constexpr (EPI == EPI_STORE) {
+    if (P.out_f32) {
+      float* o = reinterpret_cast<float*>(P.out);
+      const int ld = (int)P.ldo;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb + 8 * (r >> 2) + (r & 3);
+        if (m < M) o[m * ld + n] = acc[r] + bias;
+      }
+    } else {
+      bf16* o = reinterpret_cast<bf16*>(P.out);
+      const int ld = (int)P.ldo;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb + 8 * (r >> 2) + (r & 3);
+        if (m < M) o[m * ld + n] = (bf16)(acc[r] + bias);
+      }
+    }
+  } else if constexpr (EPI == EPI_GELU || EPI == EPI_SPLIT) {
+    if (GENERAL && EPI == EPI_SPLIT && split_side == 2) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb + 8 * (r >> 2) + (r & 3);
+        if (m < M) gemm_epilogue<EPI_SPLIT, bf16, false>(P, m, n, acc[r]);
+      }
+      return;
+    }
+    const bool to2 = EPI == EPI_SPLIT && split_side == 1;
+    const bool gelu = EPI == EPI_GELU || to2;
+    bf16* o = reinterpret_cast<bf16*>(to2 ? P.out2 : P.out);
+    const int ld = (int)(to2 ? P.ldo2 : P.ldo);
+    const int col = to2 ? n - P.split_n : n;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = mb + 8 * (r >> 2) + (r & 3);
+      float v = acc[r] + bias;
+      if (gelu) v = gelu_fast(v);
+      if (m < M) o[m * ld + col] = (bf16)v;
+    }
+  } else if constexpr (EPI == EPI_GATE_RES) {
+    if (GENERAL && !fast) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb + 8 * (r >> 2) + (r & 3);
+        if (m < M) gemm_epilogue<EPI_GATE_RES, bf16, false>(P, m, n, acc[r]);
+      }
+      return;
+    }
+    const int ldi = P.res_in.ld, ldo = P.res_out.ld;
+    if (P.res_f32) {
+      const float* __restrict__ ri = reinterpret_cast<const float*>(P.res_in.base);
+      float* __restrict__ ro = reinterpret_cast<float*>(P.res_out.base);
+      float rv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int m = mb + 8 * (r >> 2) + (r & 3);
+        m = m < M ? m : M - 1;
+        rv[r] = ri[m * ldi + n];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb + 8 * (r >> 2) + (r & 3);
+        if (m < M) ro[m * ldo + n] = rv[r] + gate * (acc[r] + bias);
+      }
+    } else {
+      const bf16* __restrict__ ri = reinterpret_cast<const bf16*>(P.res_in.base);
+      bf16* __restrict__ ro = reinterpret_cast<bf16*>(P.res_out.base);
+      float rv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int m = mb + 8 * (r >> 2) + (r & 3);
+        m = m < M ? m : M - 1;
+        rv[r] = (float)ri[m * ldi + n];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb + 8 * (r >> 2) + (r & 3);
+        if (m < M) ro[m * ldo + n] = (bf16)(rv[r] + gate * (acc[r] + bias));
+      }
+    }
+    // keep the next block's residual reads below these stores (bounds the
+    // number of values in flight, and so the registers)
+    asm volatile("" ::: "memory");
+  } else {  // EPI_EULER (float32 latent)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = mb + 8 * (r >> 2) + (r & 3);
+      if (m < M) gemm_epilogue<EPI_EULER, bf16, false>(P, m, n, acc[r]);
+    }
+  }
+}
+
+// Batch index shared by all rows [m0, m0 + rows) of a tile when the
+// residual rows are contiguous (one batch, or rows_per_batch >= M), else -1.
+__device__ __forceinline__ int tile_batch(const GemmProblem& P, int m0, int rows) {
+  const int rpb = P.res_out.rows_per_batch;
+  if (rpb <= 0) return 0;
+  if (P.res_in.rows_per_batch < P.M || rpb < P.M) return -1;
+  return 0;
+}
+
+// Which side of split_n the columns [n0, n0 + cols) fall on: 0, 1, or 2 (both).
+__device__ __forceinline__ int split_side_of(const GemmProblem& P, int n0, int cols) {
+  if (n0 + cols <= P.split_n) return 0;
+  if (n0 >= P.split_n) return 1;
+  return 2;
+}
+
 // Map a flat block id to (problem, tile_m, tile_n). Hardware hands out block
 // ids round-robin over the 8 XCDs; the first remap makes each XCD own a
 // contiguous range of logical tiles, the second walks each range in groups

@@ -176,18 +176,19 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmBatch gb) {
   }
 
   // acc[i][j][r] holds C[m0 + wm0 + 32i + 8(r/4) + 4(lane/32) + r%4][n0 + wn0 + 32j + lane%32]
+  const int bu = EPI == EPI_GATE_RES ? tile_batch(P, m0, BM) : 0;
+  const int side = EPI == EPI_SPLIT ? split_side_of(P, n0, BN) : 0;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int j = 0; j < FN; ++j) {
+    const int n = n0 + wn0 + j * 32 + (lane & 31);
+    const bool n_ok = n < N;
+    const int nc = n_ok ? n : N - 1;
+    const float bias = P.bias ? (float)reinterpret_cast<const bf16*>(P.bias)[nc] : 0.f;
+    const float gate = (EPI == EPI_GATE_RES && bu >= 0) ? P.gate[(int64_t)bu * P.gate_bstride + nc] : 0.f;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn0 + j * 32 + (lane & 31);
-      if (n >= N) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < M) gemm_epilogue<EPI, bf16, false>(P, m, n, acc[i][j][r]);
-      }
-    }
+    for (int i = 0; i < FM; ++i)
+      if (n_ok) epi_block_bf16<EPI, true>(P, m0 + wm0 + i * 32 + 4 * (lane >> 5), n, acc[i][j], bias, gate, bu >= 0, side);
+  }
 }
 
 // ------------------------------------------------------------------ launch --
@@ -224,7 +225,7 @@ static hipError_t launch_epi_fmt(const GemmProblem* p, int nprob, hipStream_t s)
   if constexpr (FMT == 0) {
     if (maxN <= 64) return launch_cfg<64, 64, 2, 2, EPI, FMT>(p, nprob, s);
   }
-  if (tiles256 >= 256) return launch_cfg<256, 256, 2, 2, EPI, FMT>(p, nprob, s);
+  (void)tiles256;
   return launch_cfg<128, 128, 2, 2, EPI, FMT>(p, nprob, s);
 }
 

@@ -120,6 +120,9 @@ struct GemmProblem {
 // Up to two problems with the same epilogue in one launch (text and image
 // streams of a dual block). bf16 operands, MFMA.
 hipError_t launch_gemm_bf16(const GemmProblem* p, int nprob, int epi, hipStream_t s);
+// Dense bf16 with direct-to-LDS staging, 256x256 tiles (large problems).
+bool gemm_dma_eligible(const GemmProblem* p, int nprob, int epi);
+hipError_t launch_gemm_dma(const GemmProblem* p, int nprob, int epi, hipStream_t s);
 // float32 operands and accumulation (VALU), dense weights only.
 hipError_t launch_gemm_f32(const GemmProblem* p, int nprob, int epi, hipStream_t s);
 

@@ -210,12 +210,14 @@ int mmdit_quantise(const float* w, int32_t n_out, int32_t k_in, int32_t bits,
 
 /* Kernel timing for benchmarks. While enabled, each launch of the selected
  * kernel class is bracketed by HIP events recorded on the launch stream.
- * classes: 1 = bf16 GEMMs (all projections), 2 = joint attention,
- * 3 = adaLN LayerNorm, 4 = QK RMSNorm + RoPE, 5 = modulation GEMV.
+ * classes: 1 = GEMMs (all projections), 2 = joint attention,
+ * 3 = adaLN LayerNorm, 4 = QK RMSNorm + RoPE, 5 = modulation / conditioning
+ * GEMV, 6 = single-block linear1 GEMM (split GELU epilogue), 7 = GEMMs with
+ * the gated-residual epilogue (out-projection, fc2, linear2).
  * mmdit_profile_begin creates up to max_launches event pairs (host call, no
  * device allocation). mmdit_profile_end waits for the recorded events and
  * returns the summed kernel time, the launch count and the summed algorithmic
- * FLOPs (classes 1, 2) or bytes (classes 3-5) of those launches. */
+ * FLOPs (classes 1, 2, 6, 7) or bytes (classes 3-5) of those launches. */
 int mmdit_profile_begin(int32_t kernel_class, int32_t max_launches);
 int mmdit_profile_end(double* total_ms, int32_t* launches, double* work);
 

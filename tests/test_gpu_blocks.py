@@ -156,6 +156,21 @@ def test_single_block_cfg3_bf16_full_size(cfg3):
     assert_parity(run_single(s, w, x, ids), oracle_single(s, w, x, ids), "bf16", "cfg3 single")
 
 
+def test_blocks_bf16_full_width_ragged_rows():
+    # h 3072 with 77 text + 40x41 image tokens: the projections take the
+    # 256x256 direct-to-LDS GEMM with partial row tiles in both streams
+    s = I.Shape(txt_len=77, grid_h=40, grid_w=41, dtype="bf16", cfg_id=38)
+    x = I.block_inputs(s)
+    ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
+    w = I.double_block_weights(s, 0)
+    img, txt = run_double(s, w, x, ids)
+    rimg, rtxt = oracle_double(s, w, x, ids)
+    assert_parity(img, rimg, "bf16", "ragged-rows dual img")
+    assert_parity(txt, rtxt, "bf16", "ragged-rows dual txt")
+    ws_ = I.single_block_weights(s, 0)
+    assert_parity(run_single(s, ws_, x, ids), oracle_single(s, ws_, x, ids), "bf16", "ragged-rows single")
+
+
 def test_blocks_quantised_weights_bf16():
     s = I.Shape(hidden=1024, heads=8, mlp_hidden=4096, txt_len=64, grid_h=16, grid_w=16, dtype="bf16",
                 cfg_id=35)
