@@ -87,6 +87,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip block, graph and quantised timings")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (calibrates HBM byte counters)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): this build has no multi-GPU path",
@@ -103,6 +105,15 @@ def main():
     bd.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.copy_probe_mib > 0:
+        n = a.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {a.copy_probe_mib} MiB read + {a.copy_probe_mib} MiB written")
+        del src, dst
     s = I.CFG4
     log(f"building random-init model: {s.n_double}+{s.n_single} blocks, h {s.hidden}, bf16")
     t0 = time.perf_counter()

@@ -38,9 +38,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmmdit.so)")
 
 
+# Per-file extra flags. The attention kernel never carries NaN through its
+# max reductions, so it is built without NaN-preserving max semantics.
+FILE_FLAGS = {"k_attn.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON + DEVICE_FLAGS + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + COMMON + DEVICE_FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -189,12 +189,11 @@ __device__ __forceinline__ int split_side_of(const GemmProblem& P, int n0, int c
 // columns in that XCD's L2.
 constexpr int kGroupM = 8;
 
-__device__ __forceinline__ void tile_of(const GemmBatch& gb, int& prob, int& tm, int& tn) {
-  const int nb = gridDim.x;
-  int bid = blockIdx.x;
-  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
-  prob = bid < gb.tile_start[1] ? 0 : 1;
-  const int t = bid - gb.tile_start[prob];
+// Coordinates of logical tile `t` (problems concatenated, each walked in
+// groups of kGroupM row-tiles).
+__device__ __forceinline__ void tile_coords(const GemmBatch& gb, int t, int& prob, int& tm, int& tn) {
+  prob = t < gb.tile_start[1] ? 0 : 1;
+  t -= gb.tile_start[prob];
   const int ntn = gb.tiles_n[prob], ntm = gb.tiles_m[prob];
   const int per_group = kGroupM * ntn;
   const int group = t / per_group;
@@ -203,6 +202,13 @@ __device__ __forceinline__ void tile_of(const GemmBatch& gb, int& prob, int& tm,
   const int w = t - group * per_group;
   tm = first_m + w % gsize;
   tn = w / gsize;
+}
+
+__device__ __forceinline__ void tile_of(const GemmBatch& gb, int& prob, int& tm, int& tn) {
+  const int nb = gridDim.x;
+  int bid = blockIdx.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  tile_coords(gb, bid, prob, tm, tn);
 }
 
 }  // namespace mmdit

@@ -15,7 +15,8 @@
 //    the MFMA B operand: no LDS round trip for P. V arrives transposed
 //    ([d, token]) from the QK-norm kernel so the A operand reads are 8-byte
 //    row segments;
-//  * online softmax in float32 with exp2 of log2(e)-scaled scores.
+//  * online softmax in float32 with exp2 of log2(e)-scaled scores; the
+//    running max is moved only when it grows by more than 2^8.
 #include "common.h"
 #include "kernels.h"
 
@@ -78,16 +79,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
-  float m_run = -INFINITY, l_run = 0.f;
+  // Scores never hold NaN here; the file is built with -fno-honor-nans so
+  // fmaxf needs no canonicalisation. kNegBig stands for minus infinity.
+  constexpr float kNegBig = -1e30f;
+  float m_run = kNegBig, l_run = 0.f;
   const float c2 = a.scale * 1.4426950408889634f;  // scale * log2(e)
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < ntiles) load_tile(kt + 1);
-    // ---- S^T for 64 keys: two 32-key blocks
+  // One 64-key tile. mask: the tile reaches past L (only the last one can).
+  // The running max m_run is moved only when some lane's tile max exceeds it
+  // by more than 2^8 (log2 units): p = exp2(s - m_run) then stays below 256,
+  // and p, l and O all use the same m_run, so the result is exact.
+  auto tile = [&](int kt, int cur, bool mask) {
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -99,39 +101,42 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
       }
     }
     // s[kb][r] = score(query l32, key kt*64 + kb*32 + 8*(r/4) + 4*g + r%4)
-    if ((kt + 1) * kAttnK > a.L) {
+    if (__builtin_expect(mask, 0)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt * kAttnK + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= a.L) s[kb][r] = -INFINITY;
+          if (key >= a.L) s[kb][r] = kNegBig;
         }
     }
-    float mx = -INFINITY;
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[0][r], s[0][r + 1]));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float alpha = exp2f(m_run - m_new);
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[1][r], s[1][r + 1]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+    if (__any(mx > m_run + 8.0f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.f;
     bf16x8 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(s[kb][r] * c2 - m_new);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -m_run));
         psum += p;
         pb[kb * 2 + (r >> 3)][r & 7] = (bf16)p;
       }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] *= alpha;
-    // ---- O^T += V^T P^T; MFMA kb2 covers keys 16*kb2 + 8*(i/4) + 4*g + i%4
+    l_run += psum;
+    // O^T += V^T P^T; MFMA kb2 covers keys 16*kb2 + 8*(i/4) + 4*g + i%4
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -143,6 +148,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb2], o[db], 0, 0, 0);
       }
     }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  const bool ragged = (a.L % kAttnK) != 0;
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < ntiles) load_tile(kt + 1);
+    tile(kt, cur, ragged && kt == ntiles - 1);
     if (kt + 1 < ntiles) store_tile(cur ^ 1);
     __syncthreads();
   }

@@ -1,48 +1,55 @@
 // Dense bf16 GEMM C = A W^T for the large projections (gfx950).
 //
-// 256 x 256 block tile, K-tile 32, 4 wavefronts (2 x 2, 128 x 128 each) on
-// v_mfma_f32_32x32x16_bf16 with the accumulators in AGPRs.
+// 256 x 256 block tile, K-tile BK (64 by default), 4 wavefronts (2 x 2,
+// 128 x 128 each) on v_mfma_f32_32x32x16_bf16 with the accumulators in AGPRs.
 //
 // Operand tiles move HBM -> LDS with the gfx950 direct-to-LDS load
 // (global_load_lds_dwordx4): no VGPR staging and no LDS store instructions.
-// LDS holds 4 stages (4 x 32 KB); the tile for k-step kt+3 is requested while
-// k-step kt is multiplied, so each load has about two k-steps (~2000 MFMA
-// cycles) to arrive. One barrier per k-step; it sits between the two 16-deep
-// halves of the k-step so that the fragment reads of the next stage overlap
-// the MFMAs of the current one.
+// LDS holds S stages (2 x 64 KB by default), one k-tile each. One barrier per
+// k-tile, placed before its last 16-MFMA substep: after it, the requests for
+// k-tile kt+S (into the stage k-tile kt just freed) and the reads of k-tile
+// kt+1's first fragments are interleaved with those last 16 MFMAs, so each
+// load has about one k-tile of MFMAs to arrive.
 //
-// LDS layout: each 64-byte row (32 bf16 of one M or N index) is stored as four
-// 16-byte chunks in the order c ^ f(r), f(r) = ((r >> 1) ^ (r >> 2)) & 3, so the
-// 16-byte fragment reads of consecutive rows fall in distinct banks (for 32 and
-// for 64 banks). The swizzle is applied on the load side: lane i of a DMA
-// instruction writes slot i, so it fetches the global chunk destined for that slot.
+// LDS layout: each row (BK bf16 of one M or N index) is stored as BK/8
+// 16-byte chunks in the order c ^ f(r) (f = swz<BK> below), so the 16-byte
+// fragment reads of consecutive rows fall in distinct banks (for 32 and for
+// 64 banks). The swizzle is applied on the load side: lane i of a DMA
+// instruction writes slot i, so it fetches the global chunk destined for that
+// slot.
 #include "gemm_common.h"
 
 namespace mmdit {
 
-constexpr int kDBM = 256, kDBN = 256, kDBK = 32;
-constexpr int kStageBytes = (kDBM + kDBN) * kDBK * 2;  // 32 KB
-constexpr int kStages = 4;
+constexpr int kDBM = 256, kDBN = 256;
 
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
 }
 
-// 64 lanes each copy 16 bytes from gptr (per lane) to LDS at m0_base + 16 * lane.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t m0_base) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "global_load_lds_dwordx4 %1, off"
-      :
-      : "s"(m0_base), "v"(gptr)
-      : "memory", "m0");
+// 64 lanes each copy 16 bytes from base + voff (per-lane 32-bit byte offset,
+// base a wave-uniform 64-bit address) to LDS at m0_base + 16 * lane.
+// CPOL selects the cache-policy bits of the load (0: default, 1: sc0, 2: nt).
+template <int CPOL>
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t m0_base) {
+  if constexpr (CPOL == 1)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 sc0" : : "s"(m0_base), "v"(voff), "s"(base) : "memory", "m0");
+  else if constexpr (CPOL == 2)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" : : "s"(m0_base), "v"(voff), "s"(base) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(m0_base), "v"(voff), "s"(base) : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(n) (expcnt and lgkmcnt unconstrained), n <= 63.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+__device__ __forceinline__ void wait_vm(int n) {
+  // n is a compile-time constant at every call site after unrolling/inlining
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+#define MMDIT_VM(N) case N: __builtin_amdgcn_s_waitcnt(((N) & 15) | (0x7 << 4) | (0xF << 8) | (((N) >> 4) << 14)); break;
+    MMDIT_VM(8) MMDIT_VM(16) MMDIT_VM(24) MMDIT_VM(32) MMDIT_VM(40) MMDIT_VM(48) MMDIT_VM(56)
+#undef MMDIT_VM
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
 }
 
 __device__ __forceinline__ void barrier() {
@@ -51,10 +58,23 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+// Chunk order inside an LDS row of BK bf16 (16-byte chunks): chunk c of row r
+// sits at position c ^ swz(r). Chosen so the 16-byte fragment reads of
+// consecutive rows (same c) hit distinct banks for 32 and for 64 banks.
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (BK == 32) return ((r >> 1) ^ (r >> 2)) & 3;
+  else return (r & 7) ^ ((r >> 3) & 1);
+}
 
-template <int EPI>
+template <int EPI, int BK, int S, int CPOL>
 __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
+  constexpr int CH = BK / 8;                       // 16-byte chunks per row
+  constexpr int KS = BK / 16;                      // MFMA k-substeps per k-tile
+  constexpr int HALF = kDBM * BK * 2;              // bytes of the A (or B) part of a stage
+  constexpr int STAGE = 2 * HALF;
+  constexpr int NJ = kDBM * CH / 256;              // DMA instructions per wave for A (and for B)
+  constexpr int G = 2 * NJ;                        // DMA instructions per wave per k-tile
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int prob, tm, tn;
   tile_of(gb, prob, tm, tn);
@@ -67,51 +87,59 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
   const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
   const uint32_t lds0 = lds_offset(smem);
 
-  // Per-lane global source of each of the 4 A and 4 B DMA instructions
-  // (row offsets fixed for the whole K loop; the k offset advances).
-  const bf16* A = reinterpret_cast<const bf16*>(P.A);
-  const bf16* W = reinterpret_cast<const bf16*>(P.W);
-  const bf16* asrc[4];
-  const bf16* bsrc[4];
+  // Per-lane source of each DMA instruction: a 32-bit byte offset (row fixed
+  // for the whole K loop) from the wave-uniform base of A or W, which advances
+  // with k. Lane i of instruction j of wave w fills 16-byte slot
+  // (w*NJ + j)*64 + i of the tile.
+  const char* abase = reinterpret_cast<const char*>(P.A);
+  const char* bbase = reinterpret_cast<const char*>(P.W);
+  uint32_t aoffg[NJ], boffg[NJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int s = (wave * 4 + j) * 64 + lane;  // slot (16 B) within the 256-row tile
-    const int r = s >> 2, c = (s & 3) ^ swz(s >> 2);
+  for (int j = 0; j < NJ; ++j) {
+    const int sl = (wave * NJ + j) * 64 + lane;
+    const int r = sl / CH, c = (sl % CH) ^ swz<BK>(sl / CH);
     int gm = m0 + r;
     gm = gm < M ? gm : M - 1;  // rows past the edge re-read a valid row; their outputs are dropped
     int gn = n0 + r;
     gn = gn < N ? gn : N - 1;
-    asrc[j] = A + (int64_t)gm * P.lda + c * 8;
-    bsrc[j] = W + (int64_t)gn * K + c * 8;
+    aoffg[j] = (uint32_t)(((int64_t)gm * P.lda + c * 8) * 2);
+    boffg[j] = (uint32_t)(((int64_t)gn * K + c * 8) * 2);
   }
+  // DMA instruction q (0 .. G-1) of k-tile kt: q < NJ for A, else B.
+  auto dma_one = [&](int kt, int q) {
+    const uint32_t st = lds0 + (uint32_t)((kt % S) * STAGE);
+    const size_t koff = (size_t)kt * BK * 2;
+    if (q < NJ) dma16<CPOL>(abase + koff, aoffg[q], st + (uint32_t)((wave * NJ + q) * 1024));
+    else dma16<CPOL>(bbase + koff, boffg[q - NJ], st + HALF + (uint32_t)((wave * NJ + q - NJ) * 1024));
+  };
   auto issue = [&](int kt) {
-    const uint32_t st = lds0 + (uint32_t)((kt & (kStages - 1)) * kStageBytes);
-    const int k0 = kt * kDBK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(asrc[j] + k0, st + (uint32_t)((wave * 4 + j) * 1024));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(bsrc[j] + k0, st + 16384u + (uint32_t)((wave * 4 + j) * 1024));
+    for (int q = 0; q < G; ++q) dma_one(kt, q);
   };
 
-  // Fragment read offsets (bytes, within a stage) for k-half kk: A rows
-  // wm0 + 32i + lane%32, chunk 2kk + lane/32; B likewise with wn0.
-  uint32_t aoff[2][4], boff[2][4];
+  // Fragment reads for k-substep kk: A rows wm0 + 32i + lane%32, chunk
+  // 2kk + lane/32. The swizzle depends only on the row's low 4 bits, so one
+  // lane offset per kk serves all i (+ i * 32 rows, an immediate).
+  uint32_t aoff[KS], boff[KS];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wm0 + i * 32 + (lane & 31);
-      const int rb = wn0 + i * 32 + (lane & 31);
-      const int c = kk * 2 + (lane >> 5);
-      aoff[kk][i] = (uint32_t)((ra * 4 + (c ^ swz(ra))) * 16);
-      boff[kk][i] = 16384u + (uint32_t)((rb * 4 + (c ^ swz(rb))) * 16);
-    }
+  for (int kk = 0; kk < KS; ++kk) {
+    const int ra = wm0 + (lane & 31);
+    const int rb = wn0 + (lane & 31);
+    const int c = kk * 2 + (lane >> 5);
+    aoff[kk] = (uint32_t)((ra * CH + (c ^ swz<BK>(ra))) * 16);
+    boff[kk] = HALF + (uint32_t)((rb * CH + (c ^ swz<BK>(rb))) * 16);
+  }
+  auto read_a = [&](int kt, int kk, int i) {
+    return *reinterpret_cast<const bf16x8*>(smem + (kt % S) * STAGE + aoff[kk] + i * 32 * CH * 16);
+  };
+  auto read_b = [&](int kt, int kk, int i) {
+    return *reinterpret_cast<const bf16x8*>(smem + (kt % S) * STAGE + boff[kk] + i * 32 * CH * 16);
+  };
   auto read_frags = [&](int kt, int kk, bf16x8* fa, bf16x8* fb) {
-    const char* st = smem + (kt & (kStages - 1)) * kStageBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(st + aoff[kk][i]);
+    for (int i = 0; i < 4; ++i) fa[i] = read_a(kt, kk, i);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fb[i] = *reinterpret_cast<const bf16x8*>(st + boff[kk][i]);
+    for (int i = 0; i < 4; ++i) fb[i] = read_b(kt, kk, i);
   };
 
   f32x16 acc[4][4];
@@ -126,43 +154,67 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
       for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
 
-  const int nk = K / kDBK;
-  // prologue: tiles 0, 1, 2 requested; wait for tile 0
-  issue(0);
-  if (nk > 1) issue(1);
-  if (nk > 2) issue(2);
-  if (nk > 2) wait_vm<16>();
-  else if (nk > 1) wait_vm<8>();
-  else wait_vm<0>();
-  barrier();
-  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-  read_frags(0, 0, fa0, fb0);
-  // every k-step but the last: the barrier path is unconditional inside the
-  // loop so the waits the compiler derives for the fragment registers do
-  // not merge with the last step's
-  for (int kt = 0; kt < nk - 1; ++kt) {
-    read_frags(kt, 1, fa1, fb1);
-    mfmas(fa0, fb0);
-    // tile kt+1 must have landed; tile kt+2 may still be in flight
-    if (kt + 2 < nk) wait_vm<8>();
-    else wait_vm<0>();
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's stage-kt reads are done
-    barrier();
-    if (kt + 3 < nk) issue(kt + 3);
-    read_frags(kt + 1, 0, fa0, fb0);
-    mfmas(fa1, fb1);
+  const int nk = K / BK;
+  // Prologue: one k-tile per stage requested; wait for k-tile 0.
+#pragma unroll
+  for (int u = 0; u < S; ++u)
+    if (u < nk) issue(u);
+  {
+    const int ahead = (S - 1) < (nk - 1) ? (S - 1) : (nk - 1);
+    wait_vm(G * ahead);
   }
-  // last k-step; column-major MFMA order keeps this tail distinct from the
-  // loop body, which the compiler would otherwise fold back into the loop
-  read_frags(nk - 1, 1, fa1, fb1);
+  barrier();
+  bf16x8 fa[2][4], fb[2][4];
+  read_frags(0, 0, fa[0], fb[0]);
+  // k-tile kt: fragments of substep kk+1 are read while substep kk multiplies.
+  // Before the last substep: wait for k-tile kt+1 (k-tiles up to kt+S-1 have
+  // been requested), barrier; then the last substep's 16 MFMAs run with the
+  // requests for k-tile kt+S (into the stage k-tile kt just freed) and the
+  // reads of k-tile kt+1's first fragments interleaved between them.
+  for (int kt = 0; kt < nk - 1; ++kt) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int kk = 0; kk < KS - 1; ++kk) {
+      read_frags(kt, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      mfmas(fa[kk & 1], fb[kk & 1]);
+    }
+    {
+      int ahead = nk - 2 - kt;
+      ahead = ahead < S - 2 ? ahead : S - 2;
+      wait_vm(G * (ahead > 0 ? ahead : 0));
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of k-tile kt are done
+    barrier();
+    const bool more = kt + S < nk;
+    constexpr int L = (KS - 1) & 1, X = KS & 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[i], fb0[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
+        const int u = i * 4 + j;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[L][i], fb[L][j], acc[i][j], 0, 0, 0);
+        // refill fragment slot X (not read by these MFMAs) for k-tile kt+1
+        if (u < 4) fa[X][u] = read_a(kt + 1, 0, u);
+        else if (u < 8) fb[X][u - 4] = read_b(kt + 1, 0, u - 4);
+        if (more && u < G) dma_one(kt + S, u);
+      }
+    if constexpr (G > 16) {
+      if (more) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[i], fb1[j], acc[i][j], 0, 0, 0);
+        for (int q = 16; q < G; ++q) dma_one(kt + S, q);
+      }
+    }
+  }
+  // Last k-tile; column-major MFMA order keeps this tail distinct from the
+  // loop body, which the compiler would otherwise fold back into the loop.
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    if (kk + 1 < KS) read_frags(nk - 1, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
+  }
 
   // acc[i][j][r] = C[m0 + wm0 + 32i + 8(r/4) + 4(lane/32) + r%4][n0 + wn0 + 32j + lane%32]
   const int bu = EPI == EPI_GATE_RES ? tile_batch(P, m0, kDBM) : 0;
@@ -180,7 +232,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
   }
 }
 
-template <int EPI>
+// Tile-loop configuration used by the library.
+#ifndef MMDIT_DMA_BK
+#define MMDIT_DMA_BK 64
+#endif
+#ifndef MMDIT_DMA_STAGES
+#define MMDIT_DMA_STAGES 2
+#endif
+#ifndef MMDIT_DMA_CPOL
+#define MMDIT_DMA_CPOL 0
+#endif
+constexpr int kDBK = MMDIT_DMA_BK;
+
+template <int EPI, int BK = MMDIT_DMA_BK, int S = MMDIT_DMA_STAGES, int CPOL = MMDIT_DMA_CPOL>
 static hipError_t launch_dma_epi(const GemmProblem* p, int nprob, hipStream_t s) {
   GemmBatch gb{};
   int total = 0;
@@ -197,14 +261,15 @@ static hipError_t launch_dma_epi(const GemmProblem* p, int nprob, hipStream_t s)
     gb.tile_start[i + 1] = total;
   }
   if (total == 0) return hipSuccess;
-  const size_t lds = (size_t)kStages * kStageBytes;
+  const size_t lds = (size_t)S * 2 * kDBM * BK * 2;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_dma<EPI>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_dma<EPI, BK, S, CPOL>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(k_gemm_dma<EPI>, dim3(total), dim3(256), lds, s, gb);
+  hipLaunchKernelGGL((k_gemm_dma<EPI, BK, S, CPOL>), dim3(total), dim3(256), lds, s, gb);
   return hipGetLastError();
 }
 
