@@ -52,6 +52,33 @@ __device__ __forceinline__ void gemm_epilogue(const GemmProblem& P, int m, int n
   }
 }
 
+// Dequantise 16 int8 codes (one 16-byte load) times scale into two bf16x8.
+__device__ __forceinline__ void deq8(const u32x4& w, float s, bf16x8& lo, bf16x8& hi) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = w[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float f = (float)(int8_t)(x >> (8 * j)) * s;
+      if (i < 2) lo[i * 4 + j] = (bf16)f;
+      else hi[(i - 2) * 4 + j] = (bf16)f;
+    }
+  }
+}
+
+// Dequantise 32 int4 codes (one 16-byte load; even k in the low nibble).
+__device__ __forceinline__ void deq4(const u32x4& w, float s, bf16x8 out[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = w[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = ((int)(x << (28 - 4 * j))) >> 28;
+      out[i][j] = (bf16)((float)q * s);
+    }
+  }
+}
+
 // GELU-tanh for the bf16 kernels: exp2 and reciprocal on the hardware
 // transcendental units (results are rounded to bf16 afterwards).
 __device__ __forceinline__ float gelu_fast(float x) {

@@ -21,33 +21,6 @@ namespace mmdit {
 constexpr int kBK = 64;
 constexpr int kLDK = kBK + 8;
 
-// Dequantise 16 int8 codes (one 16-byte load) times scale into two bf16x8.
-__device__ __forceinline__ void deq8(const u32x4& w, float s, bf16x8& lo, bf16x8& hi) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t x = w[i];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float f = (float)(int8_t)(x >> (8 * j)) * s;
-      if (i < 2) lo[i * 4 + j] = (bf16)f;
-      else hi[(i - 2) * 4 + j] = (bf16)f;
-    }
-  }
-}
-
-// Dequantise 32 int4 codes (one 16-byte load; even k in the low nibble).
-__device__ __forceinline__ void deq4(const u32x4& w, float s, bf16x8 out[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t x = w[i];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int q = ((int)(x << (28 - 4 * j))) >> 28;
-      out[i][j] = (bf16)((float)q * s);
-    }
-  }
-}
-
 template <int BM, int BN, int WM, int WN, int EPI, int FMT>
 __global__ __launch_bounds__(256) void k_gemm_bf16(GemmBatch gb) {
   constexpr int TM = BM / WM, TN = BN / WN;

@@ -67,14 +67,25 @@ __device__ __forceinline__ int swz(int r) {
   else return (r & 7) ^ ((r >> 3) & 1);
 }
 
-template <int EPI, int BK, int S, int CPOL>
+// FMT 0: dense bf16 weights, both operands by DMA. FMT 1 / 2: 4-bit / 8-bit
+// group-quantised weights (groups of 64 along k = one k-tile, so one bf16
+// scale per weight row per k-tile): the packed codes of k-tile kt+1 are
+// loaded into registers when k-tile kt+1's A DMA is issued, and dequantised
+// into the B half of its stage (same swizzled bf16 layout) just before the
+// barrier that publishes it.
+template <int EPI, int BK, int S, int CPOL, int FMT>
 __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
   constexpr int CH = BK / 8;                       // 16-byte chunks per row
   constexpr int KS = BK / 16;                      // MFMA k-substeps per k-tile
   constexpr int HALF = kDBM * BK * 2;              // bytes of the A (or B) part of a stage
   constexpr int STAGE = 2 * HALF;
-  constexpr int NJ = kDBM * CH / 256;              // DMA instructions per wave for A (and for B)
-  constexpr int G = 2 * NJ;                        // DMA instructions per wave per k-tile
+  constexpr int NJ = kDBM * CH / 256;              // DMA instructions per wave for A (and for dense B)
+  constexpr int G = FMT == 0 ? 2 * NJ : NJ;        // DMA instructions per wave per k-tile
+  // quantised B: raw 16-byte chunks per thread per k-tile (rows of BK codes)
+  constexpr int QB = FMT == 2 ? BK : BK / 2;       // bytes per weight row per k-tile
+  constexpr int QCH = kDBN * QB / 16 / 256;        // raw chunks per thread
+  constexpr int QPR = QB / 16;                     // raw chunks per row
+  static_assert(FMT == 0 || BK == 64, "quantised weights need 64-wide k-tiles (one scale group)");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int prob, tm, tn;
   tile_of(gb, prob, tm, tn);
@@ -93,28 +104,70 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
   // (w*NJ + j)*64 + i of the tile.
   const char* abase = reinterpret_cast<const char*>(P.A);
   const char* bbase = reinterpret_cast<const char*>(P.W);
-  uint32_t aoffg[NJ], boffg[NJ];
+  uint32_t aoffg[NJ], boffg[FMT == 0 ? NJ : 1];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int sl = (wave * NJ + j) * 64 + lane;
     const int r = sl / CH, c = (sl % CH) ^ swz<BK>(sl / CH);
     int gm = m0 + r;
     gm = gm < M ? gm : M - 1;  // rows past the edge re-read a valid row; their outputs are dropped
-    int gn = n0 + r;
-    gn = gn < N ? gn : N - 1;
     aoffg[j] = (uint32_t)(((int64_t)gm * P.lda + c * 8) * 2);
-    boffg[j] = (uint32_t)(((int64_t)gn * K + c * 8) * 2);
+    if constexpr (FMT == 0) {
+      int gn = n0 + r;
+      gn = gn < N ? gn : N - 1;
+      boffg[j] = (uint32_t)(((int64_t)gn * K + c * 8) * 2);
+    }
   }
   // DMA instruction q (0 .. G-1) of k-tile kt: q < NJ for A, else B.
   auto dma_one = [&](int kt, int q) {
     const uint32_t st = lds0 + (uint32_t)((kt % S) * STAGE);
     const size_t koff = (size_t)kt * BK * 2;
     if (q < NJ) dma16<CPOL>(abase + koff, aoffg[q], st + (uint32_t)((wave * NJ + q) * 1024));
-    else dma16<CPOL>(bbase + koff, boffg[q - NJ], st + HALF + (uint32_t)((wave * NJ + q - NJ) * 1024));
+    else if constexpr (FMT == 0)
+      dma16<CPOL>(bbase + koff, boffg[q - NJ], st + HALF + (uint32_t)((wave * NJ + q - NJ) * 1024));
   };
   auto issue = [&](int kt) {
 #pragma unroll
     for (int q = 0; q < G; ++q) dma_one(kt, q);
+  };
+
+  // Quantised B: raw chunk i of this thread is chunk q = tid + 256 i of the
+  // k-tile: weight row q / QPR, part q % QPR.
+  u32x4 braw[FMT == 0 ? 1 : QCH];
+  float bscale[FMT == 0 ? 1 : QCH];
+  auto load_braw = [&](int kt) {
+    if constexpr (FMT != 0) {
+#pragma unroll
+      for (int i = 0; i < QCH; ++i) {
+        const int q = tid + 256 * i;
+        int gn = n0 + q / QPR;
+        gn = gn < N ? gn : N - 1;
+        braw[i] = *reinterpret_cast<const u32x4*>(bbase + (int64_t)gn * (K / 64) * QB + (int64_t)kt * QB + (q % QPR) * 16);
+        bscale[i] = (float)reinterpret_cast<const bf16*>(P.scales)[(int64_t)gn * (K / 64) + kt];
+      }
+    }
+  };
+  auto store_b = [&](int kt) {
+    if constexpr (FMT != 0) {
+      char* st = smem + (kt % S) * STAGE + HALF;
+#pragma unroll
+      for (int i = 0; i < QCH; ++i) {
+        const int q = tid + 256 * i;
+        const int r = q / QPR, part = q % QPR;
+        const int sw = swz<BK>(r);
+        if constexpr (FMT == 2) {
+          bf16x8 lo, hi;
+          deq8(braw[i], bscale[i], lo, hi);
+          *reinterpret_cast<bf16x8*>(st + (r * CH + ((2 * part) ^ sw)) * 16) = lo;
+          *reinterpret_cast<bf16x8*>(st + (r * CH + ((2 * part + 1) ^ sw)) * 16) = hi;
+        } else {
+          bf16x8 o[4];
+          deq4(braw[i], bscale[i], o);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) *reinterpret_cast<bf16x8*>(st + (r * CH + ((4 * part + u) ^ sw)) * 16) = o[u];
+        }
+      }
+    }
   };
 
   // Fragment reads for k-substep kk: A rows wm0 + 32i + lane%32, chunk
@@ -155,34 +208,50 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
   };
 
   const int nk = K / BK;
-  // Prologue: one k-tile per stage requested; wait for k-tile 0.
+  if constexpr (FMT == 0) {
+    // Prologue: one k-tile per stage requested; wait for k-tile 0.
 #pragma unroll
-  for (int u = 0; u < S; ++u)
-    if (u < nk) issue(u);
-  {
+    for (int u = 0; u < S; ++u)
+      if (u < nk) issue(u);
     const int ahead = (S - 1) < (nk - 1) ? (S - 1) : (nk - 1);
     wait_vm(G * ahead);
+  } else {
+    static_assert(FMT == 0 || S == 2, "quantised path uses a 2-stage ring");
+    issue(0);
+    load_braw(0);
+    wait_vm(0);
+    store_b(0);
+    if (nk > 1) {
+      issue(1);
+      load_braw(1);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): B of k-tile 0 written
   }
   barrier();
   bf16x8 fa[2][4], fb[2][4];
   read_frags(0, 0, fa[0], fb[0]);
   // k-tile kt: fragments of substep kk+1 are read while substep kk multiplies.
   // Before the last substep: wait for k-tile kt+1 (k-tiles up to kt+S-1 have
-  // been requested), barrier; then the last substep's 16 MFMAs run with the
-  // requests for k-tile kt+S (into the stage k-tile kt just freed) and the
-  // reads of k-tile kt+1's first fragments interleaved between them.
+  // been requested; quantised B is dequantised into its stage here), barrier;
+  // then the last substep's 16 MFMAs run with the requests for k-tile kt+S
+  // (into the stage k-tile kt just freed) and the reads of k-tile kt+1's
+  // first fragments interleaved between them.
   for (int kt = 0; kt < nk - 1; ++kt) {
 #pragma unroll
     for (int kk = 0; kk < KS - 1; ++kk) {
       read_frags(kt, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      if (FMT != 0 && kk == KS - 2) {
+        wait_vm(0);  // A DMA and raw codes of k-tile kt+1 have landed
+        store_b(kt + 1);
+      }
       mfmas(fa[kk & 1], fb[kk & 1]);
     }
-    {
+    if constexpr (FMT == 0) {
       int ahead = nk - 2 - kt;
       ahead = ahead < S - 2 ? ahead : S - 2;
       wait_vm(G * (ahead > 0 ? ahead : 0));
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of k-tile kt are done
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of k-tile kt (and B writes) are done
     barrier();
     const bool more = kt + S < nk;
     constexpr int L = (KS - 1) & 1, X = KS & 1;
@@ -202,6 +271,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
 #pragma unroll
         for (int q = 16; q < G; ++q) dma_one(kt + S, q);
       }
+    }
+    if constexpr (FMT != 0) {
+      if (more) load_braw(kt + S);
     }
   }
   // Last k-tile; column-major MFMA order keeps this tail distinct from the
@@ -244,7 +316,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
 #endif
 constexpr int kDBK = MMDIT_DMA_BK;
 
-template <int EPI, int BK = MMDIT_DMA_BK, int S = MMDIT_DMA_STAGES, int CPOL = MMDIT_DMA_CPOL>
+template <int EPI, int BK = MMDIT_DMA_BK, int S = MMDIT_DMA_STAGES, int CPOL = MMDIT_DMA_CPOL, int FMT = 0>
 static hipError_t launch_dma_epi(const GemmProblem* p, int nprob, hipStream_t s) {
   GemmBatch gb{};
   int total = 0;
@@ -264,12 +336,12 @@ static hipError_t launch_dma_epi(const GemmProblem* p, int nprob, hipStream_t s)
   const size_t lds = (size_t)S * 2 * kDBM * BK * 2;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_dma<EPI, BK, S, CPOL>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_dma<EPI, BK, S, CPOL, FMT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemm_dma<EPI, BK, S, CPOL>), dim3(total), dim3(256), lds, s, gb);
+  hipLaunchKernelGGL((k_gemm_dma<EPI, BK, S, CPOL, FMT>), dim3(total), dim3(256), lds, s, gb);
   return hipGetLastError();
 }
 
@@ -280,9 +352,13 @@ static hipError_t launch_dma_epi(const GemmProblem* p, int nprob, hipStream_t s)
 bool gemm_dma_eligible(const GemmProblem* p, int nprob, int epi) {
   if (epi == EPI_EULER) return false;
   int64_t tiles = 0;
+  int fmt = -1;
   for (int i = 0; i < nprob; ++i) {
     if (p[i].M == 0) continue;
-    if (p[i].fmt != 0 || p[i].K % kDBK != 0 || p[i].lda % 8 != 0 || p[i].N < 128) return false;
+    if (fmt >= 0 && p[i].fmt != fmt) return false;  // one format per launch
+    fmt = p[i].fmt;
+    if (p[i].K % kDBK != 0 || p[i].lda % 8 != 0 || p[i].N < 128) return false;
+    if (fmt != 0 && (kDBK != 64 || MMDIT_DMA_STAGES != 2)) return false;
     // the epilogue here has only the contiguous-residual and tile-aligned split paths
     if (epi == EPI_GATE_RES && (p[i].res_in.rows_per_batch < p[i].M || p[i].res_out.rows_per_batch < p[i].M))
       return false;
@@ -292,13 +368,24 @@ bool gemm_dma_eligible(const GemmProblem* p, int nprob, int epi) {
   return tiles >= 200;
 }
 
+template <int EPI>
+static hipError_t launch_dma_fmt(const GemmProblem* p, int nprob, hipStream_t s) {
+  int fmt = 0;
+  for (int i = 0; i < nprob; ++i)
+    if (p[i].M > 0) fmt = p[i].fmt;
+  switch (fmt) {
+    case 1: return launch_dma_epi<EPI, MMDIT_DMA_BK, MMDIT_DMA_STAGES, MMDIT_DMA_CPOL, 1>(p, nprob, s);
+    case 2: return launch_dma_epi<EPI, MMDIT_DMA_BK, MMDIT_DMA_STAGES, MMDIT_DMA_CPOL, 2>(p, nprob, s);
+    default: return launch_dma_epi<EPI>(p, nprob, s);
+  }
+}
+
 hipError_t launch_gemm_dma(const GemmProblem* p, int nprob, int epi, hipStream_t s) {
   switch (epi) {
-    case EPI_STORE: return launch_dma_epi<EPI_STORE>(p, nprob, s);
-    case EPI_GELU: return launch_dma_epi<EPI_GELU>(p, nprob, s);
-    case EPI_GATE_RES: return launch_dma_epi<EPI_GATE_RES>(p, nprob, s);
-    case EPI_SPLIT: return launch_dma_epi<EPI_SPLIT>(p, nprob, s);
-    default: return launch_dma_epi<EPI_EULER>(p, nprob, s);
+    case EPI_STORE: return launch_dma_fmt<EPI_STORE>(p, nprob, s);
+    case EPI_GELU: return launch_dma_fmt<EPI_GELU>(p, nprob, s);
+    case EPI_GATE_RES: return launch_dma_fmt<EPI_GATE_RES>(p, nprob, s);
+    default: return launch_dma_fmt<EPI_SPLIT>(p, nprob, s);
   }
 }
 

@@ -156,19 +156,25 @@ def test_single_block_cfg3_bf16_full_size(cfg3):
     assert_parity(run_single(s, w, x, ids), oracle_single(s, w, x, ids), "bf16", "cfg3 single")
 
 
-def test_blocks_bf16_full_width_ragged_rows():
+@pytest.mark.parametrize("quant", [None, "policy"])
+def test_blocks_bf16_full_width_ragged_rows(quant):
     # h 3072 with 77 text + 40x41 image tokens: the projections take the
     # 256x256 direct-to-LDS GEMM with partial row tiles in both streams
+    # (dense weights, or 4/8-bit weights dequantised into LDS)
     s = I.Shape(txt_len=77, grid_h=40, grid_w=41, dtype="bf16", cfg_id=38)
+    q = bd.QUANT_POLICY if quant else None
     x = I.block_inputs(s)
     ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
     w = I.double_block_weights(s, 0)
-    img, txt = run_double(s, w, x, ids)
-    rimg, rtxt = oracle_double(s, w, x, ids)
-    assert_parity(img, rimg, "bf16", "ragged-rows dual img")
-    assert_parity(txt, rtxt, "bf16", "ragged-rows dual txt")
+    img, txt = run_double(s, w, x, ids, quant=q)
+    wo = dequantised(w, q) if q else w
+    rimg, rtxt = oracle_double(s, wo, x, ids)
+    assert_parity(img, rimg, "bf16", f"ragged-rows dual img {quant}")
+    assert_parity(txt, rtxt, "bf16", f"ragged-rows dual txt {quant}")
     ws_ = I.single_block_weights(s, 0)
-    assert_parity(run_single(s, ws_, x, ids), oracle_single(s, ws_, x, ids), "bf16", "ragged-rows single")
+    wso = dequantised(ws_, q) if q else ws_
+    assert_parity(run_single(s, ws_, x, ids, quant=q), oracle_single(s, wso, x, ids), "bf16",
+                  f"ragged-rows single {quant}")
 
 
 def test_blocks_quantised_weights_bf16():
