@@ -165,9 +165,21 @@ def main():
         prof[name] = dict(ms_total=tot_ms, launches=n, flops=work,
                           avg_us=1e3 * tot_ms / max(n, 1), tflops=work / max(tot_ms, 1e-9) / 1e9)
         log(f"{name}: {n} launches, avg {prof[name]['avg_us']:.1f} us, {prof[name]['tflops']:.1f} TFLOP/s")
+    # HBM-bound kernels: work counted in algorithmic bytes
+    mem = {}
+    for name, cls in (("layernorm", bd.PC_LN), ("qk_norm_rope", bd.PC_QKNORM), ("gemv", bd.PC_GEMV)):
+        bd.mmdit_profile_begin(cls, 400 * max(1, a.steps))
+        for i in range(a.steps):
+            step(i)
+        tot_ms, n, work = bd.mmdit_profile_end()
+        mem[name] = dict(ms_per_step=tot_ms / max(a.steps, 1), launches_per_step=n // max(a.steps, 1),
+                         avg_us=round(1e3 * tot_ms / max(n, 1), 2),
+                         gbps=round(work / max(tot_ms, 1e-9) / 1e6, 1))
+        log(f"{name}: {mem[name]['ms_per_step']:.3f} ms/step in {mem[name]['launches_per_step']} launches, "
+            f"{mem[name]['gbps']:.0f} GB/s")
     dom = "gemm_lin1"
     p = prof[dom]
-    roofline = {"bound": "mfma", "kernel": "k_gemm_bf16 256x256 split epilogue (single-block linear1, "
+    roofline = {"bound": "mfma", "kernel": "k_gemm_dma 256x256 direct-to-LDS, split epilogue (single-block linear1, "
                 "M 4608 N 21504 K 3072)", "achieved": round(p["tflops"], 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
                 "avg_launch_us": round(p["avg_us"], 2), "flops_per_launch": p["flops"] / max(p["launches"], 1)}
@@ -183,7 +195,8 @@ def main():
            "step_frac_of_bf16_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
            "roofline": roofline,
            "kernels": {k: {"avg_us": round(v_["avg_us"], 2), "tflops": round(v_["tflops"], 1),
-                           "launches_per_step": v_["launches"] // max(a.steps, 1)} for k, v_ in prof.items()}}
+                           "launches_per_step": v_["launches"] // max(a.steps, 1)} for k, v_ in prof.items()},
+           "hbm_kernels": mem}
 
     if not a.no_extras:
         # HIP graphs: one captured graph per schedule position (sigma differs)

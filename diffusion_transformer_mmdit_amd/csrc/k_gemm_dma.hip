@@ -67,13 +67,182 @@ __device__ __forceinline__ int swz(int r) {
   else return (r & 7) ^ ((r >> 3) & 1);
 }
 
+// Instruction order of one k-substep (8 fragment reads for the next substep,
+// 16 MFMAs): each read issued right behind an MFMA, so the LDS requests are
+// spread over the first half of the substep and have the second half to
+// return; the scheduler would otherwise pull each read next to its consumer
+// and wait on it. Operand requests (inline asm, ordered with the reads as
+// memory operations) stay behind the read they follow in the source. The
+// fences keep substeps from being merged.
+__device__ __forceinline__ void substep_schedule() {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Pins a kernel-argument value in registers: the compiler may otherwise
+// re-load it from the argument segment (and wait on that load) next to every
+// use, which dominated the epilogue.
+template <typename T>
+__device__ __forceinline__ T pin(T v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+// Global-address-space views (pinned pointers lose that information, and
+// generic accesses would be issued as flat instructions).
+typedef __attribute__((address_space(1))) char gchar;
+typedef __attribute__((address_space(1))) const char gcchar;
+typedef __attribute__((address_space(1))) f32x4 gf32x4;
+typedef __attribute__((address_space(1))) const f32x4 gcf32x4;
+typedef __attribute__((address_space(1))) bf16x4 gbf16x4;
+typedef __attribute__((address_space(1))) const bf16x4 gcbf16x4;
+
+// Epilogue of a wave's 128 x 128 tile, staged through LDS in 32-row chunks
+// (float32, row stride kEpiLd) so that each lane then owns 4 consecutive
+// columns of a row: bias, GELU and the gated residual are applied to 4-column
+// vectors, and each global access instruction covers whole 256-byte row
+// segments. The accumulator holds C transposed per register group:
+// acc[i][j][4g + e] = C[m0w + 32i + lane%32][n0w + 32j + 8g + 4(lane/32) + e],
+// so staging is one 16-byte LDS write per group. The caller has made the LDS
+// free (barrier after the last operand reads); each wave uses its own 17 KB.
+// Column counts and row strides are multiples of 4 (checked before launch):
+// a lane's 4 columns are all in range or all out of range. `bias` holds the
+// lane's 4 columns' bias (loaded by the caller ahead of time).
+constexpr int kEpiLd = 132;  // 16-byte writes of 16 consecutive rows hit distinct banks
+
+template <int EPI>
+__device__ __forceinline__ void dma_epilogue(const GemmProblem& P, char* smem, int m0w, int n0w, int wave,
+                                             int lane, const f32x16 (&acc)[4][4], int side, const float (&bias)[4]) {
+  const int M = pin(P.M), N = pin(P.N);
+  float* stg = reinterpret_cast<float*>(smem) + wave * (32 * kEpiLd);
+  const int c4 = lane & 31, rs = lane >> 5;
+  const int n = n0w + 4 * c4;  // this lane's 4 columns (read-back phase)
+  const bool n_ok = n < N;
+  // gated residual geometry
+  gcchar* ibase = nullptr;
+  gcchar* gbase = nullptr;
+  int rpb_i = 1, rpb_o = 1, ld_i = 0, ld_o = 0, gbs = 0;
+  int64_t bs_i = 0, bs_o = 0;
+  bool f32r = false, one_batch = true;
+  int b_o1 = 0, b_i1 = 0;  // batch of the wave tile's first row
+  f32x4 gate1 = {0.f, 0.f, 0.f, 0.f};
+  // plain outputs
+  gchar* obase;
+  int64_t ldo = 0;
+  bool f32o = false;
+  const bool to2 = EPI == EPI_SPLIT && side == 1;
+  if constexpr (EPI == EPI_GATE_RES) {
+    ibase = (gcchar*)pin(reinterpret_cast<const char*>(P.res_in.base));
+    obase = (gchar*)pin(reinterpret_cast<char*>(P.res_out.base));
+    gbase = (gcchar*)pin(reinterpret_cast<const char*>(P.gate));
+    rpb_i = pin(P.res_in.rows_per_batch);
+    rpb_o = pin(P.res_out.rows_per_batch);
+    ld_i = pin(P.res_in.ld);
+    ld_o = pin(P.res_out.ld);
+    gbs = pin(P.gate_bstride);
+    bs_i = pin(P.res_in.batch_stride);
+    bs_o = pin(P.res_out.batch_stride);
+    f32r = pin((int)P.res_f32) != 0;
+    // all 128 rows of the wave tile in one batch of both residual views: one gate row
+    const int mlast = (m0w + 127 < M ? m0w + 127 : M - 1);
+    b_o1 = m0w / rpb_o;
+    b_i1 = m0w / rpb_i;
+    one_batch = b_o1 == mlast / rpb_o && b_i1 == mlast / rpb_i;
+    if (one_batch && n_ok) gate1 = *(gcf32x4*)(gbase + ((int64_t)b_o1 * gbs + n) * 4);
+  } else {
+    obase = (gchar*)pin(reinterpret_cast<char*>(to2 ? P.out2 : P.out));
+    ldo = pin(to2 ? P.ldo2 : P.ldo);
+    f32o = EPI == EPI_STORE && pin((int)P.out_f32) != 0;
+  }
+  const int ncol = n - (to2 ? pin(P.split_n) : 0);  // output column (plain outputs)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // stage rows 32i .. 32i+31: lane owns row lane%32 of each group
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(stg + c4 * kEpiLd + 32 * j + 8 * g + 4 * rs) =
+            (f32x4){acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+    const int mc = m0w + 32 * i;  // first row of the chunk
+    // read back 16 rows per lane (row = 2t + lane/32) in two groups of 8; for
+    // the gated residual, a group's loads are all issued before its stores
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 a[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) a[t] = *reinterpret_cast<const f32x4*>(stg + (2 * (8 * h + t) + rs) * kEpiLd + 4 * c4);
+      if constexpr (EPI == EPI_GATE_RES) {
+        f32x4 res[8], gt[8];
+        int64_t oo[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          int m = mc + 2 * (8 * h + t) + rs;
+          const bool ok = m < M && n_ok;
+          m = m < M ? m : M - 1;
+          const int b_o = one_batch ? b_o1 : m / rpb_o, t_o = m - b_o * rpb_o;
+          const int b_i = one_batch ? b_i1 : m / rpb_i, t_i = m - b_i * rpb_i;
+          oo[t] = (int64_t)b_o * bs_o + (int64_t)t_o * ld_o + n;
+          const int64_t oi = (int64_t)b_i * bs_i + (int64_t)t_i * ld_i + n;
+          res[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          gt[t] = gate1;
+          if (ok) {
+            if (!one_batch) gt[t] = *(gcf32x4*)(gbase + ((int64_t)b_o * gbs + n) * 4);
+            if (f32r) {
+              res[t] = *(gcf32x4*)(ibase + oi * 4);
+            } else {
+              const bf16x4 r = *(gcbf16x4*)(ibase + oi * 2);
+              res[t] = (f32x4){(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
+            }
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int m = mc + 2 * (8 * h + t) + rs;
+          if (m >= M || !n_ok) continue;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = res[t][e] + gt[t][e] * (a[t][e] + bias[e]);
+          if (f32r)
+            *(gf32x4*)(obase + oo[t] * 4) = (f32x4){o[0], o[1], o[2], o[3]};
+          else
+            *(gbf16x4*)(obase + oo[t] * 2) = (bf16x4){(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
+        }
+      } else {
+        gchar* orow = obase + ((int64_t)(mc + 16 * h + rs) * ldo + ncol) * (f32o ? 4 : 2);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int m = mc + 2 * (8 * h + t) + rs;
+          gchar* o = orow + (int64_t)(2 * t) * ldo * (f32o ? 4 : 2);
+          if (m >= M || !n_ok) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = a[t][e] + bias[e];
+          if (EPI == EPI_GELU || to2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = gelu_fast(v[e]);
+          }
+          if (f32o)
+            *(gf32x4*)o = (f32x4){v[0], v[1], v[2], v[3]};
+          else
+            *(gbf16x4*)o = (bf16x4){(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+        }
+      }
+    }
+  }
+}
+
 // FMT 0: dense bf16 weights, both operands by DMA. FMT 1 / 2: 4-bit / 8-bit
 // group-quantised weights (groups of 64 along k = one k-tile, so one bf16
 // scale per weight row per k-tile): the packed codes of k-tile kt+1 are
 // loaded into registers when k-tile kt+1's A DMA is issued, and dequantised
 // into the B half of its stage (same swizzled bf16 layout) just before the
 // barrier that publishes it.
-template <int EPI, int BK, int S, int CPOL, int FMT>
+template <int EPI, int BK, int S, int CPOL, int FMT, int DS>
 __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
   constexpr int CH = BK / 8;                       // 16-byte chunks per row
   constexpr int KS = BK / 16;                      // MFMA k-substeps per k-tile
@@ -196,6 +365,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
   };
 
   f32x16 acc[4][4];
+  // Weight rows go in as the MFMA's first operand, so the accumulator holds
+  // C transposed: acc[i][j][r] = C[m0 + wm0 + 32i + lane%32]
+  //                                [n0 + wn0 + 32j + 8(r/4) + 4(lane/32) + r%4],
+  // four consecutive output columns of one row per group of four registers.
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -204,7 +377,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
 
   const int nk = K / BK;
@@ -233,18 +406,48 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
   // k-tile kt: fragments of substep kk+1 are read while substep kk multiplies.
   // Before the last substep: wait for k-tile kt+1 (k-tiles up to kt+S-1 have
   // been requested; quantised B is dequantised into its stage here), barrier;
-  // then the last substep's 16 MFMAs run with the requests for k-tile kt+S
-  // (into the stage k-tile kt just freed) and the reads of k-tile kt+1's
-  // first fragments interleaved between them.
+  // then the last substep's 16 MFMAs run with the reads of k-tile kt+1's
+  // first fragments interleaved between them, and the requests for k-tile
+  // kt+S (into the stage k-tile kt just freed) start. Dense operands spread
+  // those requests over DS substeps (the last one of k-tile kt and the first
+  // DS-1 of k-tile kt+1), so the vector-memory queue never holds a whole
+  // k-tile's requests at once and the MFMAs behind them keep issuing.
+  constexpr int DSP = FMT == 0 ? DS : 1;
+  constexpr int PER = (G + DSP - 1) / DSP;  // requests per substep
+  static_assert(DSP >= 1 && DSP <= KS, "spread must fit in one k-tile");
+  // substep with the MFMAs interleaved: reads of the next fragments behind
+  // the first 8 MFMAs, requests q0 .. q1-1 of k-tile dkt behind the first ones.
+  auto substep_dma = [&](const bf16x8* ca, const bf16x8* cb, bf16x8* na, bf16x8* nb, int rkt, int rkk,
+                         bool dma, int dkt, int q0, int q1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int u = i * 4 + j;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[j], ca[i], acc[i][j], 0, 0, 0);
+        if (u < 4) na[u] = read_a(rkt, rkk, u);
+        else if (u < 8) nb[u - 4] = read_b(rkt, rkk, u - 4);
+        if (dma && u < q1 - q0) dma_one(dkt, q0 + u);
+      }
+    substep_schedule();
+  };
   for (int kt = 0; kt < nk - 1; ++kt) {
 #pragma unroll
     for (int kk = 0; kk < KS - 1; ++kk) {
+      if (kk < DSP - 1) {
+        // continue the requests of k-tile kt-1+S begun in k-tile kt-1
+        const int q0 = (kk + 1) * PER, q1 = (kk + 2) * PER < G ? (kk + 2) * PER : G;
+        substep_dma(fa[kk & 1], fb[kk & 1], fa[(kk + 1) & 1], fb[(kk + 1) & 1], kt, kk + 1,
+                    kt >= 1 && kt - 1 + S < nk, kt - 1 + S, q0, q1);
+        continue;
+      }
       read_frags(kt, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
       if (FMT != 0 && kk == KS - 2) {
         wait_vm(0);  // A DMA and raw codes of k-tile kt+1 have landed
         store_b(kt + 1);
       }
       mfmas(fa[kk & 1], fb[kk & 1]);
+      if constexpr (FMT == 0) substep_schedule();
     }
     if constexpr (FMT == 0) {
       int ahead = nk - 2 - kt;
@@ -255,25 +458,26 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
     barrier();
     const bool more = kt + S < nk;
     constexpr int L = (KS - 1) & 1, X = KS & 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int u = i * 4 + j;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[L][i], fb[L][j], acc[i][j], 0, 0, 0);
-        // refill fragment slot X (not read by these MFMAs) for k-tile kt+1
-        if (u < 4) fa[X][u] = read_a(kt + 1, 0, u);
-        else if (u < 8) fb[X][u - 4] = read_b(kt + 1, 0, u - 4);
-        if (more && u < G) dma_one(kt + S, u);
-      }
-    if constexpr (G > 16) {
+    substep_dma(fa[L], fb[L], fa[X], fb[X], kt + 1, 0, more, kt + S, 0, PER < 16 ? PER : 16);
+    if constexpr (PER > 16) {
       if (more) {
 #pragma unroll
-        for (int q = 16; q < G; ++q) dma_one(kt + S, q);
+        for (int q = 16; q < PER; ++q) dma_one(kt + S, q);
       }
     }
     if constexpr (FMT != 0) {
       if (more) load_braw(kt + S);
+    }
+  }
+  // bias of this lane's epilogue columns, requested before the last k-tile's MFMAs
+  float ebias[4] = {0.f, 0.f, 0.f, 0.f};
+  {
+    const bf16* bp = reinterpret_cast<const bf16*>(P.bias);
+    const int n = n0 + wn0 + 4 * (lane & 31);
+    if (bp && n < N) {
+      const bf16x4 v = *reinterpret_cast<const bf16x4*>(bp + n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ebias[e] = (float)v[e];
     }
   }
   // Last k-tile; column-major MFMA order keeps this tail distinct from the
@@ -285,23 +489,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i], acc[i][j], 0, 0, 0);
   }
 
-  // acc[i][j][r] = C[m0 + wm0 + 32i + 8(r/4) + 4(lane/32) + r%4][n0 + wn0 + 32j + lane%32]
-  const int bu = EPI == EPI_GATE_RES ? tile_batch(P, m0, kDBM) : 0;
+  // every wave has finished reading the operand stages: LDS is free
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  barrier();
   const int side = EPI == EPI_SPLIT ? split_side_of(P, n0, kDBN) : 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn0 + j * 32 + (lane & 31);
-    const bool n_ok = n < N;
-    const int nc = n_ok ? n : N - 1;
-    const float bias = P.bias ? (float)reinterpret_cast<const bf16*>(P.bias)[nc] : 0.f;
-    const float gate = (EPI == EPI_GATE_RES && bu >= 0) ? P.gate[(int64_t)bu * P.gate_bstride + nc] : 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (n_ok) epi_block_bf16<EPI, false>(P, m0 + wm0 + i * 32 + 4 * (lane >> 5), n, acc[i][j], bias, gate, bu >= 0, side);
-  }
+  dma_epilogue<EPI>(P, smem, m0 + wm0, n0 + wn0, wave, lane, acc, side, ebias);
 }
 
 // Tile-loop configuration used by the library.
@@ -314,9 +509,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
 #ifndef MMDIT_DMA_CPOL
 #define MMDIT_DMA_CPOL 0
 #endif
+#ifndef MMDIT_DMA_SPREAD
+#define MMDIT_DMA_SPREAD 3
+#endif
 constexpr int kDBK = MMDIT_DMA_BK;
 
-template <int EPI, int BK = MMDIT_DMA_BK, int S = MMDIT_DMA_STAGES, int CPOL = MMDIT_DMA_CPOL, int FMT = 0>
+template <int EPI, int BK = MMDIT_DMA_BK, int S = MMDIT_DMA_STAGES, int CPOL = MMDIT_DMA_CPOL, int FMT = 0,
+          int DS = MMDIT_DMA_SPREAD>
 static hipError_t launch_dma_epi(const GemmProblem* p, int nprob, hipStream_t s) {
   GemmBatch gb{};
   int total = 0;
@@ -336,34 +535,46 @@ static hipError_t launch_dma_epi(const GemmProblem* p, int nprob, hipStream_t s)
   const size_t lds = (size_t)S * 2 * kDBM * BK * 2;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_dma<EPI, BK, S, CPOL, FMT>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_dma<EPI, BK, S, CPOL, FMT, DS>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemm_dma<EPI, BK, S, CPOL, FMT>), dim3(total), dim3(256), lds, s, gb);
+  hipLaunchKernelGGL((k_gemm_dma<EPI, BK, S, CPOL, FMT, DS>), dim3(total), dim3(256), lds, s, gb);
   return hipGetLastError();
 }
 
-// True when the DMA kernel applies: dense weights, K a multiple of 32, rows of
-// A 16-byte aligned, N >= 128, contiguous residual rows (gated epilogue), a
-// tile-aligned split column (split epilogue), and enough 256 x 256 tiles to
-// occupy most of the 256 CUs.
+static bool aligned(const void* p, int bytes) { return ((uintptr_t)p % bytes) == 0; }
+
+// True when the DMA kernel applies: no Euler epilogue, one weight format per
+// launch, K a multiple of the k-tile, rows of A 16-byte aligned, N >= 128,
+// column counts, row strides and base pointers of every output (and of bias,
+// gate and residual) aligned for 4-column vector access, a tile-aligned split
+// column (split epilogue), and enough 256 x 256 tiles to occupy most of the
+// 256 CUs.
 bool gemm_dma_eligible(const GemmProblem* p, int nprob, int epi) {
   if (epi == EPI_EULER) return false;
   int64_t tiles = 0;
   int fmt = -1;
   for (int i = 0; i < nprob; ++i) {
-    if (p[i].M == 0) continue;
-    if (fmt >= 0 && p[i].fmt != fmt) return false;  // one format per launch
-    fmt = p[i].fmt;
-    if (p[i].K % kDBK != 0 || p[i].lda % 8 != 0 || p[i].N < 128) return false;
+    const GemmProblem& q = p[i];
+    if (q.M == 0) continue;
+    if (fmt >= 0 && q.fmt != fmt) return false;  // one format per launch
+    fmt = q.fmt;
+    if (q.K % kDBK != 0 || q.lda % 8 != 0 || q.N < 128 || q.N % 4 != 0) return false;
     if (fmt != 0 && (kDBK != 64 || MMDIT_DMA_STAGES != 2)) return false;
-    // the epilogue here has only the contiguous-residual and tile-aligned split paths
-    if (epi == EPI_GATE_RES && (p[i].res_in.rows_per_batch < p[i].M || p[i].res_out.rows_per_batch < p[i].M))
-      return false;
-    if (epi == EPI_SPLIT && p[i].split_n % kDBN != 0) return false;
-    tiles += (int64_t)((p[i].M + kDBM - 1) / kDBM) * ((p[i].N + kDBN - 1) / kDBN);
+    if (q.bias && !aligned(q.bias, 8)) return false;
+    if (epi == EPI_GATE_RES) {
+      const int esz = q.res_f32 ? 16 : 8;
+      if (q.res_in.ld % 4 || q.res_out.ld % 4 || q.res_in.batch_stride % 4 || q.res_out.batch_stride % 4 ||
+          q.gate_bstride % 4 || !aligned(q.res_in.base, esz) || !aligned(q.res_out.base, esz) ||
+          !aligned(q.gate, 16) || q.res_in.rows_per_batch <= 0 || q.res_out.rows_per_batch <= 0)
+        return false;
+    } else {
+      if (q.ldo % 4 || !aligned(q.out, q.out_f32 && epi == EPI_STORE ? 16 : 8)) return false;
+      if (epi == EPI_SPLIT && (q.split_n % kDBN != 0 || q.ldo2 % 4 || !aligned(q.out2, 8))) return false;
+    }
+    tiles += (int64_t)((q.M + kDBM - 1) / kDBM) * ((q.N + kDBN - 1) / kDBN);
   }
   return tiles >= 200;
 }

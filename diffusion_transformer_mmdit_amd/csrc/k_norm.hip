@@ -19,10 +19,10 @@ __device__ __forceinline__ const char* seg_row(const RowSeg& s, int local, int e
 }
 
 // ------------------------------------------------------------------ adaLN-LN --
-// One wavefront per row; each lane holds h/64 values in 4-wide chunks.
-constexpr int kLnMaxChunks = 16;  // h <= 4096
-
-template <typename TX, typename TY>
+// One wavefront per row; each lane holds h/64 values in 4-wide chunks, all
+// loaded before the reductions (NC = h / 256 chunks per lane, a template
+// constant so the loads are issued back to back).
+template <typename TX, typename TY, int NC>
 __global__ __launch_bounds__(256) void k_adaln_ln(LnArgs a, int rows) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -34,56 +34,70 @@ __global__ __launch_bounds__(256) void k_adaln_ln(LnArgs a, int rows) {
   const float* mod = a.mod[s] + (int64_t)b * a.mod_bstride;
   const float* shift = mod + a.shift_off;
   const float* scale = mod + a.scale_off;
-  const int nc = a.h >> 8;  // chunks of 4 per lane
-  float v[kLnMaxChunks][4];
+  float v[NC][4];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) load4(x + (i * 64 + lane) * 4, v[i]);
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < kLnMaxChunks; ++i) {
-    if (i < nc) {
-      load4(x + (i * 64 + lane) * 4, v[i]);
-      sum += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
-    }
-  }
-  const float inv_h = 1.0f / (float)a.h;
+  for (int i = 0; i < NC; ++i) sum += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+  const float inv_h = 1.0f / (float)(NC * 256);
   const float mean = wave_sum(sum) * inv_h;
   float sq = 0.f;
 #pragma unroll
-  for (int i = 0; i < kLnMaxChunks; ++i) {
-    if (i < nc) {
+  for (int i = 0; i < NC; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float d = v[i][j] - mean;
-        sq += d * d;
-      }
+    for (int j = 0; j < 4; ++j) {
+      const float d = v[i][j] - mean;
+      sq += d * d;
     }
-  }
   const float var = wave_sum(sq) * inv_h;
   const float rstd = 1.0f / sqrtf(var + a.eps);
   TY* y = reinterpret_cast<TY*>(a.y) + (int64_t)r * a.h;
 #pragma unroll
-  for (int i = 0; i < kLnMaxChunks; ++i) {
-    if (i < nc) {
-      const int c = (i * 64 + lane) * 4;
-      float sh[4], sc[4], o[4];
-      load4(shift + c, sh);
-      load4(scale + c, sc);
+  for (int i = 0; i < NC; ++i) {
+    const int c = (i * 64 + lane) * 4;
+    float sh[4], sc[4], o[4];
+    load4(shift + c, sh);
+    load4(scale + c, sc);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = (1.0f + sc[j]) * ((v[i][j] - mean) * rstd) + sh[j];
-      store4(y + c, o);
-    }
+    for (int j = 0; j < 4; ++j) o[j] = (1.0f + sc[j]) * ((v[i][j] - mean) * rstd) + sh[j];
+    store4(y + c, o);
   }
 }
 
-hipError_t launch_adaln_ln(const LnArgs& a, int rows, bool x_f32, bool y_bf16, hipStream_t s) {
+template <int NC>
+static void launch_ln_nc(const LnArgs& a, int rows, bool x_f32, bool y_bf16, hipStream_t s) {
   dim3 grid((rows + 3) / 4), block(256);
   if (x_f32 && y_bf16)
-    hipLaunchKernelGGL((k_adaln_ln<float, bf16>), grid, block, 0, s, a, rows);
+    hipLaunchKernelGGL((k_adaln_ln<float, bf16, NC>), grid, block, 0, s, a, rows);
   else if (x_f32)
-    hipLaunchKernelGGL((k_adaln_ln<float, float>), grid, block, 0, s, a, rows);
+    hipLaunchKernelGGL((k_adaln_ln<float, float, NC>), grid, block, 0, s, a, rows);
   else if (y_bf16)
-    hipLaunchKernelGGL((k_adaln_ln<bf16, bf16>), grid, block, 0, s, a, rows);
+    hipLaunchKernelGGL((k_adaln_ln<bf16, bf16, NC>), grid, block, 0, s, a, rows);
   else
-    hipLaunchKernelGGL((k_adaln_ln<bf16, float>), grid, block, 0, s, a, rows);
+    hipLaunchKernelGGL((k_adaln_ln<bf16, float, NC>), grid, block, 0, s, a, rows);
+}
+
+// h is a multiple of 256 and at most 4096 (checked by the API).
+hipError_t launch_adaln_ln(const LnArgs& a, int rows, bool x_f32, bool y_bf16, hipStream_t s) {
+  switch (a.h / 256) {
+    case 1: launch_ln_nc<1>(a, rows, x_f32, y_bf16, s); break;
+    case 2: launch_ln_nc<2>(a, rows, x_f32, y_bf16, s); break;
+    case 3: launch_ln_nc<3>(a, rows, x_f32, y_bf16, s); break;
+    case 4: launch_ln_nc<4>(a, rows, x_f32, y_bf16, s); break;
+    case 5: launch_ln_nc<5>(a, rows, x_f32, y_bf16, s); break;
+    case 6: launch_ln_nc<6>(a, rows, x_f32, y_bf16, s); break;
+    case 7: launch_ln_nc<7>(a, rows, x_f32, y_bf16, s); break;
+    case 8: launch_ln_nc<8>(a, rows, x_f32, y_bf16, s); break;
+    case 9: launch_ln_nc<9>(a, rows, x_f32, y_bf16, s); break;
+    case 10: launch_ln_nc<10>(a, rows, x_f32, y_bf16, s); break;
+    case 11: launch_ln_nc<11>(a, rows, x_f32, y_bf16, s); break;
+    case 12: launch_ln_nc<12>(a, rows, x_f32, y_bf16, s); break;
+    case 13: launch_ln_nc<13>(a, rows, x_f32, y_bf16, s); break;
+    case 14: launch_ln_nc<14>(a, rows, x_f32, y_bf16, s); break;
+    case 15: launch_ln_nc<15>(a, rows, x_f32, y_bf16, s); break;
+    default: launch_ln_nc<16>(a, rows, x_f32, y_bf16, s); break;
+  }
   return hipGetLastError();
 }
 
@@ -92,51 +106,27 @@ hipError_t launch_adaln_ln(const LnArgs& a, int rows, bool x_f32, bool y_bf16, h
 // token, 8 dims per lane; RMS over the 128 dims of the head, times the
 // per-stream scale g, then rotation of the adjacent pairs (2j, 2j+1) by the
 // table's angle. V is copied, transposed to [d, token] for the MFMA path.
+// Every thread issues all of its loads (4 tokens x q, k, v and the angle
+// table) before the first reduction, so 12+ 16-byte loads are in flight.
 constexpr int kQkTile = 64;
+constexpr int kQkPass = kQkTile / 16;
 constexpr int kVPad = 130;  // LDS row stride (elements) of the V transpose tile
 
-template <typename T>
-__device__ __forceinline__ void qk_rows(const QkNormArgs& a, int b, int hh, int t0, int col_off,
-                                        int which, T* dst) {
-  const int tid = threadIdx.x;
-  const int part = tid & 15;
-  const int d0 = part * 8;
-  for (int p = 0; p < kQkTile / 16; ++p) {
-    const int t = t0 + p * 16 + (tid >> 4);
-    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    float g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const bool valid = t < a.L;
-    if (valid) {
-      const int s = t < a.seg_len0 ? 0 : 1;
-      const int local = (s == 0 ? t : t - a.seg_len0) + b * (s == 0 ? a.seg_len0 : a.L - a.seg_len0);
-      const T* src = reinterpret_cast<const T*>(seg_row(a.seg[s], local, sizeof(T)));
-      load8(src + col_off + hh * 128 + d0, x);
-      load8(reinterpret_cast<const T*>(which == 0 ? a.qn[s] : a.kn[s]) + d0, g);
-    }
-    float ss = 0.f;
+__device__ __forceinline__ void qk_rotate(const float (&x)[8], const float (&g)[8],
+                                          const float (&cs)[8], float eps, bool valid,
+                                          float (&y)[8]) {
+  float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
-    ss = group_sum<16>(ss);
-    const float rstd = 1.0f / sqrtf(ss * (1.0f / 128.0f) + a.eps);
-    float y[8];
-    if (valid) {
-      const float* tb = a.table + ((int64_t)t * 64 + (d0 >> 1)) * 2;
-      f32x4 cs0 = *reinterpret_cast<const f32x4*>(tb);
-      f32x4 cs1 = *reinterpret_cast<const f32x4*>(tb + 4);
-      float cs[8] = {cs0[0], cs0[1], cs0[2], cs0[3], cs1[0], cs1[1], cs1[2], cs1[3]};
+  for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+  ss = group_sum<16>(ss);
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / 128.0f) + eps);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float y0 = x[2 * j] * rstd * g[2 * j];
-        const float y1 = x[2 * j + 1] * rstd * g[2 * j + 1];
-        const float c = cs[2 * j], sn = cs[2 * j + 1];
-        y[2 * j] = c * y0 - sn * y1;
-        y[2 * j + 1] = sn * y0 + c * y1;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = 0.f;
-    }
-    if (t < a.Lpad) store8(dst + (int64_t)t * 128 + d0, y);
+  for (int j = 0; j < 4; ++j) {
+    const float y0 = x[2 * j] * rstd * g[2 * j];
+    const float y1 = x[2 * j + 1] * rstd * g[2 * j + 1];
+    const float c = cs[2 * j], sn = cs[2 * j + 1];
+    y[2 * j] = valid ? c * y0 - sn * y1 : 0.f;
+    y[2 * j + 1] = valid ? sn * y0 + c * y1 : 0.f;
   }
 }
 
@@ -147,42 +137,73 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
   const int b = blockIdx.z;
   const int h = a.H * 128;
   const int64_t head_off = ((int64_t)b * a.H + hh) * (int64_t)a.Lpad * 128;
-  qk_rows<T>(a, b, hh, t0, 0, 0, reinterpret_cast<T*>(a.Q) + head_off);
-  qk_rows<T>(a, b, hh, t0, h, 1, reinterpret_cast<T*>(a.K) + head_off);
-
   const int tid = threadIdx.x;
-  const int part = tid & 15;
-  const int d0 = part * 8;
+  const int d0 = (tid & 15) * 8;
+
+  float xq[kQkPass][8], xk[kQkPass][8], xv[kQkPass][8], cs[kQkPass][8];
+  float gq[2][8], gk[2][8];
+  bool valid[kQkPass];
+  int seg_of[kQkPass];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    load8(reinterpret_cast<const T*>(a.qn[s]) + d0, gq[s]);
+    load8(reinterpret_cast<const T*>(a.kn[s]) + d0, gk[s]);
+  }
+#pragma unroll
+  for (int p = 0; p < kQkPass; ++p) {
+    const int t = t0 + p * 16 + (tid >> 4);
+    valid[p] = t < a.L;
+    const int s = t < a.seg_len0 ? 0 : 1;
+    seg_of[p] = s;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xq[p][i] = xk[p][i] = xv[p][i] = cs[p][i] = 0.f;
+    if (valid[p]) {
+      const int local = (s == 0 ? t : t - a.seg_len0) + b * (s == 0 ? a.seg_len0 : a.L - a.seg_len0);
+      const T* src = reinterpret_cast<const T*>(seg_row(a.seg[s], local, sizeof(T))) + hh * 128 + d0;
+      load8(src, xq[p]);
+      load8(src + h, xk[p]);
+      load8(src + 2 * h, xv[p]);
+      const float* tb = a.table + ((int64_t)t * 64 + (d0 >> 1)) * 2;
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(tb);
+      const f32x4 c1 = *reinterpret_cast<const f32x4*>(tb + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        cs[p][i] = c0[i];
+        cs[p][4 + i] = c1[i];
+      }
+    }
+  }
+  T* Q = reinterpret_cast<T*>(a.Q) + head_off;
+  T* K = reinterpret_cast<T*>(a.K) + head_off;
+#pragma unroll
+  for (int p = 0; p < kQkPass; ++p) {
+    const int t = t0 + p * 16 + (tid >> 4);
+    float y[8];
+    qk_rotate(xq[p], seg_of[p] ? gq[1] : gq[0], cs[p], a.eps, valid[p], y);
+    if (t < a.Lpad) store8(Q + (int64_t)t * 128 + d0, y);
+    qk_rotate(xk[p], seg_of[p] ? gk[1] : gk[0], cs[p], a.eps, valid[p], y);
+    if (t < a.Lpad) store8(K + (int64_t)t * 128 + d0, y);
+  }
+
   if constexpr (!VT) {
     T* V = reinterpret_cast<T*>(a.V) + head_off;
-    for (int p = 0; p < kQkTile / 16; ++p) {
+#pragma unroll
+    for (int p = 0; p < kQkPass; ++p) {
       const int t = t0 + p * 16 + (tid >> 4);
-      float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (t < a.L) {
-        const int s = t < a.seg_len0 ? 0 : 1;
-        const int local = (s == 0 ? t : t - a.seg_len0) + b * (s == 0 ? a.seg_len0 : a.L - a.seg_len0);
-        load8(reinterpret_cast<const T*>(seg_row(a.seg[s], local, sizeof(T))) + 2 * h + hh * 128 + d0, x);
-      }
-      if (t < a.Lpad) store8(V + (int64_t)t * 128 + d0, x);
+      if (t < a.Lpad) store8(V + (int64_t)t * 128 + d0, xv[p]);
     }
   } else {
     __shared__ bf16 vs[kQkTile * kVPad];
-    for (int p = 0; p < kQkTile / 16; ++p) {
-      const int tl = p * 16 + (tid >> 4);
-      const int t = t0 + tl;
-      bf16x8 v = {};
-      if (t < a.L) {
-        const int s = t < a.seg_len0 ? 0 : 1;
-        const int local = (s == 0 ? t : t - a.seg_len0) + b * (s == 0 ? a.seg_len0 : a.L - a.seg_len0);
-        v = *reinterpret_cast<const bf16x8*>(
-            reinterpret_cast<const bf16*>(seg_row(a.seg[s], local, 2)) + 2 * h + hh * 128 + d0);
-      }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) vs[tl * kVPad + d0 + i] = v[i];
+    for (int p = 0; p < kQkPass; ++p) {
+      const int tl = p * 16 + (tid >> 4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vs[tl * kVPad + d0 + i] = bf16(xv[p][i]);
     }
     __syncthreads();
     // Vt[b, hh, d, t0 .. t0+63]: 128 rows of 64 tokens, 8 tokens per thread
     bf16* Vt = reinterpret_cast<bf16*>(a.V) + head_off;
+#pragma unroll
     for (int c = tid; c < 128 * (kQkTile / 8); c += 256) {
       const int d = c >> 3;
       const int tc = (c & 7) * 8;
