@@ -101,40 +101,30 @@ typedef __attribute__((address_space(1))) const f32x4 gcf32x4;
 typedef __attribute__((address_space(1))) bf16x4 gbf16x4;
 typedef __attribute__((address_space(1))) const bf16x4 gcbf16x4;
 
-// Epilogue of a wave's 128 x 128 tile, staged through LDS in 32-row chunks
-// (float32, row stride kEpiLd) so that each lane then owns 4 consecutive
-// columns of a row: bias, GELU and the gated residual are applied to 4-column
-// vectors, and each global access instruction covers whole 256-byte row
-// segments. The accumulator holds C transposed per register group:
-// acc[i][j][4g + e] = C[m0w + 32i + lane%32][n0w + 32j + 8g + 4(lane/32) + e],
-// so staging is one 16-byte LDS write per group. The caller has made the LDS
-// free (barrier after the last operand reads); each wave uses its own 17 KB.
-// Column counts and row strides are multiples of 4 (checked before launch):
-// a lane's 4 columns are all in range or all out of range. `bias` holds the
-// lane's 4 columns' bias (loaded by the caller ahead of time).
 constexpr int kEpiLd = 132;  // 16-byte writes of 16 consecutive rows hit distinct banks
 
-template <int EPI>
-__device__ __forceinline__ void dma_epilogue(const GemmProblem& P, char* smem, int m0w, int n0w, int wave,
-                                             int lane, const f32x16 (&acc)[4][4], int side, const float (&bias)[4]) {
+// FULL: every row and column of the wave tile is in range and (gated
+// residual) all its rows lie in one batch of both residual views, so rows
+// advance by a fixed stride and no per-row checks are needed. ALT: for the
+// split epilogue, the tile lies after the split column (GELU, second
+// output); for the gated residual, the residual is float32.
+template <int EPI, bool FULL, bool ALT>
+__device__ __forceinline__ void dma_epilogue_impl(const GemmProblem& P, float* stg, int m0w, int n0w, int lane,
+                                                  const f32x16 (&acc)[4][4], const float (&bias)[4]) {
   const int M = pin(P.M), N = pin(P.N);
-  float* stg = reinterpret_cast<float*>(smem) + wave * (32 * kEpiLd);
   const int c4 = lane & 31, rs = lane >> 5;
   const int n = n0w + 4 * c4;  // this lane's 4 columns (read-back phase)
-  const bool n_ok = n < N;
-  // gated residual geometry
-  gcchar* ibase = nullptr;
-  gcchar* gbase = nullptr;
-  int rpb_i = 1, rpb_o = 1, ld_i = 0, ld_o = 0, gbs = 0;
-  int64_t bs_i = 0, bs_o = 0;
-  bool f32r = false, one_batch = true;
-  int b_o1 = 0, b_i1 = 0;  // batch of the wave tile's first row
-  f32x4 gate1 = {0.f, 0.f, 0.f, 0.f};
-  // plain outputs
+  const bool n_ok = FULL || n < N;
+  constexpr bool to2 = EPI == EPI_SPLIT && ALT;
   gchar* obase;
-  int64_t ldo = 0;
-  bool f32o = false;
-  const bool to2 = EPI == EPI_SPLIT && side == 1;
+  int64_t ld;  // row stride in bytes of the written rows
+  gcchar* ibase = nullptr;
+  int64_t ldi = 0;
+  f32x4 gate1 = {0.f, 0.f, 0.f, 0.f};
+  int rpb_i = 1, rpb_o = 1, gbs = 0;
+  int64_t bs_i = 0, bs_o = 0, ld_i = 0, ld_o = 0;
+  constexpr bool f32r = EPI == EPI_GATE_RES && ALT;
+  gcchar* gbase = nullptr;
   if constexpr (EPI == EPI_GATE_RES) {
     ibase = (gcchar*)pin(reinterpret_cast<const char*>(P.res_in.base));
     obase = (gchar*)pin(reinterpret_cast<char*>(P.res_out.base));
@@ -146,19 +136,21 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& P, char* smem, i
     gbs = pin(P.gate_bstride);
     bs_i = pin(P.res_in.batch_stride);
     bs_o = pin(P.res_out.batch_stride);
-    f32r = pin((int)P.res_f32) != 0;
-    // all 128 rows of the wave tile in one batch of both residual views: one gate row
-    const int mlast = (m0w + 127 < M ? m0w + 127 : M - 1);
-    b_o1 = m0w / rpb_o;
-    b_i1 = m0w / rpb_i;
-    one_batch = b_o1 == mlast / rpb_o && b_i1 == mlast / rpb_i;
-    if (one_batch && n_ok) gate1 = *(gcf32x4*)(gbase + ((int64_t)b_o1 * gbs + n) * 4);
+    const int esz = f32r ? 4 : 2;
+    if constexpr (FULL) {
+      // one batch for all rows: rows are affine in m
+      const int b_o = m0w / rpb_o, b_i = m0w / rpb_i;
+      obase += ((int64_t)b_o * bs_o + (int64_t)(m0w - b_o * rpb_o) * ld_o + n) * esz;
+      ibase += ((int64_t)b_i * bs_i + (int64_t)(m0w - b_i * rpb_i) * ld_i + n) * esz;
+      gate1 = *(gcf32x4*)(gbase + ((int64_t)b_o * gbs + n) * 4);
+    }
+    ld = ld_o * esz;
+    ldi = ld_i * esz;
   } else {
     obase = (gchar*)pin(reinterpret_cast<char*>(to2 ? P.out2 : P.out));
-    ldo = pin(to2 ? P.ldo2 : P.ldo);
-    f32o = EPI == EPI_STORE && pin((int)P.out_f32) != 0;
+    ld = pin(to2 ? P.ldo2 : P.ldo) * 2;
+    obase += ((int64_t)m0w * (ld / 2) + n - (to2 ? pin(P.split_n) : 0)) * 2;
   }
-  const int ncol = n - (to2 ? pin(P.split_n) : 0);  // output column (plain outputs)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     // stage rows 32i .. 32i+31: lane owns row lane%32 of each group
@@ -168,9 +160,8 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& P, char* smem, i
       for (int g = 0; g < 4; ++g)
         *reinterpret_cast<f32x4*>(stg + c4 * kEpiLd + 32 * j + 8 * g + 4 * rs) =
             (f32x4){acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-    const int mc = m0w + 32 * i;  // first row of the chunk
-    // read back 16 rows per lane (row = 2t + lane/32) in two groups of 8; for
-    // the gated residual, a group's loads are all issued before its stores
+    // read back 16 rows per lane (row 32i + 2t + lane/32) in two groups of 8;
+    // for the gated residual, a group's loads are all issued before its stores
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f32x4 a[8];
@@ -178,61 +169,102 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& P, char* smem, i
       for (int t = 0; t < 8; ++t) a[t] = *reinterpret_cast<const f32x4*>(stg + (2 * (8 * h + t) + rs) * kEpiLd + 4 * c4);
       if constexpr (EPI == EPI_GATE_RES) {
         f32x4 res[8], gt[8];
-        int64_t oo[8];
+        int64_t oo[8];  // byte offsets of the written rows (general case)
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          int m = mc + 2 * (8 * h + t) + rs;
-          const bool ok = m < M && n_ok;
-          m = m < M ? m : M - 1;
-          const int b_o = one_batch ? b_o1 : m / rpb_o, t_o = m - b_o * rpb_o;
-          const int b_i = one_batch ? b_i1 : m / rpb_i, t_i = m - b_i * rpb_i;
-          oo[t] = (int64_t)b_o * bs_o + (int64_t)t_o * ld_o + n;
-          const int64_t oi = (int64_t)b_i * bs_i + (int64_t)t_i * ld_i + n;
-          res[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-          gt[t] = gate1;
-          if (ok) {
-            if (!one_batch) gt[t] = *(gcf32x4*)(gbase + ((int64_t)b_o * gbs + n) * 4);
-            if (f32r) {
-              res[t] = *(gcf32x4*)(ibase + oi * 4);
+          const int r = 32 * i + 2 * (8 * h + t) + rs;  // row within the wave tile
+          if constexpr (FULL) {
+            gt[t] = gate1;
+            if constexpr (f32r) {
+              res[t] = *(gcf32x4*)(ibase + r * ldi);
             } else {
-              const bf16x4 r = *(gcbf16x4*)(ibase + oi * 2);
-              res[t] = (f32x4){(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
+              const bf16x4 v = *(gcbf16x4*)(ibase + r * ldi);
+              res[t] = (f32x4){(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+            }
+          } else {
+            int m = m0w + r;
+            const bool ok = m < M && n_ok;
+            m = m < M ? m : M - 1;
+            const int b_o = m / rpb_o, t_o = m - b_o * rpb_o;
+            const int b_i = m / rpb_i, t_i = m - b_i * rpb_i;
+            const int esz = f32r ? 4 : 2;
+            oo[t] = ((int64_t)b_o * bs_o + (int64_t)t_o * ld_o + n) * esz;
+            const int64_t oi = ((int64_t)b_i * bs_i + (int64_t)t_i * ld_i + n) * esz;
+            res[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            gt[t] = res[t];
+            if (ok) {
+              gt[t] = *(gcf32x4*)(gbase + ((int64_t)b_o * gbs + n) * 4);
+              if constexpr (f32r) {
+                res[t] = *(gcf32x4*)(ibase + oi);
+              } else {
+                const bf16x4 v = *(gcbf16x4*)(ibase + oi);
+                res[t] = (f32x4){(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+              }
             }
           }
         }
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const int m = mc + 2 * (8 * h + t) + rs;
-          if (m >= M || !n_ok) continue;
+          const int r = 32 * i + 2 * (8 * h + t) + rs;
+          if (!FULL && (m0w + r >= M || !n_ok)) continue;
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = res[t][e] + gt[t][e] * (a[t][e] + bias[e]);
-          if (f32r)
-            *(gf32x4*)(obase + oo[t] * 4) = (f32x4){o[0], o[1], o[2], o[3]};
+          gchar* dst = FULL ? obase + r * ld : obase + oo[t];
+          if constexpr (f32r)
+            *(gf32x4*)dst = (f32x4){o[0], o[1], o[2], o[3]};
           else
-            *(gbf16x4*)(obase + oo[t] * 2) = (bf16x4){(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
+            *(gbf16x4*)dst = (bf16x4){(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
         }
       } else {
-        gchar* orow = obase + ((int64_t)(mc + 16 * h + rs) * ldo + ncol) * (f32o ? 4 : 2);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const int m = mc + 2 * (8 * h + t) + rs;
-          gchar* o = orow + (int64_t)(2 * t) * ldo * (f32o ? 4 : 2);
-          if (m >= M || !n_ok) continue;
+          const int r = 32 * i + 2 * (8 * h + t) + rs;
+          if (!FULL && (m0w + r >= M || !n_ok)) continue;
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = a[t][e] + bias[e];
-          if (EPI == EPI_GELU || to2) {
+          if constexpr (EPI == EPI_GELU || to2) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = gelu_fast(v[e]);
           }
-          if (f32o)
-            *(gf32x4*)o = (f32x4){v[0], v[1], v[2], v[3]};
-          else
-            *(gbf16x4*)o = (bf16x4){(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+          *(gbf16x4*)(obase + r * ld) = (bf16x4){(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
         }
       }
     }
+  }
+}
+
+// Epilogue of a wave's 128 x 128 tile, staged through LDS in 32-row chunks
+// (float32, row stride kEpiLd) so that each lane then owns 4 consecutive
+// columns of a row: bias, GELU and the gated residual are applied to 4-column
+// vectors, and each global access instruction covers whole 256-byte row
+// segments. The accumulator holds C transposed per register group:
+// acc[i][j][4g + e] = C[m0w + 32i + lane%32][n0w + 32j + 8g + 4(lane/32) + e],
+// so staging is one 16-byte LDS write per group. The caller has made the LDS
+// free (barrier after the last operand reads); each wave uses its own 17 KB.
+// Column counts and row strides are multiples of 4 (checked before launch):
+// a lane's 4 columns are all in range or all out of range. `bias` holds the
+// lane's 4 columns' bias (loaded by the caller ahead of time). Outputs are
+// bf16 (plain) or bf16 / float32 (gated residual).
+template <int EPI>
+__device__ __forceinline__ void dma_epilogue(const GemmProblem& P, char* smem, int m0w, int n0w, int wave,
+                                             int lane, const f32x16 (&acc)[4][4], int side, const float (&bias)[4]) {
+  float* stg = reinterpret_cast<float*>(smem) + wave * (32 * kEpiLd);
+  bool full = m0w + 128 <= P.M && n0w + 128 <= P.N;
+  if constexpr (EPI == EPI_GATE_RES) {
+    const int rpb_o = P.res_out.rows_per_batch, rpb_i = P.res_in.rows_per_batch;
+    full = full && m0w / rpb_o == (m0w + 127) / rpb_o && m0w / rpb_i == (m0w + 127) / rpb_i;
+  }
+  bool alt = false;
+  if constexpr (EPI == EPI_SPLIT) alt = side == 1;
+  if constexpr (EPI == EPI_GATE_RES) alt = P.res_f32;
+  if (full) {
+    if (alt) dma_epilogue_impl<EPI, true, true>(P, stg, m0w, n0w, lane, acc, bias);
+    else dma_epilogue_impl<EPI, true, false>(P, stg, m0w, n0w, lane, acc, bias);
+  } else {
+    if (alt) dma_epilogue_impl<EPI, false, true>(P, stg, m0w, n0w, lane, acc, bias);
+    else dma_epilogue_impl<EPI, false, false>(P, stg, m0w, n0w, lane, acc, bias);
   }
 }
 
@@ -571,7 +603,7 @@ bool gemm_dma_eligible(const GemmProblem* p, int nprob, int epi) {
           !aligned(q.gate, 16) || q.res_in.rows_per_batch <= 0 || q.res_out.rows_per_batch <= 0)
         return false;
     } else {
-      if (q.ldo % 4 || !aligned(q.out, q.out_f32 && epi == EPI_STORE ? 16 : 8)) return false;
+      if (q.out_f32 || q.ldo % 4 || !aligned(q.out, 8)) return false;  // bf16 outputs only
       if (epi == EPI_SPLIT && (q.split_n % kDBN != 0 || q.ldo2 % 4 || !aligned(q.out2, 8))) return false;
     }
     tiles += (int64_t)((q.M + kDBM - 1) / kDBM) * ((q.N + kDBN - 1) / kDBN);
