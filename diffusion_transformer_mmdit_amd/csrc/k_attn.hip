@@ -25,7 +25,14 @@ namespace mmdit {
 constexpr int kAttnQ = 128;   // queries per block
 constexpr int kAttnK = 64;    // keys per tile
 constexpr int kKPad = 136;    // K tile row stride (elements)
-constexpr int kVPadT = 68;    // V^T tile row stride (elements)
+constexpr int kVPadT = 72;    // V^T tile row stride (elements): 16-byte aligned rows
+
+// Position of key k (within a 64-key tile) in a V^T tile row: bits 2 and 3
+// swapped, i.e. within each group of 16 keys the order is 0-3, 8-11, 4-7,
+// 12-15.
+__device__ __forceinline__ int vkey_pos(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
 
 __device__ __forceinline__ bf16* out_row(const AttnArgs& a, int b, int t) {
   const int s = t < a.seg_len0 ? 0 : 1;
@@ -68,11 +75,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int c = tid + i * 256;
       *reinterpret_cast<bf16x8*>(&Ks[buf][(c >> 4) * kKPad + (c & 15) * 8]) = rk[i];
-      bf16* vd = &Vs[buf][(c >> 3) * kVPadT + (c & 7) * 8];
+      // keys are stored with bits 2 and 3 of their index swapped, so the 8
+      // keys one lane feeds to the P.V MFMA are contiguous (one 16-byte read)
+      bf16* vd = &Vs[buf][(c >> 3) * kVPadT];
+      const int k0 = (c & 7) * 8;  // first key of this 8-key chunk
       bf16x4 lo = {rv[i][0], rv[i][1], rv[i][2], rv[i][3]};
       bf16x4 hi = {rv[i][4], rv[i][5], rv[i][6], rv[i][7]};
-      *reinterpret_cast<bf16x4*>(vd) = lo;
-      *reinterpret_cast<bf16x4*>(vd + 4) = hi;
+      *reinterpret_cast<bf16x4*>(vd + vkey_pos(k0)) = lo;
+      *reinterpret_cast<bf16x4*>(vd + vkey_pos(k0 + 4)) = hi;
     }
   };
 
@@ -141,10 +151,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 4; ++kb2) {
-        const bf16* vp = &Vs[cur][(db * 32 + l32) * kVPadT + 16 * kb2 + 4 * g];
-        bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vp);
-        bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vp + 8);
-        bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        // keys 16 kb2 + 4g + {0..3} and 16 kb2 + 8 + 4g + {0..3}, stored contiguously
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[cur][(db * 32 + l32) * kVPadT + 16 * kb2 + 8 * g]);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb2], o[db], 0, 0, 0);
       }
     }

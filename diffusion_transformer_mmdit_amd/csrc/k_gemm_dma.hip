@@ -412,6 +412,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
       for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
 
+  // bias of this lane's epilogue columns (requested now, used at the end)
+  float ebias[4] = {0.f, 0.f, 0.f, 0.f};
+  {
+    const bf16* bp = reinterpret_cast<const bf16*>(P.bias);
+    const int n = n0 + wn0 + 4 * (lane & 31);
+    if (bp && n < N) {
+      const bf16x4 v = *reinterpret_cast<const bf16x4*>(bp + n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ebias[e] = (float)v[e];
+    }
+  }
+
   const int nk = K / BK;
   if constexpr (FMT == 0) {
     // Prologue: one k-tile per stage requested; wait for k-tile 0.
@@ -499,17 +511,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
     }
     if constexpr (FMT != 0) {
       if (more) load_braw(kt + S);
-    }
-  }
-  // bias of this lane's epilogue columns, requested before the last k-tile's MFMAs
-  float ebias[4] = {0.f, 0.f, 0.f, 0.f};
-  {
-    const bf16* bp = reinterpret_cast<const bf16*>(P.bias);
-    const int n = n0 + wn0 + 4 * (lane & 31);
-    if (bp && n < N) {
-      const bf16x4 v = *reinterpret_cast<const bf16x4*>(bp + n);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ebias[e] = (float)v[e];
     }
   }
   // Last k-tile; column-major MFMA order keeps this tail distinct from the
