@@ -570,18 +570,38 @@ int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, 
   if ((r = gemv(c, w->time_in1, hid, true, h, vec, h, true, false))) return r;
   if ((r = gemv(c, w->vec_in0, y, false, cfg->vec_in_dim, hid, h, false, false))) return r;
   if ((r = gemv(c, w->vec_in1, hid, true, h, vec, h, true, true))) return r;
-  // every block's modulation up front
-  for (int i = 0; i < cfg->n_double; ++i) {
-    float* md = mods + lay.mod_dual + (size_t)i * 2 * B * 6 * h;
-    if ((r = gemv(c, w->dbl[i].txt.mod, vec, true, h, md, 6 * h, true, false))) return r;
-    if ((r = gemv(c, w->dbl[i].img.mod, vec, true, h, md + (size_t)B * 6 * h, 6 * h, true, false))) return r;
+  // every block's modulation up front, all from SiLU(vec): batched into
+  // launches of up to kGemvMaxSeg weight matrices
+  {
+    GemvMultiArgs ga{};
+    ga.x = vec; ga.K = h; ga.B = B; ga.x_bstride = h;
+    double bytes = 0;
+    auto flush = [&]() -> int {
+      if (ga.nseg == 0) return MMDIT_OK;
+      ProfScope ps(PC_GEMV, bytes, c.s);
+      HIP_TRY(launch_gemv_multi(ga, g.bf16, c.s));
+      ga.nseg = 0;
+      bytes = 0;
+      return MMDIT_OK;
+    };
+    auto add = [&](const mmdit_linear& l, float* y, int y_bstride) -> int {
+      if (B > kGemvMaxB) return gemv(c, l, vec, true, h, y, y_bstride, true, false);
+      GemvSeg& sg = ga.seg[ga.nseg++];
+      sg.W = l.w; sg.bias = l.bias; sg.y = y; sg.N = l.n_out; sg.y_bstride = y_bstride;
+      bytes += (double)l.n_out * l.k_in * g.esz;
+      return ga.nseg == kGemvMaxSeg ? flush() : MMDIT_OK;
+    };
+    for (int i = 0; i < cfg->n_double; ++i) {
+      float* md = mods + lay.mod_dual + (size_t)i * 2 * B * 6 * h;
+      if ((r = add(w->dbl[i].txt.mod, md, 6 * h))) return r;
+      if ((r = add(w->dbl[i].img.mod, md + (size_t)B * 6 * h, 6 * h))) return r;
+    }
+    for (int i = 0; i < cfg->n_single; ++i) {
+      if ((r = add(w->sgl[i].mod, mods + lay.mod_single + (size_t)i * B * 3 * h, 3 * h))) return r;
+    }
+    if ((r = add(w->final_mod, mods + lay.mod_final, 2 * h))) return r;
+    if ((r = flush())) return r;
   }
-  for (int i = 0; i < cfg->n_single; ++i) {
-    float* ms = mods + lay.mod_single + (size_t)i * B * 3 * h;
-    if ((r = gemv(c, w->sgl[i].mod, vec, true, h, ms, 3 * h, true, false))) return r;
-  }
-  float* mf = mods + lay.mod_final;
-  if ((r = gemv(c, w->final_mod, vec, true, h, mf, 2 * h, true, false))) return r;
   if ((r = rope(c, &cfg->dims, ids, table))) return r;
 
   // input projections into the f32 residual
@@ -629,7 +649,7 @@ int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, 
   }
   // final layer on the image rows, Euler update fused into the epilogue
   Part fin = parts[1];
-  fin.mod = mf;
+  fin.mod = mods + lay.mod_final;
   void* xn = ptr(ws, lay.blk.xn);
   if ((r = run_ln(c, &fin, 1, 2 * h, 0, h, true, xn))) return r;
   GemmProblem f = base_problem(w->final_lin);

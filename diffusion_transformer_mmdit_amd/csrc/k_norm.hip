@@ -262,24 +262,25 @@ hipError_t launch_rope_table(const int32_t* ids, int L, int a0, int a1, int a2, 
 // staged in LDS as float32 (after SiLU); each wavefront reduces two weight
 // rows at a time with 16-byte loads along K. Up to 4 batch rows per launch.
 constexpr int kGemvRowsPerWave = 2;
-constexpr int kGemvMaxB = 4;
 
-template <typename TW, typename TX>
-__global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
-  extern __shared__ float xs[];  // [B, K]
-  const int K = a.K;
-  for (int i = threadIdx.x; i < a.B * K; i += 256) {
+// Stages f(x) (SiLU or identity, float32) for B batch rows into LDS.
+template <typename TX>
+__device__ __forceinline__ void gemv_stage_x(float* xs, const void* x, int B, int K, int x_bstride, bool silu) {
+  for (int i = threadIdx.x; i < B * K; i += 256) {
     const int bb = i / K, k = i - bb * K;
-    float v = to_f32(reinterpret_cast<const TX*>(a.x)[(int64_t)bb * a.x_bstride + k]);
-    xs[i] = a.silu_in ? silu_f<true>(v) : v;
+    float v = to_f32(reinterpret_cast<const TX*>(x)[(int64_t)bb * x_bstride + k]);
+    xs[i] = silu ? silu_f<true>(v) : v;
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int n0 = (blockIdx.x * 4 + wave) * kGemvRowsPerWave;
+}
+
+// Rows n0 .. n0 + kGemvRowsPerWave - 1 of y[b, :] (+)= bias + W f(x[b, :]) for
+// one wavefront; f(x) is staged in LDS.
+template <typename TW>
+__device__ __forceinline__ void gemv_rows(const float* xs, const TW* W, const TW* bias, float* y, int N, int K, int B,
+                                          int y_bstride, bool accumulate, int n0, int lane) {
   constexpr int VEC = 16 / sizeof(TW);
   const int nchunk = K / VEC;
-  const TW* W = reinterpret_cast<const TW*>(a.W);
   float acc[kGemvRowsPerWave][kGemvMaxB];
 #pragma unroll
   for (int r = 0; r < kGemvRowsPerWave; ++r)
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
     for (int r = 0; r < kGemvRowsPerWave; ++r) {
       const int n = n0 + r;
-      if (n < a.N) {
+      if (n < N) {
         if constexpr (VEC == 8) load8(W + (int64_t)n * K + c * VEC, w[r]);
         else load4(W + (int64_t)n * K + c * VEC, w[r]);
       } else {
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     }
 #pragma unroll
     for (int bb = 0; bb < kGemvMaxB; ++bb) {
-      if (bb < a.B) {
+      if (bb < B) {
         const float* xv = xs + bb * K + c * VEC;
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
@@ -317,13 +318,56 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     for (int bb = 0; bb < kGemvMaxB; ++bb) {
       const float v = wave_sum(acc[r][bb]);
       const int n = n0 + r;
-      if (lane == 0 && bb < a.B && n < a.N) {
-        float o = v + (a.bias ? to_f32(reinterpret_cast<const TW*>(a.bias)[n]) : 0.f);
-        float* dst = a.y + (int64_t)bb * a.y_bstride + n;
-        *dst = a.accumulate ? *dst + o : o;
+      if (lane == 0 && bb < B && n < N) {
+        float o = v + (bias ? to_f32(bias[n]) : 0.f);
+        float* dst = y + (int64_t)bb * y_bstride + n;
+        *dst = accumulate ? *dst + o : o;
       }
     }
   }
+}
+
+template <typename TW, typename TX>
+__global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
+  extern __shared__ float xs[];  // [B, K]
+  gemv_stage_x<TX>(xs, a.x, a.B, a.K, a.x_bstride, a.silu_in);
+  const int lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kGemvRowsPerWave;
+  gemv_rows<TW>(xs, reinterpret_cast<const TW*>(a.W), reinterpret_cast<const TW*>(a.bias), a.y, a.N, a.K, a.B,
+                a.y_bstride, a.accumulate, n0, lane);
+}
+
+// Several GEMVs over the same input in one launch (float32 x, SiLU applied):
+// block b serves the segment whose block range holds b.
+template <typename TW>
+__global__ __launch_bounds__(256) void k_gemv_multi(GemvMultiArgs a) {
+  extern __shared__ float xs[];  // [B, K]
+  int sg = 0;
+  for (int i = 1; i < a.nseg; ++i)
+    if ((int)blockIdx.x >= a.seg[i].block0) sg = i;
+  const GemvSeg& g = a.seg[sg];
+  gemv_stage_x<float>(xs, a.x, a.B, a.K, a.x_bstride, true);
+  const int lane = threadIdx.x & 63;
+  const int n0 = (((int)blockIdx.x - g.block0) * 4 + (threadIdx.x >> 6)) * kGemvRowsPerWave;
+  gemv_rows<TW>(xs, reinterpret_cast<const TW*>(g.W), reinterpret_cast<const TW*>(g.bias), g.y, g.N, a.K, a.B,
+                g.y_bstride, false, n0, lane);
+}
+
+hipError_t launch_gemv_multi(const GemvMultiArgs& a0, bool w_bf16, hipStream_t s) {
+  GemvMultiArgs a = a0;
+  int blocks = 0;
+  const int rows_per_block = 4 * kGemvRowsPerWave;
+  for (int i = 0; i < a.nseg; ++i) {
+    a.seg[i].block0 = blocks;
+    blocks += (a.seg[i].N + rows_per_block - 1) / rows_per_block;
+  }
+  if (blocks == 0) return hipSuccess;
+  const size_t lds = (size_t)a.B * a.K * sizeof(float);
+  if (w_bf16)
+    hipLaunchKernelGGL((k_gemv_multi<bf16>), dim3(blocks), dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL((k_gemv_multi<float>), dim3(blocks), dim3(256), lds, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv(const GemvArgs& a0, bool w_bf16, bool x_f32, hipStream_t s) {

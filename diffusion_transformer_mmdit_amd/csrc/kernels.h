@@ -73,6 +73,24 @@ struct GemvArgs {
   bool silu_in, accumulate;
 };
 hipError_t launch_gemv(const GemvArgs& a, bool w_bf16, bool x_f32, hipStream_t s);
+// Up to kGemvMaxSeg GEMVs sharing one float32 input (SiLU applied), B <= 4
+// batch rows, one launch: y_s[b, :] = bias_s + W_s SiLU(x[b, :]).
+constexpr int kGemvMaxSeg = 24;
+constexpr int kGemvMaxB = 4;  // batch rows per GEMV launch
+struct GemvSeg {
+  const void* W;
+  const void* bias;
+  float* y;  // [B, y_bstride]
+  int32_t N, y_bstride;
+  int32_t block0;  // set by the launcher
+};
+struct GemvMultiArgs {
+  const void* x;  // float32 [B, x_bstride]
+  int32_t K, B, x_bstride;
+  int32_t nseg;
+  GemvSeg seg[kGemvMaxSeg];
+};
+hipError_t launch_gemv_multi(const GemvMultiArgs& a, bool w_bf16, hipStream_t s);
 
 // ---- sinusoidal timestep embedding: t[b, i], tau = 1000 * sigma ---------------
 hipError_t launch_timestep_embedding(float* out, int B, int dim, double sigma, hipStream_t s);
