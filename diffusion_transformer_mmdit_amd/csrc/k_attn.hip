@@ -7,14 +7,20 @@
 // bf16 path (flash attention, gfx950 MFMA 32x32x16):
 //  * a block owns 128 queries of one (batch, head); each of its 4 wavefronts
 //    owns 32 queries; K and V^T tiles of 64 keys are staged in LDS, double
-//    buffered, and shared by the 4 wavefronts;
+//    buffered, and shared by the 4 wavefronts. They arrive by direct-to-LDS
+//    loads (global_load_lds_dwordx4: no registers, no LDS store
+//    instructions), issued one tile ahead;
+//  * LDS rows are stored with their 16-byte chunks XOR-swizzled by the row
+//    index, so the MFMA operand reads (one 16-byte read per lane) of 16
+//    consecutive rows hit distinct banks;
 //  * S^T = K Q^T is computed so that each lane holds the scores of ONE query
-//    (its MFMA column): the running max needs one cross-lane exchange and the
-//    running sum none until the end;
+//    (its MFMA column): the running max needs one cross-lane exchange;
 //  * the probabilities stay in registers and feed O^T += V^T P^T directly as
-//    the MFMA B operand: no LDS round trip for P. V arrives transposed
-//    ([d, token]) from the QK-norm kernel so the A operand reads are 8-byte
-//    row segments;
+//    the MFMA B operand. V^T arrives from the QK-norm kernel with its tokens
+//    in vkey_pos order, so each lane's 8 keys are one contiguous 16 bytes;
+//  * the softmax denominator is produced by the MFMA too: a fifth output
+//    block multiplies P^T by a matrix of ones, so every row of it holds the
+//    running sum of the (bf16) probabilities, with no per-score adds;
 //  * online softmax in float32 with exp2 of log2(e)-scaled scores; the
 //    running max is moved only when it grows by more than 2^8.
 #include "common.h"
@@ -24,15 +30,9 @@ namespace mmdit {
 
 constexpr int kAttnQ = 128;   // queries per block
 constexpr int kAttnK = 64;    // keys per tile
-constexpr int kKPad = 136;    // K tile row stride (elements)
-constexpr int kVPadT = 72;    // V^T tile row stride (elements): 16-byte aligned rows
-
-// Position of key k (within a 64-key tile) in a V^T tile row: bits 2 and 3
-// swapped, i.e. within each group of 16 keys the order is 0-3, 8-11, 4-7,
-// 12-15.
-__device__ __forceinline__ int vkey_pos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
+constexpr int kKBuf = kAttnK * 256;  // bytes of a K tile (64 rows x 256 B)
+constexpr int kVBuf = 128 * 128;     // bytes of a V^T tile (128 rows x 128 B)
+constexpr int kStage = kKBuf + kVBuf;
 
 __device__ __forceinline__ bf16* out_row(const AttnArgs& a, int b, int t) {
   const int s = t < a.seg_len0 ? 0 : 1;
@@ -41,18 +41,26 @@ __device__ __forceinline__ bf16* out_row(const AttnArgs& a, int b, int t) {
   return reinterpret_cast<bf16*>(g.base) + (int64_t)b * g.batch_stride + (int64_t)local_t * g.ld;
 }
 
+// 64 lanes each copy 16 bytes from base + voff to LDS at m0_base + 16 * lane.
+__device__ __forceinline__ void attn_dma16(const void* base, uint32_t voff, uint32_t m0_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(m0_base), "v"(voff), "s"(base) : "memory", "m0");
+}
+
+// LDS layouts (one stage): K tile row r (key) at r*256, 16-byte chunk c
+// (dims 8c..8c+7) at position c ^ (r & 15); V^T tile row r (dim) at
+// kKBuf + r*128, chunk c (positions 8c..8c+7) at c ^ ((r >> 1) & 7).
 __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
-  __shared__ bf16 Ks[2][kAttnK * kKPad];
-  __shared__ bf16 Vs[2][128 * kVPadT];
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 5, l32 = lane & 31;
   const int q0 = blockIdx.x * kAttnQ;
   const int hh = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * a.H + hh;
   const bf16* Qh = reinterpret_cast<const bf16*>(a.Q) + bh * a.Lpad * 128;
-  const bf16* Kh = reinterpret_cast<const bf16*>(a.K) + bh * a.Lpad * 128;
-  const bf16* Vh = reinterpret_cast<const bf16*>(a.V) + bh * 128 * (int64_t)a.Lpad;
+  const char* Kh = reinterpret_cast<const char*>(a.K) + bh * a.Lpad * 128 * 2;
+  const char* Vh = reinterpret_cast<const char*>(a.V) + bh * 128 * (int64_t)a.Lpad * 2;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
 
   // Q as the B operand of S^T = K Q^T: column = query, 8 consecutive dims.
   const int qrow = q0 + wave * 32 + l32;
@@ -60,55 +68,78 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qrow * 128 + kk * 16 + g * 8);
 
-  const int ntiles = (a.L + kAttnK - 1) / kAttnK;
-  bf16x8 rk[4], rv[4];
-  auto load_tile = [&](int kt) {
+  // Direct-to-LDS requests of one tile: this wave's 4 K and 4 V^T
+  // instructions; lane i of instruction j fills LDS slot j*64 + i.
+  uint32_t koff[4], voff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      rk[i] = *reinterpret_cast<const bf16x8*>(Kh + ((int64_t)kt * kAttnK + (c >> 4)) * 128 + (c & 15) * 8);
-      rv[i] = *reinterpret_cast<const bf16x8*>(Vh + (int64_t)(c >> 3) * a.Lpad + kt * kAttnK + (c & 7) * 8);
+  for (int j = 0; j < 4; ++j) {
+    const int jj = wave * 4 + j;
+    {  // K: row r = 4 jj + lane/16, slot lane%16 holds chunk (slot ^ (r & 15))
+      const int r = jj * 4 + (lane >> 4);
+      const int c = (lane & 15) ^ (r & 15);
+      koff[j] = (uint32_t)((r * 128 + c * 8) * 2);
     }
-  };
-  auto store_tile = [&](int buf) {
+    {  // V^T: row r = 8 jj + lane/8, slot lane%8 holds chunk (slot ^ ((r >> 1) & 7))
+      const int r = jj * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      voff[j] = (uint32_t)(r * a.Lpad * 2 + c * 16);
+    }
+  }
+  auto issue_tile = [&](int kt, int buf) {
+    const uint32_t st = lds0 + (uint32_t)(buf * kStage);
+    const char* kb = Kh + (size_t)kt * kAttnK * 256;
+    const char* vb = Vh + (size_t)kt * kAttnK * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      *reinterpret_cast<bf16x8*>(&Ks[buf][(c >> 4) * kKPad + (c & 15) * 8]) = rk[i];
-      // keys are stored with bits 2 and 3 of their index swapped, so the 8
-      // keys one lane feeds to the P.V MFMA are contiguous (one 16-byte read)
-      bf16* vd = &Vs[buf][(c >> 3) * kVPadT];
-      const int k0 = (c & 7) * 8;  // first key of this 8-key chunk
-      bf16x4 lo = {rv[i][0], rv[i][1], rv[i][2], rv[i][3]};
-      bf16x4 hi = {rv[i][4], rv[i][5], rv[i][6], rv[i][7]};
-      *reinterpret_cast<bf16x4*>(vd + vkey_pos(k0)) = lo;
-      *reinterpret_cast<bf16x4*>(vd + vkey_pos(k0 + 4)) = hi;
+    for (int j = 0; j < 4; ++j) {
+      attn_dma16(kb, koff[j], st + (uint32_t)((wave * 4 + j) * 1024));
+      attn_dma16(vb, voff[j], st + (uint32_t)(kKBuf + (wave * 4 + j) * 1024));
     }
   };
 
-  f32x16 o[4];
+  // Per-lane LDS read offsets: K fragment (row kb*32 + l32, chunk 2kk + g),
+  // V^T fragment (row db*32 + l32, chunk 2kb2 + g); the swizzle depends only
+  // on l32, the block offsets (kb, db) are immediates.
+  uint32_t kro[8], vro[4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
+  for (int kk = 0; kk < 8; ++kk) kro[kk] = (uint32_t)(l32 * 256 + (((2 * kk + g) ^ (l32 & 15)) * 16));
+#pragma unroll
+  for (int kb2 = 0; kb2 < 4; ++kb2)
+    vro[kb2] = (uint32_t)(kKBuf + l32 * 128 + (((2 * kb2 + g) ^ ((l32 >> 1) & 7)) * 16));
+
+  // o[0..3]: O^T blocks of 32 dims; o[4]: P^T times ones (row sums)
+  f32x16 o[5];
+#pragma unroll
+  for (int db = 0; db < 5; ++db) o[db] = (f32x16){};
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.0f;
   // Scores never hold NaN here; the file is built with -fno-honor-nans so
   // fmaxf needs no canonicalisation. kNegBig stands for minus infinity.
   constexpr float kNegBig = -1e30f;
-  float m_run = kNegBig, l_run = 0.f;
+  float m_run = kNegBig;
   const float c2 = a.scale * 1.4426950408889634f;  // scale * log2(e)
 
-  // One 64-key tile. mask: the tile reaches past L (only the last one can).
-  // The running max m_run is moved only when some lane's tile max exceeds it
-  // by more than 2^8 (log2 units): p = exp2(s - m_run) then stays below 256,
-  // and p, l and O all use the same m_run, so the result is exact.
+  // One 64-key tile in stage `cur`. mask: the tile reaches past L (only the
+  // last one can). The running max m_run is moved only when some lane's tile
+  // max exceeds it by more than 2^8 (log2 units): p = exp2(s - m_run) then
+  // stays below 256, and p and O (including the row sums) use the same
+  // m_run, so the result is exact.
   auto tile = [&](int kt, int cur, bool mask) {
+    const char* st = smem + cur * kStage;
     f32x16 s[2];
+    s[0] = (f32x16){};
+    s[1] = (f32x16){};
+    bf16x8 kf[2][2];
+    kf[0][0] = *reinterpret_cast<const bf16x8*>(st + kro[0]);
+    kf[0][1] = *reinterpret_cast<const bf16x8*>(st + kro[0] + 32 * 256);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = (f32x16){};
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[cur][(kb * 32 + l32) * kKPad + kk * 16 + g * 8]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
+    for (int kk = 0; kk < 8; ++kk) {
+      if (kk + 1 < 8) {
+        kf[(kk + 1) & 1][0] = *reinterpret_cast<const bf16x8*>(st + kro[kk + 1]);
+        kf[(kk + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(st + kro[kk + 1] + 32 * 256);
       }
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk & 1][0], qf[kk], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk & 1][1], qf[kk], s[1], 0, 0, 0);
     }
     // s[kb][r] = score(query l32, key kt*64 + kb*32 + 8*(r/4) + 4*g + r%4)
     if (__builtin_expect(mask, 0)) {
@@ -120,57 +151,55 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
           if (key >= a.L) s[kb][r] = kNegBig;
         }
     }
-    float mx = fmaxf(s[0][0], s[0][1]);
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[0][r], s[0][r + 1]));
+    for (int r = 3; r < 15; r += 2) mx = fmaxf(mx, fmaxf(s[0][r], s[0][r + 1]));
+    mx = fmaxf(mx, fmaxf(s[0][15], s[1][0]));
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[1][r], s[1][r + 1]));
+    for (int r = 1; r < 15; r += 2) mx = fmaxf(mx, fmaxf(s[1][r], s[1][r + 1]));
+    mx = fmaxf(mx, s[1][15]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
     if (__any(mx > m_run + 8.0f)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      for (int db = 0; db < 5; ++db) o[db] *= alpha;
       m_run = m_new;
     }
-    float psum = 0.f;
     bf16x8 pb[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -m_run));
-        psum += p;
-        pb[kb * 2 + (r >> 3)][r & 7] = (bf16)p;
-      }
-    }
-    l_run += psum;
-    // O^T += V^T P^T; MFMA kb2 covers keys 16*kb2 + 8*(i/4) + 4*g + i%4
+      for (int r = 0; r < 16; ++r)
+        pb[kb * 2 + (r >> 3)][r & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -m_run));
+    // O^T += V^T P^T; MFMA kb2 covers keys 16*kb2 + 8*(i/4) + 4*g + i%4,
+    // stored contiguously; o[4] += ones P^T
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
+      bf16x8 va[4];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 4; ++kb2) {
-        // keys 16 kb2 + 4g + {0..3} and 16 kb2 + 8 + 4g + {0..3}, stored contiguously
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[cur][(db * 32 + l32) * kVPadT + 16 * kb2 + 8 * g]);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb2], o[db], 0, 0, 0);
-      }
+      for (int kb2 = 0; kb2 < 4; ++kb2) va[kb2] = *reinterpret_cast<const bf16x8*>(st + vro[kb2] + db * 32 * 128);
+#pragma unroll
+      for (int kb2 = 0; kb2 < 4; ++kb2) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb2], pb[kb2], o[db], 0, 0, 0);
     }
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2) o[4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[kb2], o[4], 0, 0, 0);
   };
 
-  load_tile(0);
-  store_tile(0);
+  const int ntiles = (a.L + kAttnK - 1) / kAttnK;
+  issue_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 (and Q) landed
   __syncthreads();
   const bool ragged = (a.L % kAttnK) != 0;
   for (int kt = 0; kt < ntiles; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < ntiles) load_tile(kt + 1);
+    if (kt + 1 < ntiles) issue_tile(kt + 1, cur ^ 1);  // its stage was freed by the last barrier
     tile(kt, cur, ragged && kt == ntiles - 1);
-    if (kt + 1 < ntiles) store_tile(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile kt+1 landed
     __syncthreads();
   }
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l_tot;
+  // every row of o[4] holds this lane's query's probability sum
+  const float inv = 1.0f / o[4][0];
   if (qrow < a.L) {
     bf16* dst = out_row(a, b, qrow) + hh * 128;
 #pragma unroll
@@ -187,8 +216,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
 }
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s) {
+  // K/V byte offsets from the per-(batch, head) base are 32-bit
+  if ((int64_t)a.Lpad * 128 * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   dim3 grid(a.Lpad / kAttnQ, a.H, a.B), block(256);
-  hipLaunchKernelGGL(k_attn_bf16, grid, block, 0, s, a);
+  const size_t lds = 2 * kStage;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_attn_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_attn_bf16, grid, block, lds, s, a);
   return hipGetLastError();
 }
 

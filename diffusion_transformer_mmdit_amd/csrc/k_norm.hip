@@ -201,7 +201,8 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
       for (int i = 0; i < 8; ++i) vs[tl * kVPad + d0 + i] = bf16(xv[p][i]);
     }
     __syncthreads();
-    // Vt[b, hh, d, t0 .. t0+63]: 128 rows of 64 tokens, 8 tokens per thread
+    // Vt[b, hh, d, t0 .. t0+63]: 128 rows of 64 tokens, 8 positions per
+    // thread; position p holds token vkey_pos(p) (t0 is a multiple of 16)
     bf16* Vt = reinterpret_cast<bf16*>(a.V) + head_off;
 #pragma unroll
     for (int c = tid; c < 128 * (kQkTile / 8); c += 256) {
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
       if (t0 + tc < a.Lpad) {
         bf16x8 o;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = vs[(tc + i) * kVPad + d];
+        for (int i = 0; i < 8; ++i) o[i] = vs[vkey_pos(tc + i) * kVPad + d];
         *reinterpret_cast<bf16x8*>(Vt + (int64_t)d * a.Lpad + t0 + tc) = o;
       }
     }

@@ -147,10 +147,17 @@ hipError_t launch_gemm_f32(const GemmProblem* p, int nprob, int epi, hipStream_t
 // ---- joint attention ------------------------------------------------------------
 // O rows: token t of batch b goes to seg[0] row (b, t) if t < seg_len0 else
 // seg[1] row (b, t - seg_len0), at column offset head * d.
+// Token order inside V^T rows (bf16 path): within each aligned group of 16
+// tokens, position p holds token vkey_pos(p) (bits 2 and 3 of the index
+// swapped; the map is its own inverse), so that the 8 keys one lane feeds to
+// the P.V MFMA (keys 4g..4g+3 and 8+4g..8+4g+3 of a 16-key step) are
+// contiguous.
+__host__ __device__ inline int vkey_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
 struct AttnArgs {
-  const void* Q;
-  const void* K;
-  const void* V;
+  const void* Q;  // [B, H, Lpad, 128]
+  const void* K;  // [B, H, Lpad, 128]
+  const void* V;  // bf16: V^T [B, H, 128, Lpad] in vkey_pos token order; f32: [B, H, Lpad, 128]
   RowSeg out[2];
   int32_t seg_len0;
   int32_t B, H, L, Lpad;
