@@ -129,18 +129,23 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
     f32x16 s[2];
     s[0] = (f32x16){};
     s[1] = (f32x16){};
-    bf16x8 kf[2][2];
-    kf[0][0] = *reinterpret_cast<const bf16x8*>(st + kro[0]);
-    kf[0][1] = *reinterpret_cast<const bf16x8*>(st + kro[0] + 32 * 256);
+    // all 16 K fragments requested up front: one LDS latency per tile
+    bf16x8 kf[8][2];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      if (kk + 1 < 8) {
-        kf[(kk + 1) & 1][0] = *reinterpret_cast<const bf16x8*>(st + kro[kk + 1]);
-        kf[(kk + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(st + kro[kk + 1] + 32 * 256);
-      }
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk & 1][0], qf[kk], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk & 1][1], qf[kk], s[1], 0, 0, 0);
+      kf[kk][0] = *reinterpret_cast<const bf16x8*>(st + kro[kk]);
+      kf[kk][1] = *reinterpret_cast<const bf16x8*>(st + kro[kk] + 32 * 256);
     }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk][0], qf[kk], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk][1], qf[kk], s[1], 0, 0, 0);
+    }
+    // keep that order: the scheduler would otherwise pull each read next to
+    // its MFMA and wait on it
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // 16 LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // 16 MFMAs
+    __builtin_amdgcn_sched_barrier(0);
     // s[kb][r] = score(query l32, key kt*64 + kb*32 + 8*(r/4) + 4*g + r%4)
     if (__builtin_expect(mask, 0)) {
 #pragma unroll
