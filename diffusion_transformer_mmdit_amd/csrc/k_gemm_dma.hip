@@ -320,6 +320,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
     }
   }
   // DMA instruction q (0 .. G-1) of k-tile kt: q < NJ for A, else B.
+  // request q of k-tile `src` into the stage of k-tile `dst` (src == dst
+  // except for the harmless re-reads described at the main loop)
+  auto dma_to = [&](int src, int dst, int q) {
+    const uint32_t st = lds0 + (uint32_t)((dst % S) * STAGE);
+    const size_t koff = (size_t)src * BK * 2;
+    if (q < NJ) dma16<CPOL>(abase + koff, aoffg[q], st + (uint32_t)((wave * NJ + q) * 1024));
+    else if constexpr (FMT == 0)
+      dma16<CPOL>(bbase + koff, boffg[q - NJ], st + HALF + (uint32_t)((wave * NJ + q - NJ) * 1024));
+  };
   auto dma_one = [&](int kt, int q) {
     const uint32_t st = lds0 + (uint32_t)((kt % S) * STAGE);
     const size_t koff = (size_t)kt * BK * 2;
@@ -425,7 +434,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
   }
 
   const int nk = K / BK;
-  if constexpr (FMT == 0) {
+  constexpr int DSP = FMT == 0 ? DS : 1;
+  constexpr int PER = (G + DSP - 1) / DSP;  // requests per substep
+  // Dense operands, 2 stages: the loop issues every request unconditionally
+  // (no branch per request). Requests past the last k-tile re-read k-tile
+  // nk-1 into a stage that is never read again; the prologue issues only the
+  // first PER requests of k-tile 1, and iteration 0 continues them exactly as
+  // every later iteration continues the previous one's.
+  constexpr bool UNCOND = FMT == 0 && S == 2;
+  if constexpr (UNCOND) {
+    issue(0);
+    const int k1 = nk > 1 ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) dma_to(k1, 1, q);
+    wait_vm(PER);
+  } else if constexpr (FMT == 0) {
     // Prologue: one k-tile per stage requested; wait for k-tile 0.
 #pragma unroll
     for (int u = 0; u < S; ++u)
@@ -456,8 +479,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
   // those requests over DS substeps (the last one of k-tile kt and the first
   // DS-1 of k-tile kt+1), so the vector-memory queue never holds a whole
   // k-tile's requests at once and the MFMAs behind them keep issuing.
-  constexpr int DSP = FMT == 0 ? DS : 1;
-  constexpr int PER = (G + DSP - 1) / DSP;  // requests per substep
   static_assert(DSP >= 1 && DSP <= KS, "spread must fit in one k-tile");
   // substep with the MFMAs interleaved: reads of the next fragments behind
   // the first 8 MFMAs, requests q0 .. q1-1 of k-tile dkt behind the first ones.
@@ -471,7 +492,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[j], ca[i], acc[i][j], 0, 0, 0);
         if (u < 4) na[u] = read_a(rkt, rkk, u);
         else if (u < 8) nb[u - 4] = read_b(rkt, rkk, u - 4);
-        if (dma && u < q1 - q0) dma_one(dkt, q0 + u);
+        if constexpr (UNCOND) {
+          if (u < q1 - q0) dma_to(dkt < nk ? dkt : nk - 1, dkt, q0 + u);
+        } else {
+          if (dma && u < q1 - q0) dma_one(dkt, q0 + u);
+        }
       }
     substep_schedule();
   };
@@ -482,7 +507,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
         // continue the requests of k-tile kt-1+S begun in k-tile kt-1
         const int q0 = (kk + 1) * PER, q1 = (kk + 2) * PER < G ? (kk + 2) * PER : G;
         substep_dma(fa[kk & 1], fb[kk & 1], fa[(kk + 1) & 1], fb[(kk + 1) & 1], kt, kk + 1,
-                    kt >= 1 && kt - 1 + S < nk, kt - 1 + S, q0, q1);
+                    (UNCOND || kt >= 1) && kt - 1 + S < nk, kt - 1 + S, q0, q1);
         continue;
       }
       read_frags(kt, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
@@ -525,7 +550,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i], acc[i][j], 0, 0, 0);
   }
 
-  // every wave has finished reading the operand stages: LDS is free
+  // every wave has finished reading the operand stages and no request is
+  // still writing one: LDS is free
+  wait_vm(0);
   __builtin_amdgcn_s_waitcnt(0xC07F);
   barrier();
   const int side = EPI == EPI_SPLIT ? split_side_of(P, n0, kDBN) : 0;
