@@ -67,20 +67,21 @@ __device__ __forceinline__ int swz(int r) {
   else return (r & 7) ^ ((r >> 3) & 1);
 }
 
-// Instruction order of one k-substep (8 fragment reads for the next substep,
-// 16 MFMAs): each read issued right behind an MFMA, so the LDS requests are
+// Instruction order of one k-substep (NR fragment reads for the next substep,
+// NM MFMAs): each read issued right behind an MFMA, so the LDS requests are
 // spread over the first half of the substep and have the second half to
 // return; the scheduler would otherwise pull each read next to its consumer
 // and wait on it. Operand requests (inline asm, ordered with the reads as
 // memory operations) stay behind the read they follow in the source. The
 // fences keep substeps from being merged.
+template <int NR, int NM>
 __device__ __forceinline__ void substep_schedule() {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NR; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -101,18 +102,24 @@ typedef __attribute__((address_space(1))) const f32x4 gcf32x4;
 typedef __attribute__((address_space(1))) bf16x4 gbf16x4;
 typedef __attribute__((address_space(1))) const bf16x4 gcbf16x4;
 
-constexpr int kEpiLd = 132;  // 16-byte writes of 16 consecutive rows hit distinct banks
 
 // FULL: every row and column of the wave tile is in range and (gated
 // residual) all its rows lie in one batch of both residual views, so rows
 // advance by a fixed stride and no per-row checks are needed. ALT: for the
 // split epilogue, the tile lies after the split column (GELU, second
 // output); for the gated residual, the residual is float32.
-template <int EPI, bool FULL, bool ALT>
+template <int EPI, int TN, bool FULL, bool ALT>
 __device__ __forceinline__ void dma_epilogue_impl(const GemmProblem& P, float* stg, int m0w, int n0w, int lane,
-                                                  const f32x16 (&acc)[4][4], const float (&bias)[4]) {
+                                                  const f32x16 (&acc)[4][TN / 32], const float (&bias)[4]) {
+  constexpr int NJF = TN / 32;          // 32-column blocks of the wavefront tile
+  constexpr int LPR = TN / 4;           // lanes per row in the read-back phase
+  constexpr int RPI = 64 / LPR;         // rows per read-back instruction
+  constexpr int RPL = 32 / RPI;         // rows per lane per 32-row chunk
+  constexpr int LD = TN + 4;            // staging row stride (floats)
+  // rows per group of in-flight residual loads (bounded by registers)
+  constexpr int GR = EPI == EPI_GATE_RES && NJF == 2 ? 4 : 8;
   const int M = pin(P.M), N = pin(P.N);
-  const int c4 = lane & 31, rs = lane >> 5;
+  const int c4 = lane % LPR, rs = lane / LPR;
   const int n = n0w + 4 * c4;  // this lane's 4 columns (read-back phase)
   const bool n_ok = FULL || n < N;
   constexpr bool to2 = EPI == EPI_SPLIT && ALT;
@@ -155,24 +162,24 @@ __device__ __forceinline__ void dma_epilogue_impl(const GemmProblem& P, float* s
   for (int i = 0; i < 4; ++i) {
     // stage rows 32i .. 32i+31: lane owns row lane%32 of each group
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJF; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4*>(stg + c4 * kEpiLd + 32 * j + 8 * g + 4 * rs) =
+        *reinterpret_cast<f32x4*>(stg + (lane & 31) * LD + 32 * j + 8 * g + 4 * (lane >> 5)) =
             (f32x4){acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-    // read back 16 rows per lane (row 32i + 2t + lane/32) in two groups of 8;
-    // for the gated residual, a group's loads are all issued before its stores
+    // read back RPL rows per lane (row 32i + RPI t + rs) in groups of GR; for
+    // the gated residual, a group's loads are all issued before its stores
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f32x4 a[8];
+    for (int h = 0; h < RPL / GR; ++h) {
+      f32x4 a[GR];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) a[t] = *reinterpret_cast<const f32x4*>(stg + (2 * (8 * h + t) + rs) * kEpiLd + 4 * c4);
+      for (int t = 0; t < GR; ++t) a[t] = *reinterpret_cast<const f32x4*>(stg + (RPI * (GR * h + t) + rs) * LD + 4 * c4);
       if constexpr (EPI == EPI_GATE_RES) {
-        f32x4 res[8], gt[8];
-        int64_t oo[8];  // byte offsets of the written rows (general case)
+        f32x4 res[GR], gt[GR];
+        int64_t oo[GR];  // byte offsets of the written rows (general case)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int r = 32 * i + 2 * (8 * h + t) + rs;  // row within the wave tile
+        for (int t = 0; t < GR; ++t) {
+          const int r = 32 * i + RPI * (GR * h + t) + rs;  // row within the wave tile
           if constexpr (FULL) {
             gt[t] = gate1;
             if constexpr (f32r) {
@@ -204,8 +211,8 @@ __device__ __forceinline__ void dma_epilogue_impl(const GemmProblem& P, float* s
           }
         }
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int r = 32 * i + 2 * (8 * h + t) + rs;
+        for (int t = 0; t < GR; ++t) {
+          const int r = 32 * i + RPI * (GR * h + t) + rs;
           if (!FULL && (m0w + r >= M || !n_ok)) continue;
           float o[4];
 #pragma unroll
@@ -218,8 +225,8 @@ __device__ __forceinline__ void dma_epilogue_impl(const GemmProblem& P, float* s
         }
       } else {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int r = 32 * i + 2 * (8 * h + t) + rs;
+        for (int t = 0; t < GR; ++t) {
+          const int r = 32 * i + RPI * (GR * h + t) + rs;
           if (!FULL && (m0w + r >= M || !n_ok)) continue;
           float v[4];
 #pragma unroll
@@ -235,23 +242,25 @@ __device__ __forceinline__ void dma_epilogue_impl(const GemmProblem& P, float* s
   }
 }
 
-// Epilogue of a wave's 128 x 128 tile, staged through LDS in 32-row chunks
-// (float32, row stride kEpiLd) so that each lane then owns 4 consecutive
-// columns of a row: bias, GELU and the gated residual are applied to 4-column
-// vectors, and each global access instruction covers whole 256-byte row
-// segments. The accumulator holds C transposed per register group:
+// Epilogue of a wave's 128 x TN tile, staged through LDS in 32-row chunks
+// (float32, row stride TN + 4, so 16-byte writes of 16 consecutive rows hit
+// distinct banks) so that each lane then owns 4 consecutive columns of a row:
+// bias, GELU and the gated residual are applied to 4-column vectors, and each
+// global access instruction covers whole row segments. The accumulator holds
+// C transposed per register group:
 // acc[i][j][4g + e] = C[m0w + 32i + lane%32][n0w + 32j + 8g + 4(lane/32) + e],
 // so staging is one 16-byte LDS write per group. The caller has made the LDS
-// free (barrier after the last operand reads); each wave uses its own 17 KB.
+// free (barrier after the last operand reads); each wave uses its own slice.
 // Column counts and row strides are multiples of 4 (checked before launch):
 // a lane's 4 columns are all in range or all out of range. `bias` holds the
 // lane's 4 columns' bias (loaded by the caller ahead of time). Outputs are
 // bf16 (plain) or bf16 / float32 (gated residual).
-template <int EPI>
+template <int EPI, int TN>
 __device__ __forceinline__ void dma_epilogue(const GemmProblem& P, char* smem, int m0w, int n0w, int wave,
-                                             int lane, const f32x16 (&acc)[4][4], int side, const float (&bias)[4]) {
-  float* stg = reinterpret_cast<float*>(smem) + wave * (32 * kEpiLd);
-  bool full = m0w + 128 <= P.M && n0w + 128 <= P.N;
+                                             int lane, const f32x16 (&acc)[4][TN / 32], int side,
+                                             const float (&bias)[4]) {
+  float* stg = reinterpret_cast<float*>(smem) + wave * (32 * (TN + 4));
+  bool full = m0w + 128 <= P.M && n0w + TN <= P.N;
   if constexpr (EPI == EPI_GATE_RES) {
     const int rpb_o = P.res_out.rows_per_batch, rpb_i = P.res_in.rows_per_batch;
     full = full && m0w / rpb_o == (m0w + 127) / rpb_o && m0w / rpb_i == (m0w + 127) / rpb_i;
@@ -260,11 +269,11 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& P, char* smem, i
   if constexpr (EPI == EPI_SPLIT) alt = side == 1;
   if constexpr (EPI == EPI_GATE_RES) alt = P.res_f32;
   if (full) {
-    if (alt) dma_epilogue_impl<EPI, true, true>(P, stg, m0w, n0w, lane, acc, bias);
-    else dma_epilogue_impl<EPI, true, false>(P, stg, m0w, n0w, lane, acc, bias);
+    if (alt) dma_epilogue_impl<EPI, TN, true, true>(P, stg, m0w, n0w, lane, acc, bias);
+    else dma_epilogue_impl<EPI, TN, true, false>(P, stg, m0w, n0w, lane, acc, bias);
   } else {
-    if (alt) dma_epilogue_impl<EPI, false, true>(P, stg, m0w, n0w, lane, acc, bias);
-    else dma_epilogue_impl<EPI, false, false>(P, stg, m0w, n0w, lane, acc, bias);
+    if (alt) dma_epilogue_impl<EPI, TN, false, true>(P, stg, m0w, n0w, lane, acc, bias);
+    else dma_epilogue_impl<EPI, TN, false, false>(P, stg, m0w, n0w, lane, acc, bias);
   }
 }
 
@@ -274,19 +283,24 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& P, char* smem, i
 // loaded into registers when k-tile kt+1's A DMA is issued, and dequantised
 // into the B half of its stage (same swizzled bf16 layout) just before the
 // barrier that publishes it.
-template <int EPI, int BK, int S, int CPOL, int FMT, int DS>
-__global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
+template <int EPI, int BK, int S, int CPOL, int FMT, int DS, int W>
+__global__ __launch_bounds__(64 * W, 1) void k_gemm_dma(GemmBatch gb) {
+  constexpr int NT = 64 * W;                       // threads
+  constexpr int WN = W / 2;                        // wavefront columns (2 rows of wavefronts)
+  constexpr int TN = kDBN / WN;                    // columns of a wavefront tile (128 rows)
+  constexpr int NJF = TN / 32;                     // 32-column MFMA blocks per wavefront
   constexpr int CH = BK / 8;                       // 16-byte chunks per row
   constexpr int KS = BK / 16;                      // MFMA k-substeps per k-tile
   constexpr int HALF = kDBM * BK * 2;              // bytes of the A (or B) part of a stage
   constexpr int STAGE = 2 * HALF;
-  constexpr int NJ = kDBM * CH / 256;              // DMA instructions per wave for A (and for dense B)
+  constexpr int NJ = kDBM * CH / NT;               // DMA instructions per wave for A (and for dense B)
   constexpr int G = FMT == 0 ? 2 * NJ : NJ;        // DMA instructions per wave per k-tile
   // quantised B: raw 16-byte chunks per thread per k-tile (rows of BK codes)
   constexpr int QB = FMT == 2 ? BK : BK / 2;       // bytes per weight row per k-tile
-  constexpr int QCH = kDBN * QB / 16 / 256;        // raw chunks per thread
+  constexpr int QCH = kDBN * QB / 16 / NT;         // raw chunks per thread
   constexpr int QPR = QB / 16;                     // raw chunks per row
   static_assert(FMT == 0 || BK == 64, "quantised weights need 64-wide k-tiles (one scale group)");
+  static_assert(S * STAGE >= W * 32 * (TN + 4) * 4, "epilogue staging must fit in the operand stages");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int prob, tm, tn;
   tile_of(gb, prob, tm, tn);
@@ -296,7 +310,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
+  const int wm0 = (wave / WN) * 128, wn0 = (wave % WN) * TN;
   const uint32_t lds0 = lds_offset(smem);
 
   // Per-lane source of each DMA instruction: a 32-bit byte offset (row fixed
@@ -341,7 +355,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
     for (int q = 0; q < G; ++q) dma_one(kt, q);
   };
 
-  // Quantised B: raw chunk i of this thread is chunk q = tid + 256 i of the
+  // Quantised B: raw chunk i of this thread is chunk q = tid + NT i of the
   // k-tile: weight row q / QPR, part q % QPR.
   u32x4 braw[FMT == 0 ? 1 : QCH];
   float bscale[FMT == 0 ? 1 : QCH];
@@ -349,7 +363,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
     if constexpr (FMT != 0) {
 #pragma unroll
       for (int i = 0; i < QCH; ++i) {
-        const int q = tid + 256 * i;
+        const int q = tid + NT * i;
         int gn = n0 + q / QPR;
         gn = gn < N ? gn : N - 1;
         braw[i] = *reinterpret_cast<const u32x4*>(bbase + (int64_t)gn * (K / 64) * QB + (int64_t)kt * QB + (q % QPR) * 16);
@@ -362,7 +376,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
       char* st = smem + (kt % S) * STAGE + HALF;
 #pragma unroll
       for (int i = 0; i < QCH; ++i) {
-        const int q = tid + 256 * i;
+        const int q = tid + NT * i;
         const int r = q / QPR, part = q % QPR;
         const int sw = swz<BK>(r);
         if constexpr (FMT == 2) {
@@ -402,10 +416,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[i] = read_a(kt, kk, i);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fb[i] = read_b(kt, kk, i);
+    for (int j = 0; j < NJF; ++j) fb[j] = read_b(kt, kk, j);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NJF];
   // Weight rows go in as the MFMA's first operand, so the accumulator holds
   // C transposed: acc[i][j][r] = C[m0 + wm0 + 32i + lane%32]
   //                                [n0 + wn0 + 32j + 8(r/4) + 4(lane/32) + r%4],
@@ -413,19 +427,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+    for (int j = 0; j < NJF; ++j) acc[i][j] = (f32x16){};
   auto mfmas = [&](const bf16x8* fa, const bf16x8* fb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < NJF; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
 
   // bias of this lane's epilogue columns (requested now, used at the end)
   float ebias[4] = {0.f, 0.f, 0.f, 0.f};
   {
     const bf16* bp = reinterpret_cast<const bf16*>(P.bias);
-    const int n = n0 + wn0 + 4 * (lane & 31);
+    const int n = n0 + wn0 + 4 * (lane % (TN / 4));
     if (bp && n < N) {
       const bf16x4 v = *reinterpret_cast<const bf16x4*>(bp + n);
 #pragma unroll
@@ -468,7 +482,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): B of k-tile 0 written
   }
   barrier();
-  bf16x8 fa[2][4], fb[2][4];
+  bf16x8 fa[2][4], fb[2][NJF];
   read_frags(0, 0, fa[0], fb[0]);
   // k-tile kt: fragments of substep kk+1 are read while substep kk multiplies.
   // Before the last substep: wait for k-tile kt+1 (k-tiles up to kt+S-1 have
@@ -487,18 +501,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int u = i * 4 + j;
+      for (int j = 0; j < NJF; ++j) {
+        const int u = i * NJF + j;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[j], ca[i], acc[i][j], 0, 0, 0);
         if (u < 4) na[u] = read_a(rkt, rkk, u);
-        else if (u < 8) nb[u - 4] = read_b(rkt, rkk, u - 4);
+        else if (u < 4 + NJF) nb[u - 4] = read_b(rkt, rkk, u - 4);
         if constexpr (UNCOND) {
           if (u < q1 - q0) dma_to(dkt < nk ? dkt : nk - 1, dkt, q0 + u);
         } else {
           if (dma && u < q1 - q0) dma_one(dkt, q0 + u);
         }
       }
-    substep_schedule();
+    substep_schedule<4 + NJF, 4 * NJF>();
   };
   for (int kt = 0; kt < nk - 1; ++kt) {
 #pragma unroll
@@ -516,7 +530,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
         store_b(kt + 1);
       }
       mfmas(fa[kk & 1], fb[kk & 1]);
-      if constexpr (FMT == 0) substep_schedule();
+      if constexpr (FMT == 0) substep_schedule<4 + NJF, 4 * NJF>();
     }
     if constexpr (FMT == 0) {
       int ahead = nk - 2 - kt;
@@ -527,11 +541,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
     barrier();
     const bool more = kt + S < nk;
     constexpr int L = (KS - 1) & 1, X = KS & 1;
-    substep_dma(fa[L], fb[L], fa[X], fb[X], kt + 1, 0, more, kt + S, 0, PER < 16 ? PER : 16);
-    if constexpr (PER > 16) {
+    substep_dma(fa[L], fb[L], fa[X], fb[X], kt + 1, 0, more, kt + S, 0, PER < 4 * NJF ? PER : 4 * NJF);
+    if constexpr (PER > 4 * NJF) {
       if (more) {
 #pragma unroll
-        for (int q = 16; q < PER; ++q) dma_one(kt + S, q);
+        for (int q = 4 * NJF; q < PER; ++q) dma_one(kt + S, q);
       }
     }
     if constexpr (FMT != 0) {
@@ -544,7 +558,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
   for (int kk = 0; kk < KS; ++kk) {
     if (kk + 1 < KS) read_frags(nk - 1, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJF; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i], acc[i][j], 0, 0, 0);
@@ -556,7 +570,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
   __builtin_amdgcn_s_waitcnt(0xC07F);
   barrier();
   const int side = EPI == EPI_SPLIT ? split_side_of(P, n0, kDBN) : 0;
-  dma_epilogue<EPI>(P, smem, m0 + wm0, n0 + wn0, wave, lane, acc, side, ebias);
+  dma_epilogue<EPI, TN>(P, smem, m0 + wm0, n0 + wn0, wave, lane, acc, side, ebias);
 }
 
 // Tile-loop configuration used by the library.
@@ -572,10 +586,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(GemmBatch gb) {
 #ifndef MMDIT_DMA_SPREAD
 #define MMDIT_DMA_SPREAD 3
 #endif
+#ifndef MMDIT_DMA_WAVES
+#define MMDIT_DMA_WAVES 4
+#endif
 constexpr int kDBK = MMDIT_DMA_BK;
 
 template <int EPI, int BK = MMDIT_DMA_BK, int S = MMDIT_DMA_STAGES, int CPOL = MMDIT_DMA_CPOL, int FMT = 0,
-          int DS = MMDIT_DMA_SPREAD>
+          int DS = MMDIT_DMA_SPREAD, int W = MMDIT_DMA_WAVES>
 static hipError_t launch_dma_epi(const GemmProblem* p, int nprob, hipStream_t s) {
   GemmBatch gb{};
   int total = 0;
@@ -595,12 +612,12 @@ static hipError_t launch_dma_epi(const GemmProblem* p, int nprob, hipStream_t s)
   const size_t lds = (size_t)S * 2 * kDBM * BK * 2;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_dma<EPI, BK, S, CPOL, FMT, DS>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_dma<EPI, BK, S, CPOL, FMT, DS, W>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemm_dma<EPI, BK, S, CPOL, FMT, DS>), dim3(total), dim3(256), lds, s, gb);
+  hipLaunchKernelGGL((k_gemm_dma<EPI, BK, S, CPOL, FMT, DS, W>), dim3(total), dim3(64 * W), lds, s, gb);
   return hipGetLastError();
 }
 

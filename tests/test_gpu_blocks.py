@@ -177,6 +177,22 @@ def test_blocks_bf16_full_width_ragged_rows(quant):
                   f"ragged-rows single {quant}")
 
 
+def test_blocks_bf16_full_width_two_batches():
+    # h 3072, batch 2, 77 text + 48x48 image tokens: the 256x256 GEMM's gated
+    # residual rows cross a batch boundary inside a tile (image rows per batch
+    # 2304), and the joint attention runs over two (batch, head) sets
+    s = I.Shape(txt_len=77, grid_h=48, grid_w=48, batch=2, dtype="bf16", cfg_id=39)
+    x = I.block_inputs(s)
+    ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
+    w = I.double_block_weights(s, 0)
+    img, txt = run_double(s, w, x, ids)
+    rimg, rtxt = oracle_double(s, w, x, ids)
+    assert_parity(img, rimg, "bf16", "two-batch dual img")
+    assert_parity(txt, rtxt, "bf16", "two-batch dual txt")
+    ws_ = I.single_block_weights(s, 0)
+    assert_parity(run_single(s, ws_, x, ids), oracle_single(s, ws_, x, ids), "bf16", "two-batch single")
+
+
 def test_blocks_quantised_weights_bf16():
     s = I.Shape(hidden=1024, heads=8, mlp_hidden=4096, txt_len=64, grid_h=16, grid_w=16, dtype="bf16",
                 cfg_id=35)
