@@ -45,6 +45,25 @@ def step_flops(s):
     return blocks + io
 
 
+def lin1_traffic():
+    """HBM bytes per launch of the linear1 GEMM from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE passes (scaled by a 1 GiB copy's counts), or None
+    when the kernel's sources have changed since those counters were taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        rec = json.load(open(os.path.join(here, "profiles", "gemm_lin1_traffic.json")))
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(here, "diffusion_transformer_mmdit_amd", "csrc", src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None
+        return int(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -172,16 +191,18 @@ def main():
         for i in range(a.steps):
             step(i)
         tot_ms, n, work = bd.mmdit_profile_end()
-        mem[name] = dict(ms_per_step=tot_ms / max(a.steps, 1), launches_per_step=n // max(a.steps, 1),
-                         avg_us=round(1e3 * tot_ms / max(n, 1), 2),
-                         gbps=round(work / max(tot_ms, 1e-9) / 1e6, 1))
+        gbps = work / max(tot_ms, 1e-9) / 1e6
+        mem[name] = dict(ms_per_step=round(tot_ms / max(a.steps, 1), 4), launches_per_step=n // max(a.steps, 1),
+                         avg_us=round(1e3 * tot_ms / max(n, 1), 2), gbps=round(gbps, 1),
+                         frac=round(gbps / PEAK_HBM_GBS, 4))
         log(f"{name}: {mem[name]['ms_per_step']:.3f} ms/step in {mem[name]['launches_per_step']} launches, "
             f"{mem[name]['gbps']:.0f} GB/s")
     dom = "gemm_lin1"
     p = prof[dom]
+    traffic = lin1_traffic()
     roofline = {"bound": "mfma", "kernel": "k_gemm_dma 256x256 direct-to-LDS, split epilogue (single-block linear1, "
                 "M 4608 N 21504 K 3072)", "achieved": round(p["tflops"], 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "avg_launch_us": round(p["avg_us"], 2), "flops_per_launch": p["flops"] / max(p["launches"], 1)}
 
     out = {"metric": METRIC, "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": a.steps,
@@ -195,6 +216,7 @@ def main():
            "step_frac_of_bf16_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
            "roofline": roofline,
            "kernels": {k: {"avg_us": round(v_["avg_us"], 2), "tflops": round(v_["tflops"], 1),
+                           "frac": round(v_["tflops"] / PEAK_BF16_TFLOPS, 4),
                            "launches_per_step": v_["launches"] // max(a.steps, 1)} for k, v_ in prof.items()},
            "hbm_kernels": mem}
 
