@@ -5,11 +5,16 @@
 // scaled_dot_product_attention it relies on).
 //
 // bf16 path (flash attention, gfx950 MFMA 32x32x16):
-//  * a block owns 128 queries of one (batch, head); each of its 4 wavefronts
-//    owns 32 queries; K and V^T tiles of 64 keys are staged in LDS, double
-//    buffered, and shared by the 4 wavefronts. They arrive by direct-to-LDS
-//    loads (global_load_lds_dwordx4: no registers, no LDS store
-//    instructions), issued one tile ahead;
+//  * a block owns 32 * NW queries of one (batch, head); each of its NW
+//    wavefronts owns 32 queries; K and V^T tiles of 64 keys are staged in
+//    LDS, double buffered, and shared by the NW wavefronts. They arrive by
+//    direct-to-LDS loads (global_load_lds_dwordx4: no registers, no LDS
+//    store instructions), issued one tile ahead;
+//  * NW = 8: one block of 8 wavefronts per CU (two per SIMD). Two resident
+//    blocks of 4 would run at unequal speeds (the older block's wavefronts
+//    win issue), leaving one of them alone on the CU at the end of a round;
+//    one block, in step at every tile barrier, avoids that and stages each
+//    K/V tile once for 256 queries;
 //  * LDS rows are stored with their 16-byte chunks XOR-swizzled by the row
 //    index, so the MFMA operand reads (one 16-byte read per lane) of 16
 //    consecutive rows hit distinct banks;
@@ -28,7 +33,6 @@
 
 namespace mmdit {
 
-constexpr int kAttnQ = 128;   // queries per block
 constexpr int kAttnK = 64;    // keys per tile
 constexpr int kKBuf = kAttnK * 256;  // bytes of a K tile (64 rows x 256 B)
 constexpr int kVBuf = 128 * 128;     // bytes of a V^T tile (128 rows x 128 B)
@@ -49,13 +53,24 @@ __device__ __forceinline__ void attn_dma16(const void* base, uint32_t voff, uint
 // LDS layouts (one stage): K tile row r (key) at r*256, 16-byte chunk c
 // (dims 8c..8c+7) at position c ^ (r & 15); V^T tile row r (dim) at
 // kKBuf + r*128, chunk c (positions 8c..8c+7) at c ^ ((r >> 1) & 7).
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
+// Query blocks of 32 * NW rows per (batch, head); the last may reach past
+// Lpad (its rows there load row Lpad - 1 and write nothing).
+template <int NW>
+__host__ __device__ __forceinline__ int attn_qblocks(const AttnArgs& a) {
+  return (a.Lpad + 32 * NW - 1) / (32 * NW);
+}
+
+// Unit u = (b * H + head) * qblocks + query block: the unit's 32 * NW
+// queries against all keys; writes the normalised output rows.
+template <int NW>
+__device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int unit) {
+  constexpr int J = 16 / NW;  // DMA instructions per wave and operand
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 5, l32 = lane & 31;
-  const int q0 = blockIdx.x * kAttnQ;
-  const int hh = blockIdx.y, b = blockIdx.z;
+  const int qb_n = attn_qblocks<NW>(a);
+  const int q0 = (unit % qb_n) * (32 * NW);
+  const int hh = (unit / qb_n) % a.H, b = unit / qb_n / a.H;
   const int64_t bh = (int64_t)b * a.H + hh;
   const bf16* Qh = reinterpret_cast<const bf16*>(a.Q) + bh * a.Lpad * 128;
   const char* Kh = reinterpret_cast<const char*>(a.K) + bh * a.Lpad * 128 * 2;
@@ -64,16 +79,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
 
   // Q as the B operand of S^T = K Q^T: column = query, 8 consecutive dims.
   const int qrow = q0 + wave * 32 + l32;
+  const int qld = qrow < a.Lpad ? qrow : a.Lpad - 1;
   bf16x8 qf[8];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qrow * 128 + kk * 16 + g * 8);
+  for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qld * 128 + kk * 16 + g * 8);
 
-  // Direct-to-LDS requests of one tile: this wave's 4 K and 4 V^T
-  // instructions; lane i of instruction j fills LDS slot j*64 + i.
-  uint32_t koff[4], voff[4];
+  // Direct-to-LDS requests of one tile: 16 K and 16 V^T instructions of 64
+  // lanes, J of each per wave; lane i of instruction jj fills LDS slot
+  // jj*64 + i.
+  uint32_t koff[J], voff[J];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int jj = wave * 4 + j;
+  for (int j = 0; j < J; ++j) {
+    const int jj = wave * J + j;
     {  // K: row r = 4 jj + lane/16, slot lane%16 holds chunk (slot ^ (r & 15))
       const int r = jj * 4 + (lane >> 4);
       const int c = (lane & 15) ^ (r & 15);
@@ -90,9 +107,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
     const char* kb = Kh + (size_t)kt * kAttnK * 256;
     const char* vb = Vh + (size_t)kt * kAttnK * 2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      attn_dma16(kb, koff[j], st + (uint32_t)((wave * 4 + j) * 1024));
-      attn_dma16(vb, voff[j], st + (uint32_t)(kKBuf + (wave * 4 + j) * 1024));
+    for (int j = 0; j < J; ++j) {
+      attn_dma16(kb, koff[j], st + (uint32_t)((wave * J + j) * 1024));
+      attn_dma16(vb, voff[j], st + (uint32_t)(kKBuf + (wave * J + j) * 1024));
     }
   };
 
@@ -193,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
 
   const int ntiles = (a.L + kAttnK - 1) / kAttnK;
   issue_tile(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 (and Q) landed
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first tile (and Q) landed
   __syncthreads();
   const bool ragged = (a.L % kAttnK) != 0;
   for (int kt = 0; kt < ntiles; ++kt) {
@@ -220,20 +237,31 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
   }
 }
 
-hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s) {
+// One block per unit, units in order (the query blocks of a head are
+// adjacent, so blocks running together share that head's K/V tiles in L2).
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  attn_unit<NW>(a, smem, blockIdx.x);
+}
+
+template <int NW>
+hipError_t launch_attention_nw(const AttnArgs& a, hipStream_t s) {
   // K/V byte offsets from the per-(batch, head) base are 32-bit
   if ((int64_t)a.Lpad * 128 * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  dim3 grid(a.Lpad / kAttnQ, a.H, a.B), block(256);
+  const int units = attn_qblocks<NW>(a) * a.H * a.B;
   const size_t lds = 2 * kStage;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_attn_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)k_attn_bf16<NW>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(k_attn_bf16, grid, block, lds, s, a);
+  hipLaunchKernelGGL(k_attn_bf16<NW>, dim3(units), dim3(64 * NW), lds, s, a);
   return hipGetLastError();
 }
+
+hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s) { return launch_attention_nw<kAttnWaves>(a, s); }
 
 // ------------------------------------------------------------- float32 path --
 // One wavefront per query at a time; lane j scores key j of a 64-key chunk,

@@ -163,6 +163,9 @@ struct AttnArgs {
   int32_t B, H, L, Lpad;
   float scale;  // 1/sqrt(d)
 };
+// bf16 attention blocks: kAttnWaves wavefronts of 32 queries each, one
+// block per CU.
+constexpr int kAttnWaves = 8;
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t s);
 
