@@ -5,16 +5,18 @@
 // scaled_dot_product_attention it relies on).
 //
 // bf16 path (flash attention, gfx950 MFMA 32x32x16):
-//  * a block owns 32 * NW queries of one (batch, head); each of its NW
-//    wavefronts owns 32 queries; K and V^T tiles of 64 keys are staged in
-//    LDS, double buffered, and shared by the NW wavefronts. They arrive by
-//    direct-to-LDS loads (global_load_lds_dwordx4: no registers, no LDS
-//    store instructions), issued one tile ahead;
-//  * NW = 8: one block of 8 wavefronts per CU (two per SIMD). Two resident
-//    blocks of 4 would run at unequal speeds (the older block's wavefronts
-//    win issue), leaving one of them alone on the CU at the end of a round;
-//    one block, in step at every tile barrier, avoids that and stages each
-//    K/V tile once for 256 queries;
+//  * a block of 8 wavefronts owns 256 queries of one (batch, head), each
+//    wavefront 32 of them; one block per CU (two wavefronts per SIMD). K and
+//    V^T tiles of 64 keys are staged in LDS, double buffered, and shared by
+//    the 8 wavefronts. They arrive by direct-to-LDS loads
+//    (global_load_lds_dwordx4: no registers, no LDS store instructions);
+//  * ping-pong: waves 0-3 and 4-7 (one of each per SIMD) run the same phase
+//    sequence one phase apart, with a block barrier after every phase. A
+//    wave alternates an MFMA phase [O^T += V^T(t-1) P^T(t-1) and
+//    S^T(t) = K(t) Q^T] and a VALU phase [online softmax of S(t)], so in
+//    every phase one wavefront of each SIMD feeds the matrix core while the
+//    other computes its exponentials. The MFMA phase issues its LDS operand
+//    reads one MFMA group ahead of use, at raised wave priority;
 //  * LDS rows are stored with their 16-byte chunks XOR-swizzled by the row
 //    index, so the MFMA operand reads (one 16-byte read per lane) of 16
 //    consecutive rows hit distinct banks;
@@ -23,11 +25,9 @@
 //  * the probabilities stay in registers and feed O^T += V^T P^T directly as
 //    the MFMA B operand. V^T arrives from the QK-norm kernel with its tokens
 //    in vkey_pos order, so each lane's 8 keys are one contiguous 16 bytes;
-//  * the softmax denominator is produced by the MFMA too: a fifth output
-//    block multiplies P^T by a matrix of ones, so every row of it holds the
-//    running sum of the (bf16) probabilities, with no per-score adds;
 //  * online softmax in float32 with exp2 of log2(e)-scaled scores; the
-//    running max is moved only when it grows by more than 2^8.
+//    running max is moved only when it grows by more than 2^8; row sums are
+//    float32 VALU adds in the softmax phase.
 #include "common.h"
 #include "kernels.h"
 
@@ -53,22 +53,22 @@ __device__ __forceinline__ void attn_dma16(const void* base, uint32_t voff, uint
 // LDS layouts (one stage): K tile row r (key) at r*256, 16-byte chunk c
 // (dims 8c..8c+7) at position c ^ (r & 15); V^T tile row r (dim) at
 // kKBuf + r*128, chunk c (positions 8c..8c+7) at c ^ ((r >> 1) & 7).
-// Query blocks of 32 * NW rows per (batch, head); the last may reach past
-// Lpad (its rows there load row Lpad - 1 and write nothing).
-template <int NW>
+// Query blocks of 32 * kAttnWaves rows per (batch, head); the last may reach
+// past Lpad (its rows there load row Lpad - 1 and write nothing).
 __host__ __device__ __forceinline__ int attn_qblocks(const AttnArgs& a) {
-  return (a.Lpad + 32 * NW - 1) / (32 * NW);
+  return (a.Lpad + 32 * kAttnWaves - 1) / (32 * kAttnWaves);
 }
 
-// Unit u = (b * H + head) * qblocks + query block: the unit's 32 * NW
-// queries against all keys; writes the normalised output rows.
-template <int NW>
+// Unit u = (b * H + head) * qblocks + query block: the unit's 256 queries
+// against all keys; writes the normalised output rows. Phase 2t + grp is a
+// wave's MFMA phase of tile t, phase 2t + 1 + grp its softmax of tile t.
 __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int unit) {
-  constexpr int J = 16 / NW;  // DMA instructions per wave and operand
+  constexpr int NW = kAttnWaves, J = 16 / NW;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int grp = wave >> 2;
   const int g = lane >> 5, l32 = lane & 31;
-  const int qb_n = attn_qblocks<NW>(a);
+  const int qb_n = attn_qblocks(a);
   const int q0 = (unit % qb_n) * (32 * NW);
   const int hh = (unit / qb_n) % a.H, b = unit / qb_n / a.H;
   const int64_t bh = (int64_t)b * a.H + hh;
@@ -77,45 +77,40 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
   const char* Vh = reinterpret_cast<const char*>(a.V) + bh * 128 * (int64_t)a.Lpad * 2;
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
 
-  // Q as the B operand of S^T = K Q^T: column = query, 8 consecutive dims.
   const int qrow = q0 + wave * 32 + l32;
   const int qld = qrow < a.Lpad ? qrow : a.Lpad - 1;
   bf16x8 qf[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qld * 128 + kk * 16 + g * 8);
 
-  // Direct-to-LDS requests of one tile: 16 K and 16 V^T instructions of 64
-  // lanes, J of each per wave; lane i of instruction jj fills LDS slot
-  // jj*64 + i.
   uint32_t koff[J], voff[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int jj = wave * J + j;
-    {  // K: row r = 4 jj + lane/16, slot lane%16 holds chunk (slot ^ (r & 15))
+    {
       const int r = jj * 4 + (lane >> 4);
       const int c = (lane & 15) ^ (r & 15);
       koff[j] = (uint32_t)((r * 128 + c * 8) * 2);
     }
-    {  // V^T: row r = 8 jj + lane/8, slot lane%8 holds chunk (slot ^ ((r >> 1) & 7))
+    {
       const int r = jj * 8 + (lane >> 3);
       const int c = (lane & 7) ^ ((r >> 1) & 7);
       voff[j] = (uint32_t)(r * a.Lpad * 2 + c * 16);
     }
   }
-  auto issue_tile = [&](int kt, int buf) {
-    const uint32_t st = lds0 + (uint32_t)(buf * kStage);
+  auto issue_k = [&](int kt) {
+    const uint32_t st = lds0 + (uint32_t)((kt & 1) * kStage);
     const char* kb = Kh + (size_t)kt * kAttnK * 256;
+#pragma unroll
+    for (int j = 0; j < J; ++j) attn_dma16(kb, koff[j], st + (uint32_t)((wave * J + j) * 1024));
+  };
+  auto issue_v = [&](int kt) {
+    const uint32_t st = lds0 + (uint32_t)((kt & 1) * kStage);
     const char* vb = Vh + (size_t)kt * kAttnK * 2;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      attn_dma16(kb, koff[j], st + (uint32_t)((wave * J + j) * 1024));
-      attn_dma16(vb, voff[j], st + (uint32_t)(kKBuf + (wave * J + j) * 1024));
-    }
+    for (int j = 0; j < J; ++j) attn_dma16(vb, voff[j], st + (uint32_t)(kKBuf + (wave * J + j) * 1024));
   };
 
-  // Per-lane LDS read offsets: K fragment (row kb*32 + l32, chunk 2kk + g),
-  // V^T fragment (row db*32 + l32, chunk 2kb2 + g); the swizzle depends only
-  // on l32, the block offsets (kb, db) are immediates.
   uint32_t kro[8], vro[4];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) kro[kk] = (uint32_t)(l32 * 256 + (((2 * kk + g) ^ (l32 & 15)) * 16));
@@ -123,47 +118,107 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
   for (int kb2 = 0; kb2 < 4; ++kb2)
     vro[kb2] = (uint32_t)(kKBuf + l32 * 128 + (((2 * kb2 + g) ^ ((l32 >> 1) & 7)) * 16));
 
-  // o[0..3]: O^T blocks of 32 dims; o[4]: P^T times ones (row sums)
-  f32x16 o[5];
+  f32x16 o[4];
 #pragma unroll
-  for (int db = 0; db < 5; ++db) o[db] = (f32x16){};
-  bf16x8 ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.0f;
-  // Scores never hold NaN here; the file is built with -fno-honor-nans so
-  // fmaxf needs no canonicalisation. kNegBig stands for minus infinity.
+  for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
+  f32x16 s[2];
+  bf16x8 pb[4];
   constexpr float kNegBig = -1e30f;
-  float m_run = kNegBig;
-  const float c2 = a.scale * 1.4426950408889634f;  // scale * log2(e)
+  float m_run = kNegBig, l_run = 0.f;
+  const float c2 = a.scale * 1.4426950408889634f;
 
-  // One 64-key tile in stage `cur`. mask: the tile reaches past L (only the
-  // last one can). The running max m_run is moved only when some lane's tile
-  // max exceeds it by more than 2^8 (log2 units): p = exp2(s - m_run) then
-  // stays below 256, and p and O (including the row sums) use the same
-  // m_run, so the result is exact.
-  auto tile = [&](int kt, int cur, bool mask) {
-    const char* st = smem + cur * kStage;
-    f32x16 s[2];
+  // MFMA phase pieces. V^T fragments of dim blocks db0, db0+1 (8 reads) and
+  // K fragments of dims 16*kk0 .. 16*kk0+63 (8 reads); MFMA groups of 8:
+  // O^T[db0..db0+1] += V^T P^T, and S^T += K Q^T (two chains each, alternated).
+  auto rd_v = [&](bf16x8 (&v)[8], const char* st, int db0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const bf16x8*>(st + vro[i & 3] + (db0 + (i >> 2)) * 32 * 128);
+  };
+  auto rd_k = [&](bf16x8 (&k)[8], const char* st, int kk0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      k[2 * i] = *reinterpret_cast<const bf16x8*>(st + kro[kk0 + i]);
+      k[2 * i + 1] = *reinterpret_cast<const bf16x8*>(st + kro[kk0 + i] + 32 * 256);
+    }
+  };
+  auto mm_v = [&](const bf16x8 (&v)[8], int db0) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2) {
+      o[db0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[kb2], pb[kb2], o[db0], 0, 0, 0);
+      o[db0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[4 + kb2], pb[kb2], o[db0 + 1], 0, 0, 0);
+    }
+  };
+  // key blocks kb0, kb0+1 of all four dim blocks (four chains alternated)
+  auto mm_v4 = [&](const bf16x8 (&v01)[8], const bf16x8 (&v23)[8], int kb0) {
+#pragma unroll
+    for (int kb2 = kb0; kb2 < kb0 + 2; ++kb2) {
+      o[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v01[kb2], pb[kb2], o[0], 0, 0, 0);
+      o[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v01[4 + kb2], pb[kb2], o[1], 0, 0, 0);
+      o[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v23[kb2], pb[kb2], o[2], 0, 0, 0);
+      o[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v23[4 + kb2], pb[kb2], o[3], 0, 0, 0);
+    }
+  };
+  auto mm_k = [&](const bf16x8 (&k)[8], int kk0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[2 * i], qf[kk0 + i], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[2 * i + 1], qf[kk0 + i], s[1], 0, 0, 0);
+    }
+  };
+  // Each read group is issued one MFMA group ahead of its use (the
+  // scheduler would otherwise issue every read just before its MFMA and
+  // wait on it).
+  auto phase_pv_qk = [&](int t) {  // O^T += V^T(t-1) P^T(t-1); S^T(t) = K(t) Q^T
+    const char* sv = smem + ((t + 1) & 1) * kStage;
+    const char* sk = smem + (t & 1) * kStage;
+    bf16x8 va[8], vb[8], ka[8], kc[8];
+    rd_v(va, sv, 0);
+    rd_v(vb, sv, 2);
+    mm_v4(va, vb, 0);
+    rd_k(ka, sk, 0);
+    mm_v4(va, vb, 2);
+    rd_k(kc, sk, 4);
     s[0] = (f32x16){};
     s[1] = (f32x16){};
-    // all 16 K fragments requested up front: one LDS latency per tile
-    bf16x8 kf[8][2];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      kf[kk][0] = *reinterpret_cast<const bf16x8*>(st + kro[kk]);
-      kf[kk][1] = *reinterpret_cast<const bf16x8*>(st + kro[kk] + 32 * 256);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk][0], qf[kk], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk][1], qf[kk], s[1], 0, 0, 0);
-    }
-    // keep that order: the scheduler would otherwise pull each read next to
-    // its MFMA and wait on it
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // 16 LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // 16 MFMAs
+    mm_k(ka, 0);
+    mm_k(kc, 4);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // s[kb][r] = score(query l32, key kt*64 + kb*32 + 8*(r/4) + 4*g + r%4)
+  };
+  auto phase_qk = [&](int t) {  // first tile: S^T(t) only
+    const char* sk = smem + (t & 1) * kStage;
+    bf16x8 ka[8], kc[8];
+    rd_k(ka, sk, 0);
+    rd_k(kc, sk, 4);
+    s[0] = (f32x16){};
+    s[1] = (f32x16){};
+    mm_k(ka, 0);
+    mm_k(kc, 4);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto phase_pv = [&](int t) {  // after the last tile: O^T += V^T(t-1) P^T(t-1) only
+    const char* sv = smem + ((t + 1) & 1) * kStage;
+    bf16x8 va[8], vb[8];
+    rd_v(va, sv, 0);
+    rd_v(vb, sv, 2);
+    mm_v(va, 0);
+    mm_v(vb, 2);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // softmax of S(kt): running max, probabilities to bf16, row sums. The
+  // running max is moved only when some lane's tile max exceeds it by more
+  // than 2^8 (log2 units): p = exp2(s - m_run) then stays below 256, and p,
+  // O and the row sums all use the same m_run, so the result is exact.
+  auto softmax = [&](int kt, bool mask) {
     if (__builtin_expect(mask, 0)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -185,43 +240,99 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-      for (int db = 0; db < 5; ++db) o[db] *= alpha;
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      l_run *= alpha;
       m_run = m_new;
     }
-    bf16x8 pb[4];
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        pb[kb * 2 + (r >> 3)][r & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -m_run));
-    // O^T += V^T P^T; MFMA kb2 covers keys 16*kb2 + 8*(i/4) + 4*g + i%4,
-    // stored contiguously; o[4] += ones P^T
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -m_run));
+        if (r & 1) ps1 += p; else ps0 += p;
+        pb[kb * 2 + (r >> 3)][r & 7] = (bf16)p;
+      }
+    l_run += ps0 + ps1;
+    // keep the conversions in this phase (they would sink to their MFMAs)
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      bf16x8 va[4];
-#pragma unroll
-      for (int kb2 = 0; kb2 < 4; ++kb2) va[kb2] = *reinterpret_cast<const bf16x8*>(st + vro[kb2] + db * 32 * 128);
-#pragma unroll
-      for (int kb2 = 0; kb2 < 4; ++kb2) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb2], pb[kb2], o[db], 0, 0, 0);
-    }
-#pragma unroll
-    for (int kb2 = 0; kb2 < 4; ++kb2) o[4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[kb2], o[4], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[i]));
   };
 
   const int ntiles = (a.L + kAttnK - 1) / kAttnK;
-  issue_tile(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first tile (and Q) landed
-  __syncthreads();
   const bool ragged = (a.L % kAttnK) != 0;
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < ntiles) issue_tile(kt + 1, cur ^ 1);  // its stage was freed by the last barrier
-    tile(kt, cur, ragged && kt == ntiles - 1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile kt+1 landed
+  issue_k(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(0) (and Q) landed
+  __syncthreads();
+  // Phase 2u + grp of a wave is its MFMA phase of tile u, phase 2u + 1 + grp
+  // its softmax of tile u; every wave passes 2 * ntiles + 2 barriers. At
+  // the start of each even phase 2u, K(u+1) and V(u) are requested (their
+  // buffers held K(u-1) and V(u-2), last read in phase 2u - 1); each odd
+  // phase ends with vmcnt(0), so they have landed before phase 2u + 2.
+  auto bar = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto issue = [&](int u) {
+    if (u + 1 < ntiles) issue_k(u + 1);
+    if (u < ntiles) issue_v(u);
+  };
+  auto hi = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto lo = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto sm = [&](int t) { softmax(t, ragged && t == ntiles - 1); };
+  auto wait_vm = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
+  // first tile (MFMA phase: S(0) only), tiles 1 .. ntiles-1, then the last
+  // PV; group 1 runs the same sequence one phase later
+  if (grp == 0) {
+    issue(0);
+    hi(); phase_qk(0); lo();
+    bar();
+    sm(0);
+    wait_vm();
+    bar();
+    for (int t = 1; t < ntiles; ++t) {
+      issue(t);
+      hi(); phase_pv_qk(t); lo();
+      bar();
+      sm(t);
+      wait_vm();
+      bar();
+    }
+    hi(); phase_pv(ntiles); lo();
+    bar();
+    wait_vm();
+    bar();
+  } else {
+    issue(0);
+    bar();
+    hi(); phase_qk(0); lo();
+    wait_vm();
+    bar();
+    for (int t = 1; t < ntiles; ++t) {
+      issue(t);
+      sm(t - 1);
+      bar();
+      hi(); phase_pv_qk(t); lo();
+      wait_vm();
+      bar();
+    }
+    sm(ntiles - 1);
+    bar();
+    hi(); phase_pv(ntiles); lo();
+    wait_vm();
+    bar();
   }
-  // every row of o[4] holds this lane's query's probability sum
-  const float inv = 1.0f / o[4][0];
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l_tot;
   if (qrow < a.L) {
     bf16* dst = out_row(a, b, qrow) + hh * 128;
 #pragma unroll
@@ -237,31 +348,25 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
   }
 }
 
-// One block per unit, units in order (the query blocks of a head are
-// adjacent, so blocks running together share that head's K/V tiles in L2).
-template <int NW>
-__global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16(AttnArgs a) {
+__global__ __launch_bounds__(64 * kAttnWaves, 2) void k_attn_bf16(AttnArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  attn_unit<NW>(a, smem, blockIdx.x);
+  attn_unit(a, smem, blockIdx.x);
 }
 
-template <int NW>
-hipError_t launch_attention_nw(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s) {
   // K/V byte offsets from the per-(batch, head) base are 32-bit
   if ((int64_t)a.Lpad * 128 * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  const int units = attn_qblocks<NW>(a) * a.H * a.B;
+  const int units = attn_qblocks(a) * a.H * a.B;
   const size_t lds = 2 * kStage;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_attn_bf16<NW>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)k_attn_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(k_attn_bf16<NW>, dim3(units), dim3(64 * NW), lds, s, a);
+  hipLaunchKernelGGL(k_attn_bf16, dim3(units), dim3(64 * kAttnWaves), lds, s, a);
   return hipGetLastError();
 }
-
-hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s) { return launch_attention_nw<kAttnWaves>(a, s); }
 
 // ------------------------------------------------------------- float32 path --
 // One wavefront per query at a time; lane j scores key j of a 64-key chunk,

@@ -119,7 +119,7 @@ def test_double_block_cfg2_bf16():
     assert_parity(txt, rtxt, "bf16", "cfg2 txt")
 
 
-@pytest.mark.parametrize("txt_len,gh,gw,batch", [(77, 9, 13, 2), (0, 16, 12, 1), (200, 1, 1, 1)])
+@pytest.mark.parametrize("txt_len,gh,gw,batch", [(77, 9, 13, 2), (0, 16, 12, 1), (200, 1, 1, 1), (5, 3, 4, 1), (40, 5, 5, 2)])
 def test_blocks_bf16_ragged(txt_len, gh, gw, batch):
     s = I.Shape(hidden=512, heads=4, mlp_hidden=1024, txt_len=txt_len, grid_h=gh, grid_w=gw, batch=batch,
                 dtype="bf16", cfg_id=32)
