@@ -214,7 +214,10 @@ __device__ __forceinline__ int split_side_of(const GemmProblem& P, int n0, int c
 // contiguous range of logical tiles, the second walks each range in groups
 // of kGroupM row-tiles so that neighbouring blocks share A rows and weight
 // columns in that XCD's L2.
-constexpr int kGroupM = 8;
+#ifndef MMDIT_GEMM_GROUP_M
+#define MMDIT_GEMM_GROUP_M 6
+#endif
+constexpr int kGroupM = MMDIT_GEMM_GROUP_M;
 
 // Coordinates of logical tile `t` (problems concatenated, each walked in
 // groups of kGroupM row-tiles).
