@@ -17,6 +17,7 @@ and the CPU oracle on a bounded sample.
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -76,7 +77,6 @@ def cpu_baseline(s):
 
     import oracle
     from diffusion_transformer_mmdit_amd import inputs as I
-    import dataclasses
     sb = dataclasses.replace(I.CFG3, txt_len=s.txt_len, grid_h=s.grid_h, grid_w=s.grid_w)
     x = I.block_inputs(sb)
     ids = oracle.make_ids(sb.grid_h, sb.grid_w, sb.txt_len)
@@ -285,6 +285,31 @@ def main():
         out["quantised_ms_per_step"] = round(qms, 3)
         log(f"quantised step: {qms:.2f} ms")
         del Mq, mqc
+
+        # reference-image (Kontext-style) step: 4096 context tokens with frame
+        # id 1 after the 4096 generated ones, L = 512 + 8192 = 8704
+        ck = bd.make_config(s)
+        Lc = s.img_len
+        ck.dims.img_len = s.img_len + Lc
+        Xk = X.clone()
+        Xc = torch.randn((s.batch, Lc, s.in_ch), generator=g, device=dev)
+        idk = torch.from_numpy(np.concatenate([bd.mmdit_make_ids(s.grid_h, s.grid_w, s.txt_len),
+                                               bd.mmdit_make_ids(s.grid_h, s.grid_w, 0, frame=1)])).to(dev)
+        wsk = torch.empty(bd.mmdit_step_workspace(ck), dtype=torch.uint8, device=dev)
+
+        def kstep(i):
+            j = i % 4
+            bd.mmdit_step_ctx(ck, mc, Xk, v, Xc, Lc, T, y, idk, sig[j], sig[j + 1], wsk)
+        for i in range(2):
+            kstep(i)
+        kn = max(a.steps // 2, 3)
+        kms = timed(kstep, kn)
+        kfl = step_flops(dataclasses.replace(s, grid_w=2 * s.grid_w))
+        out["kontext_step"] = {"ms_per_step": round(kms, 3), "seq_len": s.txt_len + 2 * s.img_len,
+                               "context_tokens": Lc, "tflops": round(kfl / kms / 1e9, 1),
+                               "frac_of_bf16_peak": round(kfl / kms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        log(f"kontext step (L {s.txt_len + 2 * s.img_len}): {kms:.2f} ms ({kfl / kms / 1e9:.0f} TFLOP/s)")
+        del wsk, Xk, Xc
 
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

@@ -82,6 +82,8 @@ _SIGS = {
                                          _P, C.c_size_t, _P]),
     "mmdit_step": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(mmdit_model_w), _P, _P, _P, _P, _P,
                              C.c_double, C.c_double, _P, C.c_size_t, _P]),
+    "mmdit_step_ctx": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(mmdit_model_w), _P, _P, _P, C.c_int32, _P,
+                                 _P, _P, C.c_double, C.c_double, _P, C.c_size_t, _P]),
     "mmdit_schedule": (C.c_int, [C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double, C.c_int32, _P]),
     "mmdit_make_ids": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P]),
     "mmdit_pack_latents": (C.c_int, [_P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P]),
@@ -299,6 +301,14 @@ def mmdit_step(cfg, w: mmdit_model_w, x_packed, v_out, txt_emb, y, ids, sigma: f
                             _ptr(ids), float(sigma), float(sigma_next), _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream)),
            "mmdit_step")
+
+
+def mmdit_step_ctx(cfg, w: mmdit_model_w, x_packed, v_out, ctx_packed, ctx_len: int, txt_emb, y, ids,
+                   sigma: float, sigma_next: float, ws, stream=None):
+    _check(lib().mmdit_step_ctx(C.byref(cfg), C.byref(w), _ptr(x_packed), _ptr(v_out), _ptr(ctx_packed),
+                                int(ctx_len), _ptr(txt_emb), _ptr(y), _ptr(ids), float(sigma), float(sigma_next),
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "mmdit_step_ctx")
 
 
 def mmdit_schedule(n_steps: int, img_len: int, base_shift=0.5, max_shift=1.15, sigma_terminal=0.0,

@@ -523,13 +523,21 @@ int mmdit_step_workspace(const mmdit_config* cfg, size_t* bytes) {
   return MMDIT_OK;
 }
 
-int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, void* v_out,
-               const void* txt_emb, const void* y, const int32_t* ids, double sigma,
-               double sigma_next, void* ws, size_t ws_bytes, void* hip_stream) {
+// One step; the image stream holds Lg = Li - ctx_len generated tokens
+// followed by ctx_len context tokens per batch (ctx_packed [B, ctx_len,
+// in_ch] float32). Only the generated rows get the final layer and update.
+static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, void* v_out,
+                     const void* ctx_packed, int32_t ctx_len, const void* txt_emb, const void* y,
+                     const int32_t* ids, double sigma, double sigma_next, void* ws, size_t ws_bytes,
+                     void* hip_stream) {
   Geo g;
   int r;
   if ((r = check_config(cfg, g))) return r;
   if (!w || !x_packed || !y || !ids) return fail(MMDIT_ERR_NULL, "NULL weights, latent, y or ids");
+  if (ctx_len < 0 || ctx_len >= g.Li)
+    return fail(MMDIT_ERR_SHAPE, "ctx_len %d must be in [0, img_len %d)", ctx_len, g.Li);
+  if (ctx_len > 0 && !ctx_packed) return fail(MMDIT_ERR_NULL, "ctx_packed is NULL with ctx_len > 0");
+  const int Lg = g.Li - ctx_len;  // generated image tokens per batch
   if (g.Lt > 0 && !txt_emb) return fail(MMDIT_ERR_NULL, "txt_emb is NULL with txt_len > 0");
   if ((cfg->n_double > 0 && !w->dbl) || (cfg->n_single > 0 && !w->sgl)) return fail(MMDIT_ERR_NULL, "block weight arrays are NULL");
   if (!std::isfinite(sigma) || !std::isfinite(sigma_next)) return fail(MMDIT_ERR_SHAPE, "sigma values must be finite");
@@ -606,7 +614,17 @@ int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, 
 
   // input projections into the f32 residual
   const void* xa = x_packed;
-  if (g.bf16) {
+  if (ctx_len > 0) {
+    // per batch: [generated rows; context rows] staged in the activation dtype
+    const int64_t ci = cfg->in_ch;
+    for (int b = 0; b < B; ++b) {
+      char* dst = ptr(ws, lay.xin + (size_t)b * g.Li * ci * g.esz);
+      HIP_TRY(launch_convert((const float*)x_packed + (size_t)b * Lg * ci, true, dst, !g.bf16, (int64_t)Lg * ci, c.s));
+      HIP_TRY(launch_convert((const float*)ctx_packed + (size_t)b * ctx_len * ci, true, dst + (size_t)Lg * ci * g.esz,
+                             !g.bf16, (int64_t)ctx_len * ci, c.s));
+    }
+    xa = ptr(ws, lay.xin);
+  } else if (g.bf16) {
     HIP_TRY(launch_convert(x_packed, true, ptr(ws, lay.xin), false, (int64_t)B * g.Li * cfg->in_ch, c.s));
     xa = ptr(ws, lay.xin);
   }
@@ -647,18 +665,35 @@ int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, 
       if ((r = run_single(c, w->sgl[i], &parts[1], 1, true, table, ws, lay.blk))) return r;
     }
   }
-  // final layer on the image rows, Euler update fused into the epilogue
+  // final layer on the generated image rows, Euler update fused into the epilogue
   Part fin = parts[1];
+  fin.len = Lg;
+  fin.x_in.rows_per_batch = Lg;  // batch stride stays Li rows
   fin.mod = mods + lay.mod_final;
   void* xn = ptr(ws, lay.blk.xn);
   if ((r = run_ln(c, &fin, 1, 2 * h, 0, h, true, xn))) return r;
   GemmProblem f = base_problem(w->final_lin);
-  f.A = xn; f.lda = h; f.M = B * g.Li;
-  f.res_out = rows_of(x_packed, 0, g.Li, cfg->in_ch, 4);
+  f.A = xn; f.lda = h; f.M = B * Lg;
+  f.res_out = rows_of(x_packed, 0, Lg, cfg->in_ch, 4);
   f.res_in = f.res_out;
   f.dsigma = (float)(sigma_next - sigma);
   f.v_out = (float*)v_out;
   return gemm(c, &f, 1, EPI_EULER);
+}
+
+int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, void* v_out,
+               const void* txt_emb, const void* y, const int32_t* ids, double sigma,
+               double sigma_next, void* ws, size_t ws_bytes, void* hip_stream) {
+  return step_impl(cfg, w, x_packed, v_out, nullptr, 0, txt_emb, y, ids, sigma, sigma_next, ws, ws_bytes,
+                   hip_stream);
+}
+
+int mmdit_step_ctx(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, void* v_out,
+                   const void* ctx_packed, int32_t ctx_len, const void* txt_emb, const void* y,
+                   const int32_t* ids, double sigma, double sigma_next, void* ws, size_t ws_bytes,
+                   void* hip_stream) {
+  return step_impl(cfg, w, x_packed, v_out, ctx_packed, ctx_len, txt_emb, y, ids, sigma, sigma_next, ws,
+                   ws_bytes, hip_stream);
 }
 
 int mmdit_pack_latents(const void* z, void* x, int32_t B, int32_t C, int32_t H, int32_t W,

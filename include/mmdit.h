@@ -169,6 +169,27 @@ int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w,
                const int32_t* ids, double sigma, double sigma_next,
                void* ws, size_t ws_bytes, void* hip_stream);
 
+/* One denoising step with reference-image tokens in the image stream
+ * (FLUX.1-Kontext instruction editing: stable-diffusion.rs README, the
+ * Kontext example with a reference picture; the frame axis of the ids:
+ * mflux-rs card, 3D RoPE visualiser, axis 0 temporal). Reading where the
+ * pages are silent: per batch, the image stream is the Lg = img_len - ctx_len
+ * generated tokens followed by the ctx_len context tokens; the context latent
+ * goes through the same input projection; ids carry frame 1 for the context
+ * tokens (the caller builds them); the velocity and the update cover the
+ * generated tokens only.
+ * cfg->dims.img_len = Lg + ctx_len, 0 <= ctx_len < img_len (ctx_len 0 is
+ * mmdit_step). x_packed, v_out [B, Lg, in_ch]: as for mmdit_step.
+ * ctx_packed [B, ctx_len, in_ch]: device float32 packed context latent, read
+ * only. ids [txt_len + img_len, 3]: text, generated, then context rows.
+ * The workspace is mmdit_step_workspace(cfg). Errors as for mmdit_step;
+ * MMDIT_ERR_SHAPE for ctx_len out of range, MMDIT_ERR_NULL for a NULL
+ * ctx_packed with ctx_len > 0. */
+int mmdit_step_ctx(const mmdit_config* cfg, const mmdit_model_w* w,
+                   void* x_packed, void* v_out, const void* ctx_packed, int32_t ctx_len,
+                   const void* txt_emb, const void* y, const int32_t* ids,
+                   double sigma, double sigma_next, void* ws, size_t ws_bytes, void* hip_stream);
+
 /* ---- helpers ---------------------------------------------------------- */
 
 /* Host. sigmas[0..n_steps] of the shifted flow-matching schedule: t_i = 1 - i/n,

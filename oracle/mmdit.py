@@ -300,14 +300,22 @@ def final_layer(g: Dict[str, np.ndarray], img: np.ndarray, vec: np.ndarray) -> n
 # ------------------------------------------------------------------ step ---
 def step(g: Dict[str, np.ndarray], dbl: Sequence, sgl: Sequence, X: np.ndarray, T: np.ndarray,
          y: np.ndarray, ids: np.ndarray, sigma: float, sigma_next: float, heads: int,
-         axes_dim=(16, 56, 56), theta: float = 10000.0):
+         axes_dim=(16, 56, 56), theta: float = 10000.0, Xc: np.ndarray = None):
     """One denoising step (mflux-rs architecture cards and "Flow-Matching
     Euler"): project packed latents [B, Li, 64] and text embeddings
     [B, Lt, 4096] to width h, run the dual-stream blocks, concatenate
     [txt; img], run the single-stream blocks, take the image rows, apply the
-    final layer to get v, and return (X + (sigma_next - sigma) v, v)."""
+    final layer to get v, and return (X + (sigma_next - sigma) v, v).
+
+    Xc [B, Lc, 64]: optional packed reference-image latent (FLUX.1-Kontext
+    editing, stable-diffusion.rs README; frame axis of the ids, mflux-rs 3D
+    RoPE visualiser). Reading: its tokens follow the generated ones in the
+    image stream, through the same input projection, with ids carrying frame
+    1 (ids covers [txt; generated; context]); v and the update are taken for
+    the generated rows only."""
     dt = X.dtype
-    img = linear(X, g["img_in_w"], g["img_in_b"])
+    Lg = X.shape[1]
+    img = linear(X if Xc is None else np.concatenate([X, Xc.astype(dt)], axis=1), g["img_in_w"], g["img_in_b"])
     txt = linear(T.astype(dt), g["txt_in_w"], g["txt_in_b"])
     vec = conditioning_vec(g, sigma, y.astype(dt), temb_dim=g["time_in0_w"].shape[1])
     for i in range(len(dbl)):
@@ -315,7 +323,7 @@ def step(g: Dict[str, np.ndarray], dbl: Sequence, sgl: Sequence, X: np.ndarray, 
     x = np.concatenate([txt, img], axis=1)
     for i in range(len(sgl)):
         x = single_block(sgl[i], x, vec, ids, heads, axes_dim, theta)
-    v = final_layer(g, x[:, T.shape[1]:], vec)
+    v = final_layer(g, x[:, T.shape[1]:T.shape[1] + Lg], vec)
     return euler_update(X, v, sigma, sigma_next), v
 
 

@@ -132,6 +132,56 @@ def test_step_bf16_full_tokens_two_plus_two_blocks():
     assert_parity(Xg, Xr, "bf16", "bf16 step x_next")
 
 
+def ctx_ids(s: I.Shape, cgh: int, cgw: int) -> np.ndarray:
+    """[txt; generated (frame 0); context (frame 1)] ids."""
+    return np.concatenate([oracle.make_ids(s.grid_h, s.grid_w, s.txt_len),
+                           oracle.make_ids(cgh, cgw, 0, frame=1)]).astype(np.int32)
+
+
+def run_step_ctx(s: I.Shape, cgh: int, cgw: int, sig_i: int, n_steps: int = 4):
+    """mmdit_step_ctx with a context latent of cgh x cgw packed tokens against
+    the oracle step with the same context."""
+    t = torch()
+    g, dbl, sgl = model_numpy(s)
+    inp = I.step_inputs(s)
+    Lc = cgh * cgw
+    Xc = np.random.default_rng(1000 + s.cfg_id).standard_normal((s.batch, Lc, s.in_ch)).astype(np.float32)
+    ids = ctx_ids(s, cgh, cgw)
+    sig = oracle.schedule(n_steps, s.img_len)
+    dt = dtype_code(s.dtype)
+    cfg = bd.make_config(s)
+    cfg.dims.img_len = s.img_len + Lc
+    M = bd.ModelW(g, [bd.DoubleW(d, dt, "cuda") for d in dbl], [bd.SingleW(w, dt, "cuda") for w in sgl], dt, "cuda")
+    z = t.from_numpy(inp["z"]).cuda()
+    X = t.empty((s.batch, s.img_len, s.in_ch), dtype=t.float32, device="cuda")
+    bd.mmdit_pack_latents(z, X)
+    v = t.empty_like(X)
+    ws = workspace(bd.mmdit_step_workspace(cfg))
+    print(f"step_ctx B={s.batch} h={s.hidden} {s.n_double}+{s.n_single} blocks Lt={s.txt_len} Lg={s.img_len} "
+          f"Lc={Lc} {s.dtype}", flush=True)
+    bd.mmdit_step_ctx(cfg, M.c(), X, v, t.from_numpy(Xc).cuda(), Lc, up(inp["T"], s.dtype), up(inp["y"], s.dtype),
+                      up_i32(ids), sig[sig_i], sig[sig_i + 1], ws)
+    sync()
+    Xr, vr = oracle.step(g, dbl, sgl, oracle.pack_latents(inp["z"]), inp["T"], inp["y"], ids, sig[sig_i],
+                         sig[sig_i + 1], s.heads, s.axes_dim, s.theta, Xc=Xc)
+    return (down(X), down(v)), (Xr, vr)
+
+
+def test_step_ctx_f32_tiny_batch2():
+    s = dataclasses.replace(TINY_F32, batch=2, txt_len=11, grid_h=6, grid_w=5, cfg_id=45)
+    (Xg, vg), (Xr, vr) = run_step_ctx(s, 4, 7, 1)
+    assert_parity(vg, vr, "f32", "step_ctx v")
+    assert_parity(Xg, Xr, "f32", "step_ctx x_next")
+
+
+def test_step_ctx_bf16_width3072():
+    # h 3072 / 24 heads, 256 text + 32x32 generated + 32x32 context tokens
+    s = dataclasses.replace(I.CFG4, n_double=1, n_single=1, txt_len=256, grid_h=32, grid_w=32, cfg_id=46)
+    (Xg, vg), (Xr, vr) = run_step_ctx(s, 32, 32, 0)
+    assert_parity(vg, vr, "bf16", "bf16 step_ctx v")
+    assert_parity(Xg, Xr, "bf16", "bf16 step_ctx x_next")
+
+
 def test_step_quantised_full_tokens_one_plus_one_blocks():
     s = dataclasses.replace(I.CFG5, n_double=1, n_single=1)
     g, dbl, sgl = model_numpy(s)

@@ -405,6 +405,48 @@ def test_step_gate_zero_reduces_to_final_layer():
     assert np.array_equal(v, oracle.final_layer(g, img, vec))
 
 
+def _ctx_case():
+    s = tiny_shape(txt_len=3, grid_h=2, grid_w=3)
+    g = I.global_weights(s)
+    dbl = [I.double_block_weights(s, i) for i in range(2)]
+    sgl = [I.single_block_weights(s, i) for i in range(2)]
+    inp = I.step_inputs(s)
+    X = oracle.pack_latents(inp["z"])
+    Xc = np.random.default_rng(21).standard_normal((1, 5, X.shape[2])).astype(np.float32)
+    ids = np.concatenate([oracle.make_ids(s.grid_h, s.grid_w, s.txt_len),
+                          np.array([[1, r, c] for r, c in [(0, 0), (0, 1), (1, 0), (1, 1), (2, 0)]], np.int32)])
+    return s, g, dbl, sgl, inp, X, Xc, ids
+
+
+def test_step_context_tokens_are_a_set():
+    # Reference-image tokens reach the generated rows only through joint
+    # attention, which sees them as a set: permuting them together with their
+    # ids leaves v unchanged; dropping them changes v.
+    s, g, dbl, sgl, inp, X, Xc, ids = _ctx_case()
+    args = (_f64(g), [_f64(w) for w in dbl], [_f64(w) for w in sgl], _f64(X), _f64(inp["T"]), _f64(inp["y"]))
+    Xn, v = oracle.step(*args, ids, 0.8, 0.6, s.heads, Xc=_f64(Xc))
+    assert v.shape == X.shape and Xn.shape == X.shape
+    perm = np.random.default_rng(22).permutation(Xc.shape[1])
+    Lf = s.txt_len + s.img_len
+    ids_p = np.concatenate([ids[:Lf], ids[Lf:][perm]])
+    _, vp = oracle.step(*args, ids_p, 0.8, 0.6, s.heads, Xc=_f64(Xc[:, perm]))
+    assert rel_l2(vp, v) < 1e-12
+    _, v0 = oracle.step(*args, ids[:Lf], 0.8, 0.6, s.heads)
+    assert rel_l2(v0, v) > 1e-3
+
+
+def test_step_context_gate_zero_takes_generated_rows():
+    # With every modulation zero the blocks are the identity, so v is the
+    # final layer of the generated tokens' input projection whatever the
+    # context tokens hold: the update uses exactly the first Lg image rows.
+    s, g, dbl, sgl, inp, X, Xc, ids = _ctx_case()
+    dbl = [I.zero_modulation(w) for w in dbl]
+    sgl = [I.zero_modulation(w) for w in sgl]
+    _, v = oracle.step(g, dbl, sgl, X, inp["T"], inp["y"], ids, 1.0, 0.9, s.heads, Xc=Xc)
+    vec = oracle.conditioning_vec(g, 1.0, inp["y"])
+    assert np.array_equal(v, oracle.final_layer(g, oracle.linear(X, g["img_in_w"], g["img_in_b"]), vec))
+
+
 # ------------------------------------------------------- schedule, Euler ---
 def test_schedule_page_invariants():
     sh = PAGES["shift"]
