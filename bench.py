@@ -299,7 +299,7 @@ def main():
 
         def kstep(i):
             j = i % 4
-            bd.mmdit_step_ctx(ck, mc, Xk, v, Xc, Lc, T, y, idk, sig[j], sig[j + 1], wsk)
+            bd.mmdit_step_ex(ck, mc, Xk, v, T, y, idk, sig[j], sig[j + 1], wsk, ctx_packed=Xc, ctx_len=Lc)
         for i in range(2):
             kstep(i)
         kn = max(a.steps // 2, 3)
@@ -310,6 +310,30 @@ def main():
                                "frac_of_bf16_peak": round(kfl / kms / 1e9 / PEAK_BF16_TFLOPS, 4)}
         log(f"kontext step (L {s.txt_len + 2 * s.img_len}): {kms:.2f} ms ({kfl / kms / 1e9:.0f} TFLOP/s)")
         del wsk, Xk, Xc
+
+        # guidance-distilled (dev) generation: the same blocks plus a guidance
+        # embedder, 50 shifted steps at guidance 4.0, timed as one loop
+        Gd = RI._Gen(44, dev)
+        dt16 = torch.bfloat16
+        M.guidance = [RI._linear(Gd, s.hidden, s.temb_dim, dt16), RI._linear(Gd, s.hidden, s.hidden, dt16)]
+        keep = (M._dbl_arr, M._sgl_arr)  # mc's block arrays stay alive: M.c() builds new ones
+        mdc = M.c()
+        nd = 50
+        sigd = bd.mmdit_schedule(nd, s.img_len)
+        Xd = X.clone()
+        bd.mmdit_step_ex(cfg, mdc, Xd, v, T, y, ids, sigd[0], sigd[1], ws, guidance=4.0)
+        Xd.copy_(X)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(nd):
+            bd.mmdit_step_ex(cfg, mdc, Xd, v, T, y, ids, sigd[i], sigd[i + 1], ws, guidance=4.0)
+        torch.cuda.synchronize()
+        dsec = time.perf_counter() - t1
+        out["dev_generation"] = {"steps": nd, "guidance": 4.0, "seconds": round(dsec, 3),
+                                 "ms_per_step": round(dsec * 1e3 / nd, 3)}
+        log(f"dev generation: {nd} steps in {dsec:.2f} s ({dsec * 1e3 / nd:.2f} ms/step)")
+        M.guidance = None
+        del Xd, mdc, keep
 
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

@@ -67,7 +67,13 @@ class mmdit_model_w(C.Structure):
     _fields_ = [("img_in", mmdit_linear), ("txt_in", mmdit_linear), ("time_in0", mmdit_linear),
                 ("time_in1", mmdit_linear), ("vec_in0", mmdit_linear), ("vec_in1", mmdit_linear),
                 ("final_mod", mmdit_linear), ("final_lin", mmdit_linear),
-                ("dbl", C.POINTER(mmdit_double_w)), ("sgl", C.POINTER(mmdit_single_w))]
+                ("dbl", C.POINTER(mmdit_double_w)), ("sgl", C.POINTER(mmdit_single_w)),
+                ("guidance_in0", mmdit_linear), ("guidance_in1", mmdit_linear)]
+
+
+class mmdit_step_opts(C.Structure):
+    _fields_ = [("ctx_packed", C.c_void_p), ("ctx_len", C.c_int32), ("has_guidance", C.c_int32),
+                ("guidance", C.c_double)]
 
 
 # Every function the header declares, with its ctypes signature.
@@ -82,8 +88,8 @@ _SIGS = {
                                          _P, C.c_size_t, _P]),
     "mmdit_step": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(mmdit_model_w), _P, _P, _P, _P, _P,
                              C.c_double, C.c_double, _P, C.c_size_t, _P]),
-    "mmdit_step_ctx": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(mmdit_model_w), _P, _P, _P, C.c_int32, _P,
-                                 _P, _P, C.c_double, C.c_double, _P, C.c_size_t, _P]),
+    "mmdit_step_ex": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(mmdit_model_w), _P, _P, _P, _P, _P,
+                                C.c_double, C.c_double, C.POINTER(mmdit_step_opts), _P, C.c_size_t, _P]),
     "mmdit_schedule": (C.c_int, [C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double, C.c_int32, _P]),
     "mmdit_make_ids": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P]),
     "mmdit_pack_latents": (C.c_int, [_P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P]),
@@ -219,6 +225,7 @@ class SingleW:
 QUANT_POLICY = {"qkv": 4, "fc1": 4, "lin1": 4, "proj": 8, "fc2": 8, "lin2": 8}
 
 GLOBAL_LINEARS = ("img_in", "txt_in", "time_in0", "time_in1", "vec_in0", "vec_in1", "final_mod", "final_lin")
+GUIDANCE_LINEARS = ("guidance_in0", "guidance_in1")
 
 
 class ModelW:
@@ -230,17 +237,23 @@ class ModelW:
             names = {n: n for n in GLOBAL_LINEARS}
             names["final_lin"] = "final"
             linears = {n: Linear.from_numpy(g[k + "_w"], g[k + "_b"], dtype, device) for n, k in names.items()}
+            if g.get("guidance_in0_w") is not None:
+                for n in GUIDANCE_LINEARS:
+                    linears[n] = Linear.from_numpy(g[n + "_w"], g[n + "_b"], dtype, device)
         for n in GLOBAL_LINEARS:
             setattr(self, n, linears[n])
+        # guidance embedder (guidance-distilled models), absent -> zeroed structs
+        self.guidance = [linears[n] for n in GUIDANCE_LINEARS] if GUIDANCE_LINEARS[0] in linears else None
         self.dbl: List = list(dbl)
         self.sgl: List = list(sgl)
 
     def c(self) -> mmdit_model_w:
         self._dbl_arr = (mmdit_double_w * max(1, len(self.dbl)))(*[d.c() for d in self.dbl])
         self._sgl_arr = (mmdit_single_w * max(1, len(self.sgl)))(*[s.c() for s in self.sgl])
+        gl = [x.c() for x in self.guidance] if self.guidance else [mmdit_linear(), mmdit_linear()]
         return mmdit_model_w(*[getattr(self, n).c() for n in GLOBAL_LINEARS],
                              C.cast(self._dbl_arr, C.POINTER(mmdit_double_w)),
-                             C.cast(self._sgl_arr, C.POINTER(mmdit_single_w)))
+                             C.cast(self._sgl_arr, C.POINTER(mmdit_single_w)), *gl)
 
 
 def make_dims(s, dtype: Optional[int] = None) -> mmdit_dims:
@@ -303,12 +316,17 @@ def mmdit_step(cfg, w: mmdit_model_w, x_packed, v_out, txt_emb, y, ids, sigma: f
            "mmdit_step")
 
 
-def mmdit_step_ctx(cfg, w: mmdit_model_w, x_packed, v_out, ctx_packed, ctx_len: int, txt_emb, y, ids,
-                   sigma: float, sigma_next: float, ws, stream=None):
-    _check(lib().mmdit_step_ctx(C.byref(cfg), C.byref(w), _ptr(x_packed), _ptr(v_out), _ptr(ctx_packed),
-                                int(ctx_len), _ptr(txt_emb), _ptr(y), _ptr(ids), float(sigma), float(sigma_next),
-                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
-           "mmdit_step_ctx")
+def mmdit_step_ex(cfg, w: mmdit_model_w, x_packed, v_out, txt_emb, y, ids, sigma: float, sigma_next: float, ws,
+                  ctx_packed=None, ctx_len: int = 0, guidance: Optional[float] = None, stream=None):
+    o = mmdit_step_opts()
+    o.ctx_packed = _ptr(ctx_packed)
+    o.ctx_len = int(ctx_len)
+    o.has_guidance = 0 if guidance is None else 1
+    o.guidance = 0.0 if guidance is None else float(guidance)
+    _check(lib().mmdit_step_ex(C.byref(cfg), C.byref(w), _ptr(x_packed), _ptr(v_out), _ptr(txt_emb), _ptr(y),
+                               _ptr(ids), float(sigma), float(sigma_next), C.byref(o), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)),
+           "mmdit_step_ex")
 
 
 def mmdit_schedule(n_steps: int, img_len: int, base_shift=0.5, max_shift=1.15, sigma_terminal=0.0,

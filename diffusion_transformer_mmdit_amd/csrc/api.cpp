@@ -527,17 +527,26 @@ int mmdit_step_workspace(const mmdit_config* cfg, size_t* bytes) {
 // followed by ctx_len context tokens per batch (ctx_packed [B, ctx_len,
 // in_ch] float32). Only the generated rows get the final layer and update.
 static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, void* v_out,
-                     const void* ctx_packed, int32_t ctx_len, const void* txt_emb, const void* y,
-                     const int32_t* ids, double sigma, double sigma_next, void* ws, size_t ws_bytes,
-                     void* hip_stream) {
+                     const void* txt_emb, const void* y, const int32_t* ids, double sigma, double sigma_next,
+                     const mmdit_step_opts* opts, void* ws, size_t ws_bytes, void* hip_stream) {
   Geo g;
   int r;
   if ((r = check_config(cfg, g))) return r;
   if (!w || !x_packed || !y || !ids) return fail(MMDIT_ERR_NULL, "NULL weights, latent, y or ids");
+  const mmdit_step_opts none{};
+  if (!opts) opts = &none;
+  const void* ctx_packed = opts->ctx_packed;
+  const int ctx_len = opts->ctx_len;
   if (ctx_len < 0 || ctx_len >= g.Li)
     return fail(MMDIT_ERR_SHAPE, "ctx_len %d must be in [0, img_len %d)", ctx_len, g.Li);
   if (ctx_len > 0 && !ctx_packed) return fail(MMDIT_ERR_NULL, "ctx_packed is NULL with ctx_len > 0");
   const int Lg = g.Li - ctx_len;  // generated image tokens per batch
+  const bool guided = w->guidance_in0.w != nullptr;
+  if (guided) {
+    if (!opts->has_guidance)
+      return fail(MMDIT_ERR_NULL, "the model has a guidance embedder: pass a guidance value (mmdit_step_ex)");
+    if (!std::isfinite(opts->guidance)) return fail(MMDIT_ERR_SHAPE, "guidance must be finite");
+  }
   if (g.Lt > 0 && !txt_emb) return fail(MMDIT_ERR_NULL, "txt_emb is NULL with txt_len > 0");
   if ((cfg->n_double > 0 && !w->dbl) || (cfg->n_single > 0 && !w->sgl)) return fail(MMDIT_ERR_NULL, "block weight arrays are NULL");
   if (!std::isfinite(sigma) || !std::isfinite(sigma_next)) return fail(MMDIT_ERR_SHAPE, "sigma values must be finite");
@@ -548,6 +557,10 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   if ((r = check_gemv(w->time_in1, h, h, "time_in1"))) return r;
   if ((r = check_gemv(w->vec_in0, h, cfg->vec_in_dim, "vec_in0"))) return r;
   if ((r = check_gemv(w->vec_in1, h, h, "vec_in1"))) return r;
+  if (guided) {
+    if ((r = check_gemv(w->guidance_in0, h, cfg->temb_dim, "guidance_in0"))) return r;
+    if ((r = check_gemv(w->guidance_in1, h, h, "guidance_in1"))) return r;
+  }
   if ((r = check_gemv(w->final_mod, 2 * h, h, "final_mod"))) return r;
   if ((r = check_linear(w->final_lin, cfg->in_ch, h, g, "final_lin"))) return r;
   for (int i = 0; i < cfg->n_double; ++i) {
@@ -576,6 +589,11 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   HIP_TRY(launch_timestep_embedding(temb, B, cfg->temb_dim, sigma, c.s));
   if ((r = gemv(c, w->time_in0, temb, true, cfg->temb_dim, hid, h, false, false))) return r;
   if ((r = gemv(c, w->time_in1, hid, true, h, vec, h, true, false))) return r;
+  if (guided) {  // + G1(SiLU(G0(temb(guidance))))
+    HIP_TRY(launch_timestep_embedding(temb, B, cfg->temb_dim, opts->guidance, c.s));
+    if ((r = gemv(c, w->guidance_in0, temb, true, cfg->temb_dim, hid, h, false, false))) return r;
+    if ((r = gemv(c, w->guidance_in1, hid, true, h, vec, h, true, true))) return r;
+  }
   if ((r = gemv(c, w->vec_in0, y, false, cfg->vec_in_dim, hid, h, false, false))) return r;
   if ((r = gemv(c, w->vec_in1, hid, true, h, vec, h, true, true))) return r;
   // every block's modulation up front, all from SiLU(vec): batched into
@@ -684,16 +702,13 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
 int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, void* v_out,
                const void* txt_emb, const void* y, const int32_t* ids, double sigma,
                double sigma_next, void* ws, size_t ws_bytes, void* hip_stream) {
-  return step_impl(cfg, w, x_packed, v_out, nullptr, 0, txt_emb, y, ids, sigma, sigma_next, ws, ws_bytes,
-                   hip_stream);
+  return step_impl(cfg, w, x_packed, v_out, txt_emb, y, ids, sigma, sigma_next, nullptr, ws, ws_bytes, hip_stream);
 }
 
-int mmdit_step_ctx(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, void* v_out,
-                   const void* ctx_packed, int32_t ctx_len, const void* txt_emb, const void* y,
-                   const int32_t* ids, double sigma, double sigma_next, void* ws, size_t ws_bytes,
-                   void* hip_stream) {
-  return step_impl(cfg, w, x_packed, v_out, ctx_packed, ctx_len, txt_emb, y, ids, sigma, sigma_next, ws,
-                   ws_bytes, hip_stream);
+int mmdit_step_ex(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, void* v_out,
+                  const void* txt_emb, const void* y, const int32_t* ids, double sigma, double sigma_next,
+                  const mmdit_step_opts* opts, void* ws, size_t ws_bytes, void* hip_stream) {
+  return step_impl(cfg, w, x_packed, v_out, txt_emb, y, ids, sigma, sigma_next, opts, ws, ws_bytes, hip_stream);
 }
 
 int mmdit_pack_latents(const void* z, void* x, int32_t B, int32_t C, int32_t H, int32_t W,

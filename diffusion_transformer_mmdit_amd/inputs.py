@@ -184,6 +184,19 @@ def global_weights(s: Shape) -> Dict[str, np.ndarray]:
             for i, n in enumerate(GLOBAL_TENSORS)}
 
 
+GUIDANCE_TENSORS = ["guidance_in0_w", "guidance_in0_b", "guidance_in1_w", "guidance_in1_b"]
+GUIDANCE_INDEX0 = 100  # tensor_idx of the first guidance tensor (clear of GLOBAL_TENSORS)
+
+
+def guidance_weights(s: Shape) -> Dict[str, np.ndarray]:
+    """Guidance embedder of a guidance-distilled model: temb_dim -> h -> h."""
+    h = s.hidden
+    shapes = {"guidance_in0_w": (h, s.temb_dim), "guidance_in0_b": (h,),
+              "guidance_in1_w": (h, h), "guidance_in1_b": (h,)}
+    return {n: _draw(n, shapes[n], (s.cfg_id, GLOBAL_BLOCK, GUIDANCE_INDEX0 + i), s.dtype)
+            for i, n in enumerate(GUIDANCE_TENSORS)}
+
+
 def zero_modulation(w: Dict) -> Dict:
     """Copy of block weights with the modulation linear set to zero."""
     if "txt" in w:

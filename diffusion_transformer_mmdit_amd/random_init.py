@@ -76,7 +76,7 @@ def single_block(s: Shape, seed: int, device="cuda", quant: Optional[dict] = Non
                       k_norm=G.normal(d, mean=1.0, dtype=dt))
 
 
-def model(s: Shape, seed: int, device="cuda", quant: Optional[dict] = None) -> bd.ModelW:
+def model(s: Shape, seed: int, device="cuda", quant: Optional[dict] = None, guidance: bool = False) -> bd.ModelW:
     G = _Gen(seed, device)
     dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
     h = s.hidden
@@ -84,6 +84,9 @@ def model(s: Shape, seed: int, device="cuda", quant: Optional[dict] = None) -> b
            "time_in0": _linear(G, h, s.temb_dim, dt), "time_in1": _linear(G, h, h, dt),
            "vec_in0": _linear(G, h, s.vec_in_dim, dt), "vec_in1": _linear(G, h, h, dt),
            "final_mod": _linear(G, 2 * h, h, dt), "final_lin": _linear(G, s.in_ch, h, dt)}
+    if guidance:  # guidance embedder of a guidance-distilled model
+        lin["guidance_in0"] = _linear(G, h, s.temb_dim, dt)
+        lin["guidance_in1"] = _linear(G, h, h, dt)
     dbl = [double_block(s, seed * 1000 + 1 + i, device, quant) for i in range(s.n_double)]
     sgl = [single_block(s, seed * 1000 + 500 + i, device, quant) for i in range(s.n_single)]
     return bd.ModelW(None, dbl, sgl, linears=lin)

@@ -124,11 +124,16 @@ typedef struct {
 /* Whole-model weights. img_in: in_ch -> h. txt_in: txt_in_dim -> h.
  * time_in0: temb_dim -> h, time_in1: h -> h. vec_in0: vec_in_dim -> h,
  * vec_in1: h -> h. final_mod: h -> 2h split (shift, scale). final_lin: h -> in_ch.
- * dbl / sgl: HOST arrays of n_double / n_single block weight structs. */
+ * dbl / sgl: HOST arrays of n_double / n_single block weight structs.
+ * guidance_in0: temb_dim -> h, guidance_in1: h -> h: the guidance embedder of
+ * guidance-distilled models (FLUX.1-dev: mflux-rs card, generation with a
+ * guidance scale; mistral.rs article, FluxStepper guidance_scale). All-zero
+ * (guidance_in0.w == NULL) for models without one (schnell). */
 typedef struct {
   mmdit_linear img_in, txt_in, time_in0, time_in1, vec_in0, vec_in1, final_mod, final_lin;
   const mmdit_double_w* dbl;
   const mmdit_single_w* sgl;
+  mmdit_linear guidance_in0, guidance_in1;
 } mmdit_model_w;
 
 /* Workspace sizes in bytes (host-only; no device work). */
@@ -169,26 +174,45 @@ int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w,
                const int32_t* ids, double sigma, double sigma_next,
                void* ws, size_t ws_bytes, void* hip_stream);
 
-/* One denoising step with reference-image tokens in the image stream
- * (FLUX.1-Kontext instruction editing: stable-diffusion.rs README, the
- * Kontext example with a reference picture; the frame axis of the ids:
- * mflux-rs card, 3D RoPE visualiser, axis 0 temporal). Reading where the
- * pages are silent: per batch, the image stream is the Lg = img_len - ctx_len
- * generated tokens followed by the ctx_len context tokens; the context latent
- * goes through the same input projection; ids carry frame 1 for the context
- * tokens (the caller builds them); the velocity and the update cover the
- * generated tokens only.
- * cfg->dims.img_len = Lg + ctx_len, 0 <= ctx_len < img_len (ctx_len 0 is
- * mmdit_step). x_packed, v_out [B, Lg, in_ch]: as for mmdit_step.
- * ctx_packed [B, ctx_len, in_ch]: device float32 packed context latent, read
- * only. ids [txt_len + img_len, 3]: text, generated, then context rows.
- * The workspace is mmdit_step_workspace(cfg). Errors as for mmdit_step;
- * MMDIT_ERR_SHAPE for ctx_len out of range, MMDIT_ERR_NULL for a NULL
- * ctx_packed with ctx_len > 0. */
-int mmdit_step_ctx(const mmdit_config* cfg, const mmdit_model_w* w,
-                   void* x_packed, void* v_out, const void* ctx_packed, int32_t ctx_len,
-                   const void* txt_emb, const void* y, const int32_t* ids,
-                   double sigma, double sigma_next, void* ws, size_t ws_bytes, void* hip_stream);
+/* Options of mmdit_step_ex; a zeroed struct (or opts == NULL) is mmdit_step.
+ *
+ * Reference-image tokens (FLUX.1-Kontext instruction editing:
+ * stable-diffusion.rs README, the Kontext example with a reference picture;
+ * the frame axis of the ids: mflux-rs card, 3D RoPE visualiser, axis 0
+ * temporal). Reading where the pages are silent: per batch, the image stream
+ * is the Lg = img_len - ctx_len generated tokens followed by the ctx_len
+ * context tokens; the context latent goes through the same input projection;
+ * ids carry frame 1 for the context tokens (the caller builds them); the
+ * velocity and the update cover the generated tokens only.
+ *   ctx_packed [B, ctx_len, in_ch]: device float32 packed context latent, read
+ *   only; NULL when ctx_len is 0. 0 <= ctx_len < cfg->dims.img_len.
+ *
+ * Guidance (FLUX.1-dev: mflux-rs card, generation with guidance 3.5;
+ * mistral.rs article: guidance models run 50 shifted steps with
+ * guidance_scale 4.0). Reading: like the timestep, the guidance value g is
+ * embedded as temb(1000 g) and mapped by guidance_in0 / SiLU / guidance_in1;
+ * the result is added to the conditioning vector.
+ *   has_guidance: 1 to pass `guidance`; required (and only used) when the
+ *   model has a guidance embedder. */
+typedef struct {
+  const void* ctx_packed;
+  int32_t ctx_len;
+  int32_t has_guidance;
+  double guidance;
+} mmdit_step_opts;
+
+/* One denoising step with options (context tokens, guidance). Arguments as
+ * for mmdit_step, except: cfg->dims.img_len counts generated plus context
+ * tokens; x_packed, v_out are [B, Lg, in_ch]; ids [txt_len + img_len, 3] are
+ * text, generated, then context rows. The workspace is
+ * mmdit_step_workspace(cfg). Errors as for mmdit_step; MMDIT_ERR_SHAPE for
+ * ctx_len out of range or a non-finite guidance; MMDIT_ERR_NULL for a NULL
+ * ctx_packed with ctx_len > 0, or a guidance model called without a guidance
+ * value (mmdit_step on such a model fails the same way). */
+int mmdit_step_ex(const mmdit_config* cfg, const mmdit_model_w* w,
+                  void* x_packed, void* v_out, const void* txt_emb, const void* y,
+                  const int32_t* ids, double sigma, double sigma_next, const mmdit_step_opts* opts,
+                  void* ws, size_t ws_bytes, void* hip_stream);
 
 /* ---- helpers ---------------------------------------------------------- */
 

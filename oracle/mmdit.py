@@ -278,16 +278,29 @@ def timestep_embedding(sigma: float, dim: int = 256, max_period: float = 10000.0
     return np.concatenate([np.cos(a), np.sin(a)]).astype(dtype)
 
 
-def conditioning_vec(g: Dict[str, np.ndarray], sigma, y: np.ndarray, temb_dim: int = 256) -> np.ndarray:
+def conditioning_vec(g: Dict[str, np.ndarray], sigma, y: np.ndarray, temb_dim: int = 256,
+                     guidance=None) -> np.ndarray:
     """vec [B, h] = L1(SiLU(L0(temb(sigma)))) + V1(SiLU(V0(y))) with y the
     pooled text vector (mistral.rs article: FluxStepper encodes with T5 and
-    CLIP; reading: no guidance input, as for schnell)."""
+    CLIP). Without guidance weights (schnell) that is all.
+
+    Guidance-distilled models (FLUX.1-dev: mflux-rs card, generation with a
+    guidance scale; mistral.rs article, guidance models with guidance_scale
+    4.0) also add G1(SiLU(G0(temb(guidance)))): reading, the guidance value
+    is embedded exactly like the timestep (1000 g, the same sinusoid) by its
+    own two-layer map. `guidance` is required when g holds guidance_in0_w."""
     dt = y.dtype
     B = y.shape[0]
     t = np.broadcast_to(timestep_embedding(sigma, temb_dim, dtype=dt), (B, temb_dim))
     vt = linear(silu(linear(t, g["time_in0_w"], g["time_in0_b"])), g["time_in1_w"], g["time_in1_b"])
     vy = linear(silu(linear(y, g["vec_in0_w"], g["vec_in0_b"])), g["vec_in1_w"], g["vec_in1_b"])
-    return vt + vy
+    if g.get("guidance_in0_w") is None:
+        return vt + vy
+    if guidance is None:
+        raise ValueError("guidance-distilled weights need a guidance value")
+    e = np.broadcast_to(timestep_embedding(guidance, temb_dim, dtype=dt), (B, temb_dim))
+    vg = linear(silu(linear(e, g["guidance_in0_w"], g["guidance_in0_b"])), g["guidance_in1_w"], g["guidance_in1_b"])
+    return vt + vg + vy
 
 
 def final_layer(g: Dict[str, np.ndarray], img: np.ndarray, vec: np.ndarray) -> np.ndarray:
@@ -300,7 +313,7 @@ def final_layer(g: Dict[str, np.ndarray], img: np.ndarray, vec: np.ndarray) -> n
 # ------------------------------------------------------------------ step ---
 def step(g: Dict[str, np.ndarray], dbl: Sequence, sgl: Sequence, X: np.ndarray, T: np.ndarray,
          y: np.ndarray, ids: np.ndarray, sigma: float, sigma_next: float, heads: int,
-         axes_dim=(16, 56, 56), theta: float = 10000.0, Xc: np.ndarray = None):
+         axes_dim=(16, 56, 56), theta: float = 10000.0, Xc: np.ndarray = None, guidance=None):
     """One denoising step (mflux-rs architecture cards and "Flow-Matching
     Euler"): project packed latents [B, Li, 64] and text embeddings
     [B, Lt, 4096] to width h, run the dual-stream blocks, concatenate
@@ -312,12 +325,12 @@ def step(g: Dict[str, np.ndarray], dbl: Sequence, sgl: Sequence, X: np.ndarray, 
     RoPE visualiser). Reading: its tokens follow the generated ones in the
     image stream, through the same input projection, with ids carrying frame
     1 (ids covers [txt; generated; context]); v and the update are taken for
-    the generated rows only."""
+    the generated rows only. guidance: passed to conditioning_vec."""
     dt = X.dtype
     Lg = X.shape[1]
     img = linear(X if Xc is None else np.concatenate([X, Xc.astype(dt)], axis=1), g["img_in_w"], g["img_in_b"])
     txt = linear(T.astype(dt), g["txt_in_w"], g["txt_in_b"])
-    vec = conditioning_vec(g, sigma, y.astype(dt), temb_dim=g["time_in0_w"].shape[1])
+    vec = conditioning_vec(g, sigma, y.astype(dt), temb_dim=g["time_in0_w"].shape[1], guidance=guidance)
     for i in range(len(dbl)):
         img, txt = double_block(dbl[i], img, txt, vec, ids, heads, axes_dim, theta)
     x = np.concatenate([txt, img], axis=1)

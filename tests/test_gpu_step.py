@@ -138,15 +138,18 @@ def ctx_ids(s: I.Shape, cgh: int, cgw: int) -> np.ndarray:
                            oracle.make_ids(cgh, cgw, 0, frame=1)]).astype(np.int32)
 
 
-def run_step_ctx(s: I.Shape, cgh: int, cgw: int, sig_i: int, n_steps: int = 4):
-    """mmdit_step_ctx with a context latent of cgh x cgw packed tokens against
-    the oracle step with the same context."""
+def run_step_ex(s: I.Shape, cgh: int, cgw: int, sig_i: int, guidance=None, n_steps: int = 4):
+    """mmdit_step_ex with a context latent of cgh x cgw packed tokens (none
+    when 0) and an optional guidance value (the model then has a guidance
+    embedder) against the oracle step with the same options."""
     t = torch()
     g, dbl, sgl = model_numpy(s)
+    if guidance is not None:
+        g = dict(g, **I.guidance_weights(s))
     inp = I.step_inputs(s)
     Lc = cgh * cgw
     Xc = np.random.default_rng(1000 + s.cfg_id).standard_normal((s.batch, Lc, s.in_ch)).astype(np.float32)
-    ids = ctx_ids(s, cgh, cgw)
+    ids = ctx_ids(s, cgh, cgw) if Lc else oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
     sig = oracle.schedule(n_steps, s.img_len)
     dt = dtype_code(s.dtype)
     cfg = bd.make_config(s)
@@ -157,19 +160,20 @@ def run_step_ctx(s: I.Shape, cgh: int, cgw: int, sig_i: int, n_steps: int = 4):
     bd.mmdit_pack_latents(z, X)
     v = t.empty_like(X)
     ws = workspace(bd.mmdit_step_workspace(cfg))
-    print(f"step_ctx B={s.batch} h={s.hidden} {s.n_double}+{s.n_single} blocks Lt={s.txt_len} Lg={s.img_len} "
-          f"Lc={Lc} {s.dtype}", flush=True)
-    bd.mmdit_step_ctx(cfg, M.c(), X, v, t.from_numpy(Xc).cuda(), Lc, up(inp["T"], s.dtype), up(inp["y"], s.dtype),
-                      up_i32(ids), sig[sig_i], sig[sig_i + 1], ws)
+    print(f"step_ex B={s.batch} h={s.hidden} {s.n_double}+{s.n_single} blocks Lt={s.txt_len} Lg={s.img_len} "
+          f"Lc={Lc} guidance={guidance} {s.dtype}", flush=True)
+    bd.mmdit_step_ex(cfg, M.c(), X, v, up(inp["T"], s.dtype), up(inp["y"], s.dtype), up_i32(ids), sig[sig_i],
+                     sig[sig_i + 1], ws, ctx_packed=t.from_numpy(Xc).cuda() if Lc else None, ctx_len=Lc,
+                     guidance=guidance)
     sync()
     Xr, vr = oracle.step(g, dbl, sgl, oracle.pack_latents(inp["z"]), inp["T"], inp["y"], ids, sig[sig_i],
-                         sig[sig_i + 1], s.heads, s.axes_dim, s.theta, Xc=Xc)
+                         sig[sig_i + 1], s.heads, s.axes_dim, s.theta, Xc=Xc if Lc else None, guidance=guidance)
     return (down(X), down(v)), (Xr, vr)
 
 
 def test_step_ctx_f32_tiny_batch2():
     s = dataclasses.replace(TINY_F32, batch=2, txt_len=11, grid_h=6, grid_w=5, cfg_id=45)
-    (Xg, vg), (Xr, vr) = run_step_ctx(s, 4, 7, 1)
+    (Xg, vg), (Xr, vr) = run_step_ex(s, 4, 7, 1)
     assert_parity(vg, vr, "f32", "step_ctx v")
     assert_parity(Xg, Xr, "f32", "step_ctx x_next")
 
@@ -177,9 +181,25 @@ def test_step_ctx_f32_tiny_batch2():
 def test_step_ctx_bf16_width3072():
     # h 3072 / 24 heads, 256 text + 32x32 generated + 32x32 context tokens
     s = dataclasses.replace(I.CFG4, n_double=1, n_single=1, txt_len=256, grid_h=32, grid_w=32, cfg_id=46)
-    (Xg, vg), (Xr, vr) = run_step_ctx(s, 32, 32, 0)
+    (Xg, vg), (Xr, vr) = run_step_ex(s, 32, 32, 0)
     assert_parity(vg, vr, "bf16", "bf16 step_ctx v")
     assert_parity(Xg, Xr, "bf16", "bf16 step_ctx x_next")
+
+
+def test_step_guidance_f32_tiny():
+    s = dataclasses.replace(TINY_F32, txt_len=9, grid_h=5, grid_w=7, cfg_id=47)
+    (Xg, vg), (Xr, vr) = run_step_ex(s, 0, 0, 2, guidance=3.5)
+    assert_parity(vg, vr, "f32", "guided step v")
+    assert_parity(Xg, Xr, "f32", "guided step x_next")
+
+
+def test_step_guidance_with_context_bf16_width3072():
+    # guidance plus reference-image tokens (instruction editing with a
+    # guidance-distilled model), h 3072, 128 + 24x24 generated + 24x24 context
+    s = dataclasses.replace(I.CFG4, n_double=1, n_single=1, txt_len=128, grid_h=24, grid_w=24, cfg_id=48)
+    (Xg, vg), (Xr, vr) = run_step_ex(s, 24, 24, 1, guidance=2.5)
+    assert_parity(vg, vr, "bf16", "bf16 guided step_ex v")
+    assert_parity(Xg, Xr, "bf16", "bf16 guided step_ex x_next")
 
 
 def test_step_quantised_full_tokens_one_plus_one_blocks():

@@ -44,7 +44,7 @@ def test_struct_layout_matches_c_compiler(lib):
     structs = {"mmdit_dims": bd.mmdit_dims, "mmdit_linear": bd.mmdit_linear,
                "mmdit_stream_w": bd.mmdit_stream_w, "mmdit_double_w": bd.mmdit_double_w,
                "mmdit_single_w": bd.mmdit_single_w, "mmdit_config": bd.mmdit_config,
-               "mmdit_model_w": bd.mmdit_model_w}
+               "mmdit_model_w": bd.mmdit_model_w, "mmdit_step_opts": bd.mmdit_step_opts}
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){"]
     for name, cls in structs.items():
         lines.append(f'printf("{name} size %zu\\n", sizeof({name}));')
@@ -162,6 +162,32 @@ def test_block_errors_before_launch(lib):
     assert _call_double(lib, d, bad, need) == 3                            # modulation must be dense
     assert lib.mmdit_double_block_fwd(C.byref(d), None, 0x6000, 0x6000, 0x6000, 0x6000, 0x6000, 0x6000,
                                       0x5000, need, None) == 1
+
+
+def test_step_ex_errors_before_launch(lib):
+    # option checks run before any weight is read or kernel launched: the
+    # model below has only a (fake) guidance embedder pointer
+    s = I.Shape(hidden=256, heads=2, mlp_hidden=512, txt_len=16, grid_h=8, grid_w=8, dtype="f32", cfg_id=41,
+                n_double=1, n_single=1, txt_in_dim=256, vec_in_dim=256)
+    cfg = bd.make_config(s)
+    w = bd.mmdit_model_w()
+    w.guidance_in0.w = 0x1000
+    fake = 0x6000
+
+    def call(opts):
+        return lib.mmdit_step_ex(C.byref(cfg), C.byref(w), fake, None, fake, fake, fake, 1.0, 0.5, opts, fake,
+                                 1 << 40, None)
+    assert call(None) == 1                                                  # guidance model, no value
+    assert lib.mmdit_step(C.byref(cfg), C.byref(w), fake, None, fake, fake, fake, 1.0, 0.5, fake, 1 << 40,
+                          None) == 1
+    o = bd.mmdit_step_opts(has_guidance=1, guidance=float("nan"))
+    assert call(C.byref(o)) == 2                                            # non-finite guidance
+    o = bd.mmdit_step_opts(ctx_packed=fake, ctx_len=s.img_len, has_guidance=1, guidance=3.5)
+    assert call(C.byref(o)) == 2                                            # no generated tokens left
+    o = bd.mmdit_step_opts(ctx_packed=None, ctx_len=4, has_guidance=1, guidance=3.5)
+    assert call(C.byref(o)) == 1                                            # NULL context latent
+    o = bd.mmdit_step_opts(ctx_packed=fake, ctx_len=-1)
+    assert call(C.byref(o)) == 2
 
 
 def test_workspace_sizes_scale_with_tokens(lib):

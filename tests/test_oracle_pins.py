@@ -447,6 +447,28 @@ def test_step_context_gate_zero_takes_generated_rows():
     assert np.array_equal(v, oracle.final_layer(g, oracle.linear(X, g["img_in_w"], g["img_in_b"]), vec))
 
 
+def test_guidance_embedding_is_a_second_timestep_map():
+    # With the guidance map's weights equal to the timestep map's and
+    # guidance == sigma, the guidance term equals the timestep term: vec gains
+    # exactly the timestep part (the guidance value is embedded like sigma).
+    s = tiny_shape(txt_len=3, grid_h=2, grid_w=3)
+    g = _f64(I.global_weights(s))
+    y = _f64(I.step_inputs(s)["y"])
+    vec = oracle.conditioning_vec(g, 0.7, y)
+    gg = dict(g, guidance_in0_w=g["time_in0_w"], guidance_in0_b=g["time_in0_b"],
+              guidance_in1_w=g["time_in1_w"], guidance_in1_b=g["time_in1_b"])
+    vt = oracle.conditioning_vec(dict(g, vec_in1_w=0 * g["vec_in1_w"], vec_in1_b=0 * g["vec_in1_b"]), 0.7, y)
+    assert rel_l2(oracle.conditioning_vec(gg, 0.7, y, guidance=0.7) - vec, vt) < 1e-12
+    # a zero output layer adds nothing; a different value changes vec
+    gw = dict(g, **{k: _f64(v) for k, v in I.guidance_weights(s).items()})
+    z = dict(gw, guidance_in1_w=0 * gw["guidance_in1_w"], guidance_in1_b=0 * gw["guidance_in1_b"])
+    assert np.array_equal(oracle.conditioning_vec(z, 0.7, y, guidance=4.0), vec)
+    assert rel_l2(oracle.conditioning_vec(gw, 0.7, y, guidance=4.0),
+                  oracle.conditioning_vec(gw, 0.7, y, guidance=3.5)) > 1e-4
+    with pytest.raises(ValueError):
+        oracle.conditioning_vec(gw, 0.7, y)
+
+
 # ------------------------------------------------------- schedule, Euler ---
 def test_schedule_page_invariants():
     sh = PAGES["shift"]
