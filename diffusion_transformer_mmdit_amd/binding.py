@@ -17,7 +17,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmmdit.s
 _lib = None
 
 F32, BF16 = 0, 1
-W_DENSE, W_Q4G64, W_Q8G64 = 0, 1, 2
+W_DENSE, W_Q4G64, W_Q8G64, W_Q1G128, W_TQ2G128 = 0, 1, 2, 3, 4
 PC_GEMM, PC_ATTN, PC_LN, PC_QKNORM, PC_GEMV, PC_GEMM_LIN1, PC_GEMM_RES = 1, 2, 3, 4, 5, 6, 7
 
 
@@ -166,7 +166,8 @@ class Linear:
         packed, scales = mmdit_quantise(w, bits)
         st = torch.from_numpy(scales.view(np.int16)).to(device).view(torch.bfloat16)
         pt = torch.from_numpy(packed).to(device)
-        return Linear(pt, bt, st, W_Q4G64 if bits == 4 else W_Q8G64, w.shape[0], w.shape[1])
+        fmt = {4: W_Q4G64, 8: W_Q8G64, 1: W_Q1G128, 2: W_TQ2G128}[bits]
+        return Linear(pt, bt, st, fmt, w.shape[0], w.shape[1])
 
 
 def _vec(a, dtype, device):
@@ -365,8 +366,12 @@ def mmdit_quantise(w: np.ndarray, bits: int):
     """Returns (packed uint8/int8 codes, scales as uint16 bf16 bits)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     n, k = w.shape
-    packed = np.zeros((n, k // 2) if bits == 4 else (n, k), dtype=np.uint8 if bits == 4 else np.int8)
-    scales = np.zeros((n, k // 64), dtype=np.uint16)
+    if bits in (1, 2):  # Q1G128 / TQ2G128
+        packed = np.zeros((n, k * bits // 8), dtype=np.uint8)
+        scales = np.zeros((n, k // 128), dtype=np.uint16)
+    else:
+        packed = np.zeros((n, k // 2) if bits == 4 else (n, k), dtype=np.uint8 if bits == 4 else np.int8)
+        scales = np.zeros((n, k // 64), dtype=np.uint16)
     _check(lib().mmdit_quantise(w.ctypes.data_as(C.c_void_p), n, k, bits, packed.ctypes.data_as(C.c_void_p),
                                 scales.ctypes.data_as(C.c_void_p)), "mmdit_quantise")
     return packed, scales

@@ -62,9 +62,50 @@ static float bits_f32(uint32_t u) {
 // stable-diffusion.rs README: weights held as packed bits at rest (4-bit and
 // 8-bit). Per row and group of 64 k, in float32: s = smallest bf16 >=
 // max|w| / qmax, q = round-half-even(w / s), so |q| <= qmax without clamping.
+// float -> bf16 bits, round to nearest even (finite inputs)
+static uint16_t bf16_rne(float f) {
+  const uint32_t u = f32_bits(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Sub-byte formats, groups of 128 along k: absmean scale, sign or ternary codes.
+static int quantise_g128(const float* w, int32_t n_out, int32_t k_in, int32_t bits, uint8_t* out,
+                         uint16_t* scales_bf16) {
+  if (n_out < 1 || k_in < 128 || k_in % 128) return MMDIT_ERR_SHAPE;
+  const int groups = k_in / 128;
+  const size_t row_bytes = bits == 1 ? (size_t)k_in / 8 : (size_t)k_in / 4;
+  std::memset(out, 0, (size_t)n_out * row_bytes);
+  for (int n = 0; n < n_out; ++n) {
+    for (int gi = 0; gi < groups; ++gi) {
+      const float* wg = w + (size_t)n * k_in + (size_t)gi * 128;
+      double sum = 0.0;
+      for (int j = 0; j < 128; ++j) sum += std::fabs((double)wg[j]);
+      const uint16_t sb = bf16_rne((float)(sum / 128.0));
+      scales_bf16[(size_t)n * groups + gi] = sb;
+      const double s = (double)bits_f32((uint32_t)sb << 16);
+      for (int j = 0; j < 128; ++j) {
+        const size_t k = (size_t)gi * 128 + j;
+        uint8_t& byte = out[(size_t)n * row_bytes + (bits == 1 ? k / 8 : k / 4)];
+        if (bits == 1) {
+          if (wg[j] >= 0.0f) byte = (uint8_t)(byte | (1u << (k % 8)));
+        } else {
+          double q = 0.0;
+          if (s > 0.0) {
+            q = std::nearbyint((double)wg[j] / s);
+            q = q > 1.0 ? 1.0 : (q < -1.0 ? -1.0 : q);
+          }
+          byte = (uint8_t)(byte | ((uint32_t)((int)q + 1) << (2 * (k % 4))));
+        }
+      }
+    }
+  }
+  return MMDIT_OK;
+}
+
 int mmdit_quantise(const float* w, int32_t n_out, int32_t k_in, int32_t bits, void* packed,
                    uint16_t* scales_bf16) {
   if (!w || !packed || !scales_bf16) return MMDIT_ERR_NULL;
+  if (bits == 1 || bits == 2) return quantise_g128(w, n_out, k_in, bits, static_cast<uint8_t*>(packed), scales_bf16);
   if (n_out < 1 || k_in < 64 || k_in % 64) return MMDIT_ERR_SHAPE;
   if (bits != 4 && bits != 8) return MMDIT_ERR_DTYPE;
   const float qmax = bits == 4 ? 7.0f : 127.0f;

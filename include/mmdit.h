@@ -61,7 +61,17 @@ typedef enum { MMDIT_F32 = 0, MMDIT_BF16 = 1 } mmdit_dtype;
  * The dequantised weight is code * scale. Quantised formats need bf16
  * activations and k_in % 64 == 0. (stable-diffusion.rs README: weights held
  * quantised at rest and dequantised inside the matmul a tile at a time.) */
-typedef enum { MMDIT_W_DENSE = 0, MMDIT_W_Q4G64 = 1, MMDIT_W_Q8G64 = 2 } mmdit_wfmt;
+/* Sub-byte formats with groups of 128 along k (pictor-tokenizer page: 1-bit
+ * Q1_0_g128 and ternary TQ2_0_g128 weights; reading for the layout and the
+ * scale, which the page does not give): per row and group, one bf16 scale
+ * s >= 0 in scales bf16 [n_out, k_in/128];
+ * Q1G128: one bit per weight, uint8 [n_out, k_in/8], weight k at bit k%8 of
+ *   byte k/8; bit 1 -> +s, bit 0 -> -s.
+ * TQ2G128: two bits per weight, uint8 [n_out, k_in/4], weight k at bits
+ *   2(k%4), 2(k%4)+1 of byte k/4; code 0 -> -s, 2 -> +s, 1 and 3 -> 0.
+ * They need bf16 activations and k_in % 128 == 0. */
+typedef enum { MMDIT_W_DENSE = 0, MMDIT_W_Q4G64 = 1, MMDIT_W_Q8G64 = 2, MMDIT_W_Q1G128 = 3,
+               MMDIT_W_TQ2G128 = 4 } mmdit_wfmt;
 
 typedef struct {
   int32_t batch;       /* B >= 1 */
@@ -80,7 +90,7 @@ typedef struct {
 
 typedef struct {
   const void* w;       /* device; layout per mmdit_wfmt */
-  const void* scales;  /* device bf16 [n_out, k_in/64] for Q4G64/Q8G64, else NULL */
+  const void* scales;  /* device bf16 [n_out, k_in/64] (Q4G64/Q8G64) or [n_out, k_in/128] (Q1G128/TQ2G128), else NULL */
   const void* bias;    /* device [n_out] in the activation dtype, or NULL for no bias */
   int32_t fmt;         /* mmdit_wfmt */
   int32_t n_out;
@@ -244,12 +254,19 @@ int mmdit_unpack_latents(const void* x, void* z, int32_t B, int32_t C, int32_t H
 int mmdit_rope_table(const int32_t* ids, int32_t L, const int32_t* axes_dim, double theta,
                      float* table, void* hip_stream);
 
-/* Host. Symmetric group quantiser for w [n_out, k_in] float32 (host),
- * k_in % 64 == 0, bits 4 or 8: per row and group of 64 k,
+/* Host. Symmetric group quantiser for w [n_out, k_in] float32 (host).
+ * bits 4 or 8 (k_in % 64 == 0): per row and group of 64 k,
  * s = smallest bf16 >= max|w| / qmax (qmax 7 or 127), q = round-half-even(w / s),
  * all-zero group -> s = 0, q = 0. packed: host, n_out*k_in/2 bytes (4-bit,
  * even k in the low nibble) or n_out*k_in bytes (8-bit); scales_bf16: host
- * [n_out, k_in/64]. */
+ * [n_out, k_in/64].
+ * bits 1 (Q1G128) or 2 (TQ2G128), k_in % 128 == 0: per row and group of 128
+ * k, m = sum of |w| in k order in float64, divided by 128, rounded to float32
+ * then to bf16 (both to nearest even): s. 1-bit: bit = (w >= 0). 2-bit:
+ * q = round-half-even(w / s) in float64 clamped to [-1, 1] (q = 0 when
+ * s = 0), code q + 1. (The absmean scale; for sign codes it is the
+ * least-squares scale.) packed: n_out*k_in/8 or n_out*k_in/4 bytes;
+ * scales_bf16: [n_out, k_in/128]. */
 int mmdit_quantise(const float* w, int32_t n_out, int32_t k_in, int32_t bits,
                    void* packed, uint16_t* scales_bf16);
 

@@ -33,5 +33,5 @@ from .mmdit import (  # noqa: F401
     attention, double_block, single_block, timestep_embedding,
     conditioning_vec, final_layer, step, mu_for_tokens, time_shift,
     schedule, euler_update, quantise, dequantise, pack_int4, unpack_int4,
-    bf16_round_up,
+    bf16_round_up, bf16_rne, quantise_g128, dequantise_g128, pack_g128, unpack_g128,
 )

@@ -439,3 +439,68 @@ def unpack_int4(p: np.ndarray) -> np.ndarray:
     out[:, 0::2] = lo
     out[:, 1::2] = hi
     return out
+
+
+# ------------------------------------------- sub-byte weights (group 128) ---
+def bf16_rne(a: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bf16 (ties to even), returned as float32."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return (r << np.uint32(16)).view(np.float32)
+
+
+def quantise_g128(w: np.ndarray, bits: int):
+    """1-bit (Q1_0_g128) and ternary (TQ2_0_g128) weights with groups of 128
+    along K (pictor-tokenizer page: 1-bit and ternary {-1, 0, +1} formats
+    with group 128; the page gives neither layout nor scale, so this is a
+    reading). Per output row n and group of 128 consecutive k:
+      m = (sum of |w| over the group, in k order, float64) / 128,
+      s = m rounded to float32, then to bf16 (both to nearest even);
+      1-bit: code 1 where w >= 0 (value +s), else 0 (value -s);
+      2-bit: q = round_half_even(w / s) in float64 clamped to [-1, 1], q = 0
+             when s = 0; code q + 1.
+    For sign codes, s = mean |w| is the least-squares scale. Returns codes
+    [N, K] uint8 and s [N, K/128] float32 (bf16-valued)."""
+    if bits not in (1, 2):
+        raise ValueError("bits must be 1 or 2")
+    N, K = w.shape
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    g = np.asarray(w, dtype=np.float32).reshape(N, K // 128, 128).astype(np.float64)
+    m = np.cumsum(np.abs(g), axis=-1)[..., -1] / 128.0
+    s = bf16_rne(m.astype(np.float32))
+    if bits == 1:
+        return (g >= 0).astype(np.uint8).reshape(N, K), s
+    sd = s.astype(np.float64)[..., None]
+    q = np.clip(np.rint(g / np.where(sd > 0, sd, 1.0)), -1.0, 1.0)
+    q = np.where(sd > 0, q, 0.0)
+    return (q + 1).astype(np.uint8).reshape(N, K), s
+
+
+def dequantise_g128(codes: np.ndarray, s: np.ndarray, bits: int) -> np.ndarray:
+    """w_hat [N, K] float32: 1-bit code 1 -> +s, 0 -> -s; 2-bit code
+    0 -> -s, 2 -> +s, 1 and 3 -> 0 (exact in float32)."""
+    N, K = codes.shape
+    if bits == 1:
+        v = np.where(codes == 1, 1.0, -1.0)
+    else:
+        v = np.select([codes == 0, codes == 2], [-1.0, 1.0], 0.0)
+    return (v.reshape(N, K // 128, 128) * s[..., None].astype(np.float64)).astype(np.float32).reshape(N, K)
+
+
+def pack_g128(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Codes [N, K] -> bytes [N, K*bits/8]: weight k at bit (k % (8/bits)) *
+    bits of byte k // (8/bits), low bits first."""
+    per = 8 // bits
+    N, K = codes.shape
+    c = codes.astype(np.uint32).reshape(N, K // per, per)
+    shifts = (np.arange(per, dtype=np.uint32) * bits)[None, None, :]
+    return np.bitwise_or.reduce(c << shifts, axis=-1).astype(np.uint8)
+
+
+def unpack_g128(p: np.ndarray, bits: int) -> np.ndarray:
+    per = 8 // bits
+    N, B = p.shape
+    shifts = (np.arange(per, dtype=np.uint32) * bits)[None, None, :]
+    return ((p.astype(np.uint32)[..., None] >> shifts) & np.uint32((1 << bits) - 1)).astype(np.uint8).reshape(N, B * per)
+

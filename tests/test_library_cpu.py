@@ -97,6 +97,19 @@ def test_quantiser_bit_exact(lib, bits):
         assert np.array_equal(packed, q)
 
 
+@pytest.mark.parametrize("bits", [1, 2])
+def test_quantiser_g128_bit_exact(lib, bits):
+    w = I.normal((40, 384), (998, 0, bits), std=0.02)
+    w[5, 128:256] = 0.0
+    w[7, :128] *= 1e-30                     # subnormal-scale group
+    w[9, 3] = 0.5                           # one outlier
+    w[11, 7] = -0.0
+    packed, scales = bd.mmdit_quantise(w, bits)
+    c, s = oracle.quantise_g128(w, bits)
+    assert np.array_equal(scales, I.bf16_bits(s))
+    assert np.array_equal(packed, oracle.pack_g128(c, bits))
+
+
 def _dims(**kw):
     s = I.Shape(**{**dict(hidden=256, heads=2, mlp_hidden=512, txt_len=16, grid_h=8, grid_w=8,
                           dtype="bf16"), **kw})

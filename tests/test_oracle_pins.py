@@ -554,6 +554,68 @@ def test_quantised_gemm_equals_dense_on_dequantised():
     assert np.max(np.abs(y - ref)) < 1e-12
 
 
+def test_g128_hand_worked_row():
+    # one group: w = [0.5, -0.25, 0, 1, 0 ...]; sum |w| = 1.75, m = 7/512
+    # (exact in bf16). 1-bit: signs with w >= 0 -> 1: byte 0 = 0b11111101.
+    # 2-bit: w/s = 36.6, -18.3, 0, 73.1 -> q = 1, -1, 0, 1 -> codes 2, 0, 1, 2
+    # -> byte 0 = 2 | 0 << 2 | 1 << 4 | 2 << 6 = 0x92; zeros -> code 1 -> 0x55.
+    w = np.zeros((1, 128), np.float32)
+    w[0, :4] = [0.5, -0.25, 0.0, 1.0]
+    for bits, b0, rest in ((1, 0xFD, 0xFF), (2, 0x92, 0x55)):
+        c, sc = oracle.quantise_g128(w, bits)
+        assert sc[0, 0] == 7.0 / 512.0
+        p = oracle.pack_g128(c, bits)
+        assert p.shape == (1, 128 * bits // 8) and p[0, 0] == b0 and np.all(p[0, 1:] == rest)
+    wh = oracle.dequantise_g128(oracle.quantise_g128(w, 2)[0], np.array([[7.0 / 512.0]], np.float32), 2)
+    assert wh[0, :4].tolist() == [7.0 / 512.0, -7.0 / 512.0, 0.0, 7.0 / 512.0]
+
+
+def test_g128_scale_is_least_squares_for_sign_codes():
+    from scipy.optimize import minimize_scalar
+    rng = np.random.default_rng(23)
+    w = (rng.standard_normal((6, 256)) * 0.02).astype(np.float32)
+    c, sc = oracle.quantise_g128(w, 1)
+    for n in range(6):
+        for gi in range(2):
+            g = w[n, 128 * gi:128 * (gi + 1)].astype(np.float64)
+            sg = np.where(g >= 0, 1.0, -1.0)
+            best = minimize_scalar(lambda t: float(np.sum((g - t * sg) ** 2)), bounds=(0.0, 1.0), method="bounded",
+                                   options={"xatol": 1e-12}).x
+            assert abs(sc[n, gi] - best) <= 2.0 ** -8 * best   # bf16 rounding of the minimiser
+    assert np.array_equal(c, (w >= 0).astype(np.uint8))
+
+
+def test_g128_ternary_codes_are_nearest_levels():
+    rng = np.random.default_rng(24)
+    w = (rng.standard_normal((5, 384)) * 0.02).astype(np.float32)
+    w[2, 128:256] = 0.0
+    c, sc = oracle.quantise_g128(w, 2)
+    assert set(np.unique(c)) <= {0, 1, 2} and sc[2, 1] == 0.0 and np.all(c[2, 128:256] == 1)
+    s_full = np.repeat(sc, 128, axis=1).astype(np.float64)
+    levels = np.array([-1.0, 0.0, 1.0])
+    for n in range(5):
+        for k in range(384):
+            if s_full[n, k] == 0:
+                continue
+            d = np.abs(w[n, k] / s_full[n, k] - levels)
+            want = 1 if abs(abs(w[n, k] / s_full[n, k]) - 0.5) < 1e-12 else int(np.argmin(d))
+            assert c[n, k] == want
+    # absmean: the scale is within bf16 rounding of the mean |w| of the group
+    m = np.abs(w.astype(np.float64)).reshape(5, 3, 128).mean(-1)
+    assert np.all(np.abs(sc - m) <= 2.0 ** -8 * m + 1e-30)
+
+
+def test_g128_packing_round_trip():
+    rng = np.random.default_rng(25)
+    for bits in (1, 2):
+        codes = rng.integers(0, 1 << bits, size=(4, 256)).astype(np.uint8)
+        p = oracle.pack_g128(codes, bits)
+        assert p.dtype == np.uint8 and p.shape == (4, 256 * bits // 8)
+        assert np.array_equal(oracle.unpack_g128(p, bits), codes)
+    # code 3 decodes to 0 like code 1
+    assert oracle.dequantise_g128(np.array([[3] * 128], np.uint8), np.array([[0.5]], np.float32), 2).max() == 0.0
+
+
 # ------------------------------------------------------------- inputs ------
 def test_box_muller_moments_page_bounds():
     bm = PAGES["box_muller"]
