@@ -286,6 +286,17 @@ def main():
         log(f"quantised step: {qms:.2f} ms")
         del Mq, mqc
 
+        # ternary-weight step (TQ2G128 in every block projection)
+        Mt = RI.model(I.CFG5, seed=45, device=dev, quant=bd.TERNARY_POLICY)
+        mtc = Mt.c()
+        Xt = X.clone()
+        for i in range(2):
+            step(i, mtc, Xt)
+        tms = timed(lambda i: step(i, mtc, Xt), max(a.steps // 2, 3))
+        out["ternary_ms_per_step"] = round(tms, 3)
+        log(f"ternary step: {tms:.2f} ms")
+        del Mt, mtc, Xt
+
         # reference-image (Kontext-style) step: 4096 context tokens with frame
         # id 1 after the 4096 generated ones, L = 512 + 8192 = 8704
         ck = bd.make_config(s)

@@ -224,6 +224,9 @@ class SingleW:
 # Quantisation policy: the layers writing into the residual stream keep 8
 # bits, the inner projections 4 bits (stable-diffusion.rs README).
 QUANT_POLICY = {"qkv": 4, "fc1": 4, "lin1": 4, "proj": 8, "fc2": 8, "lin2": 8}
+# every block projection ternary (TQ2G128), as the pictor-tokenizer page's
+# text-to-image DiT holds its weights; modulation and embedders stay bf16
+TERNARY_POLICY = {"qkv": 2, "fc1": 2, "lin1": 2, "proj": 2, "fc2": 2, "lin2": 2}
 
 GLOBAL_LINEARS = ("img_in", "txt_in", "time_in0", "time_in1", "vec_in0", "vec_in1", "final_mod", "final_lin")
 GUIDANCE_LINEARS = ("guidance_in0", "guidance_in1")

@@ -113,9 +113,11 @@ int check_linear(const mmdit_linear& l, int n, int k, const Geo& g, const char* 
     if (g.bf16 && k % 64) return fail(MMDIT_ERR_SHAPE, "%s: k_in %d must be a multiple of 64 for bf16", name, k);
     return MMDIT_OK;
   }
-  if (l.fmt != MMDIT_W_Q4G64 && l.fmt != MMDIT_W_Q8G64) return fail(MMDIT_ERR_DTYPE, "%s: unknown weight format %d", name, l.fmt);
+  const bool sub = l.fmt == MMDIT_W_Q1G128 || l.fmt == MMDIT_W_TQ2G128;
+  if (l.fmt != MMDIT_W_Q4G64 && l.fmt != MMDIT_W_Q8G64 && !sub)
+    return fail(MMDIT_ERR_DTYPE, "%s: unknown weight format %d", name, l.fmt);
   if (!g.bf16) return fail(MMDIT_ERR_DTYPE, "%s: quantised weights need bf16 activations", name);
-  if (k % 64) return fail(MMDIT_ERR_SHAPE, "%s: quantised k_in %d must be a multiple of 64", name, k);
+  if (k % (sub ? 128 : 64)) return fail(MMDIT_ERR_SHAPE, "%s: quantised k_in %d must be a multiple of %d", name, k, sub ? 128 : 64);
   if (!l.scales) return fail(MMDIT_ERR_NULL, "%s.scales is NULL", name);
   return MMDIT_OK;
 }

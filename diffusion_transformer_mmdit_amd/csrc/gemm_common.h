@@ -79,6 +79,42 @@ __device__ __forceinline__ void deq4(const u32x4& w, float s, bf16x8 out[4]) {
   }
 }
 
+// Sub-byte weights, groups of 128 along k. 32 weights (k ascending) into four
+// bf16x8, built as bit patterns from the bf16 scale s16 (s >= 0):
+// Q1: bit j of `bits` -> weight j, 1 -> +s, 0 -> -s.
+__device__ __forceinline__ void deq_q1_32(uint32_t bits, uint32_t s16, bf16x8 out[4]) {
+  const uint32_t sp = s16 | (s16 << 16);
+  const uint32_t nb = ~bits;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t t = nb >> (8 * q + 2 * i);  // bits 0, 1: the pair's negated signs
+      o[i] = sp | ((t & 1u) << 15) | ((t & 2u) << 30);
+    }
+    out[q] = __builtin_bit_cast(bf16x8, o);
+  }
+}
+// TQ2: the 2-bit code of weight j at bits 2j, 2j+1 of (w0 | w1 << 32);
+// code 0 -> -s, 2 -> +s, 1 and 3 -> 0.
+__device__ __forceinline__ uint32_t tq2_half(uint32_t c, uint32_t s16) {
+  return (c & 1u) ? 0u : (s16 | ((~c & 2u) << 14));
+}
+__device__ __forceinline__ void deq_tq2_32(uint32_t w0, uint32_t w1, uint32_t s16, bf16x8 out[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t w = q < 2 ? w0 : w1;
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t t = w >> (16 * (q & 1) + 4 * i);  // codes of weights 8q + 2i, 8q + 2i + 1
+      o[i] = tq2_half(t & 3u, s16) | (tq2_half((t >> 2) & 3u, s16) << 16);
+    }
+    out[q] = __builtin_bit_cast(bf16x8, o);
+  }
+}
+
 // GELU-tanh for the bf16 kernels: exp2 and reciprocal on the hardware
 // transcendental units (results are rounded to bf16 afterwards).
 __device__ __forceinline__ float gelu_fast(float x) {

@@ -26,6 +26,8 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmBatch gb) {
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int A_CH = BM * 8 / 256;                                  // 16-byte A chunks per thread
+  // 16-byte B chunks per thread; sub-byte formats (3, 4): pieces of 32 weights
+  constexpr bool SUB = FMT == 3 || FMT == 4;
   constexpr int B_CH = FMT == 0 ? BN * 8 / 256 : (FMT == 2 ? BN * 4 / 256 : BN * 2 / 256);
   static_assert(WM * WN == 4, "4 wavefronts");
   static_assert(B_CH >= 1, "tile too small for this weight format");
@@ -45,6 +47,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmBatch gb) {
   bf16x8 ra[A_CH];
   u32x4 rb[B_CH];
   float rs[B_CH];
+  uint32_t rq[B_CH][2], rqs[B_CH];  // sub-byte piece i: row c / 2, weights 32 (c % 2) ..
 
   auto load_tile = [&](int kt) {
     const int k0 = kt * kBK;
@@ -58,7 +61,24 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmBatch gb) {
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       const int c = tid + i * 256;
-      if constexpr (FMT == 0) {
+      if constexpr (SUB) {
+        const int gn = n0 + (c >> 1), half = c & 1;
+        const uint8_t* wq = reinterpret_cast<const uint8_t*>(P.W);
+        if (gn < N) {
+          rqs[i] = reinterpret_cast<const uint16_t*>(P.scales)[(int64_t)gn * (K / 128) + kt / 2];
+          if constexpr (FMT == 3) {
+            rq[i][0] = *reinterpret_cast<const uint32_t*>(wq + (int64_t)gn * (K / 8) + k0 / 8 + half * 4);
+            rq[i][1] = 0;
+          } else {
+            const uint2 v = *reinterpret_cast<const uint2*>(wq + (int64_t)gn * (K / 4) + k0 / 4 + half * 8);
+            rq[i][0] = v.x;
+            rq[i][1] = v.y;
+          }
+        } else {
+          rqs[i] = 0;
+          rq[i][0] = rq[i][1] = 0;
+        }
+      } else if constexpr (FMT == 0) {
         const int row = c >> 3, kc = c & 7;
         const int gn = n0 + row;
         rb[i] = gn < N ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16*>(P.W) + (int64_t)gn * K + k0 + kc * 8)
@@ -95,7 +115,14 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmBatch gb) {
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       const int c = tid + i * 256;
-      if constexpr (FMT == 0) {
+      if constexpr (SUB) {
+        bf16x8 o[4];
+        if constexpr (FMT == 3) deq_q1_32(rq[i][0], rqs[i], o);
+        else deq_tq2_32(rq[i][0], rq[i][1], rqs[i], o);
+        bf16* d = &Bs[buf][(c >> 1) * kLDK + (c & 1) * 32];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(d + 8 * j) = o[j];
+      } else if constexpr (FMT == 0) {
         *reinterpret_cast<u32x4*>(&Bs[buf][(c >> 3) * kLDK + (c & 7) * 8]) = rb[i];
       } else if constexpr (FMT == 2) {
         bf16x8 lo, hi;
@@ -207,6 +234,8 @@ static hipError_t launch_epi(const GemmProblem* p, int nprob, hipStream_t s) {
   switch (p[0].fmt) {
     case 0: return launch_epi_fmt<EPI, 0>(p, nprob, s);
     case 1: return launch_epi_fmt<EPI, 1>(p, nprob, s);
+    case 3: return launch_epi_fmt<EPI, 3>(p, nprob, s);
+    case 4: return launch_epi_fmt<EPI, 4>(p, nprob, s);
     default: return launch_epi_fmt<EPI, 2>(p, nprob, s);
   }
 }

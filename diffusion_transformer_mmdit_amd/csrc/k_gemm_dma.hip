@@ -282,7 +282,9 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& P, char* smem, i
 // scale per weight row per k-tile): the packed codes of k-tile kt+1 are
 // loaded into registers when k-tile kt+1's A DMA is issued, and dequantised
 // into the B half of its stage (same swizzled bf16 layout) just before the
-// barrier that publishes it.
+// barrier that publishes it. FMT 3 / 4: 1-bit / ternary codes with groups of
+// 128 along k (two k-tiles share a scale), staged the same way in pieces of
+// 32 weights.
 template <int EPI, int BK, int S, int CPOL, int FMT, int DS, int W>
 __global__ __launch_bounds__(64 * W, 1) void k_gemm_dma(GemmBatch gb) {
   constexpr int NT = 64 * W;                       // threads
@@ -295,11 +297,15 @@ __global__ __launch_bounds__(64 * W, 1) void k_gemm_dma(GemmBatch gb) {
   constexpr int STAGE = 2 * HALF;
   constexpr int NJ = kDBM * CH / NT;               // DMA instructions per wave for A (and for dense B)
   constexpr int G = FMT == 0 ? 2 * NJ : NJ;        // DMA instructions per wave per k-tile
-  // quantised B: raw 16-byte chunks per thread per k-tile (rows of BK codes)
+  // quantised B (4/8-bit): raw 16-byte chunks per thread per k-tile (rows of BK codes)
+  constexpr bool SUB = FMT == 3 || FMT == 4;       // sub-byte, groups of 128 along k
   constexpr int QB = FMT == 2 ? BK : BK / 2;       // bytes per weight row per k-tile
-  constexpr int QCH = kDBN * QB / 16 / NT;         // raw chunks per thread
-  constexpr int QPR = QB / 16;                     // raw chunks per row
+  constexpr int QCH = SUB ? 1 : kDBN * QB / 16 / NT;  // raw chunks per thread
+  constexpr int QPR = SUB ? 1 : QB / 16;           // raw chunks per row
+  // sub-byte B: pieces of 32 weights (4 bytes 1-bit, 8 bytes ternary), 2 per row
+  constexpr int PCS = SUB ? 2 * kDBN / NT : 1;     // pieces per thread per k-tile
   static_assert(FMT == 0 || BK == 64, "quantised weights need 64-wide k-tiles (one scale group)");
+  static_assert(!SUB || PCS >= 1, "one sub-byte piece per thread at least");
   static_assert(S * STAGE >= W * 32 * (TN + 4) * 4, "epilogue staging must fit in the operand stages");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int prob, tm, tn;
@@ -359,8 +365,29 @@ __global__ __launch_bounds__(64 * W, 1) void k_gemm_dma(GemmBatch gb) {
   // k-tile: weight row q / QPR, part q % QPR.
   u32x4 braw[FMT == 0 ? 1 : QCH];
   float bscale[FMT == 0 ? 1 : QCH];
+  // sub-byte piece i of this thread is piece pc = tid * PCS + i: weight row
+  // pc / 2, weights 32 (pc % 2) .. + 31 of the k-tile
+  uint32_t sraw[PCS][2];
+  uint32_t sscale[PCS];
   auto load_braw = [&](int kt) {
-    if constexpr (FMT != 0) {
+    if constexpr (SUB) {
+      const uint16_t* sc = reinterpret_cast<const uint16_t*>(P.scales);
+#pragma unroll
+      for (int i = 0; i < PCS; ++i) {
+        const int pc = tid * PCS + i;
+        int gn = n0 + pc / 2;
+        gn = gn < N ? gn : N - 1;
+        sscale[i] = sc[(int64_t)gn * (K / 128) + kt / 2];
+        if constexpr (FMT == 3) {
+          sraw[i][0] = *reinterpret_cast<const uint32_t*>(bbase + (int64_t)gn * (K / 8) + (int64_t)kt * 8 + (pc % 2) * 4);
+          sraw[i][1] = 0;
+        } else {
+          const uint2 v = *reinterpret_cast<const uint2*>(bbase + (int64_t)gn * (K / 4) + (int64_t)kt * 16 + (pc % 2) * 8);
+          sraw[i][0] = v.x;
+          sraw[i][1] = v.y;
+        }
+      }
+    } else if constexpr (FMT != 0) {
 #pragma unroll
       for (int i = 0; i < QCH; ++i) {
         const int q = tid + NT * i;
@@ -372,7 +399,20 @@ __global__ __launch_bounds__(64 * W, 1) void k_gemm_dma(GemmBatch gb) {
     }
   };
   auto store_b = [&](int kt) {
-    if constexpr (FMT != 0) {
+    if constexpr (SUB) {
+      char* st = smem + (kt % S) * STAGE + HALF;
+#pragma unroll
+      for (int i = 0; i < PCS; ++i) {
+        const int pc = tid * PCS + i;
+        const int r = pc / 2, half = pc % 2;
+        const int sw = swz<BK>(r);
+        bf16x8 o[4];
+        if constexpr (FMT == 3) deq_q1_32(sraw[i][0], sscale[i], o);
+        else deq_tq2_32(sraw[i][0], sraw[i][1], sscale[i], o);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) *reinterpret_cast<bf16x8*>(st + (r * CH + ((4 * half + u) ^ sw)) * 16) = o[u];
+      }
+    } else if constexpr (FMT != 0) {
       char* st = smem + (kt % S) * STAGE + HALF;
 #pragma unroll
       for (int i = 0; i < QCH; ++i) {
@@ -640,6 +680,7 @@ bool gemm_dma_eligible(const GemmProblem* p, int nprob, int epi) {
     fmt = q.fmt;
     if (q.K % kDBK != 0 || q.lda % 8 != 0 || q.N < 128 || q.N % 4 != 0) return false;
     if (fmt != 0 && (kDBK != 64 || MMDIT_DMA_STAGES != 2)) return false;
+    if ((fmt == 3 || fmt == 4) && q.K % 128 != 0) return false;
     if (q.bias && !aligned(q.bias, 8)) return false;
     if (epi == EPI_GATE_RES) {
       const int esz = q.res_f32 ? 16 : 8;
@@ -664,6 +705,8 @@ static hipError_t launch_dma_fmt(const GemmProblem* p, int nprob, hipStream_t s)
   switch (fmt) {
     case 1: return launch_dma_epi<EPI, MMDIT_DMA_BK, MMDIT_DMA_STAGES, MMDIT_DMA_CPOL, 1>(p, nprob, s);
     case 2: return launch_dma_epi<EPI, MMDIT_DMA_BK, MMDIT_DMA_STAGES, MMDIT_DMA_CPOL, 2>(p, nprob, s);
+    case 3: return launch_dma_epi<EPI, MMDIT_DMA_BK, MMDIT_DMA_STAGES, MMDIT_DMA_CPOL, 3>(p, nprob, s);
+    case 4: return launch_dma_epi<EPI, MMDIT_DMA_BK, MMDIT_DMA_STAGES, MMDIT_DMA_CPOL, 4>(p, nprob, s);
     default: return launch_dma_epi<EPI>(p, nprob, s);
   }
 }

@@ -41,6 +41,16 @@ def _linear(G: _Gen, n: int, k: int, dtype, bits: int = 0) -> bd.Linear:
     b = G.normal(n, dtype=dtype)
     if bits == 0:
         return bd.Linear(G.normal(n, k, dtype=dtype), b)
+    if bits in (1, 2):  # sign / ternary codes, groups of 128, absmean-sized scales
+        codes = G.randint(0, 2 if bits == 1 else 3, n, k).to(torch.int32)
+        per = 8 // bits
+        c = codes.reshape(n, k // per, per)
+        packed = torch.zeros(n, k // per, dtype=torch.int32, device=codes.device)
+        for j in range(per):
+            packed |= c[:, :, j] << (bits * j)
+        scales = G.uniform(0.5 * STD, 1.0 * STD, n, k // 128).to(torch.bfloat16)
+        fmt = bd.W_Q1G128 if bits == 1 else bd.W_TQ2G128
+        return bd.Linear(packed.to(torch.uint8).contiguous(), b, scales, fmt, n, k)
     qmax = 7 if bits == 4 else 127
     q = G.randint(-qmax, qmax + 1, n, k)
     scales = G.uniform(2.0 * STD / qmax, 4.0 * STD / qmax, n, k // 64).to(torch.bfloat16)

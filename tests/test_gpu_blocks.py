@@ -66,9 +66,18 @@ def dequantised(w, quant):
     out = dict(w)
     for name, bits in quant.items():
         if name + "_w" in w:
-            q, sc = oracle.quantise(w[name + "_w"], bits)
-            out[name + "_w"] = oracle.dequantise(q, sc)
+            if bits in (1, 2):
+                c, sc = oracle.quantise_g128(w[name + "_w"], bits)
+                out[name + "_w"] = oracle.dequantise_g128(c, sc, bits)
+            else:
+                q, sc = oracle.quantise(w[name + "_w"], bits)
+                out[name + "_w"] = oracle.dequantise(q, sc)
     return out
+
+
+# 1-bit and ternary weights (groups of 128): ternary inner projections,
+# 1-bit residual-writing layers, so one block runs both formats
+SUB_BYTE_MIX = {"qkv": 2, "fc1": 2, "lin1": 2, "proj": 1, "fc2": 1, "lin2": 1}
 
 
 # ------------------------------------------------------------- float32 ------
@@ -156,13 +165,13 @@ def test_single_block_cfg3_bf16_full_size(cfg3):
     assert_parity(run_single(s, w, x, ids), oracle_single(s, w, x, ids), "bf16", "cfg3 single")
 
 
-@pytest.mark.parametrize("quant", [None, "policy"])
+@pytest.mark.parametrize("quant", [None, "policy", "sub_byte"])
 def test_blocks_bf16_full_width_ragged_rows(quant):
     # h 3072 with 77 text + 40x41 image tokens: the projections take the
     # 256x256 direct-to-LDS GEMM with partial row tiles in both streams
-    # (dense weights, or 4/8-bit weights dequantised into LDS)
+    # (dense weights, 4/8-bit or 1-bit/ternary weights dequantised into LDS)
     s = I.Shape(txt_len=77, grid_h=40, grid_w=41, dtype="bf16", cfg_id=38)
-    q = bd.QUANT_POLICY if quant else None
+    q = {None: None, "policy": bd.QUANT_POLICY, "sub_byte": SUB_BYTE_MIX}[quant]
     x = I.block_inputs(s)
     ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
     w = I.double_block_weights(s, 0)
@@ -193,19 +202,22 @@ def test_blocks_bf16_full_width_two_batches():
     assert_parity(run_single(s, ws_, x, ids), oracle_single(s, ws_, x, ids), "bf16", "two-batch single")
 
 
-def test_blocks_quantised_weights_bf16():
+@pytest.mark.parametrize("policy", ["q4q8", "sub_byte"])
+def test_blocks_quantised_weights_bf16(policy):
+    # h 1024: small problems, the register-staged GEMM dequantises B
     s = I.Shape(hidden=1024, heads=8, mlp_hidden=4096, txt_len=64, grid_h=16, grid_w=16, dtype="bf16",
                 cfg_id=35)
+    qp = bd.QUANT_POLICY if policy == "q4q8" else SUB_BYTE_MIX
     x = I.block_inputs(s)
     ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
     w = I.double_block_weights(s, 0)
-    img, txt = run_double(s, w, x, ids, quant=bd.QUANT_POLICY)
-    rimg, rtxt = oracle_double(s, dequantised(w, bd.QUANT_POLICY), x, ids)
-    assert_parity(img, rimg, "bf16", "q dual img")
-    assert_parity(txt, rtxt, "bf16", "q dual txt")
+    img, txt = run_double(s, w, x, ids, quant=qp)
+    rimg, rtxt = oracle_double(s, dequantised(w, qp), x, ids)
+    assert_parity(img, rimg, "bf16", f"{policy} dual img")
+    assert_parity(txt, rtxt, "bf16", f"{policy} dual txt")
     ws_ = I.single_block_weights(s, 0)
-    got = run_single(s, ws_, x, ids, quant=bd.QUANT_POLICY)
-    assert_parity(got, oracle_single(s, dequantised(ws_, bd.QUANT_POLICY), x, ids), "bf16", "q single")
+    got = run_single(s, ws_, x, ids, quant=qp)
+    assert_parity(got, oracle_single(s, dequantised(ws_, qp), x, ids), "bf16", f"{policy} single")
 
 
 # ------------------------------------------------------------ properties ----
