@@ -19,7 +19,8 @@ Sources (the pages this follows):
     sampling parameters (base/max shift, step counts).
   * stable-diffusion.rs README: quantised weights dequantised inside the
     matmul, 8-bit residual-writing layers with 4-bit elsewhere; the fused
-    SDPA / layer_norm / rms_norm kernels it relies on.
+    SDPA / layer_norm / rms_norm kernels it relies on; step caching behind
+    a cache threshold (deterministic samplers only).
   * pictor README, numerics section: fp32 accumulation, cosine >= 0.999
     stage gates.
 
@@ -34,4 +35,5 @@ from .mmdit import (  # noqa: F401
     conditioning_vec, final_layer, step, mu_for_tokens, time_shift,
     schedule, euler_update, quantise, dequantise, pack_int4, unpack_int4,
     bf16_round_up, bf16_rne, quantise_g128, dequantise_g128, pack_g128, unpack_g128,
+    rel_l1, cache_decide, new_cache_state, step_cached,
 )

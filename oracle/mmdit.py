@@ -340,6 +340,80 @@ def step(g: Dict[str, np.ndarray], dbl: Sequence, sgl: Sequence, X: np.ndarray, 
     return euler_update(X, v, sigma, sigma_next), v
 
 
+# ---------------------------------------------------------- step caching ---
+# stable-diffusion.rs README: step caching behind a cache threshold, only
+# with a deterministic sampler, credited to TeaCache. The pages give no
+# formula; reading: the change of the first dual block's modulated image
+# input between consecutive steps, measured as a relative L1 distance and
+# summed since the last step that ran the blocks, decides whether the blocks
+# run again (sum >= threshold) or their image-stream residual from that step
+# is added to this step's image tokens instead.
+def rel_l1(a: np.ndarray, p: np.ndarray) -> float:
+    """sum |a - p| / sum |p| over every element, in float64 (0 when both sums
+    are 0, inf when only the second is)."""
+    num = float(np.abs(a.astype(np.float64) - p.astype(np.float64)).sum())
+    den = float(np.abs(p.astype(np.float64)).sum())
+    if den == 0.0:
+        return 0.0 if num == 0.0 else math.inf
+    return num / den
+
+
+def cache_decide(valid: bool, acc: float, rel: float, threshold: float):
+    """(run_blocks, new_acc): a first step always runs the blocks; later
+    steps add rel to the running sum and reuse the residual while the sum
+    stays below the threshold; running the blocks resets the sum to 0."""
+    if not valid:
+        return True, 0.0
+    acc = acc + rel
+    if acc < threshold:
+        return False, acc
+    return True, 0.0
+
+
+def new_cache_state() -> dict:
+    """Cache state of one generation: prev (last modulated input), resid
+    (image-stream residual of the last step that ran the blocks), acc, valid."""
+    return {"prev": None, "resid": None, "acc": 0.0, "valid": False}
+
+
+def step_cached(g: Dict[str, np.ndarray], dbl: Sequence, sgl: Sequence, X: np.ndarray, T: np.ndarray,
+                y: np.ndarray, ids: np.ndarray, sigma: float, sigma_next: float, heads: int, state: dict,
+                threshold: float, axes_dim=(16, 56, 56), theta: float = 10000.0, Xc: np.ndarray = None,
+                guidance=None):
+    """One denoising step with step caching (reading above). Needs a dual
+    block. The indicator is a = modulate(img0; shift1, scale1) of the first
+    dual block's image stream, img0 the image tokens after the input
+    projection (context tokens included). state (new_cache_state()) is
+    updated in place. Returns (X_next, v, ran_blocks, rel)."""
+    if len(dbl) == 0:
+        raise ValueError("step caching needs a dual-stream block")
+    dt = X.dtype
+    Lg = X.shape[1]
+    img0 = linear(X if Xc is None else np.concatenate([X, Xc.astype(dt)], axis=1), g["img_in_w"], g["img_in_b"])
+    vec = conditioning_vec(g, sigma, y.astype(dt), temb_dim=g["time_in0_w"].shape[1], guidance=guidance)
+    sh1, sc1 = _chunks(linear(silu(vec.astype(dt)), dbl[0]["img"]["mod_w"], dbl[0]["img"]["mod_b"]), 6)[:2]
+    a = modulate(img0, sh1, sc1)
+    rel = rel_l1(a, state["prev"]) if state["valid"] else 0.0
+    run, acc = cache_decide(state["valid"], state["acc"], rel, threshold)
+    if run:
+        img = img0
+        txt = linear(T.astype(dt), g["txt_in_w"], g["txt_in_b"])
+        for i in range(len(dbl)):
+            img, txt = double_block(dbl[i], img, txt, vec, ids, heads, axes_dim, theta)
+        x = np.concatenate([txt, img], axis=1)
+        for i in range(len(sgl)):
+            x = single_block(sgl[i], x, vec, ids, heads, axes_dim, theta)
+        img = x[:, T.shape[1]:]
+        state["resid"] = img - img0
+    else:
+        img = img0 + state["resid"]
+    state["prev"] = a
+    state["acc"] = acc
+    state["valid"] = True
+    v = final_layer(g, img[:, :Lg], vec)
+    return euler_update(X, v, sigma, sigma_next), v, run, rel
+
+
 # -------------------------------------------------------------- schedule ---
 def mu_for_tokens(img_len: int, base_shift: float = 0.5, max_shift: float = 1.15,
                   lo: int = 256, hi: int = 4096) -> float:

@@ -469,6 +469,101 @@ def test_guidance_embedding_is_a_second_timestep_map():
         oracle.conditioning_vec(gw, 0.7, y)
 
 
+# --------------------------------------------------------- step caching ---
+def test_rel_l1_hand_worked():
+    # |1-2| + |2-2| + |-3+1| = 3 over |2| + |2| + |-1| = 5
+    assert oracle.rel_l1(np.array([1.0, 2.0, -3.0]), np.array([2.0, 2.0, -1.0])) == 0.6
+    assert oracle.rel_l1(np.zeros(3), np.zeros(3)) == 0.0
+    assert oracle.rel_l1(np.ones(3), np.zeros(3)) == np.inf
+
+
+def test_cache_decide_hand_traced():
+    # threshold 0.5, every later step changes by 0.25: run, reuse (0.25),
+    # run (0.5 reaches the threshold, sum reset), reuse (0.25), run (0.5)
+    valid, acc, got = False, 0.0, []
+    for _ in range(5):
+        run, acc = oracle.cache_decide(valid, acc, 0.25, 0.5)
+        valid = True
+        got.append((run, acc))
+    assert got == [(True, 0.0), (False, 0.25), (True, 0.0), (False, 0.25), (True, 0.0)]
+    # threshold 0: every step runs the blocks
+    assert all(oracle.cache_decide(True, a, r, 0.0)[0] for a in (0.0, 3.0) for r in (0.0, 1.0))
+
+
+def _cache_case(**kw):
+    s = tiny_shape(txt_len=3, grid_h=2, grid_w=3, **kw)
+    g = _f64(I.global_weights(s))
+    dbl = [_f64(I.double_block_weights(s, i)) for i in range(2)]
+    sgl = [_f64(I.single_block_weights(s, i)) for i in range(2)]
+    inp = _f64(I.step_inputs(s))
+    X = oracle.pack_latents(inp["z"])
+    ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
+    return s, g, dbl, sgl, inp, X, ids
+
+
+def test_step_cached_threshold_zero_is_the_plain_step():
+    s, g, dbl, sgl, inp, X, ids = _cache_case()
+    sig = oracle.schedule(3, s.img_len)
+    st = oracle.new_cache_state()
+    for i in range(3):
+        Xn, v, run, rel = oracle.step_cached(g, dbl, sgl, X, inp["T"], inp["y"], ids, sig[i], sig[i + 1],
+                                             s.heads, st, 0.0)
+        Xr, vr = oracle.step(g, dbl, sgl, X, inp["T"], inp["y"], ids, sig[i], sig[i + 1], s.heads)
+        assert run and np.array_equal(v, vr) and np.array_equal(Xn, Xr)
+        assert (rel == 0.0) if i == 0 else (rel > 0.0)
+        X = Xn
+
+
+def test_step_cached_repeat_reuses_the_residual():
+    # The same latent and sigma twice: the indicator does not move (rel 0),
+    # the second step reuses the residual, and img0 + (img - img0) gives the
+    # first step's v up to rounding. Context tokens ride in the residual.
+    s, g, dbl, sgl, inp, X, Xc, ids = _ctx_case()
+    g, dbl, sgl, X, Xc = _f64(g), [_f64(w) for w in dbl], [_f64(w) for w in sgl], _f64(X), _f64(Xc)
+    st = oracle.new_cache_state()
+    out = [oracle.step_cached(g, dbl, sgl, X, inp["T"], inp["y"], ids, 1.0, 0.9, s.heads, st, 1e-9, Xc=Xc)
+           for _ in range(2)]
+    assert out[0][2] and not out[1][2] and out[1][3] == 0.0
+    assert rel_l2(out[1][1], out[0][1]) < 1e-13
+    _, vr = oracle.step(g, dbl, sgl, X, inp["T"], inp["y"], ids, 1.0, 0.9, s.heads, Xc=Xc)
+    assert np.array_equal(out[0][1], vr)
+
+
+def test_step_cached_identity_blocks_skip_equals_compute():
+    # With every modulation zero the blocks add nothing: the residual is
+    # exactly zero, so a reused step is exactly the plain step at the new
+    # latent and sigma (the residual is added to this step's tokens).
+    s, g, dbl, sgl, inp, X, ids = _cache_case()
+    dbl = [I.zero_modulation(w) for w in dbl]
+    sgl = [I.zero_modulation(w) for w in sgl]
+    st = oracle.new_cache_state()
+    X1, _, run1, _ = oracle.step_cached(g, dbl, sgl, X, inp["T"], inp["y"], ids, 1.0, 0.6, s.heads, st, np.inf)
+    X2, v2, run2, rel = oracle.step_cached(g, dbl, sgl, X1, inp["T"], inp["y"], ids, 0.6, 0.2, s.heads, st, np.inf)
+    assert run1 and not run2 and rel > 0.0
+    Xr, vr = oracle.step(g, dbl, sgl, X1, inp["T"], inp["y"], ids, 0.6, 0.2, s.heads)
+    assert np.array_equal(v2, vr) and np.array_equal(X2, Xr)
+
+
+def test_step_cached_indicator_reads_the_first_dual_block_image_input():
+    # rel depends on the latent, sigma and the first dual block's image
+    # modulation only: new text or a different second block leave it as is.
+    s, g, dbl, sgl, inp, X, ids = _cache_case()
+    def rels(T, blocks):
+        st = oracle.new_cache_state()
+        out = []
+        for Xi, a, b in ((X, 1.0, 0.7), (1.1 * X, 0.7, 0.3)):
+            out.append(oracle.step_cached(g, blocks, sgl, Xi, T, inp["y"], ids, a, b, s.heads, st, 0.0)[3])
+        return out
+    base = rels(inp["T"], dbl)
+    assert base[0] == 0.0 and base[1] > 0.0
+    assert rels(2.0 * inp["T"] + 1.0, dbl) == base
+    assert rels(inp["T"], [dbl[0], dbl[0]]) == base
+    d0 = {"txt": dbl[0]["txt"], "img": dict(dbl[0]["img"], mod_b=dbl[0]["img"]["mod_b"] + 0.5)}
+    assert rels(inp["T"], [d0, dbl[1]])[1] != base[1]
+    with pytest.raises(ValueError):
+        oracle.step_cached(g, [], sgl, X, inp["T"], inp["y"], ids, 1.0, 0.7, s.heads, oracle.new_cache_state(), 0.0)
+
+
 # ------------------------------------------------------- schedule, Euler ---
 def test_schedule_page_invariants():
     sh = PAGES["shift"]
