@@ -71,9 +71,14 @@ class mmdit_model_w(C.Structure):
                 ("guidance_in0", mmdit_linear), ("guidance_in1", mmdit_linear)]
 
 
+class mmdit_step_cache(C.Structure):
+    _fields_ = [("buf", C.c_void_p), ("bytes", C.c_size_t), ("valid", C.c_int32), ("ran_blocks", C.c_int32),
+                ("acc", C.c_double), ("rel", C.c_double)]
+
+
 class mmdit_step_opts(C.Structure):
     _fields_ = [("ctx_packed", C.c_void_p), ("ctx_len", C.c_int32), ("has_guidance", C.c_int32),
-                ("guidance", C.c_double)]
+                ("guidance", C.c_double), ("cache", C.POINTER(mmdit_step_cache)), ("cache_threshold", C.c_double)]
 
 
 # Every function the header declares, with its ctypes signature.
@@ -82,6 +87,7 @@ _SIGS = {
     "mmdit_double_block_workspace": (C.c_int, [C.POINTER(mmdit_dims), C.POINTER(C.c_size_t)]),
     "mmdit_single_block_workspace": (C.c_int, [C.POINTER(mmdit_dims), C.POINTER(C.c_size_t)]),
     "mmdit_step_workspace": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(C.c_size_t)]),
+    "mmdit_step_cache_bytes": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(C.c_size_t)]),
     "mmdit_double_block_fwd": (C.c_int, [C.POINTER(mmdit_dims), C.POINTER(mmdit_double_w), _P, _P, _P, _P,
                                          _P, _P, _P, C.c_size_t, _P]),
     "mmdit_single_block_fwd": (C.c_int, [C.POINTER(mmdit_dims), C.POINTER(mmdit_single_w), _P, _P, _P, _P,
@@ -320,13 +326,49 @@ def mmdit_step(cfg, w: mmdit_model_w, x_packed, v_out, txt_emb, y, ids, sigma: f
            "mmdit_step")
 
 
+def mmdit_step_cache_bytes(cfg: mmdit_config) -> int:
+    n = C.c_size_t()
+    _check(lib().mmdit_step_cache_bytes(C.byref(cfg), C.byref(n)), "mmdit_step_cache_bytes")
+    return n.value
+
+
+class StepCache:
+    """Step-cache state of one generation: the device buffer (a torch uint8
+    tensor) and the mmdit_step_cache struct the library updates."""
+
+    def __init__(self, cfg: mmdit_config, device="cuda"):
+        import torch
+        self.buf = torch.empty(mmdit_step_cache_bytes(cfg), dtype=torch.uint8, device=device)
+        self.c = mmdit_step_cache()
+        self.c.buf = self.buf.data_ptr()
+        self.c.bytes = self.buf.numel()
+        self.reset()
+
+    def reset(self):
+        """Start a new generation (the next step runs the blocks)."""
+        self.c.valid = 0
+        self.c.acc = 0.0
+
+    @property
+    def ran_blocks(self) -> bool:
+        return bool(self.c.ran_blocks)
+
+    @property
+    def rel(self) -> float:
+        return self.c.rel
+
+
 def mmdit_step_ex(cfg, w: mmdit_model_w, x_packed, v_out, txt_emb, y, ids, sigma: float, sigma_next: float, ws,
-                  ctx_packed=None, ctx_len: int = 0, guidance: Optional[float] = None, stream=None):
+                  ctx_packed=None, ctx_len: int = 0, guidance: Optional[float] = None, stream=None,
+                  cache: Optional[StepCache] = None, cache_threshold: float = 0.0):
     o = mmdit_step_opts()
     o.ctx_packed = _ptr(ctx_packed)
     o.ctx_len = int(ctx_len)
     o.has_guidance = 0 if guidance is None else 1
     o.guidance = 0.0 if guidance is None else float(guidance)
+    if cache is not None:
+        o.cache = C.pointer(cache.c)
+        o.cache_threshold = float(cache_threshold)
     _check(lib().mmdit_step_ex(C.byref(cfg), C.byref(w), _ptr(x_packed), _ptr(v_out), _ptr(txt_emb), _ptr(y),
                                _ptr(ids), float(sigma), float(sigma_next), C.byref(o), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream)),

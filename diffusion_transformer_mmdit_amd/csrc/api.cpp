@@ -525,6 +525,30 @@ int mmdit_step_workspace(const mmdit_config* cfg, size_t* bytes) {
   return MMDIT_OK;
 }
 
+// Step-cache buffer: a_prev [B Li h], residual [B Li h] (float32), per-row
+// partial sums [B Li 2].
+struct CacheLay {
+  size_t prev, resid, part, total;
+};
+static CacheLay plan_cache(const Geo& g) {
+  CacheLay c;
+  const size_t n = (size_t)g.B * g.Li * g.h;
+  c.prev = 0;
+  c.resid = align_up(n * 4);
+  c.part = align_up(c.resid + n * 4);
+  c.total = align_up(c.part + (size_t)g.B * g.Li * 2 * 4);
+  return c;
+}
+
+int mmdit_step_cache_bytes(const mmdit_config* cfg, size_t* bytes) {
+  Geo g;
+  int r;
+  if (!bytes) return fail(MMDIT_ERR_NULL, "bytes is NULL");
+  if ((r = check_config(cfg, g))) return r;
+  *bytes = plan_cache(g).total;
+  return MMDIT_OK;
+}
+
 // One step; the image stream holds Lg = Li - ctx_len generated tokens
 // followed by ctx_len context tokens per batch (ctx_packed [B, ctx_len,
 // in_ch] float32). Only the generated rows get the final layer and update.
@@ -548,6 +572,15 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
     if (!opts->has_guidance)
       return fail(MMDIT_ERR_NULL, "the model has a guidance embedder: pass a guidance value (mmdit_step_ex)");
     if (!std::isfinite(opts->guidance)) return fail(MMDIT_ERR_SHAPE, "guidance must be finite");
+  }
+  mmdit_step_cache* cache = opts->cache;
+  if (cache) {
+    if (std::isnan(opts->cache_threshold) || opts->cache_threshold < 0)
+      return fail(MMDIT_ERR_SHAPE, "cache_threshold must be >= 0");
+    if (cfg->n_double < 1) return fail(MMDIT_ERR_SHAPE, "step caching needs a dual-stream block");
+    if (!cache->buf) return fail(MMDIT_ERR_NULL, "cache->buf is NULL");
+    if (cache->bytes < plan_cache(g).total)
+      return fail(MMDIT_ERR_WORKSPACE, "cache buffer %zu bytes, need %zu", cache->bytes, plan_cache(g).total);
   }
   if (g.Lt > 0 && !txt_emb) return fail(MMDIT_ERR_NULL, "txt_emb is NULL with txt_len > 0");
   if ((cfg->n_double > 0 && !w->dbl) || (cfg->n_single > 0 && !w->sgl)) return fail(MMDIT_ERR_NULL, "block weight arrays are NULL");
@@ -598,41 +631,33 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   }
   if ((r = gemv(c, w->vec_in0, y, false, cfg->vec_in_dim, hid, h, false, false))) return r;
   if ((r = gemv(c, w->vec_in1, hid, true, h, vec, h, true, true))) return r;
-  // every block's modulation up front, all from SiLU(vec): batched into
-  // launches of up to kGemvMaxSeg weight matrices
-  {
-    GemvMultiArgs ga{};
-    ga.x = vec; ga.K = h; ga.B = B; ga.x_bstride = h;
-    double bytes = 0;
-    auto flush = [&]() -> int {
-      if (ga.nseg == 0) return MMDIT_OK;
-      ProfScope ps(PC_GEMV, bytes, c.s);
-      HIP_TRY(launch_gemv_multi(ga, g.bf16, c.s));
-      ga.nseg = 0;
-      bytes = 0;
-      return MMDIT_OK;
-    };
-    auto add = [&](const mmdit_linear& l, float* y, int y_bstride) -> int {
-      if (B > kGemvMaxB) return gemv(c, l, vec, true, h, y, y_bstride, true, false);
-      GemvSeg& sg = ga.seg[ga.nseg++];
-      sg.W = l.w; sg.bias = l.bias; sg.y = y; sg.N = l.n_out; sg.y_bstride = y_bstride;
-      bytes += (double)l.n_out * l.k_in * g.esz;
-      return ga.nseg == kGemvMaxSeg ? flush() : MMDIT_OK;
-    };
-    for (int i = 0; i < cfg->n_double; ++i) {
-      float* md = mods + lay.mod_dual + (size_t)i * 2 * B * 6 * h;
-      if ((r = add(w->dbl[i].txt.mod, md, 6 * h))) return r;
-      if ((r = add(w->dbl[i].img.mod, md + (size_t)B * 6 * h, 6 * h))) return r;
-    }
-    for (int i = 0; i < cfg->n_single; ++i) {
-      if ((r = add(w->sgl[i].mod, mods + lay.mod_single + (size_t)i * B * 3 * h, 3 * h))) return r;
-    }
-    if ((r = add(w->final_mod, mods + lay.mod_final, 2 * h))) return r;
-    if ((r = flush())) return r;
-  }
-  if ((r = rope(c, &cfg->dims, ids, table))) return r;
+  // every block's modulation, all from SiLU(vec): batched into launches of
+  // up to kGemvMaxSeg weight matrices. The final layer's and the first dual
+  // block's image modulation come first: a step that reuses the cached
+  // residual needs only those two.
+  GemvMultiArgs ga{};
+  ga.x = vec; ga.K = h; ga.B = B; ga.x_bstride = h;
+  double gemv_bytes = 0;
+  auto flush = [&]() -> int {
+    if (ga.nseg == 0) return MMDIT_OK;
+    ProfScope ps(PC_GEMV, gemv_bytes, c.s);
+    HIP_TRY(launch_gemv_multi(ga, g.bf16, c.s));
+    ga.nseg = 0;
+    gemv_bytes = 0;
+    return MMDIT_OK;
+  };
+  auto add = [&](const mmdit_linear& l, float* out, int y_bstride) -> int {
+    if (B > kGemvMaxB) return gemv(c, l, vec, true, h, out, y_bstride, true, false);
+    GemvSeg& sg = ga.seg[ga.nseg++];
+    sg.W = l.w; sg.bias = l.bias; sg.y = out; sg.N = l.n_out; sg.y_bstride = y_bstride;
+    gemv_bytes += (double)l.n_out * l.k_in * g.esz;
+    return ga.nseg == kGemvMaxSeg ? flush() : MMDIT_OK;
+  };
+  if ((r = add(w->final_mod, mods + lay.mod_final, 2 * h))) return r;
+  if (cfg->n_double > 0 && (r = add(w->dbl[0].img.mod, mods + lay.mod_dual + (size_t)B * 6 * h, 6 * h))) return r;
+  if (cache && (r = flush())) return r;
 
-  // input projections into the f32 residual
+  // image input projection into the f32 residual
   const void* xa = x_packed;
   if (ctx_len > 0) {
     // per batch: [generated rows; context rows] staged in the activation dtype
@@ -648,42 +673,91 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
     HIP_TRY(launch_convert(x_packed, true, ptr(ws, lay.xin), false, (int64_t)B * g.Li * cfg->in_ch, c.s));
     xa = ptr(ws, lay.xin);
   }
-  GemmProblem gp[2];
-  int np = 0;
-  gp[np] = base_problem(w->img_in);
-  gp[np].A = xa; gp[np].lda = cfg->in_ch; gp[np].M = B * g.Li;
-  gp[np].out = x + (size_t)B * g.Lt * h; gp[np].ldo = h; gp[np].out_f32 = true;
-  ++np;
-  if (g.Lt > 0) {
-    gp[np] = base_problem(w->txt_in);
-    gp[np].A = txt_emb; gp[np].lda = cfg->txt_in_dim; gp[np].M = B * g.Lt;
-    gp[np].out = x; gp[np].ldo = h; gp[np].out_f32 = true;
-    ++np;
+  float* ximg = x + (size_t)B * g.Lt * h;  // image rows, contiguous [B Li h]
+  const int64_t nimg = (int64_t)B * g.Li * h;
+  {
+    GemmProblem gi = base_problem(w->img_in);
+    gi.A = xa; gi.lda = cfg->in_ch; gi.M = B * g.Li;
+    gi.out = ximg; gi.ldo = h; gi.out_f32 = true;
+    if ((r = gemm(c, &gi, 1, EPI_STORE))) return r;
   }
-  // the two projections have different K: one launch each
-  for (int i = 0; i < np; ++i)
-    if ((r = gemm(c, &gp[i], 1, EPI_STORE))) return r;
+
+  // step cache: indicator, decision, residual
+  bool run_blocks = true;
+  double rel = 0.0, acc = 0.0;
+  float* resid = nullptr;
+  if (cache) {
+    const CacheLay cl = plan_cache(g);
+    resid = (float*)ptr(cache->buf, cl.resid);
+    float* part = (float*)ptr(cache->buf, cl.part);
+    CacheDeltaArgs ca{};
+    ca.x = ximg;
+    ca.mod = mods + lay.mod_dual + (size_t)B * 6 * h;  // shift1 at 0, scale1 at h
+    ca.mod_bstride = 6 * h;
+    ca.rows_per_batch = g.Li;
+    ca.prev = (float*)ptr(cache->buf, cl.prev);
+    ca.part = part;
+    ca.rows = B * g.Li;
+    ca.h = h;
+    ca.eps = c.ln_eps;
+    ca.first = cache->valid ? 0 : 1;
+    HIP_TRY(launch_cache_delta(ca, c.s));
+    if (cache->valid) {
+      std::vector<float> hp((size_t)2 * B * g.Li);
+      HIP_TRY(hipMemcpyAsync(hp.data(), part, hp.size() * sizeof(float), hipMemcpyDeviceToHost, c.s));
+      HIP_TRY(hipStreamSynchronize(c.s));
+      double num = 0.0, den = 0.0;
+      for (size_t k = 0; k < hp.size(); k += 2) {
+        num += hp[k];
+        den += hp[k + 1];
+      }
+      rel = den > 0.0 ? num / den : (num > 0.0 ? INFINITY : 0.0);
+      acc = cache->acc + rel;
+      run_blocks = !(acc < opts->cache_threshold);
+      if (run_blocks) acc = 0.0;
+    }
+    if (run_blocks) HIP_TRY(launch_axpby(resid, ximg, 0.f, 1.f, nimg, c.s));  // resid <- img0
+    else HIP_TRY(launch_axpby(ximg, resid, 1.f, 1.f, nimg, c.s));             // img0 + residual
+  }
 
   Part parts[2];
   parts[0] = {g.Lt, 0, rows_of(x, 0, g.Lt, h, 4), rows_of(x, 0, g.Lt, h, 4), nullptr};
   parts[1] = {g.Li, (int64_t)B * g.Lt, rows_of(x, (int64_t)B * g.Lt, g.Li, h, 4),
               rows_of(x, (int64_t)B * g.Lt, g.Li, h, 4), nullptr};
-  for (int i = 0; i < cfg->n_double; ++i) {
-    float* md = mods + lay.mod_dual + (size_t)i * 2 * B * 6 * h;
-    parts[0].mod = md;
-    parts[1].mod = md + (size_t)B * 6 * h;
-    const mmdit_stream_w* sw[2] = {&w->dbl[i].txt, &w->dbl[i].img};
-    if ((r = run_double(c, sw, parts, true, table, ws, lay.blk))) return r;
-  }
-  for (int i = 0; i < cfg->n_single; ++i) {
-    float* ms = mods + lay.mod_single + (size_t)i * B * 3 * h;
-    parts[0].mod = ms;
-    parts[1].mod = ms;
-    if (g.Lt > 0) {
-      if ((r = run_single(c, w->sgl[i], parts, 2, true, table, ws, lay.blk))) return r;
-    } else {
-      if ((r = run_single(c, w->sgl[i], &parts[1], 1, true, table, ws, lay.blk))) return r;
+  if (run_blocks) {
+    for (int i = 0; i < cfg->n_double; ++i) {
+      float* md = mods + lay.mod_dual + (size_t)i * 2 * B * 6 * h;
+      if ((r = add(w->dbl[i].txt.mod, md, 6 * h))) return r;
+      if (i > 0 && (r = add(w->dbl[i].img.mod, md + (size_t)B * 6 * h, 6 * h))) return r;
     }
+    for (int i = 0; i < cfg->n_single; ++i)
+      if ((r = add(w->sgl[i].mod, mods + lay.mod_single + (size_t)i * B * 3 * h, 3 * h))) return r;
+    if ((r = flush())) return r;
+    if ((r = rope(c, &cfg->dims, ids, table))) return r;
+    if (g.Lt > 0) {
+      GemmProblem gt = base_problem(w->txt_in);
+      gt.A = txt_emb; gt.lda = cfg->txt_in_dim; gt.M = B * g.Lt;
+      gt.out = x; gt.ldo = h; gt.out_f32 = true;
+      if ((r = gemm(c, &gt, 1, EPI_STORE))) return r;
+    }
+    for (int i = 0; i < cfg->n_double; ++i) {
+      float* md = mods + lay.mod_dual + (size_t)i * 2 * B * 6 * h;
+      parts[0].mod = md;
+      parts[1].mod = md + (size_t)B * 6 * h;
+      const mmdit_stream_w* sw[2] = {&w->dbl[i].txt, &w->dbl[i].img};
+      if ((r = run_double(c, sw, parts, true, table, ws, lay.blk))) return r;
+    }
+    for (int i = 0; i < cfg->n_single; ++i) {
+      float* ms = mods + lay.mod_single + (size_t)i * B * 3 * h;
+      parts[0].mod = ms;
+      parts[1].mod = ms;
+      if (g.Lt > 0) {
+        if ((r = run_single(c, w->sgl[i], parts, 2, true, table, ws, lay.blk))) return r;
+      } else {
+        if ((r = run_single(c, w->sgl[i], &parts[1], 1, true, table, ws, lay.blk))) return r;
+      }
+    }
+    if (cache) HIP_TRY(launch_axpby(resid, ximg, -1.f, 1.f, nimg, c.s));  // resid <- img - img0
   }
   // final layer on the generated image rows, Euler update fused into the epilogue
   Part fin = parts[1];
@@ -698,7 +772,14 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   f.res_in = f.res_out;
   f.dsigma = (float)(sigma_next - sigma);
   f.v_out = (float*)v_out;
-  return gemm(c, &f, 1, EPI_EULER);
+  if ((r = gemm(c, &f, 1, EPI_EULER))) return r;
+  if (cache) {
+    cache->valid = 1;
+    cache->ran_blocks = run_blocks ? 1 : 0;
+    cache->acc = acc;
+    cache->rel = rel;
+  }
+  return MMDIT_OK;
 }
 
 int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, void* v_out,

@@ -101,6 +101,118 @@ hipError_t launch_adaln_ln(const LnArgs& a, int rows, bool x_f32, bool y_bf16, h
   return hipGetLastError();
 }
 
+// ------------------------------------------------------- step-cache indicator --
+// stable-diffusion.rs README, step caching: the change of the first dual
+// block's modulated image input between steps. One wavefront per row, the
+// LayerNorm arithmetic of k_adaln_ln; the per-row sums are reduced on the
+// host in a fixed order.
+template <int NC>
+__global__ __launch_bounds__(256) void k_cache_delta(CacheDeltaArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= a.rows) return;
+  const float* x = a.x + (int64_t)r * a.h;
+  const int b = r / a.rows_per_batch;
+  const float* shift = a.mod + (int64_t)b * a.mod_bstride;
+  const float* scale = shift + a.h;
+  float v[NC][4];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) load4(x + (i * 64 + lane) * 4, v[i]);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) sum += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+  const float inv_h = 1.0f / (float)(NC * 256);
+  const float mean = wave_sum(sum) * inv_h;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float d = v[i][j] - mean;
+      sq += d * d;
+    }
+  const float var = wave_sum(sq) * inv_h;
+  const float rstd = 1.0f / sqrtf(var + a.eps);
+  float* prev = a.prev + (int64_t)r * a.h;
+  float dsum = 0.f, psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = (i * 64 + lane) * 4;
+    float sh[4], sc[4], o[4], p[4];
+    load4(shift + c, sh);
+    load4(scale + c, sc);
+    load4(prev + c, p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[j] = (1.0f + sc[j]) * ((v[i][j] - mean) * rstd) + sh[j];
+      dsum += fabsf(o[j] - p[j]);
+      psum += fabsf(p[j]);
+    }
+    store4(prev + c, o);
+  }
+  dsum = wave_sum(dsum);
+  psum = wave_sum(psum);
+  if (!a.first && lane == 0) {
+    a.part[2 * r] = dsum;
+    a.part[2 * r + 1] = psum;
+  }
+}
+
+template <int NC>
+static void launch_cd_nc(const CacheDeltaArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((k_cache_delta<NC>), dim3((a.rows + 3) / 4), dim3(256), 0, s, a);
+}
+
+// h is a multiple of 256 and at most 4096 (checked by the API).
+hipError_t launch_cache_delta(const CacheDeltaArgs& a, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  switch (a.h / 256) {
+    case 1: launch_cd_nc<1>(a, s); break;
+    case 2: launch_cd_nc<2>(a, s); break;
+    case 3: launch_cd_nc<3>(a, s); break;
+    case 4: launch_cd_nc<4>(a, s); break;
+    case 5: launch_cd_nc<5>(a, s); break;
+    case 6: launch_cd_nc<6>(a, s); break;
+    case 7: launch_cd_nc<7>(a, s); break;
+    case 8: launch_cd_nc<8>(a, s); break;
+    case 9: launch_cd_nc<9>(a, s); break;
+    case 10: launch_cd_nc<10>(a, s); break;
+    case 11: launch_cd_nc<11>(a, s); break;
+    case 12: launch_cd_nc<12>(a, s); break;
+    case 13: launch_cd_nc<13>(a, s); break;
+    case 14: launch_cd_nc<14>(a, s); break;
+    case 15: launch_cd_nc<15>(a, s); break;
+    default: launch_cd_nc<16>(a, s); break;
+  }
+  return hipGetLastError();
+}
+
+// y = alpha y + beta x, four floats per thread, grid-stride.
+__global__ __launch_bounds__(256) void k_axpby(float4* y, const float4* x, float alpha, float beta, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const float4 xv = x[i];
+    float4 o;
+    if (alpha == 0.f) {
+      o = make_float4(beta * xv.x, beta * xv.y, beta * xv.z, beta * xv.w);
+    } else {
+      const float4 yv = y[i];
+      o = make_float4(alpha * yv.x + beta * xv.x, alpha * yv.y + beta * xv.y, alpha * yv.z + beta * xv.z,
+                      alpha * yv.w + beta * xv.w);
+    }
+    y[i] = o;
+  }
+}
+
+hipError_t launch_axpby(float* y, const float* x, float alpha, float beta, int64_t n, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  const int64_t want = (n4 + 255) / 256;
+  const int grid = (int)(want < 2048 ? want : 2048);
+  hipLaunchKernelGGL(k_axpby, dim3(grid), dim3(256), 0, s, reinterpret_cast<float4*>(y),
+                     reinterpret_cast<const float4*>(x), alpha, beta, n4);
+  return hipGetLastError();
+}
+
 // ----------------------------------------------------------- QK RMSNorm + RoPE --
 // Block (64-token tile, head, batch), 256 threads. q and k: 16 lanes per
 // token, 8 dims per lane; RMS over the 128 dims of the head, times the

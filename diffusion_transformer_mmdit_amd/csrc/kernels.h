@@ -37,6 +37,27 @@ struct LnArgs {
 // y_bf16: output bf16 (else float32).
 hipError_t launch_adaln_ln(const LnArgs& a, int rows, bool x_f32, bool y_bf16, hipStream_t s);
 
+// ---- step-cache indicator -------------------------------------------------------
+// For each of `rows` contiguous float32 rows x[r, :] (batch r / rows_per_batch):
+// a = (1 + scale_b) * LN(x[r, :]) + shift_b with shift_b = mod + b * mod_bstride,
+// scale_b = shift_b + h; part[2r] = sum |a - prev[r, :]|, part[2r + 1] =
+// sum |prev[r, :]| (not written when first != 0); then prev[r, :] = a.
+struct CacheDeltaArgs {
+  const float* x;
+  const float* mod;
+  int32_t mod_bstride;
+  int32_t rows_per_batch;
+  float* prev;
+  float* part;
+  int32_t rows, h;
+  float eps;
+  int32_t first;
+};
+hipError_t launch_cache_delta(const CacheDeltaArgs& a, hipStream_t s);
+// y[i] = alpha * y[i] + beta * x[i] over n floats (n % 4 == 0, 16-byte aligned);
+// alpha == 0 writes beta * x[i] without reading y.
+hipError_t launch_axpby(float* y, const float* x, float alpha, float beta, int64_t n, hipStream_t s);
+
 // ---- QK RMSNorm + RoPE + attention layout ------------------------------------
 // Token t of batch b reads q|k|v from row (b, t) of seg[0] when t < seg_len0,
 // else row (b, t - seg_len0) of seg[1] (q at col 0, k at h, v at 2h).

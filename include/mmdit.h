@@ -203,12 +203,45 @@ int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w,
  * embedded as temb(1000 g) and mapped by guidance_in0 / SiLU / guidance_in1;
  * the result is added to the conditioning vector.
  *   has_guidance: 1 to pass `guidance`; required (and only used) when the
- *   model has a guidance embedder. */
+ *   model has a guidance embedder.
+ *
+ * Step caching (stable-diffusion.rs README: step caching behind a cache
+ * threshold, for deterministic samplers only, credited to TeaCache). Reading
+ * where the pages are silent: each step computes a = (1 + scale1) LN(img0) +
+ * shift1 with the first dual block's image-stream modulation, img0 the image
+ * tokens after the input projection (context tokens included), and its
+ * relative L1 change rel = sum|a - a_prev| / sum|a_prev| against the previous
+ * step; rel is added to a running sum. While the sum stays below the
+ * threshold the step skips every block and adds the image-stream residual
+ * (image tokens after the last block minus img0) of the last step that ran
+ * the blocks to img0; otherwise it runs the blocks, stores their residual and
+ * resets the sum to 0. A first step (valid == 0) always runs the blocks.
+ *   cache: the generation's state (below), NULL for no caching.
+ *   cache_threshold: >= 0; 0 runs the blocks on every step.
+ * A cached step waits for its stream once (it reads rel back to decide), so
+ * it cannot be captured into a HIP graph. Needs n_double >= 1. */
+typedef struct {
+  void* buf;          /* device memory of mmdit_step_cache_bytes(cfg) bytes, caller-owned;
+                         the library keeps a_prev and the residual there (float32) */
+  size_t bytes;       /* size of buf */
+  int32_t valid;      /* in/out: 0 starts a generation; set to 1 by a successful step.
+                         After an error return, set it to 0 before the next step. */
+  int32_t ran_blocks; /* out: 1 if the step ran the blocks, 0 if it reused the residual */
+  double acc;         /* in/out: summed rel since the last step that ran the blocks */
+  double rel;         /* out: the step's rel (0 when it started a generation) */
+} mmdit_step_cache;
+
+/* Host. Bytes of mmdit_step_cache.buf for cfg (2 B img_len hidden floats for
+ * a_prev and the residual, plus per-row partial sums). */
+int mmdit_step_cache_bytes(const mmdit_config* cfg, size_t* bytes);
+
 typedef struct {
   const void* ctx_packed;
   int32_t ctx_len;
   int32_t has_guidance;
   double guidance;
+  mmdit_step_cache* cache;
+  double cache_threshold;
 } mmdit_step_opts;
 
 /* One denoising step with options (context tokens, guidance). Arguments as
@@ -216,9 +249,11 @@ typedef struct {
  * tokens; x_packed, v_out are [B, Lg, in_ch]; ids [txt_len + img_len, 3] are
  * text, generated, then context rows. The workspace is
  * mmdit_step_workspace(cfg). Errors as for mmdit_step; MMDIT_ERR_SHAPE for
- * ctx_len out of range or a non-finite guidance; MMDIT_ERR_NULL for a NULL
- * ctx_packed with ctx_len > 0, or a guidance model called without a guidance
- * value (mmdit_step on such a model fails the same way). */
+ * ctx_len out of range, a non-finite guidance, a negative or NaN
+ * cache_threshold, or caching without a dual block; MMDIT_ERR_NULL for a NULL
+ * ctx_packed with ctx_len > 0, a NULL cache->buf, or a guidance model called
+ * without a guidance value (mmdit_step on such a model fails the same way);
+ * MMDIT_ERR_WORKSPACE for cache->bytes below mmdit_step_cache_bytes(cfg). */
 int mmdit_step_ex(const mmdit_config* cfg, const mmdit_model_w* w,
                   void* x_packed, void* v_out, const void* txt_emb, const void* y,
                   const int32_t* ids, double sigma, double sigma_next, const mmdit_step_opts* opts,

@@ -202,6 +202,85 @@ def test_step_guidance_with_context_bf16_width3072():
     assert_parity(Xg, Xr, "bf16", "bf16 guided step_ex x_next")
 
 
+# ----------------------------------------------------------- step caching ---
+def cached_oracle(s, g, dbl, sgl, inp, ids, sig, thr, Xc=None):
+    """oracle.step_cached over the schedule: (X, v, ran_blocks, rel, acc) per step."""
+    st = oracle.new_cache_state()
+    X = oracle.pack_latents(inp["z"])
+    out = []
+    for i in range(len(sig) - 1):
+        X, v, run, rel = oracle.step_cached(g, dbl, sgl, X, inp["T"], inp["y"], ids, sig[i], sig[i + 1], s.heads,
+                                            st, thr, s.axes_dim, s.theta, Xc=Xc)
+        out.append((X, v, run, rel, st["acc"]))
+    return out
+
+
+def cached_gpu(s, g, dbl, sgl, inp, ids, sig, thr, Xc=None):
+    """mmdit_step_ex with a step cache over the schedule, same tuple per step."""
+    t = torch()
+    dt = dtype_code(s.dtype)
+    Lc = 0 if Xc is None else Xc.shape[1]
+    cfg = bd.make_config(s)
+    cfg.dims.img_len = s.img_len + Lc
+    M = bd.ModelW(g, [bd.DoubleW(d, dt, "cuda") for d in dbl], [bd.SingleW(w, dt, "cuda") for w in sgl], dt, "cuda")
+    mc = M.c()
+    z = t.from_numpy(inp["z"]).cuda()
+    X = t.empty((s.batch, s.img_len, s.in_ch), dtype=t.float32, device="cuda")
+    bd.mmdit_pack_latents(z, X)
+    v = t.empty_like(X)
+    T, y, ids_d = up(inp["T"], s.dtype), up(inp["y"], s.dtype), up_i32(ids)
+    xc = None if Xc is None else t.from_numpy(Xc).cuda()
+    ws = workspace(bd.mmdit_step_workspace(cfg))
+    cache = bd.StepCache(cfg)
+    out = []
+    for i in range(len(sig) - 1):
+        print(f"cached step {i} B={s.batch} h={s.hidden} Lt={s.txt_len} Lg={s.img_len} Lc={Lc} {s.dtype} "
+              f"threshold {thr:.4g}", flush=True)
+        bd.mmdit_step_ex(cfg, mc, X, v, T, y, ids_d, sig[i], sig[i + 1], ws, ctx_packed=xc, ctx_len=Lc,
+                         cache=cache, cache_threshold=thr)
+        sync()
+        out.append((down(X), down(v), cache.ran_blocks, cache.rel, cache.c.acc))
+    return out
+
+
+def check_cached(s, cgh=0, cgw=0, n_steps=5, rel_tol=1e-4):
+    g, dbl, sgl = model_numpy(s)
+    inp = I.step_inputs(s)
+    Lc = cgh * cgw
+    Xc = np.random.default_rng(2000 + s.cfg_id).standard_normal((s.batch, Lc, s.in_ch)).astype(np.float32) if Lc else None
+    ids = ctx_ids(s, cgh, cgw) if Lc else oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
+    sig = oracle.schedule(n_steps, s.img_len)
+    # threshold between the second step's change and the sum of the second
+    # and third steps' changes (never-recompute trajectory): the second step
+    # reuses the residual, the third runs the blocks again
+    ref_inf = cached_oracle(s, g, dbl, sgl, inp, ids, sig[:4], np.inf, Xc)
+    thr = ref_inf[1][3] + 0.5 * ref_inf[2][3]
+    ref = cached_oracle(s, g, dbl, sgl, inp, ids, sig, thr, Xc)
+    runs = [r[2] for r in ref]
+    assert runs[:3] == [True, False, True], runs
+    prev_acc = 0.0
+    for i, r in enumerate(ref):  # every decision clear of the threshold
+        if i > 0:
+            assert abs(prev_acc + r[3] - thr) > 0.02 * thr, (i, prev_acc + r[3], thr)
+        prev_acc = r[4]
+    got = cached_gpu(s, g, dbl, sgl, inp, ids, sig, thr, Xc)
+    assert [r[2] for r in got] == runs
+    for i, (a, b) in enumerate(zip(got, ref)):
+        assert abs(a[3] - b[3]) <= rel_tol * max(b[3], 1e-30), (i, a[3], b[3])
+        assert abs(a[4] - b[4]) <= rel_tol * max(b[4], 1e-30) or a[4] == b[4] == 0.0, (i, a[4], b[4])
+        assert_parity(a[1], b[1], s.dtype, f"cached step {i} v (ran blocks {b[2]})")
+        assert_parity(a[0], b[0], s.dtype, f"cached step {i} x_next")
+
+
+def test_step_cache_f32_tiny_batch2():
+    check_cached(dataclasses.replace(TINY_F32, batch=2, txt_len=11, grid_h=6, grid_w=5, cfg_id=49))
+
+
+def test_step_cache_bf16_width3072_with_context():
+    s = dataclasses.replace(I.CFG4, n_double=1, n_single=1, txt_len=128, grid_h=16, grid_w=16, cfg_id=50)
+    check_cached(s, 16, 16, rel_tol=2e-2)
+
+
 def test_step_quantised_full_tokens_one_plus_one_blocks():
     s = dataclasses.replace(I.CFG5, n_double=1, n_single=1)
     g, dbl, sgl = model_numpy(s)

@@ -2,6 +2,7 @@
 host helpers bit-exact against the oracle, and argument errors returned
 before any device work. No GPU is touched."""
 import ctypes as C
+import dataclasses
 import os
 import re
 import subprocess
@@ -44,7 +45,8 @@ def test_struct_layout_matches_c_compiler(lib):
     structs = {"mmdit_dims": bd.mmdit_dims, "mmdit_linear": bd.mmdit_linear,
                "mmdit_stream_w": bd.mmdit_stream_w, "mmdit_double_w": bd.mmdit_double_w,
                "mmdit_single_w": bd.mmdit_single_w, "mmdit_config": bd.mmdit_config,
-               "mmdit_model_w": bd.mmdit_model_w, "mmdit_step_opts": bd.mmdit_step_opts}
+               "mmdit_model_w": bd.mmdit_model_w, "mmdit_step_opts": bd.mmdit_step_opts,
+               "mmdit_step_cache": bd.mmdit_step_cache}
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){"]
     for name, cls in structs.items():
         lines.append(f'printf("{name} size %zu\\n", sizeof({name}));')
@@ -201,6 +203,30 @@ def test_step_ex_errors_before_launch(lib):
     assert call(C.byref(o)) == 1                                            # NULL context latent
     o = bd.mmdit_step_opts(ctx_packed=fake, ctx_len=-1)
     assert call(C.byref(o)) == 2
+    # step cache options
+    need = bd.mmdit_step_cache_bytes(cfg)
+    cache = bd.mmdit_step_cache(buf=fake, bytes=need)
+    for thr, want in ((float("nan"), 2), (-0.1, 2)):
+        o = bd.mmdit_step_opts(has_guidance=1, guidance=3.5, cache=C.pointer(cache), cache_threshold=thr)
+        assert call(C.byref(o)) == want
+    o = bd.mmdit_step_opts(has_guidance=1, guidance=3.5, cache=C.pointer(bd.mmdit_step_cache(bytes=need)),
+                           cache_threshold=0.1)
+    assert call(C.byref(o)) == 1                                            # NULL cache buffer
+    o = bd.mmdit_step_opts(has_guidance=1, guidance=3.5,
+                           cache=C.pointer(bd.mmdit_step_cache(buf=fake, bytes=need - 1)), cache_threshold=0.1)
+    assert call(C.byref(o)) == 4                                            # cache buffer too small
+    cfg0 = bd.make_config(dataclasses.replace(s, n_double=0))
+    o = bd.mmdit_step_opts(has_guidance=1, guidance=3.5, cache=C.pointer(cache), cache_threshold=0.1)
+    assert lib.mmdit_step_ex(C.byref(cfg0), C.byref(w), fake, None, fake, fake, fake, 1.0, 0.5, C.byref(o), fake,
+                             1 << 40, None) == 2                            # no dual block to read
+    assert cache.valid == 0
+
+
+def test_step_cache_bytes(lib):
+    s = I.CFG4
+    n = bd.mmdit_step_cache_bytes(bd.make_config(s))
+    # a_prev and the residual in float32 plus two floats per image row
+    assert 2 * s.img_len * s.hidden * 4 + s.img_len * 8 <= n <= 2 * s.img_len * s.hidden * 4 + s.img_len * 8 + 1024
 
 
 def test_workspace_sizes_scale_with_tokens(lib):
