@@ -233,7 +233,8 @@ char* ptr(void* base, size_t off) { return reinterpret_cast<char*>(base) + off; 
 int gemm(const Ctx& c, GemmProblem* p, int np, int epi) {
   double flops = 0;
   for (int i = 0; i < np; ++i) flops += 2.0 * p[i].M * (double)p[i].N * p[i].K;
-  ProfScope ps(PC_GEMM, flops, c.s, epi == EPI_SPLIT ? PC_GEMM_LIN1 : (epi == EPI_GATE_RES ? PC_GEMM_RES : -1));
+  ProfScope ps(PC_GEMM, flops, c.s,
+               epi == EPI_SPLIT || epi == EPI_SPLIT_QKV ? PC_GEMM_LIN1 : (epi == EPI_GATE_RES ? PC_GEMM_RES : -1));
   if (!c.g.bf16) HIP_TRY(launch_gemm_f32(p, np, epi, c.s));
   else if (gemm_dma_eligible(p, np, epi)) HIP_TRY(launch_gemm_dma(p, np, epi, c.s));
   else HIP_TRY(launch_gemm_bf16(p, np, epi, c.s));
@@ -297,8 +298,29 @@ int run_ln(const Ctx& c, const Part* parts, int np, int mod_bstride, int shift_o
   return MMDIT_OK;
 }
 
+// Points the q | k columns of a QKV projection at the fused RMSNorm + RoPE
+// epilogue (part p's rows start at joint token tok0) and reports whether
+// the direct-to-LDS kernel takes the launch; otherwise the separate
+// QK-norm kernel runs after a plain store.
+bool fuse_qk(const Ctx& c, GemmProblem* gp, int np, const Part* parts, const void* const qn[2],
+             const void* const kn[2], const float* table, const BlockWs& w, void* ws, int epi) {
+  const Geo& g = c.g;
+  if (!g.bf16) return false;
+  int tok0 = 0;
+  for (int p = 0; p < np; ++p) {
+    gp[p].qk_Q = ptr(ws, w.q); gp[p].qk_K = ptr(ws, w.k);
+    gp[p].qn = qn[p]; gp[p].kn = kn[p];
+    gp[p].rope = table;
+    gp[p].qk_h = g.h; gp[p].qk_rows = parts[p].len; gp[p].qk_tok0 = tok0; gp[p].qk_Lpad = g.Lpad;
+    gp[p].qk_eps = c.rms_eps;
+    tok0 += parts[p].len;
+  }
+  return gemm_dma_eligible(gp, np, epi);
+}
+
 int run_qk_attn(const Ctx& c, const Part* parts, int np, void* qkv, const void* const qn[2],
-                const void* const kn[2], const float* table, const BlockWs& w, void* ws, void* obuf, int o_ld) {
+                const void* const kn[2], const float* table, const BlockWs& w, void* ws, void* obuf, int o_ld,
+                bool qk_fused) {
   const Geo& g = c.g;
   QkNormArgs q{};
   AttnArgs at{};
@@ -313,7 +335,10 @@ int run_qk_attn(const Ctx& c, const Part* parts, int np, void* qkv, const void* 
   q.table = table;
   q.Q = ptr(ws, w.q); q.K = ptr(ws, w.k); q.V = ptr(ws, w.v);
   q.B = g.B; q.H = g.H; q.L = g.L; q.Lpad = g.Lpad; q.eps = c.rms_eps;
-  {
+  if (qk_fused) {  // Q and K are written; V still needs its transpose
+    ProfScope ps(PC_QKNORM, (double)g.B * g.L * g.h * g.esz * 2, c.s);
+    HIP_TRY(launch_v_transpose(q, c.s));
+  } else {
     ProfScope ps(PC_QKNORM, (double)g.B * g.L * 3 * g.h * g.esz * 2, c.s);
     HIP_TRY(launch_qk_norm_rope(q, g.bf16, g.bf16, c.s));
   }
@@ -355,11 +380,13 @@ int run_double(const Ctx& c, const mmdit_stream_w* const sw[2], const Part* part
     gp[p].M = g.B * parts[p].len;
     gp[p].out = ptr(qkv, (size_t)parts[p].row0 * 3 * h * g.esz); gp[p].ldo = 3 * h;
   }
-  if ((r = gemm(c, gp, 2, EPI_STORE))) return r;
-  // QK RMSNorm + RoPE, joint attention
+  // QK RMSNorm + RoPE (fused into the projection's epilogue when the
+  // direct-to-LDS kernel runs it), joint attention
   const void* qn[2] = {sw[0]->q_norm, sw[1]->q_norm};
   const void* kn[2] = {sw[0]->k_norm, sw[1]->k_norm};
-  if ((r = run_qk_attn(c, parts, 2, qkv, qn, kn, table, w, ws, o, h))) return r;
+  const bool fused = fuse_qk(c, gp, 2, parts, qn, kn, table, w, ws, EPI_QKV);
+  if ((r = gemm(c, gp, 2, fused ? EPI_QKV : EPI_STORE))) return r;
+  if ((r = run_qk_attn(c, parts, 2, qkv, qn, kn, table, w, ws, o, h, fused))) return r;
   // out-projection, x += gate1 * (.)
   for (int p = 0; p < 2; ++p) {
     gp[p] = base_problem(sw[p]->proj);
@@ -411,10 +438,11 @@ int run_single(const Ctx& c, const mmdit_single_w& sw, const Part* parts, int np
     gp[p].split_n = 3 * h;
     gp[p].out2 = ptr(cat, ((size_t)parts[p].row0 * (h + m) + h) * g.esz); gp[p].ldo2 = h + m;
   }
-  if ((r = gemm(c, gp, np, EPI_SPLIT))) return r;
   const void* qn[2] = {sw.q_norm, sw.q_norm};
   const void* kn[2] = {sw.k_norm, sw.k_norm};
-  if ((r = run_qk_attn(c, parts, np, qkv, qn, kn, table, w, ws, cat, h + m))) return r;
+  const bool fused = fuse_qk(c, gp, np, parts, qn, kn, table, w, ws, EPI_SPLIT_QKV);
+  if ((r = gemm(c, gp, np, fused ? EPI_SPLIT_QKV : EPI_SPLIT))) return r;
+  if ((r = run_qk_attn(c, parts, np, qkv, qn, kn, table, w, ws, cat, h + m, fused))) return r;
   for (int p = 0; p < np; ++p) {
     gp[p] = base_problem(sw.lin2);
     gp[p].A = ptr(cat, (size_t)parts[p].row0 * (h + m) * g.esz); gp[p].lda = h + m;

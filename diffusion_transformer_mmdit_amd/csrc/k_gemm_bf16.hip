@@ -246,7 +246,8 @@ hipError_t launch_gemm_bf16(const GemmProblem* p, int nprob, int epi, hipStream_
     case EPI_GELU: return launch_epi<EPI_GELU>(p, nprob, s);
     case EPI_GATE_RES: return launch_epi<EPI_GATE_RES>(p, nprob, s);
     case EPI_SPLIT: return launch_epi<EPI_SPLIT>(p, nprob, s);
-    default: return launch_epi_fmt<EPI_EULER, 0>(p, nprob, s);
+    case EPI_EULER: return launch_epi_fmt<EPI_EULER, 0>(p, nprob, s);
+    default: return hipErrorInvalidValue;  // fused QK epilogues: direct-to-LDS kernel only
   }
 }
 

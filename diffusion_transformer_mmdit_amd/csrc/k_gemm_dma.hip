@@ -101,6 +101,7 @@ typedef __attribute__((address_space(1))) f32x4 gf32x4;
 typedef __attribute__((address_space(1))) const f32x4 gcf32x4;
 typedef __attribute__((address_space(1))) bf16x4 gbf16x4;
 typedef __attribute__((address_space(1))) const bf16x4 gcbf16x4;
+typedef __attribute__((address_space(1))) bf16x8 gbf16x8;
 
 
 // FULL: every row and column of the wave tile is in range and (gated
@@ -274,6 +275,88 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& P, char* smem, i
   } else {
     if (alt) dma_epilogue_impl<EPI, TN, false, true>(P, stg, m0w, n0w, lane, acc, bias);
     else dma_epilogue_impl<EPI, TN, false, false>(P, stg, m0w, n0w, lane, acc, bias);
+  }
+}
+
+// Fused QK RMSNorm + RoPE for a wavefront tile of the q or k columns
+// (mflux-rs card "Dual-Stream MMDiT": q and k RMS-normalised per head;
+// card "3D RoPE Coordinates": adjacent pairs rotated by the token's angles).
+// The wavefront's 128 columns are exactly one head. Each 32-row chunk is
+// staged through LDS as in dma_epilogue_impl; lane (r = lane % 32, hf =
+// lane / 32) then takes dims 64 hf .. 64 hf + 63 of chunk row r, so a row's
+// sum of squares is the lane's 64 terms plus its partner's (lane ^ 32), and
+// every rotation pair lies in one lane. Rows go to Q (K) [B, H, Lpad, 128]
+// as 16-byte stores.
+template <int TN>
+__device__ __forceinline__ void qk_epilogue(const GemmProblem& P, char* smem, int m0w, int n0w, int wave,
+                                            int lane, const f32x16 (&acc)[4][TN / 32]) {
+  static_assert(TN == 128, "one head per wavefront tile");
+  constexpr int LD = TN + 4;
+  float* stg = reinterpret_cast<float*>(smem) + wave * (32 * LD);
+  const int M = pin(P.M);
+  const int qk_h = pin(P.qk_h);
+  const int which = n0w >= qk_h ? 1 : 0;  // 0 q, 1 k
+  const int hh = (n0w - which * qk_h) >> 7;
+  const int H = qk_h >> 7;
+  const int rows = pin(P.qk_rows), tok0 = pin(P.qk_tok0), Lpad = pin(P.qk_Lpad);
+  const float eps = P.qk_eps;
+  const int r = lane & 31, hf = lane >> 5;
+  gchar* dst = (gchar*)pin(reinterpret_cast<char*>(which ? P.qk_K : P.qk_Q));
+  const bf16* gsc = reinterpret_cast<const bf16*>(which ? P.kn : P.qn) + 64 * hf;
+  const bf16* bp = reinterpret_cast<const bf16*>(P.bias);
+  const float* rope = P.rope;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(stg + r * LD + 32 * j + 8 * g + 4 * hf) =
+            (f32x4){acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+    float v[64];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(stg + r * LD + 64 * hf + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+    }
+    if (bp) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const bf16x4 b4 = *reinterpret_cast<const bf16x4*>(bp + n0w + 64 * hf + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * q + e] += (float)b4[e];
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) ss += v[c] * v[c];
+    ss += __shfl_xor(ss, 32);
+    const float rstd = 1.0f / sqrtf(ss * (1.0f / 128.0f) + eps);
+    const int m = m0w + 32 * i + r;
+    if (m < M) {
+      const int b = m / rows;
+      const int t = tok0 + (m - b * rows);
+      const float* tb = rope + ((int64_t)t * 64 + 32 * hf) * 2;
+      gchar* out = dst + ((((int64_t)b * H + hh) * Lpad + t) * 128 + 64 * hf) * 2;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f32x4 c0 = *reinterpret_cast<const f32x4*>(tb + 8 * q);
+        const f32x4 c1 = *reinterpret_cast<const f32x4*>(tb + 8 * q + 4);
+        const bf16x8 g8 = *reinterpret_cast<const bf16x8*>(gsc + 8 * q);
+        const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+        bf16x8 o;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float y0 = v[8 * q + 2 * u] * rstd * (float)g8[2 * u];
+          const float y1 = v[8 * q + 2 * u + 1] * rstd * (float)g8[2 * u + 1];
+          const float c = cs[2 * u], sn = cs[2 * u + 1];
+          o[2 * u] = (bf16)(c * y0 - sn * y1);
+          o[2 * u + 1] = (bf16)(sn * y0 + c * y1);
+        }
+        *(gbf16x8*)(out + 16 * q) = o;
+      }
+    }
   }
 }
 
@@ -609,8 +692,20 @@ __global__ __launch_bounds__(64 * W, 1) void k_gemm_dma(GemmBatch gb) {
   wait_vm(0);
   __builtin_amdgcn_s_waitcnt(0xC07F);
   barrier();
-  const int side = EPI == EPI_SPLIT ? split_side_of(P, n0, kDBN) : 0;
-  dma_epilogue<EPI, TN>(P, smem, m0 + wm0, n0 + wn0, wave, lane, acc, side, ebias);
+  if constexpr (EPI == EPI_QKV || EPI == EPI_SPLIT_QKV) {
+    // q | k columns (tile-aligned: 2 qk_h is a multiple of the tile width)
+    // take the fused epilogue; the rest is a plain or split store
+    if (n0 < 2 * P.qk_h) {
+      if constexpr (TN == 128) qk_epilogue<TN>(P, smem, m0 + wm0, n0 + wn0, wave, lane, acc);
+    } else if constexpr (EPI == EPI_QKV) {
+      dma_epilogue<EPI_STORE, TN>(P, smem, m0 + wm0, n0 + wn0, wave, lane, acc, 0, ebias);
+    } else {
+      dma_epilogue<EPI_SPLIT, TN>(P, smem, m0 + wm0, n0 + wn0, wave, lane, acc, split_side_of(P, n0, kDBN), ebias);
+    }
+  } else {
+    const int side = EPI == EPI_SPLIT ? split_side_of(P, n0, kDBN) : 0;
+    dma_epilogue<EPI, TN>(P, smem, m0 + wm0, n0 + wn0, wave, lane, acc, side, ebias);
+  }
 }
 
 // Tile-loop configuration used by the library.
@@ -680,6 +775,9 @@ bool gemm_dma_eligible(const GemmProblem* p, int nprob, int epi) {
     fmt = q.fmt;
     if (q.K % kDBK != 0 || q.lda % 8 != 0 || q.N < 128 || q.N % 4 != 0) return false;
     if (fmt != 0 && (kDBK != 64 || MMDIT_DMA_STAGES != 2)) return false;
+    if ((epi == EPI_QKV || epi == EPI_SPLIT_QKV) &&
+        (fmt != 0 || MMDIT_DMA_WAVES != 4 || q.qk_h % kDBN != 0 || 3 * q.qk_h > q.N || q.qk_rows <= 0))
+      return false;
     if ((fmt == 3 || fmt == 4) && q.K % 128 != 0) return false;
     if (q.bias && !aligned(q.bias, 8)) return false;
     if (epi == EPI_GATE_RES) {
@@ -690,7 +788,8 @@ bool gemm_dma_eligible(const GemmProblem* p, int nprob, int epi) {
         return false;
     } else {
       if (q.out_f32 || q.ldo % 4 || !aligned(q.out, 8)) return false;  // bf16 outputs only
-      if (epi == EPI_SPLIT && (q.split_n % kDBN != 0 || q.ldo2 % 4 || !aligned(q.out2, 8))) return false;
+      if ((epi == EPI_SPLIT || epi == EPI_SPLIT_QKV) && (q.split_n % kDBN != 0 || q.ldo2 % 4 || !aligned(q.out2, 8)))
+        return false;
     }
     tiles += (int64_t)((q.M + kDBM - 1) / kDBM) * ((q.N + kDBN - 1) / kDBN);
   }
@@ -721,7 +820,10 @@ hipError_t launch_gemm_dma(const GemmProblem* p, int nprob, int epi, hipStream_t
     case EPI_STORE: return launch_dma_fmt<EPI_STORE>(p, nprob, s);
     case EPI_GELU: return launch_dma_fmt<EPI_GELU>(p, nprob, s);
     case EPI_GATE_RES: return launch_dma_fmt<EPI_GATE_RES>(p, nprob, s);
-    default: return launch_dma_fmt<EPI_SPLIT>(p, nprob, s);
+    case EPI_SPLIT: return launch_dma_fmt<EPI_SPLIT>(p, nprob, s);
+    case EPI_QKV: return launch_dma_epi<EPI_QKV>(p, nprob, s);
+    case EPI_SPLIT_QKV: return launch_dma_epi<EPI_SPLIT_QKV>(p, nprob, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

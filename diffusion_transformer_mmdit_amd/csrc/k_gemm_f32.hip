@@ -85,7 +85,8 @@ hipError_t launch_gemm_f32(const GemmProblem* p, int nprob, int epi, hipStream_t
     case EPI_GELU: return launch_f32<EPI_GELU>(p, nprob, s);
     case EPI_GATE_RES: return launch_f32<EPI_GATE_RES>(p, nprob, s);
     case EPI_SPLIT: return launch_f32<EPI_SPLIT>(p, nprob, s);
-    default: return launch_f32<EPI_EULER>(p, nprob, s);
+    case EPI_EULER: return launch_f32<EPI_EULER>(p, nprob, s);
+    default: return hipErrorInvalidValue;  // fused QK epilogues: bf16 only
   }
 }
 

@@ -242,7 +242,9 @@ __device__ __forceinline__ void qk_rotate(const float (&x)[8], const float (&g)[
   }
 }
 
-template <typename T, bool VT>
+// VONLY: q and k were written by the fused GEMM epilogue; only V is moved
+// (transposed) and the pad rows [L, Lpad) of Q and K are zeroed.
+template <typename T, bool VT, bool VONLY = false>
 __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
   const int t0 = blockIdx.x * kQkTile;
   const int hh = blockIdx.y;
@@ -256,10 +258,12 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
   float gq[2][8], gk[2][8];
   bool valid[kQkPass];
   int seg_of[kQkPass];
+  if constexpr (!VONLY) {
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    load8(reinterpret_cast<const T*>(a.qn[s]) + d0, gq[s]);
-    load8(reinterpret_cast<const T*>(a.kn[s]) + d0, gk[s]);
+    for (int s = 0; s < 2; ++s) {
+      load8(reinterpret_cast<const T*>(a.qn[s]) + d0, gq[s]);
+      load8(reinterpret_cast<const T*>(a.kn[s]) + d0, gk[s]);
+    }
   }
 #pragma unroll
   for (int p = 0; p < kQkPass; ++p) {
@@ -272,16 +276,18 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
     if (valid[p]) {
       const int local = (s == 0 ? t : t - a.seg_len0) + b * (s == 0 ? a.seg_len0 : a.L - a.seg_len0);
       const T* src = reinterpret_cast<const T*>(seg_row(a.seg[s], local, sizeof(T))) + hh * 128 + d0;
-      load8(src, xq[p]);
-      load8(src + h, xk[p]);
       load8(src + 2 * h, xv[p]);
-      const float* tb = a.table + ((int64_t)t * 64 + (d0 >> 1)) * 2;
-      const f32x4 c0 = *reinterpret_cast<const f32x4*>(tb);
-      const f32x4 c1 = *reinterpret_cast<const f32x4*>(tb + 4);
+      if constexpr (!VONLY) {
+        load8(src, xq[p]);
+        load8(src + h, xk[p]);
+        const float* tb = a.table + ((int64_t)t * 64 + (d0 >> 1)) * 2;
+        const f32x4 c0 = *reinterpret_cast<const f32x4*>(tb);
+        const f32x4 c1 = *reinterpret_cast<const f32x4*>(tb + 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        cs[p][i] = c0[i];
-        cs[p][4 + i] = c1[i];
+        for (int i = 0; i < 4; ++i) {
+          cs[p][i] = c0[i];
+          cs[p][4 + i] = c1[i];
+        }
       }
     }
   }
@@ -290,11 +296,19 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
 #pragma unroll
   for (int p = 0; p < kQkPass; ++p) {
     const int t = t0 + p * 16 + (tid >> 4);
-    float y[8];
-    qk_rotate(xq[p], seg_of[p] ? gq[1] : gq[0], cs[p], a.eps, valid[p], y);
-    if (t < a.Lpad) store8(Q + (int64_t)t * 128 + d0, y);
-    qk_rotate(xk[p], seg_of[p] ? gk[1] : gk[0], cs[p], a.eps, valid[p], y);
-    if (t < a.Lpad) store8(K + (int64_t)t * 128 + d0, y);
+    if constexpr (VONLY) {
+      if (!valid[p] && t < a.Lpad) {
+        const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        store8(Q + (int64_t)t * 128 + d0, z);
+        store8(K + (int64_t)t * 128 + d0, z);
+      }
+    } else {
+      float y[8];
+      qk_rotate(xq[p], seg_of[p] ? gq[1] : gq[0], cs[p], a.eps, valid[p], y);
+      if (t < a.Lpad) store8(Q + (int64_t)t * 128 + d0, y);
+      qk_rotate(xk[p], seg_of[p] ? gk[1] : gk[0], cs[p], a.eps, valid[p], y);
+      if (t < a.Lpad) store8(K + (int64_t)t * 128 + d0, y);
+    }
   }
 
   if constexpr (!VT) {
@@ -328,6 +342,12 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
       }
     }
   }
+}
+
+hipError_t launch_v_transpose(const QkNormArgs& a, hipStream_t s) {
+  dim3 grid((a.Lpad + kQkTile - 1) / kQkTile, a.H, a.B), block(256);
+  hipLaunchKernelGGL((k_qk_norm_rope<bf16, true, true>), grid, block, 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_qk_norm_rope(const QkNormArgs& a, bool bf16_act, bool v_trans, hipStream_t s) {

@@ -76,6 +76,9 @@ struct QkNormArgs {
   float eps;
 };
 hipError_t launch_qk_norm_rope(const QkNormArgs& a, bool bf16, bool v_trans, hipStream_t s);
+// bf16 only: V^T as above, plus zero rows t in [L, Lpad) of Q and K; Q and K
+// rows t < L are left as they are (written by the fused GEMM epilogue).
+hipError_t launch_v_transpose(const QkNormArgs& a, hipStream_t s);
 
 // ---- RoPE table -------------------------------------------------------------
 hipError_t launch_rope_table(const int32_t* ids, int L, int a0, int a1, int a2, double theta,
@@ -131,6 +134,11 @@ enum Epi : int {
   EPI_GATE_RES = 2,  // res_out = res_in + gate[b, n] * (acc + bias)
   EPI_SPLIT = 3,     // n < split_n: out = acc + bias; else out2[n - split_n] = GELU(acc + bias)
   EPI_EULER = 4,     // x[r, n] += dsigma * (acc + bias); v_out (if set) = acc + bias  (f32)
+  // as EPI_STORE / EPI_SPLIT, except that columns [0, 2 qk_h) (q | k) go
+  // through QK RMSNorm + RoPE into Q / K [B, H, Lpad, 128] instead of `out`
+  // (256x256 direct-to-LDS kernel, dense bf16 weights only)
+  EPI_QKV = 5,
+  EPI_SPLIT_QKV = 6,
 };
 
 struct GemmProblem {
@@ -154,6 +162,18 @@ struct GemmProblem {
   int32_t gate_bstride;
   float dsigma;
   float* v_out;  // EPI_EULER, contiguous [M, N], may be null
+  // EPI_QKV / EPI_SPLIT_QKV: row m is token qk_tok0 + m % qk_rows of batch
+  // m / qk_rows in the joint sequence; head hh of q (k) is columns
+  // hh * 128 .. + 127 (qk_h + ...): RMS over those columns (after the bias),
+  // times qn (kn), rotated by rope[token] pairs, written as bf16 to
+  // Q (K) [B, H, qk_Lpad, 128].
+  void* qk_Q;
+  void* qk_K;
+  const void* qn;
+  const void* kn;
+  const float* rope;  // [L, 64, 2] cos, sin
+  int32_t qk_h, qk_rows, qk_tok0, qk_Lpad;
+  float qk_eps;
 };
 
 // Up to two problems with the same epilogue in one launch (text and image
