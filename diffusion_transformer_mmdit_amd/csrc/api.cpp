@@ -298,17 +298,17 @@ int run_ln(const Ctx& c, const Part* parts, int np, int mod_bstride, int shift_o
   return MMDIT_OK;
 }
 
-// Points the q | k columns of a QKV projection at the fused RMSNorm + RoPE
-// epilogue (part p's rows start at joint token tok0) and reports whether
-// the direct-to-LDS kernel takes the launch; otherwise the separate
-// QK-norm kernel runs after a plain store.
+// Points the q | k | v columns of a QKV projection at the fused epilogues
+// (RMSNorm + RoPE into Q and K, V transposed into V^T; part p's rows start
+// at joint token tok0) and reports whether the direct-to-LDS kernel takes
+// the launch; otherwise the separate QK-norm kernel runs after a plain store.
 bool fuse_qk(const Ctx& c, GemmProblem* gp, int np, const Part* parts, const void* const qn[2],
              const void* const kn[2], const float* table, const BlockWs& w, void* ws, int epi) {
   const Geo& g = c.g;
   if (!g.bf16) return false;
   int tok0 = 0;
   for (int p = 0; p < np; ++p) {
-    gp[p].qk_Q = ptr(ws, w.q); gp[p].qk_K = ptr(ws, w.k);
+    gp[p].qk_Q = ptr(ws, w.q); gp[p].qk_K = ptr(ws, w.k); gp[p].qk_V = ptr(ws, w.v);
     gp[p].qn = qn[p]; gp[p].kn = kn[p];
     gp[p].rope = table;
     gp[p].qk_h = g.h; gp[p].qk_rows = parts[p].len; gp[p].qk_tok0 = tok0; gp[p].qk_Lpad = g.Lpad;
@@ -335,9 +335,8 @@ int run_qk_attn(const Ctx& c, const Part* parts, int np, void* qkv, const void* 
   q.table = table;
   q.Q = ptr(ws, w.q); q.K = ptr(ws, w.k); q.V = ptr(ws, w.v);
   q.B = g.B; q.H = g.H; q.L = g.L; q.Lpad = g.Lpad; q.eps = c.rms_eps;
-  if (qk_fused) {  // Q and K are written; V still needs its transpose
-    ProfScope ps(PC_QKNORM, (double)g.B * g.L * g.h * g.esz * 2, c.s);
-    HIP_TRY(launch_v_transpose(q, c.s));
+  if (qk_fused) {  // Q, K and V^T are written; only the pad rows remain
+    if (g.Lpad > g.L) HIP_TRY(launch_qkv_pad_zero(q, c.s));
   } else {
     ProfScope ps(PC_QKNORM, (double)g.B * g.L * 3 * g.h * g.esz * 2, c.s);
     HIP_TRY(launch_qk_norm_rope(q, g.bf16, g.bf16, c.s));

@@ -360,6 +360,74 @@ __device__ __forceinline__ void qk_epilogue(const GemmProblem& P, char* smem, in
   }
 }
 
+// V columns of the fused QKV epilogue: the wavefront's 128 columns are the
+// 128 dims of one head, written transposed to V^T [B, H, 128, Lpad] where
+// position p holds token vkey_pos(p) (the key order the attention kernel's
+// PV product reads). Each 32-row chunk is staged through LDS; lane l then
+// takes dims l and l + 64. When the chunk's 32 rows are consecutive tokens
+// of one batch starting at a multiple of 16, the positions are the same 32
+// tokens permuted within 16-token groups, so each dim is four 16-byte
+// stores; otherwise every element is stored at its own position.
+template <int TN>
+__device__ __forceinline__ void v_epilogue(const GemmProblem& P, char* smem, int m0w, int n0w, int wave,
+                                           int lane, const f32x16 (&acc)[4][TN / 32]) {  // 128 rows
+  static_assert(TN == 128, "one head per wavefront tile");
+  constexpr int LD = TN + 4;
+  float* stg = reinterpret_cast<float*>(smem) + wave * (32 * LD);
+  const int M = pin(P.M);
+  const int qk_h = pin(P.qk_h);
+  const int hh = (n0w - 2 * qk_h) >> 7;
+  const int H = qk_h >> 7;
+  const int rows = pin(P.qk_rows), tok0 = pin(P.qk_tok0), Lpad = pin(P.qk_Lpad);
+  gchar* vt = (gchar*)pin(reinterpret_cast<char*>(P.qk_V));
+  const bf16* bp = reinterpret_cast<const bf16*>(P.bias);
+  float bias[2] = {0.f, 0.f};
+  if (bp) {
+    bias[0] = (float)bp[n0w + lane];
+    bias[1] = (float)bp[n0w + lane + 64];
+  }
+  const int r = lane & 31, hf = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(stg + r * LD + 32 * j + 8 * g + 4 * hf) =
+            (f32x4){acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+    const int mc = m0w + 32 * i;  // first row of the chunk
+    const int bF = mc / rows;
+    const int tF = tok0 + (mc - bF * rows);
+    const bool fast = mc + 32 <= M && (mc + 31) / rows == bF && (tF & 15) == 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int d = lane + 64 * q;
+      if (fast) {
+        float x[32];
+#pragma unroll
+        for (int rr = 0; rr < 32; ++rr) x[rr] = stg[rr * LD + d] + bias[q];
+        gchar* row = vt + ((((int64_t)bF * H + hh) * 128 + d) * Lpad + tF) * 2;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          bf16x8 o;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) o[u] = (bf16)x[vkey_pos(8 * c + u)];
+          *(gbf16x8*)(row + 16 * c) = o;
+        }
+      } else {
+        for (int rr = 0; rr < 32; ++rr) {
+          const int m = mc + rr;
+          if (m >= M) break;
+          const int b = m / rows;
+          const int t = tok0 + (m - b * rows);
+          gchar* dst = vt + ((((int64_t)b * H + hh) * 128 + d) * Lpad + vkey_pos(t)) * 2;
+          *(__attribute__((address_space(1))) bf16*)dst = (bf16)(stg[rr * LD + d] + bias[q]);
+        }
+      }
+    }
+  }
+}
+
 // FMT 0: dense bf16 weights, both operands by DMA. FMT 1 / 2: 4-bit / 8-bit
 // group-quantised weights (groups of 64 along k = one k-tile, so one bf16
 // scale per weight row per k-tile): the packed codes of k-tile kt+1 are
@@ -693,10 +761,12 @@ __global__ __launch_bounds__(64 * W, 1) void k_gemm_dma(GemmBatch gb) {
   __builtin_amdgcn_s_waitcnt(0xC07F);
   barrier();
   if constexpr (EPI == EPI_QKV || EPI == EPI_SPLIT_QKV) {
-    // q | k columns (tile-aligned: 2 qk_h is a multiple of the tile width)
-    // take the fused epilogue; the rest is a plain or split store
+    // q | k and v columns (tile-aligned: qk_h is a multiple of the tile
+    // width) take the fused epilogues; the rest is a plain or split store
     if (n0 < 2 * P.qk_h) {
       if constexpr (TN == 128) qk_epilogue<TN>(P, smem, m0 + wm0, n0 + wn0, wave, lane, acc);
+    } else if (n0 < 3 * P.qk_h) {
+      if constexpr (TN == 128) v_epilogue<TN>(P, smem, m0 + wm0, n0 + wn0, wave, lane, acc);
     } else if constexpr (EPI == EPI_QKV) {
       dma_epilogue<EPI_STORE, TN>(P, smem, m0 + wm0, n0 + wn0, wave, lane, acc, 0, ebias);
     } else {

@@ -242,9 +242,7 @@ __device__ __forceinline__ void qk_rotate(const float (&x)[8], const float (&g)[
   }
 }
 
-// VONLY: q and k were written by the fused GEMM epilogue; only V is moved
-// (transposed) and the pad rows [L, Lpad) of Q and K are zeroed.
-template <typename T, bool VT, bool VONLY = false>
+template <typename T, bool VT>
 __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
   const int t0 = blockIdx.x * kQkTile;
   const int hh = blockIdx.y;
@@ -258,12 +256,10 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
   float gq[2][8], gk[2][8];
   bool valid[kQkPass];
   int seg_of[kQkPass];
-  if constexpr (!VONLY) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      load8(reinterpret_cast<const T*>(a.qn[s]) + d0, gq[s]);
-      load8(reinterpret_cast<const T*>(a.kn[s]) + d0, gk[s]);
-    }
+  for (int s = 0; s < 2; ++s) {
+    load8(reinterpret_cast<const T*>(a.qn[s]) + d0, gq[s]);
+    load8(reinterpret_cast<const T*>(a.kn[s]) + d0, gk[s]);
   }
 #pragma unroll
   for (int p = 0; p < kQkPass; ++p) {
@@ -276,18 +272,16 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
     if (valid[p]) {
       const int local = (s == 0 ? t : t - a.seg_len0) + b * (s == 0 ? a.seg_len0 : a.L - a.seg_len0);
       const T* src = reinterpret_cast<const T*>(seg_row(a.seg[s], local, sizeof(T))) + hh * 128 + d0;
+      load8(src, xq[p]);
+      load8(src + h, xk[p]);
       load8(src + 2 * h, xv[p]);
-      if constexpr (!VONLY) {
-        load8(src, xq[p]);
-        load8(src + h, xk[p]);
-        const float* tb = a.table + ((int64_t)t * 64 + (d0 >> 1)) * 2;
-        const f32x4 c0 = *reinterpret_cast<const f32x4*>(tb);
-        const f32x4 c1 = *reinterpret_cast<const f32x4*>(tb + 4);
+      const float* tb = a.table + ((int64_t)t * 64 + (d0 >> 1)) * 2;
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(tb);
+      const f32x4 c1 = *reinterpret_cast<const f32x4*>(tb + 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          cs[p][i] = c0[i];
-          cs[p][4 + i] = c1[i];
-        }
+      for (int i = 0; i < 4; ++i) {
+        cs[p][i] = c0[i];
+        cs[p][4 + i] = c1[i];
       }
     }
   }
@@ -296,19 +290,11 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
 #pragma unroll
   for (int p = 0; p < kQkPass; ++p) {
     const int t = t0 + p * 16 + (tid >> 4);
-    if constexpr (VONLY) {
-      if (!valid[p] && t < a.Lpad) {
-        const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        store8(Q + (int64_t)t * 128 + d0, z);
-        store8(K + (int64_t)t * 128 + d0, z);
-      }
-    } else {
-      float y[8];
-      qk_rotate(xq[p], seg_of[p] ? gq[1] : gq[0], cs[p], a.eps, valid[p], y);
-      if (t < a.Lpad) store8(Q + (int64_t)t * 128 + d0, y);
-      qk_rotate(xk[p], seg_of[p] ? gk[1] : gk[0], cs[p], a.eps, valid[p], y);
-      if (t < a.Lpad) store8(K + (int64_t)t * 128 + d0, y);
-    }
+    float y[8];
+    qk_rotate(xq[p], seg_of[p] ? gq[1] : gq[0], cs[p], a.eps, valid[p], y);
+    if (t < a.Lpad) store8(Q + (int64_t)t * 128 + d0, y);
+    qk_rotate(xk[p], seg_of[p] ? gk[1] : gk[0], cs[p], a.eps, valid[p], y);
+    if (t < a.Lpad) store8(K + (int64_t)t * 128 + d0, y);
   }
 
   if constexpr (!VT) {
@@ -344,9 +330,34 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
   }
 }
 
-hipError_t launch_v_transpose(const QkNormArgs& a, hipStream_t s) {
-  dim3 grid((a.Lpad + kQkTile - 1) / kQkTile, a.H, a.B), block(256);
-  hipLaunchKernelGGL((k_qk_norm_rope<bf16, true, true>), grid, block, 0, s, a);
+// One thread per (batch, head, pad row, 8 dims): Q and K rows t in [L, Lpad)
+// and V^T positions p in [L & ~15, Lpad) whose token vkey_pos(p) is >= L.
+__global__ void k_qkv_pad_zero(QkNormArgs a) {
+  const int L0 = a.L & ~15;
+  const int npos = a.Lpad - L0;
+  const int64_t n = (int64_t)a.B * a.H * npos * 16;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int d8 = (int)(i % 16);
+  const int64_t bh = i / 16 / npos;
+  const int p = L0 + (int)(i / 16 % npos);
+  const bf16x8 z = {};
+  const int64_t head = bh * (int64_t)a.Lpad * 128;
+  if (p >= a.L) {
+    *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.Q) + head + (int64_t)p * 128 + d8 * 8) = z;
+    *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.K) + head + (int64_t)p * 128 + d8 * 8) = z;
+  }
+  if (vkey_pos(p) >= a.L) {
+    bf16* vt = reinterpret_cast<bf16*>(a.V) + head;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vt[(int64_t)(d8 * 8 + j) * a.Lpad + p] = bf16(0.f);
+  }
+}
+
+hipError_t launch_qkv_pad_zero(const QkNormArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.B * a.H * (a.Lpad - (a.L & ~15)) * 16;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_qkv_pad_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

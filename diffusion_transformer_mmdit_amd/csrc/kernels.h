@@ -76,9 +76,9 @@ struct QkNormArgs {
   float eps;
 };
 hipError_t launch_qk_norm_rope(const QkNormArgs& a, bool bf16, bool v_trans, hipStream_t s);
-// bf16 only: V^T as above, plus zero rows t in [L, Lpad) of Q and K; Q and K
-// rows t < L are left as they are (written by the fused GEMM epilogue).
-hipError_t launch_v_transpose(const QkNormArgs& a, hipStream_t s);
+// bf16 only, after the fused QKV epilogue: zeroes rows t in [L, Lpad) of Q
+// and K and the positions of V^T that hold no token (vkey_pos(p) >= L).
+hipError_t launch_qkv_pad_zero(const QkNormArgs& a, hipStream_t s);
 
 // ---- RoPE table -------------------------------------------------------------
 hipError_t launch_rope_table(const int32_t* ids, int L, int a0, int a1, int a2, double theta,
@@ -135,8 +135,9 @@ enum Epi : int {
   EPI_SPLIT = 3,     // n < split_n: out = acc + bias; else out2[n - split_n] = GELU(acc + bias)
   EPI_EULER = 4,     // x[r, n] += dsigma * (acc + bias); v_out (if set) = acc + bias  (f32)
   // as EPI_STORE / EPI_SPLIT, except that columns [0, 2 qk_h) (q | k) go
-  // through QK RMSNorm + RoPE into Q / K [B, H, Lpad, 128] instead of `out`
-  // (256x256 direct-to-LDS kernel, dense bf16 weights only)
+  // through QK RMSNorm + RoPE into Q / K [B, H, Lpad, 128] and columns
+  // [2 qk_h, 3 qk_h) (v) into V^T [B, H, 128, Lpad] in vkey_pos order,
+  // instead of `out` (256x256 direct-to-LDS kernel, dense bf16 weights only)
   EPI_QKV = 5,
   EPI_SPLIT_QKV = 6,
 };
@@ -169,6 +170,7 @@ struct GemmProblem {
   // Q (K) [B, H, qk_Lpad, 128].
   void* qk_Q;
   void* qk_K;
+  void* qk_V;  // V^T
   const void* qn;
   const void* kn;
   const float* rope;  // [L, 64, 2] cos, sin
