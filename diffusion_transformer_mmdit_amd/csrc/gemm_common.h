@@ -80,36 +80,46 @@ __device__ __forceinline__ void deq4(const u32x4& w, float s, bf16x8 out[4]) {
 }
 
 // Sub-byte weights, groups of 128 along k. 32 weights (k ascending) into four
-// bf16x8, built as bit patterns from the bf16 scale s16 (s >= 0):
-// Q1: bit j of `bits` -> weight j, 1 -> +s, 0 -> -s.
+// bf16x8, built as bit patterns from the bf16 scale s16 (s >= 0).
+// Q1: bit j of `bits` -> weight j, 1 -> +s, 0 -> -s. Per 16-bit half x of
+// the negated bits (16 weights), x | x << 15 puts the two sign bits of
+// output dword i at bits 2i and 2i + 16, one shift away from bits 15 and 31.
 __device__ __forceinline__ void deq_q1_32(uint32_t bits, uint32_t s16, bf16x8 out[4]) {
   const uint32_t sp = s16 | (s16 << 16);
   const uint32_t nb = ~bits;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    u32x4 o;
+  for (int hq = 0; hq < 2; ++hq) {
+    const uint32_t x = (nb >> (16 * hq)) & 0xFFFFu;  // weights 16 hq .. 16 hq + 15
+    const uint32_t x2 = x | (x << 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t t = nb >> (8 * q + 2 * i);  // bits 0, 1: the pair's negated signs
-      o[i] = sp | ((t & 1u) << 15) | ((t & 2u) << 30);
+    for (int q = 0; q < 2; ++q) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = sp | ((x2 << (15 - 2 * (4 * q + i))) & 0x80008000u);
+      out[2 * hq + q] = __builtin_bit_cast(bf16x8, o);
     }
-    out[q] = __builtin_bit_cast(bf16x8, o);
   }
 }
 // TQ2: the 2-bit code of weight j at bits 2j, 2j+1 of (w0 | w1 << 32);
-// code 0 -> -s, 2 -> +s, 1 and 3 -> 0.
-__device__ __forceinline__ uint32_t tq2_half(uint32_t c, uint32_t s16) {
-  return (c & 1u) ? 0u : (s16 | ((~c & 2u) << 14));
-}
+// code 0 -> -s, 2 -> +s, 1 and 3 -> 0. Per 16-bit half x (8 codes): nz has
+// bit 2j set when code j is 0 or 2, ng when it is 0; spread by 14, the flags
+// of output dword i sit at bits 4i and 4i + 16, so the dword's two
+// magnitudes are one 24-bit multiply of its two nz flags by the scale and
+// its two signs one shift of the ng flags.
 __device__ __forceinline__ void deq_tq2_32(uint32_t w0, uint32_t w1, uint32_t s16, bf16x8 out[4]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t w = q < 2 ? w0 : w1;
+    const uint32_t x = ((q < 2 ? w0 : w1) >> (16 * (q & 1))) & 0xFFFFu;
+    const uint32_t nx = ~x;
+    const uint32_t nz = nx & 0x5555u;
+    const uint32_t ng = nx & (nx >> 1) & 0x5555u;
+    const uint32_t nz2 = nz | (nz << 14);
+    const uint32_t ng2 = ng | (ng << 14);
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t t = w >> (16 * (q & 1) + 4 * i);  // codes of weights 8q + 2i, 8q + 2i + 1
-      o[i] = tq2_half(t & 3u, s16) | (tq2_half((t >> 2) & 3u, s16) << 16);
+      const uint32_t mag = __umul24((nz2 >> (4 * i)) & 0x10001u, s16);
+      o[i] = mag | ((ng2 << (15 - 4 * i)) & 0x80008000u);
     }
     out[q] = __builtin_bit_cast(bf16x8, o);
   }
