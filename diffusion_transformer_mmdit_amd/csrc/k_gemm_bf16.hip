@@ -216,16 +216,18 @@ static hipError_t launch_cfg(const GemmProblem* p, int nprob, hipStream_t s) {
 
 template <int EPI, int FMT>
 static hipError_t launch_epi_fmt(const GemmProblem* p, int nprob, hipStream_t s) {
-  int64_t tiles256 = 0;
+  // dense weights take 64 x 64 tiles for narrow outputs and whenever 128 x 128
+  // tiles would leave CUs idle (e.g. the text projection: 512 x 3072 is 96
+  // tiles of 128 x 128 but 384 of 64 x 64)
+  int64_t tiles128 = 0;
   int maxN = 0;
   for (int i = 0; i < nprob; ++i) {
-    tiles256 += (int64_t)((p[i].M + 255) / 256) * ((p[i].N + 255) / 256);
+    tiles128 += (int64_t)((p[i].M + 127) / 128) * ((p[i].N + 127) / 128);
     if (p[i].N > maxN) maxN = p[i].N;
   }
   if constexpr (FMT == 0) {
-    if (maxN <= 64) return launch_cfg<64, 64, 2, 2, EPI, FMT>(p, nprob, s);
+    if (maxN <= 64 || tiles128 < 256) return launch_cfg<64, 64, 2, 2, EPI, FMT>(p, nprob, s);
   }
-  (void)tiles256;
   return launch_cfg<128, 128, 2, 2, EPI, FMT>(p, nprob, s);
 }
 
