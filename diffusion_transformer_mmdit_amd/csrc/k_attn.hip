@@ -26,8 +26,9 @@
 //    the MFMA B operand. V^T arrives from the QK-norm kernel with its tokens
 //    in vkey_pos order, so each lane's 8 keys are one contiguous 16 bytes;
 //  * online softmax in float32 with exp2 of log2(e)-scaled scores; the
-//    running max is moved only when it grows by more than 2^8; row sums are
-//    float32 VALU adds in the softmax phase.
+//    running max is moved only when a row sum of probabilities (which bounds
+//    each of them) exceeds a fixed bound, so most tiles need no tile max;
+//    row sums are float32 VALU adds in the softmax phase.
 #include "common.h"
 #include "kernels.h"
 
@@ -214,10 +215,27 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
     __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  // softmax of S(kt): running max, probabilities to bf16, row sums. The
-  // running max is moved only when some lane's tile max exceeds it by more
-  // than 2^8 (log2 units): p = exp2(s - m_run) then stays below 256, and p,
-  // O and the row sums all use the same m_run, so the result is exact.
+  // softmax of S(kt). Probabilities p = exp2(s c2 - m_run) go to bf16 for
+  // the PV product; their row sums stay float32. Fast path: m_run is kept
+  // while every p stays at most kPMax. All p are non-negative, so a row sum
+  // (both lanes of a query) at most kPMax bounds each of them, and no tile max
+  // is needed. A larger (or non-finite) sum, and the first tile, take the
+  // slow path: the tile max moves m_run, O and l are rescaled, and p is
+  // recomputed (then every p <= 1). p, O and the row sums all use the same
+  // m_run, so the result is exact either way.
+  constexpr float kPMax = 4096.f;
+  auto probs = [&]() {
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -m_run));
+        if (r & 1) ps1 += p; else ps0 += p;
+        pb[kb * 2 + (r >> 3)][r & 7] = (bf16)p;
+      }
+    return ps0 + ps1;
+  };
   auto softmax = [&](int kt, bool mask) {
     if (__builtin_expect(mask, 0)) {
 #pragma unroll
@@ -228,32 +246,30 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
           if (key >= a.L) s[kb][r] = kNegBig;
         }
     }
-    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+    float ps = 0.f;
+    bool slow = kt == 0;
+    if (!slow) {
+      ps = probs();
+      slow = __any(!(ps + __shfl_xor(ps, 32, 64) <= kPMax));
+    }
+    if (__builtin_expect(slow, 0)) {
+      float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
 #pragma unroll
-    for (int r = 3; r < 15; r += 2) mx = fmaxf(mx, fmaxf(s[0][r], s[0][r + 1]));
-    mx = fmaxf(mx, fmaxf(s[0][15], s[1][0]));
+      for (int r = 3; r < 15; r += 2) mx = fmaxf(mx, fmaxf(s[0][r], s[0][r + 1]));
+      mx = fmaxf(mx, fmaxf(s[0][15], s[1][0]));
 #pragma unroll
-    for (int r = 1; r < 15; r += 2) mx = fmaxf(mx, fmaxf(s[1][r], s[1][r + 1]));
-    mx = fmaxf(mx, s[1][15]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
-    if (__any(mx > m_run + 8.0f)) {
+      for (int r = 1; r < 15; r += 2) mx = fmaxf(mx, fmaxf(s[1][r], s[1][r + 1]));
+      mx = fmaxf(mx, s[1][15]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
       l_run *= alpha;
       m_run = m_new;
+      ps = probs();
     }
-    float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -m_run));
-        if (r & 1) ps1 += p; else ps0 += p;
-        pb[kb * 2 + (r >> 3)][r & 7] = (bf16)p;
-      }
-    l_run += ps0 + ps1;
+    l_run += ps;
     // keep the conversions in this phase (they would sink to their MFMAs)
 #pragma unroll
     for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[i]));

@@ -128,6 +128,36 @@ def test_double_block_cfg2_bf16():
     assert_parity(txt, rtxt, "bf16", "cfg2 txt")
 
 
+def _sharpened(w, a):
+    """Copy of bf16 block weights with the QK RMSNorm scales multiplied by a
+    (rounded to bf16, so both sides get the same values)."""
+    if "txt" in w:
+        return {k: _sharpened(v, a) for k, v in w.items()}
+    out = dict(w)
+    for n in ("q_norm", "k_norm"):
+        out[n] = I.round_bf16(np.asarray(w[n], np.float32) * np.float32(a))
+    return out
+
+
+def test_blocks_bf16_sharp_attention():
+    # The seeded norm scales (about 1) give scores with a standard deviation
+    # of about 1.4 in log2 units, so the running max of the online softmax
+    # settles on the first key tile. Scales of 3 make it about 13: over the
+    # 1280 keys, about half the queries' max exceeds their first tile's max
+    # by more than 12 (a probability above 2^12), so later tiles take the
+    # path that moves the running max and rescales O and the row sums.
+    s = I.CFG2
+    x = I.block_inputs(s)
+    ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
+    w = _sharpened(I.double_block_weights(s, 0), 3.0)
+    img, txt = run_double(s, w, x, ids)
+    rimg, rtxt = oracle_double(s, w, x, ids)
+    assert_parity(img, rimg, "bf16", "sharp attention img")
+    assert_parity(txt, rtxt, "bf16", "sharp attention txt")
+    ws_ = _sharpened(I.single_block_weights(s, 0), 3.0)
+    assert_parity(run_single(s, ws_, x, ids), oracle_single(s, ws_, x, ids), "bf16", "sharp attention single")
+
+
 @pytest.mark.parametrize("txt_len,gh,gw,batch", [(77, 9, 13, 2), (0, 16, 12, 1), (200, 1, 1, 1), (5, 3, 4, 1), (40, 5, 5, 2)])
 def test_blocks_bf16_ragged(txt_len, gh, gw, batch):
     s = I.Shape(hidden=512, heads=4, mlp_hidden=1024, txt_len=txt_len, grid_h=gh, grid_w=gw, batch=batch,
