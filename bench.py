@@ -327,6 +327,16 @@ def main():
         qms = timed(lambda i: step(i, mqc, Xq), a.steps)
         out["quantised_ms_per_step"] = round(qms, 3)
         log(f"quantised step: {qms:.2f} ms")
+        # at 4608 rows each quantised layer is decoded to bf16 once per launch
+        bd.mmdit_profile_begin(bd.PC_DEQUANT, 400 * max(1, a.steps))
+        for i in range(a.steps):
+            step(i, mqc, Xq)
+        dq_ms, dq_n, dq_b = bd.mmdit_profile_end()
+        out["quantised_decode"] = {"ms_per_step": round(dq_ms / max(a.steps, 1), 3),
+                                   "launches_per_step": dq_n // max(a.steps, 1),
+                                   "gbps": round(dq_b / max(dq_ms, 1e-9) / 1e6, 1)}
+        log(f"quantised decode: {out['quantised_decode']['ms_per_step']:.3f} ms/step in "
+            f"{out['quantised_decode']['launches_per_step']} launches, {out['quantised_decode']['gbps']:.0f} GB/s")
         del Mq, mqc
 
         # ternary-weight step (TQ2G128 in every block projection)

@@ -18,7 +18,7 @@ _lib = None
 
 F32, BF16 = 0, 1
 W_DENSE, W_Q4G64, W_Q8G64, W_Q1G128, W_TQ2G128 = 0, 1, 2, 3, 4
-PC_GEMM, PC_ATTN, PC_LN, PC_QKNORM, PC_GEMV, PC_GEMM_LIN1, PC_GEMM_RES = 1, 2, 3, 4, 5, 6, 7
+PC_GEMM, PC_ATTN, PC_LN, PC_QKNORM, PC_GEMV, PC_GEMM_LIN1, PC_GEMM_RES, PC_DEQUANT = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 class MMDiTError(RuntimeError):
@@ -102,6 +102,7 @@ _SIGS = {
     "mmdit_unpack_latents": (C.c_int, [_P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P]),
     "mmdit_rope_table": (C.c_int, [_P, C.c_int32, _P, C.c_double, _P, _P]),
     "mmdit_quantise": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P]),
+    "mmdit_dequantise": (C.c_int, [_P, _P, C.c_int32, C.c_int32, C.c_int32, _P, _P]),
     "mmdit_profile_begin": (C.c_int, [C.c_int32, C.c_int32]),
     "mmdit_profile_end": (C.c_int, [C.POINTER(C.c_double), C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
     "mmdit_status_str": (C.c_char_p, [C.c_int32]),
@@ -420,6 +421,13 @@ def mmdit_quantise(w: np.ndarray, bits: int):
     _check(lib().mmdit_quantise(w.ctypes.data_as(C.c_void_p), n, k, bits, packed.ctypes.data_as(C.c_void_p),
                                 scales.ctypes.data_as(C.c_void_p)), "mmdit_quantise")
     return packed, scales
+
+
+def mmdit_dequantise(w, scales, fmt: int, n_out: int, k_in: int, out, stream=None):
+    """Decodes quantised codes `w` with bf16 `scales` (device tensors) into
+    the bf16 tensor `out` [n_out, k_in]."""
+    _check(lib().mmdit_dequantise(_ptr(w), _ptr(scales), fmt, n_out, k_in, _ptr(out), _stream(stream)),
+           "mmdit_dequantise")
 
 
 def mmdit_profile_begin(kernel_class: int, max_launches: int):

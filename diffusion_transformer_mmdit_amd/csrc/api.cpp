@@ -50,7 +50,7 @@ struct Prof {
 };
 Prof g_prof;
 
-enum { PC_GEMM = 1, PC_ATTN = 2, PC_LN = 3, PC_QKNORM = 4, PC_GEMV = 5, PC_GEMM_LIN1 = 6, PC_GEMM_RES = 7 };
+enum { PC_GEMM = 1, PC_ATTN = 2, PC_LN = 3, PC_QKNORM = 4, PC_GEMV = 5, PC_GEMM_LIN1 = 6, PC_GEMM_RES = 7, PC_DEQUANT = 8 };
 
 struct ProfScope {
   hipEvent_t stop = nullptr;
@@ -161,11 +161,34 @@ int check_single(const mmdit_single_w& s, const Geo& g) {
 // Block scratch (activation dtype unless noted):
 //   xn [rows, h], qkv [rows, 3h], Q/K/V [B, H, Lpad, 128],
 //   o   [rows, h] (dual) or cat [rows, h + m] (single), mlp [rows, m] (dual).
+//   xw  bf16 weights decoded from a quantised layer (only when expanding).
 struct BlockWs {
-  size_t xn, qkv, q, k, v, o, mlp, total;
+  size_t xn, qkv, q, k, v, o, mlp, xw, xw_bytes, total;
 };
 
-BlockWs plan_block(const Geo& g, size_t base) {
+// Quantised layers of launches with at least this many rows are decoded into
+// bf16 scratch once and run on the dense kernels. Dequantising inside the GEMM
+// decodes each weight tile once per output row-tile (rows / 256 times); from
+// four row-tiles on, that repeated VALU work (which the MFMAs of the same SIMD
+// do not hide) costs more than one HBM-bound decoding pass.
+constexpr int64_t kExpandMinRows = 1024;
+
+// Bytes of the decoded-weight scratch for geometry g when the largest
+// quantised launch holds nk weights (0 when the launches do not expand).
+size_t expand_bytes(const Geo& g, size_t nk) {
+  return g.bf16 && (int64_t)g.B * g.L >= kExpandMinRows ? align_up(nk * 2) : 0;
+}
+
+// Largest weight count of one block GEMM launch: both streams' qkv or fc1 /
+// fc2 (dual), or linear1 (single).
+size_t block_launch_weights(const Geo& g) {
+  const size_t h = g.h, m = g.m;
+  const size_t dual = 2 * h * (3 * h > m ? 3 * h : m);
+  const size_t single = h * (3 * h + m);
+  return dual > single ? dual : single;
+}
+
+BlockWs plan_block(const Geo& g, size_t base, size_t xw_bytes) {
   BlockWs w;
   const size_t rows = (size_t)g.B * g.L;
   const size_t qkvh = (size_t)g.B * g.H * g.Lpad * 128;
@@ -177,6 +200,7 @@ BlockWs plan_block(const Geo& g, size_t base) {
   w.v = at; at = align_up(at + qkvh * g.esz);
   w.o = at; at = align_up(at + rows * (size_t)(g.h + g.m) * g.esz);
   w.mlp = at; at = align_up(at + rows * g.m * g.esz);
+  w.xw = at; w.xw_bytes = xw_bytes; at = align_up(at + xw_bytes);
   w.total = at;
   return w;
 }
@@ -192,7 +216,7 @@ BlockCallWs plan_block_call(const Geo& g, int mod_width) {
   size_t at = 0;
   w.table = at; at = align_up(at + (size_t)g.L * 64 * 2 * 4);
   w.mod = at; at = align_up(at + (size_t)g.B * mod_width * 4);
-  w.blk = plan_block(g, at);
+  w.blk = plan_block(g, at, expand_bytes(g, block_launch_weights(g)));
   return w;
 }
 
@@ -217,7 +241,11 @@ StepWs plan_step(const mmdit_config* c, const Geo& g) {
   w.mods = at; at = align_up(at + (w.mod_final + B * 2 * g.h) * 4);
   w.table = at; at = align_up(at + (size_t)g.L * 64 * 2 * 4);
   w.xin = at; at = align_up(at + B * g.Li * c->in_ch * g.esz);
-  w.blk = plan_block(g, at);
+  // the input and final projections may be quantised too
+  size_t nk = block_launch_weights(g);
+  const size_t nk_io = (size_t)g.h * (c->txt_in_dim > c->in_ch ? c->txt_in_dim : c->in_ch);
+  nk = nk > nk_io ? nk : nk_io;
+  w.blk = plan_block(g, at, expand_bytes(g, nk));
   return w;
 }
 
@@ -226,11 +254,48 @@ struct Ctx {
   hipStream_t s;
   Geo g;
   float ln_eps, rms_eps;
+  void* xw = nullptr;  // decoded-weight scratch (null: quantised layers stay fused)
+  size_t xw_bytes = 0;
 };
 
 char* ptr(void* base, size_t off) { return reinterpret_cast<char*>(base) + off; }
 
+// Decodes the quantised weights of a launch into the scratch (when the
+// geometry expands, see kExpandMinRows) and points the problems at the dense
+// copies. Problems sharing one weight matrix share one copy. Later launches on
+// the stream reuse the scratch, after this launch's reads.
+int expand_quantised(const Ctx& c, GemmProblem* p, int np) {
+  if (!c.xw) return MMDIT_OK;
+  const void* src[2] = {nullptr, nullptr};
+  void* dst[2] = {nullptr, nullptr};
+  size_t at = 0;
+  for (int i = 0; i < np; ++i) {
+    if (p[i].fmt == MMDIT_W_DENSE) continue;
+    void* d = nullptr;
+    for (int j = 0; j < i; ++j)
+      if (src[j] == p[i].W) d = dst[j];
+    if (!d) {
+      const size_t bytes = (size_t)p[i].N * p[i].K * 2;
+      if (at + bytes > c.xw_bytes)
+        return fail(MMDIT_ERR_WORKSPACE, "decoded-weight scratch %zu bytes, need %zu", c.xw_bytes, at + bytes);
+      d = ptr(c.xw, at);
+      at = align_up(at + bytes);
+      const double wb = p[i].fmt == MMDIT_W_Q4G64 ? 0.5 : p[i].fmt == MMDIT_W_Q8G64 ? 1.0
+                        : p[i].fmt == MMDIT_W_Q1G128 ? 0.125 : 0.25;
+      ProfScope ps(PC_DEQUANT, (double)p[i].N * p[i].K * (wb + 2.0), c.s);
+      HIP_TRY(launch_dequant(p[i].W, p[i].scales, p[i].fmt, p[i].N, p[i].K, d, c.s));
+    }
+    src[i] = p[i].W;
+    dst[i] = d;
+    p[i].W = d;
+    p[i].fmt = MMDIT_W_DENSE;
+    p[i].scales = nullptr;
+  }
+  return MMDIT_OK;
+}
+
 int gemm(const Ctx& c, GemmProblem* p, int np, int epi) {
+  if (int r = expand_quantised(c, p, np)) return r;
   double flops = 0;
   for (int i = 0; i < np; ++i) flops += 2.0 * p[i].M * (double)p[i].N * p[i].K;
   ProfScope ps(PC_GEMM, flops, c.s,
@@ -383,6 +448,7 @@ int run_double(const Ctx& c, const mmdit_stream_w* const sw[2], const Part* part
   // direct-to-LDS kernel runs it), joint attention
   const void* qn[2] = {sw[0]->q_norm, sw[1]->q_norm};
   const void* kn[2] = {sw[0]->k_norm, sw[1]->k_norm};
+  if ((r = expand_quantised(c, gp, 2))) return r;
   const bool fused = fuse_qk(c, gp, 2, parts, qn, kn, table, w, ws, EPI_QKV);
   if ((r = gemm(c, gp, 2, fused ? EPI_QKV : EPI_STORE))) return r;
   if ((r = run_qk_attn(c, parts, 2, qkv, qn, kn, table, w, ws, o, h, fused))) return r;
@@ -439,6 +505,7 @@ int run_single(const Ctx& c, const mmdit_single_w& sw, const Part* parts, int np
   }
   const void* qn[2] = {sw.q_norm, sw.q_norm};
   const void* kn[2] = {sw.k_norm, sw.k_norm};
+  if ((r = expand_quantised(c, gp, np))) return r;
   const bool fused = fuse_qk(c, gp, np, parts, qn, kn, table, w, ws, EPI_SPLIT_QKV);
   if ((r = gemm(c, gp, np, fused ? EPI_SPLIT_QKV : EPI_SPLIT))) return r;
   if ((r = run_qk_attn(c, parts, np, qkv, qn, kn, table, w, ws, cat, h + m, fused))) return r;
@@ -494,6 +561,8 @@ int mmdit_double_block_fwd(const mmdit_dims* dims, const mmdit_double_w* w, cons
   if (!ws || ws_bytes < lay.blk.total)
     return fail(MMDIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, lay.blk.total);
   Ctx c{(hipStream_t)hip_stream, g, dims->ln_eps, dims->rms_eps};
+  c.xw = lay.blk.xw_bytes ? ptr(ws, lay.blk.xw) : nullptr;
+  c.xw_bytes = lay.blk.xw_bytes;
   float* table = (float*)ptr(ws, lay.table);
   float* mod = (float*)ptr(ws, lay.mod);
   float* mod_txt = mod;
@@ -523,6 +592,8 @@ int mmdit_single_block_fwd(const mmdit_dims* dims, const mmdit_single_w* w, cons
   if (!ws || ws_bytes < lay.blk.total)
     return fail(MMDIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, lay.blk.total);
   Ctx c{(hipStream_t)hip_stream, g, dims->ln_eps, dims->rms_eps};
+  c.xw = lay.blk.xw_bytes ? ptr(ws, lay.blk.xw) : nullptr;
+  c.xw_bytes = lay.blk.xw_bytes;
   float* table = (float*)ptr(ws, lay.table);
   float* mod = (float*)ptr(ws, lay.mod);
   if ((r = rope(c, dims, ids, table))) return r;
@@ -540,6 +611,21 @@ static int check_config(const mmdit_config* cfg, Geo& g) {
   if (cfg->txt_in_dim < 64 || cfg->txt_in_dim % 64) return fail(MMDIT_ERR_SHAPE, "txt_in_dim must be a positive multiple of 64");
   if (cfg->vec_in_dim < 8 || cfg->vec_in_dim % 8 || cfg->vec_in_dim > 4096) return fail(MMDIT_ERR_SHAPE, "vec_in_dim must be a multiple of 8 in [8, 4096]");
   if (cfg->temb_dim < 8 || cfg->temb_dim % 8 || cfg->temb_dim > 4096) return fail(MMDIT_ERR_SHAPE, "temb_dim must be a multiple of 8 in [8, 4096]");
+  return MMDIT_OK;
+}
+
+int mmdit_dequantise(const void* w, const void* scales, int32_t fmt, int32_t n_out, int32_t k_in, void* out,
+                     void* hip_stream) {
+  if (!w || !scales || !out) return fail(MMDIT_ERR_NULL, "NULL weights, scales or output");
+  if (fmt != MMDIT_W_Q4G64 && fmt != MMDIT_W_Q8G64 && fmt != MMDIT_W_Q1G128 && fmt != MMDIT_W_TQ2G128)
+    return fail(MMDIT_ERR_DTYPE, "fmt %d is not a quantised weight format", fmt);
+  const int group = fmt == MMDIT_W_Q1G128 || fmt == MMDIT_W_TQ2G128 ? 128 : 64;
+  if (n_out < 0 || k_in < group || k_in % group)
+    return fail(MMDIT_ERR_SHAPE, "need n_out >= 0 and k_in a positive multiple of %d (got %d, %d)", group, n_out, k_in);
+  const uintptr_t wa = fmt == MMDIT_W_Q1G128 ? 4 : fmt == MMDIT_W_TQ2G128 ? 8 : 16;
+  if ((uintptr_t)w % wa || (uintptr_t)scales % 2 || (uintptr_t)out % 16)
+    return fail(MMDIT_ERR_SHAPE, "misaligned pointer (w %zu, scales 2, out 16 bytes)", (size_t)wa);
+  HIP_TRY(launch_dequant(w, scales, fmt, n_out, k_in, out, (hipStream_t)hip_stream));
   return MMDIT_OK;
 }
 
@@ -639,6 +725,8 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
     return fail(MMDIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, lay.blk.total);
 
   Ctx c{(hipStream_t)hip_stream, g, cfg->dims.ln_eps, cfg->dims.rms_eps};
+  c.xw = lay.blk.xw_bytes ? ptr(ws, lay.blk.xw) : nullptr;
+  c.xw_bytes = lay.blk.xw_bytes;
   const int B = g.B;
   float* x = (float*)ptr(ws, lay.x);  // residual: [B*Lt text rows; B*Li image rows] f32
   float* vec = (float*)ptr(ws, lay.vec);
@@ -852,7 +940,7 @@ int mmdit_rope_table(const int32_t* ids, int32_t L, const int32_t* axes_dim, dou
 
 int mmdit_profile_begin(int32_t kernel_class, int32_t max_launches) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
-  if (kernel_class < PC_GEMM || kernel_class > PC_GEMM_RES) return fail(MMDIT_ERR_SHAPE, "unknown kernel class %d", kernel_class);
+  if (kernel_class < PC_GEMM || kernel_class > PC_DEQUANT) return fail(MMDIT_ERR_SHAPE, "unknown kernel class %d", kernel_class);
   if (max_launches < 1 || max_launches > 1 << 20) return fail(MMDIT_ERR_SHAPE, "max_launches out of range");
   if (g_prof.active) return fail(MMDIT_ERR_UNSUPPORTED, "profiling already active");
   for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);

@@ -186,6 +186,10 @@ bool gemm_dma_eligible(const GemmProblem* p, int nprob, int epi);
 hipError_t launch_gemm_dma(const GemmProblem* p, int nprob, int epi, hipStream_t s);
 // float32 operands and accumulation (VALU), dense weights only.
 hipError_t launch_gemm_f32(const GemmProblem* p, int nprob, int epi, hipStream_t s);
+// Quantised weights (fmt 1-4, layouts as the GEMM kernels read them) decoded
+// into dense bf16 [N, K] at `out` (16-byte aligned): the same bf16 values the
+// GEMM kernels stage when they dequantise a tile.
+hipError_t launch_dequant(const void* w, const void* scales, int fmt, int N, int K, void* out, hipStream_t s);
 
 // ---- joint attention ------------------------------------------------------------
 // O rows: token t of batch b goes to seg[0] row (b, t) if t < seg_len0 else

@@ -146,7 +146,14 @@ typedef struct {
   mmdit_linear guidance_in0, guidance_in1;
 } mmdit_model_w;
 
-/* Workspace sizes in bytes (host-only; no device work). */
+/* Workspace sizes in bytes (host-only; no device work). With bf16
+ * activations and at least 1024 rows (batch * (txt_len + img_len), context
+ * tokens included) the workspace also holds room for one launch's weights
+ * decoded to bf16 (2 bytes per weight of the largest launch: both streams'
+ * fc1 or fc2, or linear1). Quantised layers of such calls are decoded there
+ * once per launch (profile class 8) and multiplied by the dense kernels;
+ * below 1024 rows the GEMM kernels dequantise weight tiles as they stage
+ * them. Both give the same bf16 weights. */
 int mmdit_double_block_workspace(const mmdit_dims* dims, size_t* bytes);
 int mmdit_single_block_workspace(const mmdit_dims* dims, size_t* bytes);
 int mmdit_step_workspace(const mmdit_config* cfg, size_t* bytes);
@@ -305,16 +312,32 @@ int mmdit_rope_table(const int32_t* ids, int32_t L, const int32_t* axes_dim, dou
 int mmdit_quantise(const float* w, int32_t n_out, int32_t k_in, int32_t bits,
                    void* packed, uint16_t* scales_bf16);
 
+/* Device. Decodes a quantised weight matrix into dense bf16 out [n_out, k_in]
+ * (stable-diffusion.rs README: weights held quantised and dequantised for
+ * the matmul; pictor page: Q1_0_g128 / TQ2_0_g128), giving the weights the
+ * GEMMs multiply: code * scale rounded to bf16 (nearest even) for
+ * MMDIT_W_Q4G64 / MMDIT_W_Q8G64, exactly +s, -s or 0 for MMDIT_W_Q1G128 /
+ * MMDIT_W_TQ2G128. w (packed codes) and scales (bf16) are device arrays in
+ * the layouts of mmdit_wfmt; out is device memory the caller owns. w must be
+ * 16-byte aligned (8 for ternary, 4 for 1-bit), scales 2-byte and out
+ * 16-byte aligned. Enqueued on hip_stream (NULL: the null stream).
+ * Errors: MMDIT_ERR_NULL; MMDIT_ERR_DTYPE for fmt not one of the four
+ * quantised formats; MMDIT_ERR_SHAPE for n_out < 0, k_in not a positive
+ * multiple of the format's group, or misaligned pointers; MMDIT_ERR_HIP. */
+int mmdit_dequantise(const void* w, const void* scales, int32_t fmt, int32_t n_out, int32_t k_in,
+                     void* out, void* hip_stream);
+
 /* Kernel timing for benchmarks. While enabled, each launch of the selected
  * kernel class is bracketed by HIP events recorded on the launch stream.
  * classes: 1 = GEMMs (all projections), 2 = joint attention,
  * 3 = adaLN LayerNorm, 4 = QK RMSNorm + RoPE, 5 = modulation / conditioning
  * GEMV, 6 = single-block linear1 GEMM (split GELU epilogue), 7 = GEMMs with
- * the gated-residual epilogue (out-projection, fc2, linear2).
+ * the gated-residual epilogue (out-projection, fc2, linear2), 8 = decoding of
+ * quantised weights to bf16 ahead of a launch.
  * mmdit_profile_begin creates up to max_launches event pairs (host call, no
  * device allocation). mmdit_profile_end waits for the recorded events and
  * returns the summed kernel time, the launch count and the summed algorithmic
- * FLOPs (classes 1, 2, 6, 7) or bytes (classes 3-5) of those launches. */
+ * FLOPs (classes 1, 2, 6, 7) or bytes (classes 3-5, 8) of those launches. */
 int mmdit_profile_begin(int32_t kernel_class, int32_t max_launches);
 int mmdit_profile_end(double* total_ms, int32_t* launches, double* work);
 

@@ -199,7 +199,8 @@ def test_single_block_cfg3_bf16_full_size(cfg3):
 def test_blocks_bf16_full_width_ragged_rows(quant):
     # h 3072 with 77 text + 40x41 image tokens: the projections take the
     # 256x256 direct-to-LDS GEMM with partial row tiles in both streams
-    # (dense weights, 4/8-bit or 1-bit/ternary weights dequantised into LDS)
+    # (dense weights; 4/8-bit or 1-bit/ternary weights, which at 1717 rows
+    # are decoded to bf16 a layer at a time first)
     s = I.Shape(txt_len=77, grid_h=40, grid_w=41, dtype="bf16", cfg_id=38)
     q = {None: None, "policy": bd.QUANT_POLICY, "sub_byte": SUB_BYTE_MIX}[quant]
     x = I.block_inputs(s)
@@ -214,6 +215,27 @@ def test_blocks_bf16_full_width_ragged_rows(quant):
     wso = dequantised(ws_, q) if q else ws_
     assert_parity(run_single(s, ws_, x, ids, quant=q), oracle_single(s, wso, x, ids), "bf16",
                   f"ragged-rows single {quant}")
+
+
+@pytest.mark.parametrize("quant", ["policy", "sub_byte"])
+def test_blocks_quantised_full_width_below_decoding_rows(quant):
+    # h 3072 with 77 text + 28x30 image tokens (917 rows, under the 1024 from
+    # which whole layers are decoded to bf16 first): the GEMM kernels
+    # dequantise weight tiles as they stage them, on the 256x256
+    # direct-to-LDS kernel (fc1: 240 tiles, linear1: 336) and on the
+    # register-staged one (qkv, out-projection, fc2, linear2)
+    s = I.Shape(txt_len=77, grid_h=28, grid_w=30, dtype="bf16", cfg_id=51)
+    q = {"policy": bd.QUANT_POLICY, "sub_byte": SUB_BYTE_MIX}[quant]
+    x = I.block_inputs(s)
+    ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
+    w = I.double_block_weights(s, 0)
+    img, txt = run_double(s, w, x, ids, quant=q)
+    rimg, rtxt = oracle_double(s, dequantised(w, q), x, ids)
+    assert_parity(img, rimg, "bf16", f"fused-dequant dual img {quant}")
+    assert_parity(txt, rtxt, "bf16", f"fused-dequant dual txt {quant}")
+    ws_ = I.single_block_weights(s, 0)
+    assert_parity(run_single(s, ws_, x, ids, quant=q), oracle_single(s, dequantised(ws_, q), x, ids), "bf16",
+                  f"fused-dequant single {quant}")
 
 
 def test_blocks_bf16_full_width_two_batches():

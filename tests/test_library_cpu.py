@@ -229,6 +229,21 @@ def test_step_cache_bytes(lib):
     assert 2 * s.img_len * s.hidden * 4 + s.img_len * 8 <= n <= 2 * s.img_len * s.hidden * 4 + s.img_len * 8 + 1024
 
 
+def test_workspace_holds_decoded_weights_from_1024_rows(lib):
+    # bf16 at 1024 rows and more: room for the largest launch's weights in
+    # bf16 (both streams' fc1 at h 3072, m 12288: 2 * 12288 * 3072 weights)
+    below = bd.mmdit_double_block_workspace(_dims(hidden=3072, heads=24, mlp_hidden=12288, txt_len=0,
+                                                  grid_h=31, grid_w=33))
+    at = bd.mmdit_double_block_workspace(_dims(hidden=3072, heads=24, mlp_hidden=12288, txt_len=0,
+                                               grid_h=32, grid_w=32))
+    assert 2 * 12288 * 3072 * 2 <= at - below <= 2 * 12288 * 3072 * 2 + 4 * 2**20
+    f32 = bd.mmdit_double_block_workspace(_dims(hidden=3072, heads=24, mlp_hidden=12288, txt_len=0,
+                                                grid_h=32, grid_w=32, dtype="f32"))
+    below32 = bd.mmdit_double_block_workspace(_dims(hidden=3072, heads=24, mlp_hidden=12288, txt_len=0,
+                                                    grid_h=31, grid_w=33, dtype="f32"))
+    assert f32 - below32 < 4 * 2**20
+
+
 def test_workspace_sizes_scale_with_tokens(lib):
     small = bd.mmdit_double_block_workspace(_dims(grid_h=8, grid_w=8))
     big = bd.mmdit_double_block_workspace(_dims(grid_h=16, grid_w=16))
