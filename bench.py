@@ -337,6 +337,14 @@ def main():
                                    "gbps": round(dq_b / max(dq_ms, 1e-9) / 1e6, 1)}
         log(f"quantised decode: {out['quantised_decode']['ms_per_step']:.3f} ms/step in "
             f"{out['quantised_decode']['launches_per_step']} launches, {out['quantised_decode']['gbps']:.0f} GB/s")
+        # the same step with every quantised layer dequantised inside its GEMM
+        qstep = lambda i: bd.mmdit_step_ex(cfg, mqc, Xq, v, T, y, ids, sig[i % 4], sig[i % 4 + 1], ws,  # noqa
+                                           dequant_in_gemm=True)
+        for i in range(2):
+            qstep(i)
+        qgms = timed(qstep, a.steps)
+        out["quantised_in_gemm_ms_per_step"] = round(qgms, 3)
+        log(f"quantised step, dequantised inside the GEMMs: {qgms:.2f} ms")
         del Mq, mqc
 
         # ternary-weight step (TQ2G128 in every block projection)

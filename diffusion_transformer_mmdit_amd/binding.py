@@ -78,7 +78,8 @@ class mmdit_step_cache(C.Structure):
 
 class mmdit_step_opts(C.Structure):
     _fields_ = [("ctx_packed", C.c_void_p), ("ctx_len", C.c_int32), ("has_guidance", C.c_int32),
-                ("guidance", C.c_double), ("cache", C.POINTER(mmdit_step_cache)), ("cache_threshold", C.c_double)]
+                ("guidance", C.c_double), ("cache", C.POINTER(mmdit_step_cache)), ("cache_threshold", C.c_double),
+                ("dequant", C.c_int32)]
 
 
 # Every function the header declares, with its ctypes signature.
@@ -361,8 +362,9 @@ class StepCache:
 
 def mmdit_step_ex(cfg, w: mmdit_model_w, x_packed, v_out, txt_emb, y, ids, sigma: float, sigma_next: float, ws,
                   ctx_packed=None, ctx_len: int = 0, guidance: Optional[float] = None, stream=None,
-                  cache: Optional[StepCache] = None, cache_threshold: float = 0.0):
+                  cache: Optional[StepCache] = None, cache_threshold: float = 0.0, dequant_in_gemm: bool = False):
     o = mmdit_step_opts()
+    o.dequant = 1 if dequant_in_gemm else 0
     o.ctx_packed = _ptr(ctx_packed)
     o.ctx_len = int(ctx_len)
     o.has_guidance = 0 if guidance is None else 1

@@ -686,6 +686,7 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
       return fail(MMDIT_ERR_NULL, "the model has a guidance embedder: pass a guidance value (mmdit_step_ex)");
     if (!std::isfinite(opts->guidance)) return fail(MMDIT_ERR_SHAPE, "guidance must be finite");
   }
+  if (opts->dequant != 0 && opts->dequant != 1) return fail(MMDIT_ERR_SHAPE, "dequant %d must be 0 or 1", opts->dequant);
   mmdit_step_cache* cache = opts->cache;
   if (cache) {
     if (std::isnan(opts->cache_threshold) || opts->cache_threshold < 0)
@@ -725,7 +726,7 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
     return fail(MMDIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, lay.blk.total);
 
   Ctx c{(hipStream_t)hip_stream, g, cfg->dims.ln_eps, cfg->dims.rms_eps};
-  c.xw = lay.blk.xw_bytes ? ptr(ws, lay.blk.xw) : nullptr;
+  c.xw = lay.blk.xw_bytes && opts->dequant == 0 ? ptr(ws, lay.blk.xw) : nullptr;
   c.xw_bytes = lay.blk.xw_bytes;
   const int B = g.B;
   float* x = (float*)ptr(ws, lay.x);  // residual: [B*Lt text rows; B*Li image rows] f32

@@ -242,6 +242,9 @@ typedef struct {
  * a_prev and the residual, plus per-row partial sums). */
 int mmdit_step_cache_bytes(const mmdit_config* cfg, size_t* bytes);
 
+/* dequant (quantised layers only): 0 = automatic (decoded once per launch
+ * into bf16 scratch from 1024 rows on, see the workspace functions), 1 =
+ * always dequantised inside the GEMM while staging weight tiles. */
 typedef struct {
   const void* ctx_packed;
   int32_t ctx_len;
@@ -249,6 +252,7 @@ typedef struct {
   double guidance;
   mmdit_step_cache* cache;
   double cache_threshold;
+  int32_t dequant;
 } mmdit_step_opts;
 
 /* One denoising step with options (context tokens, guidance). Arguments as
@@ -257,7 +261,8 @@ typedef struct {
  * text, generated, then context rows. The workspace is
  * mmdit_step_workspace(cfg). Errors as for mmdit_step; MMDIT_ERR_SHAPE for
  * ctx_len out of range, a non-finite guidance, a negative or NaN
- * cache_threshold, or caching without a dual block; MMDIT_ERR_NULL for a NULL
+ * cache_threshold, caching without a dual block, or dequant not 0 or 1;
+ * MMDIT_ERR_NULL for a NULL
  * ctx_packed with ctx_len > 0, a NULL cache->buf, or a guidance model called
  * without a guidance value (mmdit_step on such a model fails the same way);
  * MMDIT_ERR_WORKSPACE for cache->bytes below mmdit_step_cache_bytes(cfg). */

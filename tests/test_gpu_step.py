@@ -53,7 +53,8 @@ def model_numpy(s: I.Shape):
     return g, dbl, sgl
 
 
-def run_step(s: I.Shape, g, dbl, sgl, inp, sig_i: int, n_steps: int = 4, quant=None, repeat: int = 1):
+def run_step(s: I.Shape, g, dbl, sgl, inp, sig_i: int, n_steps: int = 4, quant=None, repeat: int = 1,
+             dequant_in_gemm: bool = False):
     t = torch()
     dt = dtype_code(s.dtype)
     cfg = bd.make_config(s)
@@ -74,7 +75,10 @@ def run_step(s: I.Shape, g, dbl, sgl, inp, sig_i: int, n_steps: int = 4, quant=N
         Xr = X.clone()
         print(f"step B={s.batch} h={s.hidden} {s.n_double}+{s.n_single} blocks L={s.seq_len} {s.dtype} "
               f"sigma {sig[sig_i]:.4f}->{sig[sig_i + 1]:.4f}", flush=True)
-        bd.mmdit_step(cfg, mc, Xr, v, T, y, ids, sig[sig_i], sig[sig_i + 1], ws)
+        if dequant_in_gemm:
+            bd.mmdit_step_ex(cfg, mc, Xr, v, T, y, ids, sig[sig_i], sig[sig_i + 1], ws, dequant_in_gemm=True)
+        else:
+            bd.mmdit_step(cfg, mc, Xr, v, T, y, ids, sig[sig_i], sig[sig_i + 1], ws)
         sync()
         outs.append((down(Xr), down(v)))
     return outs if repeat > 1 else outs[0]
@@ -281,11 +285,14 @@ def test_step_cache_bf16_width3072_with_context():
     check_cached(s, 16, 16, rel_tol=2e-2)
 
 
-def test_step_quantised_full_tokens_one_plus_one_blocks():
+@pytest.mark.parametrize("in_gemm", [False, True])
+def test_step_quantised_full_tokens_one_plus_one_blocks(in_gemm):
+    # 4608 tokens: layers decoded once to bf16 (automatic), or dequantised
+    # inside the GEMMs while staging weight tiles (dequant = 1)
     s = dataclasses.replace(I.CFG5, n_double=1, n_single=1)
     g, dbl, sgl = model_numpy(s)
     inp = I.step_inputs(s)
-    _, vg = run_step(s, g, dbl, sgl, inp, 1, quant=bd.QUANT_POLICY)
+    _, vg = run_step(s, g, dbl, sgl, inp, 1, quant=bd.QUANT_POLICY, dequant_in_gemm=in_gemm)
     from tests.test_gpu_blocks import dequantised
     _, vr = oracle_step(s, g, [dequantised(d, bd.QUANT_POLICY) for d in dbl],
                         [dequantised(w, bd.QUANT_POLICY) for w in sgl], inp, 1)

@@ -203,6 +203,8 @@ def test_step_ex_errors_before_launch(lib):
     assert call(C.byref(o)) == 1                                            # NULL context latent
     o = bd.mmdit_step_opts(ctx_packed=fake, ctx_len=-1)
     assert call(C.byref(o)) == 2
+    o = bd.mmdit_step_opts(has_guidance=1, guidance=3.5, dequant=2)
+    assert call(C.byref(o)) == 2                                            # unknown dequant route
     # step cache options
     need = bd.mmdit_step_cache_bytes(cfg)
     cache = bd.mmdit_step_cache(buf=fake, bytes=need)
