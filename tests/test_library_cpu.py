@@ -231,6 +231,24 @@ def test_step_cache_bytes(lib):
     assert 2 * s.img_len * s.hidden * 4 + s.img_len * 8 <= n <= 2 * s.img_len * s.hidden * 4 + s.img_len * 8 + 1024
 
 
+def test_dequantise_argument_errors(lib):
+    # checked on the host before any device work (the pointers are never used)
+    w, sc, out = 0x10000, 0x20000, 0x30000
+    call = lambda *a: lib.mmdit_dequantise(*a, None)  # noqa: E731
+    assert call(None, sc, bd.W_Q4G64, 4, 64, out) == 1                  # NULL weights
+    assert call(w, sc, bd.W_Q4G64, 4, 64, None) == 1                    # NULL output
+    assert call(w, sc, bd.W_DENSE, 4, 64, out) == 3                     # not a quantised format
+    assert call(w, sc, 9, 4, 64, out) == 3
+    assert call(w, sc, bd.W_Q8G64, 4, 96, out) == 2                     # k_in not a multiple of 64
+    assert call(w, sc, bd.W_Q1G128, 4, 64, out) == 2                    # sub-byte groups are 128
+    assert call(w, sc, bd.W_TQ2G128, -1, 128, out) == 2                 # negative rows
+    assert call(w + 8, sc, bd.W_Q4G64, 4, 64, out) == 2                 # codes not 16-byte aligned
+    assert call(w + 4, sc, bd.W_TQ2G128, 4, 128, out) == 2              # ternary codes need 8
+    assert call(w, sc + 1, bd.W_Q8G64, 4, 64, out) == 2                 # odd scale address
+    assert call(w, sc, bd.W_Q8G64, 4, 64, out + 8) == 2                 # output not 16-byte aligned
+    assert "aligned" in bd.mmdit_last_error() or "misaligned" in bd.mmdit_last_error()
+
+
 def test_workspace_holds_decoded_weights_from_1024_rows(lib):
     # bf16 at 1024 rows and more: room for the largest launch's weights in
     # bf16 (both streams' fc1 at h 3072, m 12288: 2 * 12288 * 3072 weights)
