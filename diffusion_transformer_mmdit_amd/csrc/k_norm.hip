@@ -65,6 +65,72 @@ __global__ __launch_bounds__(256) void k_adaln_ln(LnArgs a, int rows) {
   }
 }
 
+// One 256-thread block per row when h is a multiple of 1024: each thread
+// holds C = h / 1024 chunks of 4 (chunk i at column 4 (256 i + tid)); shift
+// and scale are requested together with x, before the reductions; the two
+// block reductions go through LDS.
+template <typename TX, typename TY, int C>
+__global__ __launch_bounds__(256) void k_adaln_ln_row(LnArgs a) {
+  __shared__ float red[2][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.x;
+  const int s = r < a.seg_rows[0] ? 0 : 1;
+  const int local = s == 0 ? r : r - a.seg_rows[0];
+  const TX* x = reinterpret_cast<const TX*>(seg_row(a.seg[s], local, sizeof(TX)));
+  const int b = local / a.seg[s].rows_per_batch;
+  const float* mod = a.mod[s] + (int64_t)b * a.mod_bstride;
+  float v[C][4], sh[C][4], sc[C][4];
+#pragma unroll
+  for (int i = 0; i < C; ++i) load4(x + (i * 256 + tid) * 4, v[i]);
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    load4(mod + a.shift_off + (i * 256 + tid) * 4, sh[i]);
+    load4(mod + a.scale_off + (i * 256 + tid) * 4, sc[i]);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < C; ++i) sum += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+  sum = wave_sum(sum);
+  if (lane == 0) red[0][wave] = sum;
+  __syncthreads();
+  const float inv_h = 1.0f / (float)(C * 1024);
+  const float mean = ((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) * inv_h;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < C; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float d = v[i][j] - mean;
+      sq += d * d;
+    }
+  sq = wave_sum(sq);
+  if (lane == 0) red[1][wave] = sq;
+  __syncthreads();
+  const float var = ((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) * inv_h;
+  const float rstd = 1.0f / sqrtf(var + a.eps);
+  TY* y = reinterpret_cast<TY*>(a.y) + (int64_t)r * a.h;
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    float o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = (1.0f + sc[i][j]) * ((v[i][j] - mean) * rstd) + sh[i][j];
+    store4(y + (i * 256 + tid) * 4, o);
+  }
+}
+
+template <int C>
+static void launch_ln_row(const LnArgs& a, int rows, bool x_f32, bool y_bf16, hipStream_t s) {
+  dim3 grid(rows), block(256);
+  if (x_f32 && y_bf16)
+    hipLaunchKernelGGL((k_adaln_ln_row<float, bf16, C>), grid, block, 0, s, a);
+  else if (x_f32)
+    hipLaunchKernelGGL((k_adaln_ln_row<float, float, C>), grid, block, 0, s, a);
+  else if (y_bf16)
+    hipLaunchKernelGGL((k_adaln_ln_row<bf16, bf16, C>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((k_adaln_ln_row<bf16, float, C>), grid, block, 0, s, a);
+}
+
 template <int NC>
 static void launch_ln_nc(const LnArgs& a, int rows, bool x_f32, bool y_bf16, hipStream_t s) {
   dim3 grid((rows + 3) / 4), block(256);
@@ -80,6 +146,15 @@ static void launch_ln_nc(const LnArgs& a, int rows, bool x_f32, bool y_bf16, hip
 
 // h is a multiple of 256 and at most 4096 (checked by the API).
 hipError_t launch_adaln_ln(const LnArgs& a, int rows, bool x_f32, bool y_bf16, hipStream_t s) {
+  if (a.h % 1024 == 0) {
+    switch (a.h / 1024) {
+      case 1: launch_ln_row<1>(a, rows, x_f32, y_bf16, s); break;
+      case 2: launch_ln_row<2>(a, rows, x_f32, y_bf16, s); break;
+      case 3: launch_ln_row<3>(a, rows, x_f32, y_bf16, s); break;
+      default: launch_ln_row<4>(a, rows, x_f32, y_bf16, s); break;
+    }
+    return hipGetLastError();
+  }
   switch (a.h / 256) {
     case 1: launch_ln_nc<1>(a, rows, x_f32, y_bf16, s); break;
     case 2: launch_ln_nc<2>(a, rows, x_f32, y_bf16, s); break;
