@@ -153,7 +153,7 @@ def main():
                     help="first run one plain device copy of this many MiB (calibrates HBM byte counters)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): this build has no multi-GPU path",
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): the library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
 

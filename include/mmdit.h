@@ -46,7 +46,7 @@ typedef enum {
   MMDIT_ERR_SHAPE = 2,       /* sizes inconsistent or out of the supported range */
   MMDIT_ERR_DTYPE = 3,       /* dtype / weight format not valid for this call */
   MMDIT_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
-  MMDIT_ERR_UNSUPPORTED = 5, /* valid request this build does not implement */
+  MMDIT_ERR_UNSUPPORTED = 5, /* valid request the library does not implement */
   MMDIT_ERR_HIP = 6          /* a HIP runtime call failed (detail in mmdit_last_error) */
 } mmdit_status;
 
