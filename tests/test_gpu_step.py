@@ -305,3 +305,51 @@ def test_step_is_deterministic():
     inp = I.step_inputs(s)
     (x1, v1), (x2, v2) = run_step(s, g, dbl, sgl, inp, 0, repeat=2)
     assert np.array_equal(v1, v2) and np.array_equal(x1, x2)
+
+
+def test_step_graph_replays_match_eager():
+    # The step captured into a HIP graph (torch's graph API on a side stream,
+    # as bench.py times it) and replayed three times, with eager copies and
+    # synchronisations between the replays: every replay must give the
+    # eager step's x and v bit for bit (the library issues no memsets, so
+    # the graph holds kernels only).
+    t = torch()
+    s = dataclasses.replace(I.CFG4, n_double=1, n_single=1, txt_len=128, grid_h=32, grid_w=32, cfg_id=52)
+    g, dbl, sgl = model_numpy(s)
+    inp = I.step_inputs(s)
+    dt = dtype_code(s.dtype)
+    cfg = bd.make_config(s)
+    M = bd.ModelW(g, [bd.DoubleW(d, dt, "cuda") for d in dbl], [bd.SingleW(w, dt, "cuda") for w in sgl], dt, "cuda")
+    mc = M.c()
+    X0 = t.empty((s.batch, s.img_len, s.in_ch), dtype=t.float32, device="cuda")
+    bd.mmdit_pack_latents(t.from_numpy(inp["z"]).cuda(), X0)
+    ids = up_i32(bd.mmdit_make_ids(s.grid_h, s.grid_w, s.txt_len))
+    sig = bd.mmdit_schedule(4, s.img_len)
+    T = up(inp["T"], s.dtype)
+    y = up(inp["y"], s.dtype)
+    ws = workspace(bd.mmdit_step_workspace(cfg))
+    X = X0.clone()
+    v = t.empty_like(X)
+    print("eager step", flush=True)
+    bd.mmdit_step(cfg, mc, X, v, T, y, ids, sig[1], sig[2], ws)
+    sync()
+    x_ref, v_ref = down(X), down(v)
+    X.copy_(X0)
+    v.zero_()
+    sync()
+    print("capturing the step", flush=True)
+    gr = t.cuda.CUDAGraph()
+    cap = t.cuda.Stream()
+    cap.wait_stream(t.cuda.current_stream())
+    with t.cuda.graph(gr, stream=cap):
+        bd.mmdit_step(cfg, mc, X, v, T, y, ids, sig[1], sig[2], ws)
+    sync()
+    for k in range(3):
+        X.copy_(X0)
+        v.fill_(float("nan"))
+        sync()
+        print(f"replay {k}", flush=True)
+        gr.replay()
+        sync()
+        assert np.array_equal(down(X), x_ref), f"replay {k}: x differs"
+        assert np.array_equal(down(v), v_ref), f"replay {k}: v differs"
