@@ -174,6 +174,23 @@ def test_blocks_bf16_ragged(txt_len, gh, gw, batch):
     assert_parity(run_single(s, ws_, x, ids), oracle_single(s, ws_, x, ids), "bf16", "ragged single")
 
 
+def test_blocks_bf16_max_width():
+    # the widest model the library takes: h 4096 (32 heads), MLP 16384, with
+    # 40 text + 12x13 image tokens (the LayerNorm's four chunks per thread,
+    # 4096-wide modulation GEMVs)
+    s = I.Shape(hidden=4096, heads=32, mlp_hidden=16384, txt_len=40, grid_h=12, grid_w=13, dtype="bf16",
+                cfg_id=53)
+    w = I.double_block_weights(s, 0)
+    x = I.block_inputs(s)
+    ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
+    img, txt = run_double(s, w, x, ids)
+    rimg, rtxt = oracle_double(s, w, x, ids)
+    assert_parity(img, rimg, "bf16", "max-width img")
+    assert_parity(txt, rtxt, "bf16", "max-width txt")
+    ws_ = I.single_block_weights(s, 0)
+    assert_parity(run_single(s, ws_, x, ids), oracle_single(s, ws_, x, ids), "bf16", "max-width single")
+
+
 @pytest.fixture(scope="module")
 def cfg3():
     s = I.CFG3
