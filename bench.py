@@ -110,6 +110,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def lin1_clock():
+    """Sustained shader clock (GHz) of the linear1 GEMM from the committed
+    GRBM_GUI_ACTIVE pass, or None when the kernel's sources have changed."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        rec = json.load(open(os.path.join(here, "profiles", "gemm_lin1_clock.json")))
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(here, "diffusion_transformer_mmdit_amd", "csrc", src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None
+        return float(rec["clock_ghz"]), float(rec["max_clock_ghz"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(s):
     """The oracle on the host cores: one dual and one single block at the
     full 4608-token size (config-3 weights), scaled to 19 + 38 blocks."""
@@ -133,7 +151,23 @@ def cpu_baseline(s):
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
     est_ms = 1e3 * (s.n_double * t_dual + s.n_single * t_single)
+    # one core: one dual block at 1280 tokens (256 text + 32x32 image)
+    s2 = I.CFG2
+    x2 = I.block_inputs(s2)
+    w2 = I.double_block_weights(s2, 0)
+    ids2 = oracle.make_ids(s2.grid_h, s2.grid_w, s2.txt_len)
+    with threadpoolctl.threadpool_limits(1):
+        t0 = time.perf_counter()
+        oracle.double_block(w2, x2["x_img"], x2["x_txt"], x2["vec"], ids2, s2.heads)
+        t_one = time.perf_counter() - t0
+        one_threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
+                           if i.get("user_api") == "blas"] or [1])
+    flops2 = block_flops(s2)
+    one_core = {"block": "dual, 256 text + 1024 image tokens, h 3072", "blas_threads": int(one_threads),
+                "seconds": round(t_one, 2),
+                "gflops": round(flops2 / t_one / 1e9, 1)}
     return {"value": round(est_ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
+            "gflops": round(step_flops(s) / (est_ms * 1e-3) / 1e9, 1), "one_core": one_core,
             "sample": (f"numpy float32 oracle, 1 dual block ({t_dual:.2f} s) + 1 single block ({t_single:.2f} s) "
                        f"at 4608 tokens, scaled to {s.n_double}+{s.n_single} blocks; BLAS "
                        f"{info[0].get('internal_api', '?') if info else '?'}, affinity "
@@ -215,6 +249,27 @@ def main():
     torch.cuda.synchronize()
     ms = timed(step, a.steps)
     log(f"step: {ms:.2f} ms")
+    # spread: each of a.steps further steps timed alone with events on the stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        step(i)
+        e1.record()
+    torch.cuda.synchronize()
+    per = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    spread = {"median": round(float(np.median(per)), 3), "p10": round(float(np.percentile(per, 10)), 3),
+              "p90": round(float(np.percentile(per, 90)), 3), "n": int(per.size)}
+    log(f"step spread: median {spread['median']:.2f} ms, p10 {spread['p10']:.2f}, p90 {spread['p90']:.2f}")
+    # the 4-step loop of the schedule, from the same latent each time
+    X0 = X.clone()
+
+    def loop4(_):
+        X.copy_(X0)
+        for j in range(4):
+            step(j)
+    loop4(0)
+    loop_ms = timed(loop4, max(2, a.steps // 4))
+    log(f"4-step loop: {loop_ms:.2f} ms")
     flops = step_flops(s)
 
     # roofline of the dominant kernels, timed with HIP events around each launch
@@ -247,6 +302,11 @@ def main():
                 "RMSNorm + RoPE (single-block linear1, M 4608 N 21504 K 3072)", "achieved": round(p["tflops"], 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "avg_launch_us": round(p["avg_us"], 2), "flops_per_launch": p["flops"] / max(p["launches"], 1)}
+    clk = lin1_clock()
+    if clk:
+        pk = PEAK_BF16_TFLOPS * clk[0] / clk[1]
+        roofline.update({"clock_ghz_measured": clk[0], "peak_at_measured_clock": round(pk, 1),
+                         "frac_at_measured_clock": round(p["tflops"] / pk, 4)})
 
     out = {"metric": METRIC, "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": a.steps,
            "warmup": a.warmup, "ms_per_step": round(ms, 3), "higher_is_better": False, "scaling": "weak",
@@ -255,6 +315,9 @@ def main():
                                   "hidden 3072, 24x128 heads, MLP 12288, 4096 image + 512 text tokens, batch 1",
                       "global_batch": 1, "seq_len": s.seq_len, "image_tokens": s.img_len, "text_tokens": s.txt_len,
                       "parallelism": "single GPU"},
+           "step_spread_ms": spread, "loop_4_steps_ms": round(loop_ms, 3),
+           "device": {"name": torch.cuda.get_device_name(0), "hip": torch.version.hip,
+                      "torch": torch.__version__},
            "step_tflops": round(flops / ms / 1e9, 1),
            "step_frac_of_bf16_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
            "roofline": roofline,
