@@ -191,6 +191,23 @@ def test_blocks_bf16_max_width():
     assert_parity(run_single(s, ws_, x, ids), oracle_single(s, ws_, x, ids), "bf16", "max-width single")
 
 
+def test_blocks_bf16_reference_image_length():
+    # the reference-image sequence at its full length: 512 text + 4096
+    # generated + 4096 context tokens (L 8704; the context rows carry frame
+    # id 1), dual and single blocks against the oracle on every output
+    s = I.Shape(txt_len=512, grid_h=64, grid_w=128, dtype="bf16", cfg_id=54)
+    x = I.block_inputs(s)
+    ids = np.concatenate([oracle.make_ids(64, 64, 512), oracle.make_ids(64, 64, 0, frame=1)])
+    w = I.double_block_weights(s, 0)
+    img, txt = run_double(s, w, x, ids)
+    rimg, rtxt = oracle_double(s, w, x, ids)
+    assert_parity(img, rimg, "bf16", "L 8704 dual img")
+    assert_parity(txt, rtxt, "bf16", "L 8704 dual txt")
+    del w, rimg, rtxt
+    ws_ = I.single_block_weights(s, 0)
+    assert_parity(run_single(s, ws_, x, ids), oracle_single(s, ws_, x, ids), "bf16", "L 8704 single")
+
+
 @pytest.fixture(scope="module")
 def cfg3():
     s = I.CFG3
