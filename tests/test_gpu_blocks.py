@@ -100,6 +100,22 @@ def test_single_block_cfg1_f32():
     assert_parity(run_single(s, w, x, ids), oracle_single(s, w, x, ids), "f32", "cfg1 single")
 
 
+def test_blocks_f32_width1024():
+    # float32 at h 1024 (8 heads): the LayerNorm takes its one-block-per-row
+    # form (h a multiple of 1024) with float32 input and output
+    s = I.Shape(hidden=1024, heads=8, mlp_hidden=2048, txt_len=24, grid_h=6, grid_w=7, batch=2, dtype="f32",
+                cfg_id=55)
+    w = I.double_block_weights(s, 0)
+    x = I.block_inputs(s)
+    ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
+    img, txt = run_double(s, w, x, ids)
+    rimg, rtxt = oracle_double(s, w, x, ids)
+    assert_parity(img, rimg, "f32", "h 1024 img")
+    assert_parity(txt, rtxt, "f32", "h 1024 txt")
+    ws_ = I.single_block_weights(s, 0)
+    assert_parity(run_single(s, ws_, x, ids), oracle_single(s, ws_, x, ids), "f32", "h 1024 single")
+
+
 @pytest.mark.parametrize("txt_len,gh,gw,batch", [(0, 5, 7, 1), (13, 9, 11, 2), (130, 3, 3, 1)])
 def test_blocks_f32_ragged(txt_len, gh, gw, batch):
     s = I.Shape(hidden=256, heads=2, mlp_hidden=320, txt_len=txt_len, grid_h=gh, grid_w=gw, batch=batch,
