@@ -39,12 +39,16 @@ int fail(int code, const char* fmt, ...) {
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ------------------------------------------------------------------ profiling --
+// Kernel timing (mmdit_profile_begin/end). Every access to the state holds
+// the mutex; `gen` tells a scope whose profiling session has since ended not
+// to record its stop event (its launch is then not counted).
 struct Prof {
   std::mutex mu;
   bool active = false;
   int cls = 0;
   int cap = 0;
   int used = 0;
+  uint64_t gen = 0;
   double work = 0;
   std::vector<hipEvent_t> ev;
 };
@@ -55,17 +59,22 @@ enum { PC_GEMM = 1, PC_ATTN = 2, PC_LN = 3, PC_QKNORM = 4, PC_GEMV = 5, PC_GEMM_
 struct ProfScope {
   hipEvent_t stop = nullptr;
   hipStream_t s;
+  uint64_t gen = 0;
   // records when the active class is `cls` or `cls2`
   ProfScope(int cls, double work, hipStream_t st, int cls2 = -1) : s(st) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
     if (!g_prof.active || (g_prof.cls != cls && g_prof.cls != cls2) || g_prof.used >= g_prof.cap) return;
     hipEvent_t start = g_prof.ev[2 * g_prof.used];
     stop = g_prof.ev[2 * g_prof.used + 1];
+    gen = g_prof.gen;
     g_prof.used++;
     g_prof.work += work;
     (void)hipEventRecord(start, s);
   }
   ~ProfScope() {
-    if (stop) (void)hipEventRecord(stop, s);
+    if (!stop) return;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (g_prof.active && g_prof.gen == gen) (void)hipEventRecord(stop, s);
   }
 };
 
@@ -947,6 +956,7 @@ int mmdit_profile_begin(int32_t kernel_class, int32_t max_launches) {
   for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
   g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
   for (auto& e : g_prof.ev) HIP_TRY(hipEventCreate(&e));
+  g_prof.gen++;
   g_prof.cls = kernel_class;
   g_prof.cap = max_launches;
   g_prof.used = 0;

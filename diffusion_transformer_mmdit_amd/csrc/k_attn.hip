@@ -374,12 +374,9 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s) {
   if ((int64_t)a.Lpad * 128 * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int units = attn_qblocks(a) * a.H * a.B;
   const size_t lds = 2 * kStage;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_attn_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = ensure_lds_limit((const void*)k_attn_bf16, (int)lds, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_bf16, dim3(units), dim3(64 * kAttnWaves), lds, s, a);
   return hipGetLastError();
 }

@@ -231,9 +231,13 @@ static hipError_t launch_epi_fmt(const GemmProblem* p, int nprob, hipStream_t s)
   return launch_cfg<128, 128, 2, 2, EPI, FMT>(p, nprob, s);
 }
 
+// One weight format per launch: the format of the first problem with rows
+// (a problem without rows launches no tiles, whatever its format).
 template <int EPI>
 static hipError_t launch_epi(const GemmProblem* p, int nprob, hipStream_t s) {
-  switch (p[0].fmt) {
+  int fmt = p[0].fmt;
+  if (nprob > 1 && p[0].M == 0) fmt = p[1].fmt;
+  switch (fmt) {
     case 0: return launch_epi_fmt<EPI, 0>(p, nprob, s);
     case 1: return launch_epi_fmt<EPI, 1>(p, nprob, s);
     case 3: return launch_epi_fmt<EPI, 3>(p, nprob, s);
@@ -243,12 +247,18 @@ static hipError_t launch_epi(const GemmProblem* p, int nprob, hipStream_t s) {
 }
 
 hipError_t launch_gemm_bf16(const GemmProblem* p, int nprob, int epi, hipStream_t s) {
+  // problems with rows in different weight formats (e.g. a dense text stream
+  // beside a quantised image stream) run as one launch each
+  if (nprob == 2 && p[0].M > 0 && p[1].M > 0 && p[0].fmt != p[1].fmt) {
+    const hipError_t e = launch_gemm_bf16(p, 1, epi, s);
+    return e != hipSuccess ? e : launch_gemm_bf16(p + 1, 1, epi, s);
+  }
   switch (epi) {
     case EPI_STORE: return launch_epi<EPI_STORE>(p, nprob, s);
     case EPI_GELU: return launch_epi<EPI_GELU>(p, nprob, s);
     case EPI_GATE_RES: return launch_epi<EPI_GATE_RES>(p, nprob, s);
     case EPI_SPLIT: return launch_epi<EPI_SPLIT>(p, nprob, s);
-    case EPI_EULER: return launch_epi_fmt<EPI_EULER, 0>(p, nprob, s);
+    case EPI_EULER: return launch_epi<EPI_EULER>(p, nprob, s);
     default: return hipErrorInvalidValue;  // fused QK epilogues: direct-to-LDS kernel only
   }
 }

@@ -815,13 +815,9 @@ static hipError_t launch_dma_epi(const GemmProblem* p, int nprob, hipStream_t s)
   }
   if (total == 0) return hipSuccess;
   const size_t lds = (size_t)S * 2 * kDBM * BK * 2;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_dma<EPI, BK, S, CPOL, FMT, DS, W>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = ensure_lds_limit((const void*)k_gemm_dma<EPI, BK, S, CPOL, FMT, DS, W>, (int)lds, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gemm_dma<EPI, BK, S, CPOL, FMT, DS, W>), dim3(total), dim3(64 * W), lds, s, gb);
   return hipGetLastError();
 }

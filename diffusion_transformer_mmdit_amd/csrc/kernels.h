@@ -5,7 +5,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace mmdit {
+
+// Raises the dynamic-LDS limit of kernel `fn` to `bytes` on the current
+// device, once per device (`done` holds one bit per device id). Safe to call
+// from several threads: a thread that races another repeats the call, which
+// is harmless.
+inline hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t(1) << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  done.fetch_or(bit, std::memory_order_release);
+  return hipSuccess;
+}
 
 // A set of activation rows split in up to two segments (text rows, then
 // image rows). Row r of segment s belongs to batch r / rows_per_batch and

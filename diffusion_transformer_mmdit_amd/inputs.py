@@ -207,6 +207,32 @@ def zero_modulation(w: Dict) -> Dict:
     return w
 
 
+def attention_only(w: Dict) -> Dict:
+    """Copy of block weights whose output minus input is the attention
+    branch alone, linear in the attention output O:
+      dual stream: gate2 rows of the modulation zero (rows 5h..6h of mod_w
+        and mod_b), out-projection bias zero, so x_out - x_in = gate1 * O W_proj^T;
+      single: the MLP columns of linear2 (h..h+m) and its bias zero, so
+        x_out - x_in = gate * O W_2[:, :h]^T."""
+    if "txt" in w:
+        return {k: attention_only(v) for k, v in w.items()}
+    w = dict(w)
+    if "proj_w" in w:
+        h = w["proj_w"].shape[0]
+        for n in ("mod_w", "mod_b"):
+            a = w[n].copy()
+            a[5 * h:] = 0
+            w[n] = a
+        w["proj_b"] = np.zeros_like(w["proj_b"])
+    else:
+        h = w["lin2_w"].shape[0]
+        a = w["lin2_w"].copy()
+        a[:, h:] = 0
+        w["lin2_w"] = a
+        w["lin2_b"] = np.zeros_like(w["lin2_b"])
+    return w
+
+
 class LazyBlocks:
     """Sequence of block weights generated on access (one block in memory)."""
 

@@ -297,7 +297,13 @@ int mmdit_unpack_latents(const void* x, void* z, int32_t B, int32_t C, int32_t H
                          int32_t elem_bytes, void* hip_stream);
 
 /* Device, async. RoPE table [L, sum(axes)/2, 2] float32 (cos, sin) for ids
- * [L, 3], angles evaluated in float64; the blocks build the same table. */
+ * [L, 3] (mflux-rs, card "3D RoPE Coordinates" and its RoPE visualiser: the
+ * head dimension split over the (frame, row, column) axes, here axes_dim).
+ * Pair j of axis a turns by ids[:, a] * theta^(-2j / axes_dim[a]); the pairs
+ * run axis 0, then 1, then 2. Angles are evaluated in float64 and stored as
+ * float32; the blocks build the same table. ids and table are device
+ * arrays, axes_dim a host array of 3. Errors: MMDIT_ERR_NULL,
+ * MMDIT_ERR_SHAPE (L < 0, odd or negative axes, theta <= 0), MMDIT_ERR_HIP. */
 int mmdit_rope_table(const int32_t* ids, int32_t L, const int32_t* axes_dim, double theta,
                      float* table, void* hip_stream);
 
@@ -342,7 +348,9 @@ int mmdit_dequantise(const void* w, const void* scales, int32_t fmt, int32_t n_o
  * mmdit_profile_begin creates up to max_launches event pairs (host call, no
  * device allocation). mmdit_profile_end waits for the recorded events and
  * returns the summed kernel time, the launch count and the summed algorithmic
- * FLOPs (classes 1, 2, 6, 7) or bytes (classes 3-5, 8) of those launches. */
+ * FLOPs (classes 1, 2, 6, 7) or bytes (classes 3-5, 8) of those launches.
+ * Thread-safe; a launch whose call is still in progress when
+ * mmdit_profile_end runs on another thread is not counted. */
 int mmdit_profile_begin(int32_t kernel_class, int32_t max_launches);
 int mmdit_profile_end(double* total_ms, int32_t* launches, double* work);
 

@@ -353,3 +353,33 @@ def test_step_graph_replays_match_eager():
         sync()
         assert np.array_equal(down(X), x_ref), f"replay {k}: x differs"
         assert np.array_equal(down(v), v_ref), f"replay {k}: v differs"
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_step_quantised_final_layer(bits):
+    # the final projection (h -> 64, fused Euler update) held as group-quantised
+    # codes: the Euler epilogue dequantises its weight tiles like the others
+    s = dataclasses.replace(I.CFG4, hidden=512, heads=4, mlp_hidden=1024, txt_len=24, grid_h=8, grid_w=8,
+                            n_double=1, n_single=1, txt_in_dim=256, vec_in_dim=256, cfg_id=58)
+    g, dbl, sgl = model_numpy(s)
+    inp = I.step_inputs(s)
+    t = torch()
+    cfg = bd.make_config(s)
+    M = bd.ModelW(g, [bd.DoubleW(d, bd.BF16, "cuda") for d in dbl], [bd.SingleW(w, bd.BF16, "cuda") for w in sgl],
+                  bd.BF16, "cuda")
+    M.final_lin = bd.Linear.from_numpy(g["final_w"], g["final_b"], bd.BF16, "cuda", bits)
+    X = t.from_numpy(oracle.pack_latents(inp["z"])).cuda()
+    v = t.empty_like(X)
+    ids = bd.mmdit_make_ids(s.grid_h, s.grid_w, s.txt_len)
+    sig = bd.mmdit_schedule(4, s.img_len)
+    ws = workspace(bd.mmdit_step_workspace(cfg))
+    print(f"step with a {bits}-bit final layer", flush=True)
+    bd.mmdit_step(cfg, M.c(), X, v, up(inp["T"], "bf16"), up(inp["y"], "bf16"), up_i32(ids), sig[0], sig[1], ws)
+    sync()
+    q, sc = oracle.quantise(g["final_w"], bits)
+    go = dict(g)
+    go["final_w"] = oracle.dequantise(q, sc)
+    Xr, vr = oracle.step(go, dbl, sgl, oracle.pack_latents(inp["z"]), inp["T"], inp["y"], ids, sig[0], sig[1],
+                         s.heads, s.axes_dim, s.theta)
+    assert_parity(down(v), vr, "bf16", f"{bits}-bit final layer: v")
+    assert_parity(down(X), Xr, "bf16", f"{bits}-bit final layer: x_next")

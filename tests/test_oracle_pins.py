@@ -727,3 +727,19 @@ def test_bf16_rounding_is_round_to_nearest_even():
     r = I.round_bf16(vals)
     t = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float32).numpy()
     assert np.array_equal(r, t)
+
+
+def test_oracle_bf16_rne_equals_an_exact_cast():
+    # oracle.bf16_rne against torch's float32 -> bfloat16 conversion (round to
+    # nearest, ties to even): ties in both directions, the largest finite
+    # values, subnormals, signed zeros and random bit patterns
+    rng = np.random.default_rng(26)
+    special = np.array([1.0 + 2**-8, 1.0 + 3 * 2**-8, 1.0 + 2**-9, -(1.0 + 2**-8), 3.0e-3, 0.0, -0.0,
+                        1e-40, -1e-40, 3.3895e38, -3.3895e38, 2**-126, 65504.0], np.float32)
+    bits = rng.integers(0, 2**32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    rand = bits.view(np.float32)
+    rand = rand[np.isfinite(rand) & (np.abs(rand) < 3.38e38)]
+    for vals in (special, rand):
+        got = oracle.bf16_rne(vals)
+        want = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float32).numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
