@@ -17,6 +17,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmmdit.s
 _lib = None
 
 F32, BF16 = 0, 1
+RESID_DEFAULT, RESID_F32, RESID_BF16 = 0, 1, 2
 W_DENSE, W_Q4G64, W_Q8G64, W_Q1G128, W_TQ2G128 = 0, 1, 2, 3, 4
 PC_GEMM, PC_ATTN, PC_LN, PC_QKNORM, PC_GEMV, PC_GEMM_LIN1, PC_GEMM_RES, PC_DEQUANT = 1, 2, 3, 4, 5, 6, 7, 8
 
@@ -34,7 +35,7 @@ class mmdit_dims(C.Structure):
     _fields_ = [("batch", C.c_int32), ("hidden", C.c_int32), ("heads", C.c_int32),
                 ("head_dim", C.c_int32), ("mlp_hidden", C.c_int32), ("txt_len", C.c_int32),
                 ("img_len", C.c_int32), ("axes_dim", C.c_int32 * 3), ("theta", C.c_double),
-                ("ln_eps", C.c_float), ("rms_eps", C.c_float), ("act_dtype", C.c_int32)]
+                ("ln_eps", C.c_float), ("rms_eps", C.c_float), ("act_dtype", C.c_int32), ("resid", C.c_int32)]
 
 
 class mmdit_linear(C.Structure):
@@ -89,6 +90,8 @@ _SIGS = {
     "mmdit_single_block_workspace": (C.c_int, [C.POINTER(mmdit_dims), C.POINTER(C.c_size_t)]),
     "mmdit_step_workspace": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(C.c_size_t)]),
     "mmdit_step_cache_bytes": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(C.c_size_t)]),
+    "mmdit_step_workspace_ex": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(mmdit_model_w),
+                                          C.POINTER(mmdit_step_opts), C.POINTER(C.c_size_t)]),
     "mmdit_double_block_fwd": (C.c_int, [C.POINTER(mmdit_dims), C.POINTER(mmdit_double_w), _P, _P, _P, _P,
                                          _P, _P, _P, C.c_size_t, _P]),
     "mmdit_single_block_fwd": (C.c_int, [C.POINTER(mmdit_dims), C.POINTER(mmdit_single_w), _P, _P, _P, _P,
@@ -268,9 +271,10 @@ class ModelW:
                              C.cast(self._sgl_arr, C.POINTER(mmdit_single_w)), *gl)
 
 
-def make_dims(s, dtype: Optional[int] = None) -> mmdit_dims:
+def make_dims(s, dtype: Optional[int] = None, resid: int = RESID_DEFAULT) -> mmdit_dims:
     """mmdit_dims from an inputs.Shape."""
     d = mmdit_dims()
+    d.resid = resid
     d.batch, d.hidden, d.heads, d.head_dim = s.batch, s.hidden, s.heads, s.head_dim
     d.mlp_hidden, d.txt_len, d.img_len = s.mlp_hidden, s.txt_len, s.img_len
     d.axes_dim = (C.c_int32 * 3)(*s.axes_dim)
@@ -279,9 +283,9 @@ def make_dims(s, dtype: Optional[int] = None) -> mmdit_dims:
     return d
 
 
-def make_config(s, dtype: Optional[int] = None) -> mmdit_config:
+def make_config(s, dtype: Optional[int] = None, resid: int = RESID_DEFAULT) -> mmdit_config:
     c = mmdit_config()
-    c.dims = make_dims(s, dtype)
+    c.dims = make_dims(s, dtype, resid)
     c.n_double, c.n_single = s.n_double, s.n_single
     c.in_ch, c.txt_in_dim, c.vec_in_dim, c.temb_dim = s.in_ch, s.txt_in_dim, s.vec_in_dim, s.temb_dim
     return c
@@ -326,6 +330,17 @@ def mmdit_step(cfg, w: mmdit_model_w, x_packed, v_out, txt_emb, y, ids, sigma: f
                             _ptr(ids), float(sigma), float(sigma_next), _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream)),
            "mmdit_step")
+
+
+def mmdit_step_workspace_ex(cfg: mmdit_config, w: mmdit_model_w, dequant_in_gemm: bool = False) -> int:
+    """Workspace bytes of mmdit_step_ex for these weights (no room for decoded
+    weights when no layer is decoded)."""
+    o = mmdit_step_opts()
+    o.dequant = 1 if dequant_in_gemm else 0
+    n = C.c_size_t()
+    _check(lib().mmdit_step_workspace_ex(C.byref(cfg), C.byref(w), C.byref(o), C.byref(n)),
+           "mmdit_step_workspace_ex")
+    return n.value
 
 
 def mmdit_step_cache_bytes(cfg: mmdit_config) -> int:

@@ -12,15 +12,16 @@
 #include <vector>
 
 #include "../../include/mmdit.h"
+#include "api_internal.h"
 #include "kernels.h"
 
 using namespace mmdit;
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
 
-int fail(int code, const char* fmt, ...) {
+int mmdit::fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -29,6 +30,8 @@ int fail(int code, const char* fmt, ...) {
   g_err = buf;
   return code;
 }
+
+namespace {
 
 #define HIP_TRY(expr)                                                                  \
   do {                                                                                 \
@@ -83,6 +86,7 @@ struct Geo {
   int B, h, H, m, Lt, Li, L, Lpad;
   bool bf16;
   int esz;
+  int resid;  // mmdit_dims.resid (MMDIT_RESID_*)
 };
 
 int check_dims(const mmdit_dims* d, Geo& g) {
@@ -103,11 +107,16 @@ int check_dims(const mmdit_dims* d, Geo& g) {
   }
   if (sum != d->head_dim) return fail(MMDIT_ERR_SHAPE, "axes_dim sum %d != head_dim", sum);
   if (!(d->theta > 0) || !(d->ln_eps > 0) || !(d->rms_eps > 0)) return fail(MMDIT_ERR_SHAPE, "theta and eps must be > 0");
+  if (d->resid != MMDIT_RESID_DEFAULT && d->resid != MMDIT_RESID_F32 && d->resid != MMDIT_RESID_BF16)
+    return fail(MMDIT_ERR_DTYPE, "resid %d is not one of MMDIT_RESID_DEFAULT, _F32, _BF16", d->resid);
+  if (d->resid == MMDIT_RESID_BF16 && d->act_dtype != MMDIT_BF16)
+    return fail(MMDIT_ERR_DTYPE, "a bf16 residual stream needs bf16 activations");
   g.B = d->batch; g.h = d->hidden; g.H = d->heads; g.m = d->mlp_hidden;
   g.Lt = d->txt_len; g.Li = d->img_len; g.L = g.Lt + g.Li;
   g.Lpad = (g.L + 127) / 128 * 128;
   g.bf16 = d->act_dtype == MMDIT_BF16;
   g.esz = g.bf16 ? 2 : 4;
+  g.resid = d->resid;
   const int64_t widest = 3 * (int64_t)g.h + g.m;
   if ((int64_t)g.B * g.Lpad * widest >= (int64_t(1) << 31) || (int64_t)g.B * g.H * g.Lpad * 128 >= (int64_t(1) << 31))
     return fail(MMDIT_ERR_SHAPE, "batch * tokens too large for 32-bit row indexing");
@@ -220,12 +229,14 @@ struct BlockCallWs {
   BlockWs blk;
 };
 
-BlockCallWs plan_block_call(const Geo& g, int mod_width) {
+// xw: room for decoded weights (needed only when a quantised layer is
+// decoded, see kExpandMinRows; the queries without weights assume it is).
+BlockCallWs plan_block_call(const Geo& g, int mod_width, bool xw = true) {
   BlockCallWs w;
   size_t at = 0;
   w.table = at; at = align_up(at + (size_t)g.L * 64 * 2 * 4);
   w.mod = at; at = align_up(at + (size_t)g.B * mod_width * 4);
-  w.blk = plan_block(g, at, expand_bytes(g, block_launch_weights(g)));
+  w.blk = plan_block(g, at, xw ? expand_bytes(g, block_launch_weights(g)) : 0);
   return w;
 }
 
@@ -236,11 +247,14 @@ struct StepWs {
   size_t mod_dual, mod_single, mod_final;  // offsets inside mods (floats)
 };
 
-StepWs plan_step(const mmdit_config* c, const Geo& g) {
+// Residual bytes per element inside mmdit_step.
+int step_resid_esz(const Geo& g) { return g.resid == MMDIT_RESID_BF16 ? 2 : 4; }
+
+StepWs plan_step(const mmdit_config* c, const Geo& g, bool xw = true) {
   StepWs w;
   size_t at = 0;
   const size_t B = g.B;
-  w.x = at; at = align_up(at + B * g.L * g.h * 4);
+  w.x = at; at = align_up(at + B * g.L * g.h * step_resid_esz(g));
   w.vec = at; at = align_up(at + B * g.h * 4);
   w.temb = at; at = align_up(at + B * c->temb_dim * 4);
   w.hid = at; at = align_up(at + B * g.h * 4);
@@ -254,8 +268,24 @@ StepWs plan_step(const mmdit_config* c, const Geo& g) {
   size_t nk = block_launch_weights(g);
   const size_t nk_io = (size_t)g.h * (c->txt_in_dim > c->in_ch ? c->txt_in_dim : c->in_ch);
   nk = nk > nk_io ? nk : nk_io;
-  w.blk = plan_block(g, at, expand_bytes(g, nk));
+  w.blk = plan_block(g, at, xw ? expand_bytes(g, nk) : 0);
   return w;
+}
+
+bool is_quantised(const mmdit_linear& l) { return l.fmt != MMDIT_W_DENSE; }
+bool stream_quantised(const mmdit_stream_w& s) {
+  return is_quantised(s.qkv) || is_quantised(s.proj) || is_quantised(s.fc1) || is_quantised(s.fc2);
+}
+bool single_quantised(const mmdit_single_w& s) { return is_quantised(s.lin1) || is_quantised(s.lin2); }
+
+// Whether a step with these weights decodes a quantised layer into the
+// workspace (automatic route, at least kExpandMinRows rows).
+bool step_decodes(const mmdit_config* c, const mmdit_model_w* w, const mmdit_step_opts* o, const Geo& g) {
+  if (!g.bf16 || (o && o->dequant == 1) || (int64_t)g.B * g.L < kExpandMinRows) return false;
+  bool q = is_quantised(w->img_in) || is_quantised(w->txt_in) || is_quantised(w->final_lin);
+  for (int i = 0; i < c->n_double && !q; ++i) q = stream_quantised(w->dbl[i].txt) || stream_quantised(w->dbl[i].img);
+  for (int i = 0; i < c->n_single && !q; ++i) q = single_quantised(w->sgl[i]);
+  return q;
 }
 
 // --------------------------------------------------------------- launches --
@@ -566,7 +596,8 @@ int mmdit_double_block_fwd(const mmdit_dims* dims, const mmdit_double_w* w, cons
   if (g.Lt > 0 && (!txt_in || !txt_out)) return fail(MMDIT_ERR_NULL, "NULL text buffers with txt_len > 0");
   if ((r = check_stream(w->txt, g, "txt"))) return r;
   if ((r = check_stream(w->img, g, "img"))) return r;
-  const BlockCallWs lay = plan_block_call(g, 2 * 6 * g.h);
+  const bool xw = stream_quantised(w->txt) || stream_quantised(w->img);
+  const BlockCallWs lay = plan_block_call(g, 2 * 6 * g.h, xw);
   if (!ws || ws_bytes < lay.blk.total)
     return fail(MMDIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, lay.blk.total);
   Ctx c{(hipStream_t)hip_stream, g, dims->ln_eps, dims->rms_eps};
@@ -582,11 +613,13 @@ int mmdit_double_block_fwd(const mmdit_dims* dims, const mmdit_double_w* w, cons
   Part parts[2];
   void* tin = const_cast<void*>(txt_in ? txt_in : img_in);
   void* tout = txt_out ? txt_out : img_out;
-  parts[0] = {g.Lt, 0, rows_of(tin, 0, g.Lt, g.h, g.esz), rows_of(tout, 0, g.Lt, g.h, g.esz), mod_txt};
-  parts[1] = {g.Li, (int64_t)g.B * g.Lt, rows_of(const_cast<void*>(img_in), 0, g.Li, g.h, g.esz),
-              rows_of(img_out, 0, g.Li, g.h, g.esz), mod_img};
+  const bool rf = g.resid == MMDIT_RESID_F32;
+  const int re = rf ? 4 : g.esz;
+  parts[0] = {g.Lt, 0, rows_of(tin, 0, g.Lt, g.h, re), rows_of(tout, 0, g.Lt, g.h, re), mod_txt};
+  parts[1] = {g.Li, (int64_t)g.B * g.Lt, rows_of(const_cast<void*>(img_in), 0, g.Li, g.h, re),
+              rows_of(img_out, 0, g.Li, g.h, re), mod_img};
   const mmdit_stream_w* sw[2] = {&w->txt, &w->img};
-  return run_double(c, sw, parts, false, table, ws, lay.blk);
+  return run_double(c, sw, parts, rf, table, ws, lay.blk);
 }
 
 int mmdit_single_block_fwd(const mmdit_dims* dims, const mmdit_single_w* w, const void* x_in,
@@ -597,7 +630,7 @@ int mmdit_single_block_fwd(const mmdit_dims* dims, const mmdit_single_w* w, cons
   if ((r = check_dims(dims, g))) return r;
   if (!w || !x_in || !x_out || !vec || !ids) return fail(MMDIT_ERR_NULL, "NULL weights, x, vec or ids");
   if ((r = check_single(*w, g))) return r;
-  const BlockCallWs lay = plan_block_call(g, 3 * g.h);
+  const BlockCallWs lay = plan_block_call(g, 3 * g.h, single_quantised(*w));
   if (!ws || ws_bytes < lay.blk.total)
     return fail(MMDIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, lay.blk.total);
   Ctx c{(hipStream_t)hip_stream, g, dims->ln_eps, dims->rms_eps};
@@ -607,8 +640,10 @@ int mmdit_single_block_fwd(const mmdit_dims* dims, const mmdit_single_w* w, cons
   float* mod = (float*)ptr(ws, lay.mod);
   if ((r = rope(c, dims, ids, table))) return r;
   if ((r = gemv(c, w->mod, vec, false, g.h, mod, 3 * g.h, true, false))) return r;
-  Part part = {g.L, 0, rows_of(const_cast<void*>(x_in), 0, g.L, g.h, g.esz), rows_of(x_out, 0, g.L, g.h, g.esz), mod};
-  return run_single(c, *w, &part, 1, false, table, ws, lay.blk);
+  const bool rf = g.resid == MMDIT_RESID_F32;
+  const int re = rf ? 4 : g.esz;
+  Part part = {g.L, 0, rows_of(const_cast<void*>(x_in), 0, g.L, g.h, re), rows_of(x_out, 0, g.L, g.h, re), mod};
+  return run_single(c, *w, &part, 1, rf, table, ws, lay.blk);
 }
 
 static int check_config(const mmdit_config* cfg, Geo& g) {
@@ -647,6 +682,18 @@ int mmdit_step_workspace(const mmdit_config* cfg, size_t* bytes) {
   return MMDIT_OK;
 }
 
+int mmdit_step_workspace_ex(const mmdit_config* cfg, const mmdit_model_w* w, const mmdit_step_opts* opts,
+                            size_t* bytes) {
+  Geo g;
+  int r;
+  if (!bytes) return fail(MMDIT_ERR_NULL, "bytes is NULL");
+  if ((r = check_config(cfg, g))) return r;
+  if (!w) return fail(MMDIT_ERR_NULL, "weights are NULL");
+  if ((cfg->n_double > 0 && !w->dbl) || (cfg->n_single > 0 && !w->sgl)) return fail(MMDIT_ERR_NULL, "block weight arrays are NULL");
+  *bytes = plan_step(cfg, g, step_decodes(cfg, w, opts, g)).blk.total;
+  return MMDIT_OK;
+}
+
 // Step-cache buffer: a_prev [B Li h], residual [B Li h] (float32), per-row
 // partial sums [B Li 2].
 struct CacheLay {
@@ -674,7 +721,9 @@ int mmdit_step_cache_bytes(const mmdit_config* cfg, size_t* bytes) {
 // One step; the image stream holds Lg = Li - ctx_len generated tokens
 // followed by ctx_len context tokens per batch (ctx_packed [B, ctx_len,
 // in_ch] float32). Only the generated rows get the final layer and update.
-static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, void* v_out,
+}  // extern "C"
+
+int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, void* v_out,
                      const void* txt_emb, const void* y, const int32_t* ids, double sigma, double sigma_next,
                      const mmdit_step_opts* opts, void* ws, size_t ws_bytes, void* hip_stream) {
   Geo g;
@@ -730,7 +779,9 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   }
   for (int i = 0; i < cfg->n_single; ++i)
     if ((r = check_single(w->sgl[i], g))) return fail(r, "sgl[%d]: %s", i, g_err.c_str());
-  const StepWs lay = plan_step(cfg, g);
+  const bool rb = g.resid == MMDIT_RESID_BF16;  // bf16 residual stream (else float32)
+  if (rb && cache) return fail(MMDIT_ERR_UNSUPPORTED, "step caching needs the float32 residual stream");
+  const StepWs lay = plan_step(cfg, g, step_decodes(cfg, w, opts, g));
   if (!ws || ws_bytes < lay.blk.total)
     return fail(MMDIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, lay.blk.total);
 
@@ -738,7 +789,9 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   c.xw = lay.blk.xw_bytes && opts->dequant == 0 ? ptr(ws, lay.blk.xw) : nullptr;
   c.xw_bytes = lay.blk.xw_bytes;
   const int B = g.B;
-  float* x = (float*)ptr(ws, lay.x);  // residual: [B*Lt text rows; B*Li image rows] f32
+  // residual: [B*Lt text rows; B*Li image rows], float32 (bf16 when rb)
+  void* x = ptr(ws, lay.x);
+  const int re = rb ? 2 : 4;
   float* vec = (float*)ptr(ws, lay.vec);
   float* temb = (float*)ptr(ws, lay.temb);
   float* hid = (float*)ptr(ws, lay.hid);
@@ -798,12 +851,12 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
     HIP_TRY(launch_convert(x_packed, true, ptr(ws, lay.xin), false, (int64_t)B * g.Li * cfg->in_ch, c.s));
     xa = ptr(ws, lay.xin);
   }
-  float* ximg = x + (size_t)B * g.Lt * h;  // image rows, contiguous [B Li h]
+  void* ximg = ptr(x, (size_t)B * g.Lt * h * re);  // image rows, contiguous [B Li h]
   const int64_t nimg = (int64_t)B * g.Li * h;
   {
     GemmProblem gi = base_problem(w->img_in);
     gi.A = xa; gi.lda = cfg->in_ch; gi.M = B * g.Li;
-    gi.out = ximg; gi.ldo = h; gi.out_f32 = true;
+    gi.out = ximg; gi.ldo = h; gi.out_f32 = !rb;
     if ((r = gemm(c, &gi, 1, EPI_STORE))) return r;
   }
 
@@ -816,7 +869,7 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
     resid = (float*)ptr(cache->buf, cl.resid);
     float* part = (float*)ptr(cache->buf, cl.part);
     CacheDeltaArgs ca{};
-    ca.x = ximg;
+    ca.x = (const float*)ximg;
     ca.mod = mods + lay.mod_dual + (size_t)B * 6 * h;  // shift1 at 0, scale1 at h
     ca.mod_bstride = 6 * h;
     ca.rows_per_batch = g.Li;
@@ -841,14 +894,14 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
       run_blocks = !(acc < opts->cache_threshold);
       if (run_blocks) acc = 0.0;
     }
-    if (run_blocks) HIP_TRY(launch_axpby(resid, ximg, 0.f, 1.f, nimg, c.s));  // resid <- img0
-    else HIP_TRY(launch_axpby(ximg, resid, 1.f, 1.f, nimg, c.s));             // img0 + residual
+    if (run_blocks) HIP_TRY(launch_axpby(resid, (const float*)ximg, 0.f, 1.f, nimg, c.s));  // resid <- img0
+    else HIP_TRY(launch_axpby((float*)ximg, resid, 1.f, 1.f, nimg, c.s));             // img0 + residual
   }
 
   Part parts[2];
-  parts[0] = {g.Lt, 0, rows_of(x, 0, g.Lt, h, 4), rows_of(x, 0, g.Lt, h, 4), nullptr};
-  parts[1] = {g.Li, (int64_t)B * g.Lt, rows_of(x, (int64_t)B * g.Lt, g.Li, h, 4),
-              rows_of(x, (int64_t)B * g.Lt, g.Li, h, 4), nullptr};
+  parts[0] = {g.Lt, 0, rows_of(x, 0, g.Lt, h, re), rows_of(x, 0, g.Lt, h, re), nullptr};
+  parts[1] = {g.Li, (int64_t)B * g.Lt, rows_of(x, (int64_t)B * g.Lt, g.Li, h, re),
+              rows_of(x, (int64_t)B * g.Lt, g.Li, h, re), nullptr};
   if (run_blocks) {
     for (int i = 0; i < cfg->n_double; ++i) {
       float* md = mods + lay.mod_dual + (size_t)i * 2 * B * 6 * h;
@@ -862,7 +915,7 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
     if (g.Lt > 0) {
       GemmProblem gt = base_problem(w->txt_in);
       gt.A = txt_emb; gt.lda = cfg->txt_in_dim; gt.M = B * g.Lt;
-      gt.out = x; gt.ldo = h; gt.out_f32 = true;
+      gt.out = x; gt.ldo = h; gt.out_f32 = !rb;
       if ((r = gemm(c, &gt, 1, EPI_STORE))) return r;
     }
     for (int i = 0; i < cfg->n_double; ++i) {
@@ -870,19 +923,19 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
       parts[0].mod = md;
       parts[1].mod = md + (size_t)B * 6 * h;
       const mmdit_stream_w* sw[2] = {&w->dbl[i].txt, &w->dbl[i].img};
-      if ((r = run_double(c, sw, parts, true, table, ws, lay.blk))) return r;
+      if ((r = run_double(c, sw, parts, !rb, table, ws, lay.blk))) return r;
     }
     for (int i = 0; i < cfg->n_single; ++i) {
       float* ms = mods + lay.mod_single + (size_t)i * B * 3 * h;
       parts[0].mod = ms;
       parts[1].mod = ms;
       if (g.Lt > 0) {
-        if ((r = run_single(c, w->sgl[i], parts, 2, true, table, ws, lay.blk))) return r;
+        if ((r = run_single(c, w->sgl[i], parts, 2, !rb, table, ws, lay.blk))) return r;
       } else {
-        if ((r = run_single(c, w->sgl[i], &parts[1], 1, true, table, ws, lay.blk))) return r;
+        if ((r = run_single(c, w->sgl[i], &parts[1], 1, !rb, table, ws, lay.blk))) return r;
       }
     }
-    if (cache) HIP_TRY(launch_axpby(resid, ximg, -1.f, 1.f, nimg, c.s));  // resid <- img - img0
+    if (cache) HIP_TRY(launch_axpby(resid, (const float*)ximg, -1.f, 1.f, nimg, c.s));  // resid <- img - img0
   }
   // final layer on the generated image rows, Euler update fused into the epilogue
   Part fin = parts[1];
@@ -890,7 +943,7 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   fin.x_in.rows_per_batch = Lg;  // batch stride stays Li rows
   fin.mod = mods + lay.mod_final;
   void* xn = ptr(ws, lay.blk.xn);
-  if ((r = run_ln(c, &fin, 1, 2 * h, 0, h, true, xn))) return r;
+  if ((r = run_ln(c, &fin, 1, 2 * h, 0, h, !rb, xn))) return r;
   GemmProblem f = base_problem(w->final_lin);
   f.A = xn; f.lda = h; f.M = B * Lg;
   f.res_out = rows_of(x_packed, 0, Lg, cfg->in_ch, 4);
@@ -906,6 +959,8 @@ static int step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   }
   return MMDIT_OK;
 }
+
+extern "C" {
 
 int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packed, void* v_out,
                const void* txt_emb, const void* y, const int32_t* ids, double sigma,

@@ -840,6 +840,8 @@ bool gemm_dma_eligible(const GemmProblem* p, int nprob, int epi) {
     if (fmt >= 0 && q.fmt != fmt) return false;  // one format per launch
     fmt = q.fmt;
     if (q.K % kDBK != 0 || q.lda % 8 != 0 || q.N < 128 || q.N % 4 != 0) return false;
+    // per-lane operand offsets are 32-bit
+    if ((int64_t)q.M * q.lda * 2 >= (int64_t(1) << 32) || (int64_t)q.N * q.K * 2 >= (int64_t(1) << 32)) return false;
     if (fmt != 0 && (kDBK != 64 || MMDIT_DMA_STAGES != 2)) return false;
     if ((epi == EPI_QKV || epi == EPI_SPLIT_QKV) &&
         (fmt != 0 || MMDIT_DMA_WAVES != 4 || q.qk_h % kDBN != 0 || 3 * q.qk_h > q.N || q.qk_rows <= 0))

@@ -52,6 +52,15 @@ typedef enum {
 
 typedef enum { MMDIT_F32 = 0, MMDIT_BF16 = 1 } mmdit_dtype;
 
+/* Storage of the residual stream (the block inputs and outputs that the gated
+ * residual updates add into). DEFAULT: the block calls keep it in the
+ * activation dtype, mmdit_step in float32 (pictor README: FP32 accumulate;
+ * reading: a bf16 residual random walk over 76 additions would spend a large
+ * part of the bf16 error budget). F32: float32 everywhere (block inputs and
+ * outputs are float32 arrays). BF16: bf16 everywhere (needs bf16
+ * activations; mmdit_step then holds its residual in bf16). */
+typedef enum { MMDIT_RESID_DEFAULT = 0, MMDIT_RESID_F32 = 1, MMDIT_RESID_BF16 = 2 } mmdit_resid;
+
 /* Weight storage of one linear layer y = x W^T + b.
  * DENSE: W [n_out, k_in] in the activation dtype.
  * Q4G64: symmetric 4-bit codes in -7..7, two's complement nibbles, two per
@@ -86,6 +95,7 @@ typedef struct {
   float ln_eps;        /* LayerNorm epsilon (1e-6) */
   float rms_eps;       /* QK RMSNorm epsilon (1e-6) */
   int32_t act_dtype;   /* mmdit_dtype of activations, dense weights, biases, norm scales */
+  int32_t resid;       /* mmdit_resid: storage of the residual stream (0 = default) */
 } mmdit_dims;
 
 typedef struct {
@@ -148,12 +158,16 @@ typedef struct {
 
 /* Workspace sizes in bytes (host-only; no device work). With bf16
  * activations and at least 1024 rows (batch * (txt_len + img_len), context
- * tokens included) the workspace also holds room for one launch's weights
- * decoded to bf16 (2 bytes per weight of the largest launch: both streams'
- * fc1 or fc2, or linear1). Quantised layers of such calls are decoded there
- * once per launch (profile class 8) and multiplied by the dense kernels;
+ * tokens included) a call with a quantised layer decodes each such layer
+ * once per launch into room in the workspace (2 bytes per weight of the
+ * largest launch: both streams' fc1 or fc2, or linear1; 151 MB at h 3072)
+ * and multiplies the bf16 copy with the dense kernels (profile class 8);
  * below 1024 rows the GEMM kernels dequantise weight tiles as they stage
- * them. Both give the same bf16 weights. */
+ * them. Both give the same bf16 weights. These three queries do not see the
+ * weights and always include that room; the calls themselves need it only
+ * when they decode a layer, so a dense model needs the smaller size that
+ * mmdit_step_workspace_ex reports for the step (the block calls check
+ * against the size for their own weights the same way). */
 int mmdit_double_block_workspace(const mmdit_dims* dims, size_t* bytes);
 int mmdit_single_block_workspace(const mmdit_dims* dims, size_t* bytes);
 int mmdit_step_workspace(const mmdit_config* cfg, size_t* bytes);
@@ -165,15 +179,17 @@ int mmdit_step_workspace(const mmdit_config* cfg, size_t* bytes);
  * ids [Lt + Li, 3]: device int32 position ids (frame, row, col), text first,
  *   shared by the batch; RoPE angles are ids[:, a] * theta^(-2j/axes_dim[a]).
  * ws: device workspace of at least mmdit_double_block_workspace() bytes.
- * The residual stream is kept in the activation dtype. */
+ * img_in/txt_in/img_out/txt_out are the residual stream: in the activation
+ * dtype, or float32 when dims->resid is MMDIT_RESID_F32. */
 int mmdit_double_block_fwd(const mmdit_dims* dims, const mmdit_double_w* w,
                            const void* img_in, const void* txt_in, void* img_out, void* txt_out,
                            const void* vec, const int32_t* ids,
                            void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Single-stream block forward (mflux-rs, card "Single-Stream Blocks").
- * x_in, x_out [B, Lt + Li, h]: device, activation dtype, text rows first;
- * x_out may alias x_in. vec, ids and ws as for the dual block. */
+ * x_in, x_out [B, Lt + Li, h]: device, activation dtype (float32 when
+ * dims->resid is MMDIT_RESID_F32), text rows first; x_out may alias x_in.
+ * vec, ids and ws as for the dual block. */
 int mmdit_single_block_fwd(const mmdit_dims* dims, const mmdit_single_w* w,
                            const void* x_in, void* x_out, const void* vec, const int32_t* ids,
                            void* ws, size_t ws_bytes, void* hip_stream);
@@ -185,7 +201,8 @@ int mmdit_single_block_fwd(const mmdit_dims* dims, const mmdit_single_w* w,
  * txt_emb [B, Lt, txt_in_dim], y [B, vec_in_dim]: device, activation dtype.
  * ids as for the blocks. sigma, sigma_next: the schedule pair of this step;
  * the timestep embedding uses 1000 * sigma.
- * Inside the step the residual stream is float32 whatever the activation dtype. */
+ * Inside the step the residual stream is float32 whatever the activation
+ * dtype, or bf16 when cfg->dims.resid is MMDIT_RESID_BF16. */
 int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w,
                void* x_packed, void* v_out, const void* txt_emb, const void* y,
                const int32_t* ids, double sigma, double sigma_next,
@@ -270,6 +287,14 @@ int mmdit_step_ex(const mmdit_config* cfg, const mmdit_model_w* w,
                   void* x_packed, void* v_out, const void* txt_emb, const void* y,
                   const int32_t* ids, double sigma, double sigma_next, const mmdit_step_opts* opts,
                   void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Host. The workspace mmdit_step_ex needs for these weights and options
+ * (opts may be NULL): without room for decoded weights when no layer is
+ * decoded (dense weights, fewer than 1024 rows, or opts->dequant == 1).
+ * w->dbl / w->sgl are read; device pointers are not touched. Errors:
+ * MMDIT_ERR_NULL, and those of mmdit_step_workspace. */
+int mmdit_step_workspace_ex(const mmdit_config* cfg, const mmdit_model_w* w, const mmdit_step_opts* opts,
+                            size_t* bytes);
 
 /* ---- helpers ---------------------------------------------------------- */
 

@@ -442,3 +442,33 @@ def test_blocks_mixed_stream_formats_below_decoding_rows():
         rimg, rtxt = oracle_double(s, wo, x, ids)
         assert_parity(down(img_o), rimg, "bf16", f"mixed formats ({qs} quantised) img")
         assert_parity(down(txt_o), rtxt, "bf16", f"mixed formats ({qs} quantised) txt")
+
+
+def test_blocks_float32_residual_with_bf16_operands():
+    # dims.resid = MMDIT_RESID_F32: bf16 operands, float32 block inputs and
+    # outputs (the residual the step keeps), 256 text + 32x32 image tokens
+    t = torch()
+    s = I.CFG2
+    x = I.block_inputs(s)
+    ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
+    dims = bd.make_dims(s, resid=bd.RESID_F32)
+    w = I.double_block_weights(s, 0)
+    W = bd.DoubleW(w, bd.BF16, "cuda")
+    img, txt = up(x["x_img"], "f32"), up(x["x_txt"], "f32")
+    vec = up(x["vec"], "bf16")
+    ws = workspace(bd.mmdit_double_block_workspace(dims))
+    print("double block, float32 residual", flush=True)
+    bd.mmdit_double_block_fwd(dims, W.c(), img, txt, img, txt, vec, up_i32(ids), ws)
+    sync()
+    rimg, rtxt = oracle_double(s, w, x, ids)
+    assert img.dtype == t.float32
+    assert_parity(down(img), rimg, "bf16", "f32-residual dual img")
+    assert_parity(down(txt), rtxt, "bf16", "f32-residual dual txt")
+    ws_ = I.single_block_weights(s, 0)
+    S_ = bd.SingleW(ws_, bd.BF16, "cuda")
+    xin = up(x["x"], "f32")
+    out = t.empty_like(xin)
+    print("single block, float32 residual", flush=True)
+    bd.mmdit_single_block_fwd(dims, S_.c(), xin, out, vec, up_i32(ids), ws)
+    sync()
+    assert_parity(down(out), oracle_single(s, ws_, x, ids), "bf16", "f32-residual single")

@@ -8,7 +8,8 @@ on the host. Quantised layers reach the oracle as their codes and bf16
 scales and are decoded there (oracle.unpack_int4 / oracle.dequantise).
 
 Cases:
-  * 1024^2 (4096 image + 512 text tokens, bf16): the benchmarked step;
+  * 1024^2 (4096 image + 512 text tokens, bf16): the benchmarked step, and
+    the same step with its residual stream held in bf16 (dims.resid);
   * the same with group-quantised weights (4-bit inner projections, 8-bit
     residual-writing layers), both the route that dequantises inside the GEMM
     tile loop and the automatic route (decoded once per launch);
@@ -131,9 +132,10 @@ def _inputs(s: I.Shape):
     return X, T, y, ids, sig
 
 
-def gpu_step(s: I.Shape, M: bd.ModelW, X, T, y, ids, sigma, sigma_next, dequant_in_gemm=False):
+def gpu_step(s: I.Shape, M: bd.ModelW, X, T, y, ids, sigma, sigma_next, dequant_in_gemm=False,
+             resid=bd.RESID_DEFAULT):
     t = torch()
-    cfg = bd.make_config(s)
+    cfg = bd.make_config(s, resid=resid)
     mc = M.c()
     d = t.device("cuda:0")
     Xd = t.from_numpy(X).to(d)
@@ -143,7 +145,7 @@ def gpu_step(s: I.Shape, M: bd.ModelW, X, T, y, ids, sigma, sigma_next, dequant_
     idd = t.from_numpy(ids).to(d)
     ws = t.empty(bd.mmdit_step_workspace(cfg), dtype=t.uint8, device=d)
     print(f"GPU step {s.n_double}+{s.n_single} blocks, L {s.seq_len}, sigma {sigma:.4f} -> {sigma_next:.4f}, "
-          f"dequant_in_gemm {dequant_in_gemm}", flush=True)
+          f"dequant_in_gemm {dequant_in_gemm}, resid {resid}", flush=True)
     if dequant_in_gemm:
         bd.mmdit_step_ex(cfg, mc, Xd, v, Td, yd, idd, sigma, sigma_next, ws, dequant_in_gemm=True)
     else:
@@ -166,9 +168,14 @@ def test_full_depth_step_1024_matches_oracle(dense):
     # the benchmarked step: 19 + 38 blocks at 4096 image + 512 text tokens
     X, T, y, ids, sig = _inputs(S)
     Xg, vg = gpu_step(S, dense, X, T, y, ids, sig[1], sig[2])
+    # the same step with the residual stream held in bf16 (76 rounded
+    # residual additions instead of float32 ones)
+    Xb, vb = gpu_step(S, dense, X, T, y, ids, sig[1], sig[2], resid=bd.RESID_BF16)
     Xr, vr = oracle_step(S, dense, X, T, y, ids, sig[1], sig[2])
     assert_parity(vg, vr, "bf16", "19+38 step at 1024^2: v")
     assert_parity(Xg, Xr, "bf16", "19+38 step at 1024^2: x_next")
+    assert_parity(vb, vr, "bf16", "19+38 step at 1024^2, bf16 residual: v")
+    assert_parity(Xb, Xr, "bf16", "19+38 step at 1024^2, bf16 residual: x_next")
 
 
 @pytest.mark.timeout(600)
@@ -190,9 +197,12 @@ def test_full_depth_quantised_step_1024_matches_oracle(quant):
 def test_full_depth_step_320_tokens_matches_oracle(dense, sig_i):
     X, T, y, ids, sig = _inputs(SMALL)
     Xg, vg = gpu_step(SMALL, dense, X, T, y, ids, sig[sig_i], sig[sig_i + 1])
+    Xb, vb = gpu_step(SMALL, dense, X, T, y, ids, sig[sig_i], sig[sig_i + 1], resid=bd.RESID_BF16)
     Xr, vr = oracle_step(SMALL, dense, X, T, y, ids, sig[sig_i], sig[sig_i + 1])
     assert_parity(vg, vr, "bf16", f"19+38 step at 320 tokens, sigma {sig[sig_i]:.3f}: v")
     assert_parity(Xg, Xr, "bf16", f"19+38 step at 320 tokens, sigma {sig[sig_i]:.3f}: x_next")
+    assert_parity(vb, vr, "bf16", f"19+38 step at 320 tokens, sigma {sig[sig_i]:.3f}, bf16 residual: v")
+    assert_parity(Xb, Xr, "bf16", f"19+38 step at 320 tokens, sigma {sig[sig_i]:.3f}, bf16 residual: x_next")
 
 
 @pytest.mark.timeout(300)

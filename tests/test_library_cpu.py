@@ -272,3 +272,36 @@ def test_workspace_sizes_scale_with_tokens(lib):
     n = bd.mmdit_step_workspace(cfg)
     # f32 residual (56.6 MB) + block scratch; well under a GB at 1024^2
     assert 200e6 < n < 1.5e9
+
+
+def test_step_workspace_ex_leaves_out_decoded_weight_room_for_dense_models(lib):
+    # h 3072, 1280 tokens: a dense model needs no room for decoded weights
+    # (2 * 3072 * 12288 bf16 = 151 MB); a quantised one does unless every
+    # layer is dequantised inside its GEMM
+    s = I.CFG2
+    cfg = bd.make_config(dataclasses.replace(s, n_double=1, n_single=1))
+    M = bd.mmdit_model_w()
+    dbl = (bd.mmdit_double_w * 1)()
+    sgl = (bd.mmdit_single_w * 1)()
+    M.dbl = C.cast(dbl, C.POINTER(bd.mmdit_double_w))
+    M.sgl = C.cast(sgl, C.POINTER(bd.mmdit_single_w))
+    full = bd.mmdit_step_workspace(cfg)
+    dense = bd.mmdit_step_workspace_ex(cfg, M)
+    assert full - dense >= 2 * 3072 * 12288 * 2
+    sgl[0].lin1.fmt = bd.W_Q4G64
+    assert bd.mmdit_step_workspace_ex(cfg, M) == full
+    assert bd.mmdit_step_workspace_ex(cfg, M, dequant_in_gemm=True) == dense
+
+
+def test_resid_field_is_checked(lib):
+    n = C.c_size_t()
+    d = bd.make_dims(I.CFG2, resid=7)
+    assert lib.mmdit_double_block_workspace(C.byref(d), C.byref(n)) == 3
+    d = bd.make_dims(I.CFG1, resid=bd.RESID_BF16)  # float32 activations
+    assert lib.mmdit_double_block_workspace(C.byref(d), C.byref(n)) == 3
+    d = bd.make_dims(I.CFG2, resid=bd.RESID_BF16)
+    assert lib.mmdit_double_block_workspace(C.byref(d), C.byref(n)) == 0
+    # the step's bf16 residual halves the residual buffer
+    c32 = bd.make_config(I.CFG4)
+    c16 = bd.make_config(I.CFG4, resid=bd.RESID_BF16)
+    assert bd.mmdit_step_workspace(c32) - bd.mmdit_step_workspace(c16) >= I.CFG4.seq_len * 3072 * 2
