@@ -100,6 +100,8 @@ _SIGS = {
                              C.c_double, C.c_double, _P, C.c_size_t, _P]),
     "mmdit_step_ex": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(mmdit_model_w), _P, _P, _P, _P, _P,
                                 C.c_double, C.c_double, C.POINTER(mmdit_step_opts), _P, C.c_size_t, _P]),
+    "mmdit_step_noalloc": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(mmdit_model_w), _P, _P, _P, _P, _P,
+                                     C.c_double, C.c_double, C.POINTER(mmdit_step_opts), _P]),
     "mmdit_schedule": (C.c_int, [C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double, C.c_int32, _P]),
     "mmdit_make_ids": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P]),
     "mmdit_pack_latents": (C.c_int, [_P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P]),
@@ -391,6 +393,17 @@ def mmdit_step_ex(cfg, w: mmdit_model_w, x_packed, v_out, txt_emb, y, ids, sigma
                                _ptr(ids), float(sigma), float(sigma_next), C.byref(o), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream)),
            "mmdit_step_ex")
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20  # the library's scratch per GPU (mmdit_step_noalloc)
+
+
+def mmdit_step_noalloc(cfg, w: mmdit_model_w, x_packed, v_out, txt_emb, y, ids, sigma: float, sigma_next: float,
+                       stream=None):
+    """mmdit_step on the library's own scratch (no workspace argument)."""
+    _check(lib().mmdit_step_noalloc(C.byref(cfg), C.byref(w), _ptr(x_packed), _ptr(v_out), _ptr(txt_emb), _ptr(y),
+                                    _ptr(ids), float(sigma), float(sigma_next), None, _stream(stream)),
+           "mmdit_step_noalloc")
 
 
 def mmdit_schedule(n_steps: int, img_len: int, base_shift=0.5, max_shift=1.15, sigma_terminal=0.0,

@@ -296,6 +296,24 @@ int mmdit_step_ex(const mmdit_config* cfg, const mmdit_model_w* w,
 int mmdit_step_workspace_ex(const mmdit_config* cfg, const mmdit_model_w* w, const mmdit_step_opts* opts,
                             size_t* bytes);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that must not call hipMalloc): mmdit_step_ex
+ * without a workspace argument. The workspace is a scratch array the library
+ * holds in device memory, 256 MiB (268435456 bytes) on each GPU the library
+ * is loaded on, for the life of the process. Configurations whose
+ * mmdit_step_workspace() exceeds that size are refused with
+ * MMDIT_ERR_WORKSPACE before any launch (the 512x512 step at h 3072 fits; the
+ * 1024x1024 step does not). Every call on one GPU uses that GPU's one array:
+ * calls that overlap on a GPU (other streams or threads) race and give
+ * undefined results; calls on one stream are ordered. The step initialises
+ * every scratch byte it reads, so nothing is carried between calls. The
+ * first call on a device resolves the array's device address (no
+ * allocation). Arguments and errors as for mmdit_step_ex; opts may be NULL. */
+int mmdit_step_noalloc(const mmdit_config* cfg, const mmdit_model_w* w,
+                       void* x_packed, void* v_out, const void* txt_emb, const void* y,
+                       const int32_t* ids, double sigma, double sigma_next, const mmdit_step_opts* opts,
+                       void* hip_stream);
+
 /* ---- helpers ---------------------------------------------------------- */
 
 /* Host. sigmas[0..n_steps] of the shifted flow-matching schedule: t_i = 1 - i/n,

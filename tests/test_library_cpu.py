@@ -274,6 +274,26 @@ def test_workspace_sizes_scale_with_tokens(lib):
     assert 200e6 < n < 1.5e9
 
 
+def test_step_noalloc_refuses_configurations_beyond_its_scratch(lib):
+    # the 1024^2 step needs more workspace than the library's 256 MiB scratch:
+    # refused with MMDIT_ERR_WORKSPACE before any device work (dummy pointers)
+    cfg = bd.make_config(I.CFG4)
+    M = bd.mmdit_model_w()
+    dbl = (bd.mmdit_double_w * I.CFG4.n_double)()
+    sgl = (bd.mmdit_single_w * I.CFG4.n_single)()
+    M.dbl = C.cast(dbl, C.POINTER(bd.mmdit_double_w))
+    M.sgl = C.cast(sgl, C.POINTER(bd.mmdit_single_w))
+    # dense weights: no room for decoded layers, and still above 256 MiB
+    assert bd.mmdit_step_workspace_ex(cfg, M) > bd.NOALLOC_SCRATCH_BYTES
+    assert bd.mmdit_step_workspace_ex(cfg, M) < bd.mmdit_step_workspace(cfg)
+    dummy = C.c_void_p(4096)
+    st = lib.mmdit_step_noalloc(C.byref(cfg), C.byref(M), dummy, dummy, dummy, dummy, dummy, 1.0, 0.5, None, None)
+    assert st == 4
+    assert "256" in bd.mmdit_last_error() or "268435456" in bd.mmdit_last_error()
+    # a NULL config is an argument error, also before any device work
+    assert lib.mmdit_step_noalloc(None, C.byref(M), dummy, dummy, dummy, dummy, dummy, 1.0, 0.5, None, None) == 1
+
+
 def test_step_workspace_ex_leaves_out_decoded_weight_room_for_dense_models(lib):
     # h 3072, 1280 tokens: a dense model needs no room for decoded weights
     # (2 * 3072 * 12288 bf16 = 151 MB); a quantised one does unless every
