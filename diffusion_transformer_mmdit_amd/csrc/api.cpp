@@ -179,9 +179,10 @@ int check_single(const mmdit_single_w& s, const Geo& g) {
 // Block scratch (activation dtype unless noted):
 //   xn [rows, h], qkv [rows, 3h], Q/K/V [B, H, Lpad, 128],
 //   o   [rows, h] (dual) or cat [rows, h + m] (single), mlp [rows, m] (dual).
+//   attn  partial results of key-split attention units (bf16 path).
 //   xw  bf16 weights decoded from a quantised layer (only when expanding).
 struct BlockWs {
-  size_t xn, qkv, q, k, v, o, mlp, xw, xw_bytes, total;
+  size_t xn, qkv, q, k, v, o, mlp, attn, xw, xw_bytes, total;
 };
 
 // Quantised layers of launches with at least this many rows are decoded into
@@ -218,6 +219,7 @@ BlockWs plan_block(const Geo& g, size_t base, size_t xw_bytes) {
   w.v = at; at = align_up(at + qkvh * g.esz);
   w.o = at; at = align_up(at + rows * (size_t)(g.h + g.m) * g.esz);
   w.mlp = at; at = align_up(at + rows * g.m * g.esz);
+  w.attn = at; at = align_up(at + (g.bf16 ? kAttnPartBytes : 0));
   w.xw = at; w.xw_bytes = xw_bytes; at = align_up(at + xw_bytes);
   w.total = at;
   return w;
@@ -446,6 +448,7 @@ int run_qk_attn(const Ctx& c, const Part* parts, int np, void* qkv, const void* 
     HIP_TRY(launch_qk_norm_rope(q, g.bf16, g.bf16, c.s));
   }
   at.Q = q.Q; at.K = q.K; at.V = q.V;
+  at.part = g.bf16 ? (float*)ptr(ws, w.attn) : nullptr;
   at.seg_len0 = q.seg_len0;
   at.B = g.B; at.H = g.H; at.L = g.L; at.Lpad = g.Lpad;
   at.scale = 1.0f / sqrtf(128.0f);

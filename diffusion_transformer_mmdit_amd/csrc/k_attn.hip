@@ -61,9 +61,13 @@ __host__ __device__ __forceinline__ int attn_qblocks(const AttnArgs& a) {
 }
 
 // Unit u = (b * H + head) * qblocks + query block: the unit's 256 queries
-// against all keys; writes the normalised output rows. Phase 2t + grp is a
-// wave's MFMA phase of tile t, phase 2t + 1 + grp its softmax of tile t.
-__device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int unit) {
+// against the keys of 64-key tiles [t0, t1). With rec null (t0 = 0, t1 =
+// all tiles) it writes the normalised output rows; otherwise the piece's
+// unnormalised O, running max m (scores times scale * log2 e) and row sum l
+// go to the record rec (O [256][128], m [256], l [256], float32). Phase
+// 2t + grp is a wave's MFMA phase of tile t, phase 2t + 1 + grp its softmax
+// of tile t.
+__device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int unit, int t0, int t1, float* rec) {
   constexpr int NW = kAttnWaves, J = 16 / NW;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -236,7 +240,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
       }
     return ps0 + ps1;
   };
-  auto softmax = [&](int kt, bool mask) {
+  auto softmax = [&](int kt, bool mask, bool first) {
     if (__builtin_expect(mask, 0)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -247,7 +251,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
         }
     }
     float ps = 0.f;
-    bool slow = kt == 0;
+    bool slow = first;
     if (!slow) {
       ps = probs();
       slow = __any(!(ps + __shfl_xor(ps, 32, 64) <= kPMax));
@@ -277,7 +281,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
 
   const int ntiles = (a.L + kAttnK - 1) / kAttnK;
   const bool ragged = (a.L % kAttnK) != 0;
-  issue_k(0);
+  issue_k(t0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(0) (and Q) landed
   __syncthreads();
   // Phase 2u + grp of a wave is its MFMA phase of tile u, phase 2u + 1 + grp
@@ -291,8 +295,8 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
     __builtin_amdgcn_sched_barrier(0);
   };
   auto issue = [&](int u) {
-    if (u + 1 < ntiles) issue_k(u + 1);
-    if (u < ntiles) issue_v(u);
+    if (u + 1 < t1) issue_k(u + 1);
+    if (u < t1) issue_v(u);
   };
   auto hi = [&]() {
     __builtin_amdgcn_sched_barrier(0);
@@ -304,18 +308,18 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto sm = [&](int t) { softmax(t, ragged && t == ntiles - 1); };
+  auto sm = [&](int t) { softmax(t, ragged && t == ntiles - 1, t == t0); };
   auto wait_vm = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
   // first tile (MFMA phase: S(0) only), tiles 1 .. ntiles-1, then the last
   // PV; group 1 runs the same sequence one phase later
   if (grp == 0) {
-    issue(0);
-    hi(); phase_qk(0); lo();
+    issue(t0);
+    hi(); phase_qk(t0); lo();
     bar();
-    sm(0);
+    sm(t0);
     wait_vm();
     bar();
-    for (int t = 1; t < ntiles; ++t) {
+    for (int t = t0 + 1; t < t1; ++t) {
       issue(t);
       hi(); phase_pv_qk(t); lo();
       bar();
@@ -323,17 +327,17 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
       wait_vm();
       bar();
     }
-    hi(); phase_pv(ntiles); lo();
+    hi(); phase_pv(t1); lo();
     bar();
     wait_vm();
     bar();
   } else {
-    issue(0);
+    issue(t0);
     bar();
-    hi(); phase_qk(0); lo();
+    hi(); phase_qk(t0); lo();
     wait_vm();
     bar();
-    for (int t = 1; t < ntiles; ++t) {
+    for (int t = t0 + 1; t < t1; ++t) {
       issue(t);
       sm(t - 1);
       bar();
@@ -341,13 +345,30 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
       wait_vm();
       bar();
     }
-    sm(ntiles - 1);
+    sm(t1 - 1);
     bar();
-    hi(); phase_pv(ntiles); lo();
+    hi(); phase_pv(t1); lo();
     wait_vm();
     bar();
   }
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (rec) {  // partial piece: unnormalised O, m and l of each query
+    if (qrow < a.L) {
+      const int qi = wave * 32 + l32;
+      float* dst = rec + (size_t)qi * 128;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+          *reinterpret_cast<f32x4*>(dst + db * 32 + rg * 8 + g * 4) =
+              (f32x4){o[db][rg * 4], o[db][rg * 4 + 1], o[db][rg * 4 + 2], o[db][rg * 4 + 3]};
+      if (g == 0) {
+        rec[(size_t)32 * kAttnWaves * 128 + qi] = m_run;
+        rec[(size_t)32 * kAttnWaves * 129 + qi] = l_tot;
+      }
+    }
+    return;
+  }
   const float inv = 1.0f / l_tot;
   if (qrow < a.L) {
     bf16* dst = out_row(a, b, qrow) + hh * 128;
@@ -364,20 +385,113 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
   }
 }
 
-__global__ __launch_bounds__(64 * kAttnWaves, 2) void k_attn_bf16(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
-  attn_unit(a, smem, blockIdx.x);
+// Tail split: worker w of a.workers takes tiles [begin, end) of the
+// flattened (tail unit, key tile) space, begin = w * T / workers with T =
+// tail units * tiles per unit. A share is shorter than one unit, so it holds
+// at most two pieces: the end of tail unit begin / nt (record 2w) and the
+// start of the next (record 2w + 1).
+__device__ __forceinline__ int64_t attn_share_begin(int w, int64_t T, int workers) {
+  return (int64_t)w * T / workers;
 }
 
-hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s) {
+__global__ __launch_bounds__(64 * kAttnWaves, 2) void k_attn_bf16(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int nt = (a.L + kAttnK - 1) / kAttnK;
+  if (!a.part || (int)blockIdx.x < a.full_units) {
+    attn_unit(a, smem, blockIdx.x, 0, nt, nullptr);
+    return;
+  }
+  const int w = blockIdx.x - a.full_units;
+  const int tail = attn_qblocks(a) * a.H * a.B - a.full_units;
+  const int64_t T = (int64_t)tail * nt;
+  const int64_t begin = attn_share_begin(w, T, a.workers), end = attn_share_begin(w + 1, T, a.workers);
+  if (begin >= end) return;  // uniform over the block
+  const int u0 = (int)(begin / nt);
+  const int64_t split = (int64_t)(u0 + 1) * nt;
+  attn_unit(a, smem, a.full_units + u0, (int)(begin - (int64_t)u0 * nt), (int)((end < split ? end : split) - (int64_t)u0 * nt),
+            a.part + (size_t)(2 * w) * kAttnRecFloats);
+  if (end > split) {
+    __syncthreads();
+    attn_unit(a, smem, a.full_units + u0 + 1, 0, (int)(end - split), a.part + (size_t)(2 * w + 1) * kAttnRecFloats);
+  }
+}
+
+// Combines the pieces of each tail unit: for query q and dims 4j .. 4j+3,
+// O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i with M = max_i m_i,
+// written as bf16 to the output row. 32 threads per query, 8 queries per
+// 256-thread block; unit tail u covers blocks u * 32 .. u * 32 + 31.
+// A unit of nt tiles meets at most ceil(nt / share) + 1 shares, share =
+// tail * nt / workers; the launcher splits only when tail >= workers / 6,
+// so a unit has at most 7 pieces.
+constexpr int kAttnMaxPieces = 8;
+
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  constexpr int QU = 32 * kAttnWaves;  // queries per unit
+  const int nt = (a.L + kAttnK - 1) / kAttnK;
+  const int tail = attn_qblocks(a) * a.H * a.B - a.full_units;
+  const int T = tail * nt;  // < 2^31: tail < kAttnTailWorkers, nt < 2^23
+  const int ur = blockIdx.x / (QU / 8);
+  const int q = (blockIdx.x % (QU / 8)) * 8 + (threadIdx.x >> 5);
+  const int j = threadIdx.x & 31;
+  const int unit = a.full_units + ur;
+  const int qb_n = attn_qblocks(a);
+  const int qrow = (unit % qb_n) * QU + q;
+  if (qrow >= a.L) return;
+  const int hh = (unit / qb_n) % a.H, b = unit / qb_n / a.H;
+  // the records of this unit's pieces: the workers whose share meets
+  // [ur * nt, (ur + 1) * nt)
+  const int W = a.workers;
+  const int lo = ur * nt, hi = lo + nt;
+  int slot[kAttnMaxPieces];
+  int np = 0;
+  for (int v = (int)((int64_t)lo * W / T); v < W && np < kAttnMaxPieces; ++v) {
+    const int bg = (int)((int64_t)v * T / W), en = (int)((int64_t)(v + 1) * T / W);
+    if (bg >= hi) break;
+    if (en <= lo || bg >= en) continue;
+    slot[np++] = 2 * v + (bg / nt == ur ? 0 : 1);
+  }
+  float mx = -3.0e38f;
+  for (int i = 0; i < np; ++i) mx = fmaxf(mx, a.part[(size_t)slot[i] * kAttnRecFloats + (size_t)QU * 128 + q]);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f}, lsum = 0.f;
+  for (int i = 0; i < np; ++i) {
+    const float* r = a.part + (size_t)slot[i] * kAttnRecFloats;
+    const float e = __builtin_amdgcn_exp2f(r[(size_t)QU * 128 + q] - mx);
+    lsum += e * r[(size_t)QU * 129 + q];
+    const f32x4 o = *reinterpret_cast<const f32x4*>(r + (size_t)q * 128 + 4 * j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += e * o[i];
+  }
+  const float inv = 1.0f / lsum;
+  bf16* dst = out_row(a, b, qrow) + hh * 128 + 4 * j;
+  *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)(acc[0] * inv), (bf16)(acc[1] * inv), (bf16)(acc[2] * inv),
+                                             (bf16)(acc[3] * inv)};
+}
+
+hipError_t launch_attention_bf16(const AttnArgs& in, hipStream_t s) {
   // K/V byte offsets from the per-(batch, head) base are 32-bit
-  if ((int64_t)a.Lpad * 128 * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if ((int64_t)in.Lpad * 128 * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  AttnArgs a = in;
   const int units = attn_qblocks(a) * a.H * a.B;
+  const int C = kAttnTailWorkers;
+  const int tail = units % C;
+  // Split the last round only when it would leave at least three quarters
+  // of the CUs idle. Pieces cost a start (Q loads, the first tile's max, the
+  // pipeline fill) and a float32 record, and the merge reads every record:
+  // measured at 4608 tokens (tail 176 of 256) the split call took 262 us
+  // against 251 us whole, at 1280 tokens (tail 120, 20 tiles per unit)
+  // 61 us against 40 us, and at 8704 tokens (tail 48) 780 us against 894 us.
+  // tail >= C / 6 bounds the pieces of a unit (kAttnMaxPieces).
+  const int nt = (a.L + kAttnK - 1) / kAttnK;
+  const bool split = a.part && tail >= C / 6 && tail <= C / 4 && (int64_t)tail * nt >= 4 * (int64_t)C;
+  a.full_units = split ? units - tail : units;
+  a.workers = split ? C : 0;
+  if (!split) a.part = nullptr;
   const size_t lds = 2 * kStage;
   static std::atomic<uint64_t> lds_set{0};
   const hipError_t e = ensure_lds_limit((const void*)k_attn_bf16, (int)lds, lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_bf16, dim3(units), dim3(64 * kAttnWaves), lds, s, a);
+  hipLaunchKernelGGL(k_attn_bf16, dim3(a.full_units + a.workers), dim3(64 * kAttnWaves), lds, s, a);
+  if (a.part) hipLaunchKernelGGL(k_attn_merge, dim3(tail * (32 * kAttnWaves / 8)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -227,10 +227,25 @@ struct AttnArgs {
   int32_t seg_len0;
   int32_t B, H, L, Lpad;
   float scale;  // 1/sqrt(d)
+  // bf16 path: scratch for the partial results of split units (at least
+  // kAttnPartBytes, 16-byte aligned), or null to run every unit whole.
+  // full_units and workers are set by the launcher.
+  float* part;
+  int32_t full_units, workers;
 };
 // bf16 attention blocks: kAttnWaves wavefronts of 32 queries each, one
-// block per CU.
+// block per CU. A unit is 32 * kAttnWaves queries of one (batch, head)
+// against all keys. When the unit count leaves the last round of blocks
+// short of a full round of kAttnTailWorkers (the CU count), the units of
+// that round are cut along the keys: kAttnTailWorkers worker blocks each
+// take an equal contiguous share of those units' 64-key tiles (at most two
+// pieces of two units), write unnormalised partial results, and a merge
+// kernel combines the pieces of each unit.
 constexpr int kAttnWaves = 8;
+constexpr int kAttnTailWorkers = 256;
+// one record per piece: O [256][128] float32, then m [256], l [256]
+constexpr size_t kAttnRecFloats = (size_t)32 * kAttnWaves * 130;
+constexpr size_t kAttnPartBytes = 2 * (size_t)kAttnTailWorkers * kAttnRecFloats * 4;
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t s);
 

@@ -395,13 +395,28 @@ def _delta_parity(got_out, ref_out, x_in, what):
     return assert_parity(d_got, d_ref, "bf16", what)
 
 
-@pytest.mark.parametrize("case", ["cfg3", "cfg2_sharp"])
+ISO_CASES = {
+    "cfg3": I.CFG3,
+    "cfg2_sharp": I.CFG2,
+    # 512 text + 4096 generated + 4096 context tokens (L 8704, 24 heads: 816
+    # units, the last 48 split along the keys over 256 workers and merged)
+    "ref8704": I.Shape(txt_len=512, grid_h=64, grid_w=128, dtype="bf16", cfg_id=54),
+    # h 1024 (8 heads), 77 + 40x41 = 1717 tokens: a ragged last key tile in
+    # split units (56 tail units)
+    "split_ragged": I.Shape(hidden=1024, heads=8, mlp_hidden=2048, txt_len=77, grid_h=40, grid_w=41,
+                            dtype="bf16", cfg_id=59),
+}
+
+
+@pytest.mark.parametrize("case", list(ISO_CASES))
 def test_attention_branch_isolated(case):
     # cfg3: 512 text + 4096 image tokens (L 4608); cfg2_sharp: 1280 tokens
     # with QK RMSNorm scales times 3 (the online softmax's rescaling path)
-    s = I.CFG3 if case == "cfg3" else I.CFG2
+    s = ISO_CASES[case]
     x = _small_inputs(I.block_inputs(s))
     ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
+    if case == "ref8704":
+        ids = np.concatenate([oracle.make_ids(64, 64, 512), oracle.make_ids(64, 64, 0, frame=1)])
     w = I.attention_only(I.double_block_weights(s, 0))
     if case == "cfg2_sharp":
         w = _sharpened(w, 3.0)
