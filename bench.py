@@ -9,10 +9,14 @@ A step = conditioning vector, all modulations, input projections, the 57
 blocks, the final layer and the fused Euler update (mmdit_step).
 
 Prints ONE JSON line. `value` is the step latency in ms (lower is better).
-Extra fields: HIP-graph replay latency, block TFLOP/s for one dual and one
-single block at 4608 tokens, the quantised-weight step latency, the roofline
-of the dominant GEMM kernel (timed with HIP events on the library's stream)
-and the CPU oracle on a bounded sample.
+Extra fields: every MFMA kernel class of the step (launches per step, average
+launch time from HIP events on the library's stream, TFLOP/s, fraction of the
+bf16 peak, share of the step); `roofline` for the class with the largest
+share; the HBM-bound kernels in the step and alone (cold and warm Infinity
+Cache); weight streaming of a quantised layer at 1 and 16 rows; HIP-graph
+replay; block TFLOP/s (4608 tokens) and the configuration-2 block (1280
+tokens); the bf16-residual, quantised, ternary, reference-image and guided
+variants; and the CPU oracle on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -46,86 +50,25 @@ def step_flops(s):
     return blocks + io
 
 
-def lin1_traffic():
-    """HBM bytes per launch of the linear1 GEMM from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE passes (scaled by a 1 GiB copy's counts), or None
-    when the kernel's sources have changed since those counters were taken."""
+def _profile_record(name):
+    """A committed counter record profiles/<name>.json, or None when missing
+    or when the kernel's sources have changed since the counters were taken
+    (SHA-256 of the listed sources)."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     try:
-        rec = json.load(open(os.path.join(here, "profiles", "gemm_lin1_traffic.json")))
+        rec = json.load(open(os.path.join(here, "profiles", name + ".json")))
         h = hashlib.sha256()
         for src in rec["sources"]:
             with open(os.path.join(here, "diffusion_transformer_mmdit_amd", "csrc", src), "rb") as f:
                 h.update(f.read())
-        if h.hexdigest() != rec["sources_sha256"]:
-            return None
-        return int(rec["traffic_bytes_per_launch"])
+        return rec if h.hexdigest() == rec["sources_sha256"] else None
     except (OSError, KeyError, ValueError):
         return None
-
-
-def vendor_reference(s):
-    """Context only: the ROCm libraries torch calls, on this path's two
-    dominant shapes. torch's bf16 linear (hipBLASLt) on the single-block
-    linear1 GEMM, and torch's flash SDPA on the joint attention (the flash
-    backend is forced: no math-path fallback)."""
-    import torch
-    from torch.nn.attention import SDPBackend, sdpa_kernel
-    res = {}
-    g = torch.Generator(device="cuda")
-    g.manual_seed(5)
-    M, K, N = s.seq_len, s.hidden, 3 * s.hidden + s.mlp_hidden
-    A = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
-    W = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
-
-    def t_ms(fn, n=10):
-        for _ in range(3):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
-    ms = t_ms(lambda: torch.nn.functional.linear(A, W))
-    res["torch_linear_linear1"] = {"shape": [M, N, K], "avg_us": round(ms * 1e3, 1),
-                                   "tflops": round(2.0 * M * N * K / ms / 1e9, 1)}
-    del A, W
-    H, L, D = s.heads, s.seq_len, s.head_dim
-    q, k, v = (torch.randn(1, H, L, D, device="cuda", generator=g).to(torch.bfloat16) for _ in range(3))
-    try:
-        with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
-            ms = t_ms(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v))
-        res["torch_flash_sdpa"] = {"shape": [1, H, L, D], "avg_us": round(ms * 1e3, 1),
-                                   "tflops": round(4.0 * H * L * L * D / ms / 1e9, 1)}
-    except RuntimeError as e:
-        res["torch_flash_sdpa"] = {"unavailable": str(e)[:120]}
-    torch.cuda.synchronize()
-    return res
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def lin1_clock():
-    """Sustained shader clock (GHz) of the linear1 GEMM from the committed
-    GRBM_GUI_ACTIVE pass, or None when the kernel's sources have changed."""
-    import hashlib
-    here = os.path.dirname(os.path.abspath(__file__))
-    try:
-        rec = json.load(open(os.path.join(here, "profiles", "gemm_lin1_clock.json")))
-        h = hashlib.sha256()
-        for src in rec["sources"]:
-            with open(os.path.join(here, "diffusion_transformer_mmdit_amd", "csrc", src), "rb") as f:
-                h.update(f.read())
-        if h.hexdigest() != rec["sources_sha256"]:
-            return None
-        return float(rec["clock_ghz"]), float(rec["max_clock_ghz"])
-    except (OSError, KeyError, ValueError):
-        return None
 
 
 def cpu_baseline(s):
@@ -167,9 +110,11 @@ def cpu_baseline(s):
                 "seconds": round(t_one, 2),
                 "gflops": round(flops2 / t_one / 1e9, 1)}
     return {"value": round(est_ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
+            "value_is": "extrapolated: the timed sample scaled to the full step's block count",
             "gflops": round(step_flops(s) / (est_ms * 1e-3) / 1e9, 1), "one_core": one_core,
-            "sample": (f"numpy float32 oracle, 1 dual block ({t_dual:.2f} s) + 1 single block ({t_single:.2f} s) "
-                       f"at 4608 tokens, scaled to {s.n_double}+{s.n_single} blocks; BLAS "
+            "sample": (f"numpy float32 oracle timed on 1 dual block ({t_dual:.2f} s) + 1 single block "
+                       f"({t_single:.2f} s) at 4608 tokens; value = {s.n_double} x dual + {s.n_single} x single "
+                       f"(the embedders and final layer, under 0.1% of the FLOPs, are not timed); BLAS "
                        f"{info[0].get('internal_api', '?') if info else '?'}, affinity "
                        f"{len(os.sched_getaffinity(0))} cores")}
 
@@ -272,19 +217,40 @@ def main():
     log(f"4-step loop: {loop_ms:.2f} ms")
     flops = step_flops(s)
 
-    # roofline of the dominant kernels, timed with HIP events around each launch
+    # every MFMA-bound kernel class of the step, timed with HIP events around
+    # each launch on the library's stream (mmdit_profile_begin/end)
+    kdesc = {
+        "gemm_res": ("k_gemm_dma<2> gated-residual epilogue: out-projection (K 3072), fc2 (K 12288), linear2 "
+                     "(K 15360); N 3072, M 4608", bd.PC_GEMM_RES),
+        "gemm_lin1": ("k_gemm_dma<6> single-block linear1, split GELU + fused QK RMSNorm/RoPE epilogue; "
+                      "M 4608 N 21504 K 3072", bd.PC_GEMM_LIN1),
+        "attention": ("k_attn_bf16 joint flash attention, 24 heads x 4608 tokens", bd.PC_ATTN),
+        "gemm_fc1": ("k_gemm_dma<1> dual-block fc1, GELU epilogue; M 512+4096 N 12288 K 3072", bd.PC_GEMM_FC1),
+        "gemm_qkv": ("k_gemm_dma<5> dual-block QKV, fused QK RMSNorm/RoPE epilogue; M 512+4096 N 9216 K 3072",
+                     bd.PC_GEMM_QKV),
+    }
     prof = {}
-    for name, cls in (("gemm_lin1", bd.PC_GEMM_LIN1), ("gemm_all", bd.PC_GEMM), ("attention", bd.PC_ATTN)):
+    for name, (desc, cls) in kdesc.items():
         bd.mmdit_profile_begin(cls, 400 * max(1, a.steps))
         for i in range(a.steps):
             step(i)
         tot_ms, n, work = bd.mmdit_profile_end()
-        prof[name] = dict(ms_total=tot_ms, launches=n, flops=work,
-                          avg_us=1e3 * tot_ms / max(n, 1), tflops=work / max(tot_ms, 1e-9) / 1e9)
-        log(f"{name}: {n} launches, avg {prof[name]['avg_us']:.1f} us, {prof[name]['tflops']:.1f} TFLOP/s")
-    # HBM-bound kernels: work counted in algorithmic bytes
+        tf = work / max(tot_ms, 1e-9) / 1e9
+        prof[name] = {"kernel": desc, "launches_per_step": n // max(a.steps, 1),
+                      "avg_us": round(1e3 * tot_ms / max(n, 1), 2), "tflops": round(tf, 1),
+                      "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "flops_per_launch": work / max(n, 1),
+                      "ms_per_step": round(tot_ms / max(a.steps, 1), 3),
+                      "share_of_step": round(tot_ms / max(a.steps, 1) / ms, 4)}
+        log(f"{name}: {prof[name]['launches_per_step']}/step, avg {prof[name]['avg_us']:.1f} us, "
+            f"{tf:.1f} TFLOP/s ({prof[name]['frac']:.3f}), {100 * prof[name]['share_of_step']:.1f}% of the step")
+    # HBM-bound kernels inside the step: algorithmic bytes. The modulation
+    # GEMVs stream 6.49 GB of weights per step (25x the 256 MB Infinity
+    # Cache), so their in-step rate is a cold-cache rate; the LayerNorm reads
+    # a residual the previous GEMM has just written (warm) and is also timed
+    # cold below.
     mem = {}
-    for name, cls in (("layernorm", bd.PC_LN), ("qk_norm_rope", bd.PC_QKNORM), ("gemv", bd.PC_GEMV)):
+    for name, cls in (("layernorm_in_step", bd.PC_LN), ("gemv_in_step", bd.PC_GEMV)):
         bd.mmdit_profile_begin(cls, 400 * max(1, a.steps))
         for i in range(a.steps):
             step(i)
@@ -295,17 +261,19 @@ def main():
                          frac=round(gbps / PEAK_HBM_GBS, 4))
         log(f"{name}: {mem[name]['ms_per_step']:.3f} ms/step in {mem[name]['launches_per_step']} launches, "
             f"{mem[name]['gbps']:.0f} GB/s")
-    dom = "gemm_lin1"
+    # the roofline line names the MFMA kernel class with the largest share of the step
+    dom = max(prof, key=lambda k: prof[k]["share_of_step"])
     p = prof[dom]
-    traffic = lin1_traffic()
-    roofline = {"bound": "mfma", "kernel": "k_gemm_dma 256x256 direct-to-LDS, split epilogue with fused QK "
-                "RMSNorm + RoPE (single-block linear1, M 4608 N 21504 K 3072)", "achieved": round(p["tflops"], 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "avg_launch_us": round(p["avg_us"], 2), "flops_per_launch": p["flops"] / max(p["launches"], 1)}
-    clk = lin1_clock()
+    rec = _profile_record(f"{dom}_traffic")
+    roofline = {"bound": "mfma", "kernel": p["kernel"], "class": dom, "achieved": p["tflops"],
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": p["frac"],
+                "traffic": int(rec["traffic_bytes_per_launch"]) if rec else None,
+                "avg_launch_us": p["avg_us"], "flops_per_launch": p["flops_per_launch"],
+                "share_of_step": p["share_of_step"]}
+    clk = _profile_record(f"{dom}_clock")
     if clk:
-        pk = PEAK_BF16_TFLOPS * clk[0] / clk[1]
-        roofline.update({"clock_ghz_measured": clk[0], "peak_at_measured_clock": round(pk, 1),
+        pk = PEAK_BF16_TFLOPS * float(clk["clock_ghz"]) / float(clk["max_clock_ghz"])
+        roofline.update({"clock_ghz_measured": float(clk["clock_ghz"]), "peak_at_measured_clock": round(pk, 1),
                          "frac_at_measured_clock": round(p["tflops"] / pk, 4)})
 
     out = {"metric": METRIC, "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": a.steps,
@@ -321,9 +289,7 @@ def main():
            "step_tflops": round(flops / ms / 1e9, 1),
            "step_frac_of_bf16_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
            "roofline": roofline,
-           "kernels": {k: {"avg_us": round(v_["avg_us"], 2), "tflops": round(v_["tflops"], 1),
-                           "frac": round(v_["tflops"] / PEAK_BF16_TFLOPS, 4),
-                           "launches_per_step": v_["launches"] // max(a.steps, 1)} for k, v_ in prof.items()},
+           "kernels": {k: {kk: vv for kk, vv in v_.items() if kk != "flops_per_launch"} for k, v_ in prof.items()},
            "hbm_kernels": mem}
 
     if not a.no_extras:
@@ -379,7 +345,165 @@ def main():
                         "flops_per_block": bf}
         log(f"blocks: dual {dms:.3f} ms ({bf / dms / 1e9:.0f} TFLOP/s), single {sms:.3f} ms "
             f"({bf / sms / 1e9:.0f} TFLOP/s)")
-        del dbl, sgl, dblc, sglc
+        del dbl, sgl, dblc, sglc, wsb
+
+        # configuration 2: one dual block at 512x512 (256 text + 1024 image
+        # tokens), two weight sets alternating (680 MB each)
+        s2 = I.CFG2
+        dims2 = bd.make_dims(s2)
+        d2 = [RI.double_block(s2, 300 + i, dev) for i in range(2)]
+        d2c = [d.c() for d in d2]
+        img2 = torch.randn((1, s2.img_len, s2.hidden), generator=g, device=dev).to(torch.bfloat16)
+        txt2 = torch.randn((1, s2.txt_len, s2.hidden), generator=g, device=dev).to(torch.bfloat16)
+        ids2 = torch.from_numpy(bd.mmdit_make_ids(s2.grid_h, s2.grid_w, s2.txt_len)).to(dev)
+        ws2 = torch.empty(bd.mmdit_double_block_workspace(dims2), dtype=torch.uint8, device=dev)
+        io2, to2 = torch.empty_like(img2), torch.empty_like(txt2)
+        f2 = lambda i: bd.mmdit_double_block_fwd(dims2, d2c[i % 2], img2, txt2, io2, to2, vec, ids2, ws2)  # noqa
+        for i in range(4):
+            f2(i)
+        c2ms = timed(f2, max(4 * a.steps, 16))
+        bf2 = block_flops(s2)
+        out["config2_dual_block"] = {"ms": round(c2ms, 4), "tflops": round(bf2 / c2ms / 1e9, 1),
+                                     "frac": round(bf2 / c2ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                     "block_fwd_per_s": round(1e3 / c2ms, 1), "flops": bf2,
+                                     "tokens": s2.seq_len}
+        log(f"config-2 dual block (1280 tokens): {c2ms:.4f} ms ({bf2 / c2ms / 1e9:.0f} TFLOP/s)")
+        del d2, d2c, ws2
+
+        # the step with its residual stream held in bf16 (dims.resid)
+        cfg16 = bd.make_config(s, resid=bd.RESID_BF16)
+        ws16 = torch.empty(bd.mmdit_step_workspace(cfg16), dtype=torch.uint8, device=dev)
+        X16 = X.clone()
+        st16 = lambda i: bd.mmdit_step(cfg16, mc, X16, v, T, y, ids, sig[i % 4], sig[i % 4 + 1], ws16)  # noqa
+        for i in range(2):
+            st16(i)
+        out["bf16_residual_ms_per_step"] = round(timed(st16, a.steps), 3)
+        log(f"bf16-residual step: {out['bf16_residual_ms_per_step']:.2f} ms")
+        del ws16, X16
+
+        # HBM-bound kernels alone, cold and warm. Cold: a pass that reads a
+        # 512 MB buffer evicts the 256 MB Infinity Cache before each call (a
+        # write pass would leave dirty lines whose write-back then overlaps
+        # the timed call); warm: the call repeated on the same buffers. All
+        # calls of a measurement are enqueued back to back (arguments
+        # marshalled once, raw C calls) before one synchronisation, so that
+        # no start event waits for the host.
+        import ctypes as C
+        evict = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        evict_sink = torch.empty((), dtype=torch.float32, device=dev)
+        stream_h = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+        def evict_pass():
+            torch.sum(evict, dim=0, out=evict_sink)
+
+        def kernel_times(calls, pre=None):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+            evict.fill_(7)  # head start: the GPU is busy while the host enqueues
+            sts = []
+            for (e0, e1), c in zip(ev, calls):
+                if pre is not None:
+                    pre()
+                e0.record()
+                sts.append(c())
+                e1.record()
+            torch.cuda.synchronize()
+            assert all(st == 0 for st in sts), sts
+            return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+        def rate(ts, nbytes):
+            t = float(np.median(ts))
+            return {"us": round(1e3 * t, 2), "gbps": round(nbytes / t / 1e6, 1),
+                    "frac": round(nbytes / t / 1e6 / PEAK_HBM_GBS, 4)}
+
+        def cold_warm(call, nbytes, n=12):
+            call()
+            return {"cold": rate(kernel_times([call] * n, pre=evict_pass), nbytes),
+                    "warm": rate(kernel_times([call] * n), nbytes), "bytes": int(nbytes)}
+        hbm = {}
+        rows, h = s.seq_len, s.hidden
+        xl = torch.randn((rows, h), generator=g, device=dev)
+        yl = torch.empty((rows, h), dtype=torch.bfloat16, device=dev)
+        modl = torch.randn((2, h), generator=g, device=dev) * 0.3
+        f_ln = bd.lib().mmdit_adaln_layernorm
+        ln_args = (xl.data_ptr(), 1, yl.data_ptr(), bd.BF16, rows, h, modl.data_ptr(), C.c_float(1e-6), stream_h)
+        hbm["layernorm"] = cold_warm(lambda: f_ln(*ln_args), rows * h * 6)
+        hbm["layernorm"]["shape"] = f"{rows} x {h}, float32 in, bf16 out"
+        del xl, yl
+        qd = RI._linear(RI._Gen(47, dev), 3 * h + s.mlp_hidden, h, torch.bfloat16, 4)
+        wd = torch.empty((qd.n_out, qd.k_in), dtype=torch.bfloat16, device=dev)
+        nq = qd.n_out * qd.k_in
+        f_dq = bd.lib().mmdit_dequantise
+        dq_args = (qd.w.data_ptr(), qd.scales.data_ptr(), bd.W_Q4G64, qd.n_out, qd.k_in, wd.data_ptr(), stream_h)
+        hbm["dequant_q4"] = cold_warm(lambda: f_dq(*dq_args), nq * 0.5 + nq / 64 * 2 + nq * 2)
+        hbm["dequant_q4"]["shape"] = f"{qd.n_out} x {qd.k_in} 4-bit codes -> bf16"
+        del qd, wd
+        out["hbm_alone"] = hbm
+        log(f"HBM kernels alone: {hbm}")
+
+        f_lin = bd.lib().mmdit_linear_fwd
+
+        def lin_call(lin, xm, ym, route, ws=None):
+            lc = lin.c()
+            args = (C.byref(lc), bd.BF16, xm.data_ptr(), xm.shape[0], ym.data_ptr(),
+                    int(ym.dtype == torch.float32), route, None if ws is None else ws.data_ptr(),
+                    0 if ws is None else ws.numel(), stream_h)
+            return lambda: f_lin(*args) if lc is not None else -1
+
+        # weight streaming: one linear layer (linear1's shape, 21504 x 3072)
+        # at 1 and 16 rows, every format, on the weight-streaming route; the
+        # calls cycle through enough copies of the layer (>= 512 MB) that each
+        # reads its weights from HBM. GB/s counts codes + scales.
+        n_out, k_in = 3 * h + s.mlp_hidden, h
+        stream = {}
+        wbytes = {0: 2.0, 4: 0.5 + 2 / 64, 8: 1.0 + 2 / 64, 1: 0.125 + 2 / 128, 2: 0.25 + 2 / 128}
+        for fname, bits in (("dense", 0), ("q4g64", 4), ("q8g64", 8), ("q1g128", 1), ("tq2g128", 2)):
+            per = n_out * k_in * wbytes[bits]
+            copies = max(2, int(np.ceil((512 << 20) / per)))
+            G = RI._Gen(50 + bits, dev)
+            pool = [RI._linear(G, n_out, k_in, torch.bfloat16, bits) for _ in range(copies)]
+            stream[fname] = {"weight_bytes": int(per), "copies": copies}
+            for rows_m in (1, 16):
+                xm = torch.randn((rows_m, k_in), generator=g, device=dev).to(torch.bfloat16)
+                ym = torch.empty((rows_m, n_out), dtype=torch.float32, device=dev)
+                calls = [lin_call(pool[i % copies], xm, ym, bd.ROUTE_STREAM) for i in range(4 * copies)]
+                kernel_times(calls[:copies])
+                stream[fname][f"M{rows_m}"] = rate(kernel_times(calls)[copies:], per)
+            del pool
+            # one layer 8x as wide (172032 x 3072): the per-launch start-up,
+            # a few microseconds, weighs less against the weight bytes
+            G = RI._Gen(70 + bits, dev)
+            big = [RI._linear(G, 8 * n_out, k_in, torch.bfloat16, bits) for _ in range(max(2, copies // 8))]
+            xm = torch.randn((1, k_in), generator=g, device=dev).to(torch.bfloat16)
+            ym = torch.empty((1, 8 * n_out), dtype=torch.float32, device=dev)
+            calls = [lin_call(big[i % len(big)], xm, ym, bd.ROUTE_STREAM) for i in range(4 * len(big))]
+            kernel_times(calls[:len(big)])
+            stream[fname]["M1_8x_wide"] = rate(kernel_times(calls)[len(big):], 8 * per)
+            del big
+        out["weight_streaming"] = stream
+        log(f"weight streaming (21504 x 3072): {stream}")
+
+        # routes of a 4-bit layer (linear1's shape) against the row count:
+        # weight streaming (M <= 16), dequantisation inside the tiled GEMM,
+        # and decoding the layer once to bf16 before the dense GEMM
+        G = RI._Gen(60, dev)
+        lq = RI._linear(G, n_out, k_in, torch.bfloat16, 4)
+        wsr = torch.empty(bd.mmdit_linear_workspace(lq, bd.BF16, 4608, bd.ROUTE_DECODE), dtype=torch.uint8,
+                          device=dev)
+        routes = {}
+        for rows_m in (1, 16, 256, 1024, 4608):
+            xm = torch.randn((rows_m, k_in), generator=g, device=dev).to(torch.bfloat16)
+            ym = torch.empty((rows_m, n_out), dtype=torch.bfloat16, device=dev)
+            r = {}
+            for rname, rt in (("stream", bd.ROUTE_STREAM), ("tiled", bd.ROUTE_TILED), ("decode", bd.ROUTE_DECODE)):
+                if rt == bd.ROUTE_STREAM and rows_m > 16:
+                    continue
+                c = lin_call(lq, xm, ym, rt, wsr)
+                c()
+                r[rname + "_us"] = round(1e3 * float(np.median(kernel_times([c] * 8, pre=evict_pass))), 2)
+            routes[f"M{rows_m}"] = r
+        out["q4_routes_vs_rows"] = routes
+        log(f"4-bit routes against rows (cold): {routes}")
+        del lq, wsr, evict
 
         # quantised-weight step (4-bit inner projections, 8-bit residual-writing layers)
         Mq = RI.model(I.CFG5, seed=43, device=dev, quant=bd.QUANT_POLICY)
@@ -490,10 +614,6 @@ def main():
             f"{csec:.2f} s ({dsec / csec:.2f}x), final latent rel-L2 {drift:.4f} vs uncached")
         M.guidance = None
         del Xd, Xq, mdc, keep, cache
-
-    if not a.no_extras:
-        out["vendor_reference"] = vendor_reference(s)
-        log(f"vendor reference: {out['vendor_reference']}")
 
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

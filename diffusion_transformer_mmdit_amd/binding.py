@@ -20,6 +20,8 @@ F32, BF16 = 0, 1
 RESID_DEFAULT, RESID_F32, RESID_BF16 = 0, 1, 2
 W_DENSE, W_Q4G64, W_Q8G64, W_Q1G128, W_TQ2G128 = 0, 1, 2, 3, 4
 PC_GEMM, PC_ATTN, PC_LN, PC_QKNORM, PC_GEMV, PC_GEMM_LIN1, PC_GEMM_RES, PC_DEQUANT = 1, 2, 3, 4, 5, 6, 7, 8
+PC_GEMM_QKV, PC_GEMM_FC1, PC_STREAM = 9, 10, 11
+ROUTE_AUTO, ROUTE_TILED, ROUTE_DECODE, ROUTE_STREAM = 0, 1, 2, 3
 
 
 class MMDiTError(RuntimeError):
@@ -109,6 +111,11 @@ _SIGS = {
     "mmdit_rope_table": (C.c_int, [_P, C.c_int32, _P, C.c_double, _P, _P]),
     "mmdit_quantise": (C.c_int, [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P]),
     "mmdit_dequantise": (C.c_int, [_P, _P, C.c_int32, C.c_int32, C.c_int32, _P, _P]),
+    "mmdit_adaln_layernorm": (C.c_int, [_P, C.c_int32, _P, C.c_int32, C.c_int32, C.c_int32, _P, C.c_float, _P]),
+    "mmdit_linear_workspace": (C.c_int, [C.POINTER(mmdit_linear), C.c_int32, C.c_int32, C.c_int32,
+                                         C.POINTER(C.c_size_t)]),
+    "mmdit_linear_fwd": (C.c_int, [C.POINTER(mmdit_linear), C.c_int32, _P, C.c_int32, _P, C.c_int32, C.c_int32,
+                                   _P, C.c_size_t, _P]),
     "mmdit_profile_begin": (C.c_int, [C.c_int32, C.c_int32]),
     "mmdit_profile_end": (C.c_int, [C.POINTER(C.c_double), C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
     "mmdit_status_str": (C.c_char_p, [C.c_int32]),
@@ -458,6 +465,34 @@ def mmdit_dequantise(w, scales, fmt: int, n_out: int, k_in: int, out, stream=Non
     the bf16 tensor `out` [n_out, k_in]."""
     _check(lib().mmdit_dequantise(_ptr(w), _ptr(scales), fmt, n_out, k_in, _ptr(out), _stream(stream)),
            "mmdit_dequantise")
+
+
+def mmdit_adaln_layernorm(x, y, shift_scale, eps: float = 1e-6, stream=None):
+    """y = (1 + scale) LN(x) + shift over the last axis; x float32 or in y's
+    dtype, shift_scale float32 [2, hidden]."""
+    import torch
+    act = BF16 if y.dtype == torch.bfloat16 else F32
+    rows, hidden = y.numel() // y.shape[-1], y.shape[-1]
+    _check(lib().mmdit_adaln_layernorm(_ptr(x), int(x.dtype == torch.float32), _ptr(y), act, rows, hidden,
+                                       _ptr(shift_scale), float(eps), _stream(stream)), "mmdit_adaln_layernorm")
+
+
+def mmdit_linear_workspace(lin: Linear, act_dtype: int, M: int, route: int = ROUTE_AUTO) -> int:
+    n = C.c_size_t()
+    lc = lin.c()
+    _check(lib().mmdit_linear_workspace(C.byref(lc), act_dtype, M, route, C.byref(n)), "mmdit_linear_workspace")
+    return n.value
+
+
+def mmdit_linear_fwd(lin: Linear, x, y, route: int = ROUTE_AUTO, ws=None, stream=None):
+    """y [M, n_out] = x [M, k_in] W^T + b; y float32 or x's dtype."""
+    import torch
+    act = BF16 if x.dtype == torch.bfloat16 else F32
+    M = x.numel() // x.shape[-1]
+    lc = lin.c()
+    _check(lib().mmdit_linear_fwd(C.byref(lc), act, _ptr(x), M, _ptr(y), int(y.dtype == torch.float32), route,
+                                  _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "mmdit_linear_fwd")
 
 
 def mmdit_profile_begin(kernel_class: int, max_launches: int):

@@ -57,7 +57,8 @@ struct Prof {
 };
 Prof g_prof;
 
-enum { PC_GEMM = 1, PC_ATTN = 2, PC_LN = 3, PC_QKNORM = 4, PC_GEMV = 5, PC_GEMM_LIN1 = 6, PC_GEMM_RES = 7, PC_DEQUANT = 8 };
+enum { PC_GEMM = 1, PC_ATTN = 2, PC_LN = 3, PC_QKNORM = 4, PC_GEMV = 5, PC_GEMM_LIN1 = 6, PC_GEMM_RES = 7, PC_DEQUANT = 8,
+       PC_GEMM_QKV = 9, PC_GEMM_FC1 = 10, PC_STREAM = 11 };
 
 struct ProfScope {
   hipEvent_t stop = nullptr;
@@ -340,7 +341,11 @@ int gemm(const Ctx& c, GemmProblem* p, int np, int epi) {
   double flops = 0;
   for (int i = 0; i < np; ++i) flops += 2.0 * p[i].M * (double)p[i].N * p[i].K;
   ProfScope ps(PC_GEMM, flops, c.s,
-               epi == EPI_SPLIT || epi == EPI_SPLIT_QKV ? PC_GEMM_LIN1 : (epi == EPI_GATE_RES ? PC_GEMM_RES : -1));
+               epi == EPI_SPLIT || epi == EPI_SPLIT_QKV ? PC_GEMM_LIN1
+               : epi == EPI_GATE_RES                   ? PC_GEMM_RES
+               : epi == EPI_QKV                        ? PC_GEMM_QKV
+               : epi == EPI_GELU                       ? PC_GEMM_FC1
+                                                       : -1);
   if (!c.g.bf16) HIP_TRY(launch_gemm_f32(p, np, epi, c.s));
   else if (gemm_dma_eligible(p, np, epi)) HIP_TRY(launch_gemm_dma(p, np, epi, c.s));
   else HIP_TRY(launch_gemm_bf16(p, np, epi, c.s));
@@ -419,6 +424,7 @@ bool fuse_qk(const Ctx& c, GemmProblem* gp, int np, const Part* parts, const voi
     gp[p].rope = table;
     gp[p].qk_h = g.h; gp[p].qk_rows = parts[p].len; gp[p].qk_tok0 = tok0; gp[p].qk_Lpad = g.Lpad;
     gp[p].qk_eps = c.rms_eps;
+    gp[p].qk_qscale = kAttnQScale;
     tok0 += parts[p].len;
   }
   return gemm_dma_eligible(gp, np, epi);
@@ -441,6 +447,7 @@ int run_qk_attn(const Ctx& c, const Part* parts, int np, void* qkv, const void* 
   q.table = table;
   q.Q = ptr(ws, w.q); q.K = ptr(ws, w.k); q.V = ptr(ws, w.v);
   q.B = g.B; q.H = g.H; q.L = g.L; q.Lpad = g.Lpad; q.eps = c.rms_eps;
+  q.qscale = g.bf16 ? kAttnQScale : 1.0f;
   if (qk_fused) {  // Q, K and V^T are written; only the pad rows remain
     if (g.Lpad > g.L) HIP_TRY(launch_qkv_pad_zero(q, c.s));
   } else {
@@ -977,6 +984,117 @@ int mmdit_step_ex(const mmdit_config* cfg, const mmdit_model_w* w, void* x_packe
   return step_impl(cfg, w, x_packed, v_out, txt_emb, y, ids, sigma, sigma_next, opts, ws, ws_bytes, hip_stream);
 }
 
+// ------------------------------------------------------------ single ops --
+int mmdit_adaln_layernorm(const void* x, int32_t x_f32, void* y, int32_t act_dtype, int32_t rows, int32_t hidden,
+                          const float* shift_scale, float eps, void* hip_stream) {
+  if (rows < 0) return fail(MMDIT_ERR_SHAPE, "rows %d < 0", rows);
+  if (rows == 0) return MMDIT_OK;
+  if (!x || !y || !shift_scale) return fail(MMDIT_ERR_NULL, "NULL x, y or shift_scale");
+  if (act_dtype != MMDIT_F32 && act_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "act_dtype %d", act_dtype);
+  if (hidden < 256 || hidden > 4096 || hidden % 256)
+    return fail(MMDIT_ERR_SHAPE, "hidden %d must be a multiple of 256 in [256, 4096]", hidden);
+  if (!(eps > 0)) return fail(MMDIT_ERR_SHAPE, "eps must be > 0");
+  const bool bf = act_dtype == MMDIT_BF16;
+  const bool xf = x_f32 || !bf;
+  if ((uintptr_t)x % 16 || (uintptr_t)y % 16 || (uintptr_t)shift_scale % 16)
+    return fail(MMDIT_ERR_SHAPE, "x, y and shift_scale must be 16-byte aligned");
+  LnArgs a{};
+  RowSeg r;
+  r.base = const_cast<void*>(x);
+  r.batch_stride = (int64_t)rows * hidden;
+  r.rows_per_batch = rows;
+  r.ld = hidden;
+  a.seg[0] = a.seg[1] = r;
+  a.seg_rows[0] = rows;
+  a.seg_rows[1] = 0;
+  a.mod[0] = a.mod[1] = shift_scale;
+  a.mod_bstride = 0;
+  a.shift_off = 0;
+  a.scale_off = hidden;
+  a.y = y;
+  a.h = hidden;
+  a.eps = eps;
+  ProfScope ps(PC_LN, (double)rows * hidden * ((xf ? 4 : 2) + (bf ? 2 : 4)), (hipStream_t)hip_stream);
+  HIP_TRY(launch_adaln_ln(a, rows, xf, bf, (hipStream_t)hip_stream));
+  return MMDIT_OK;
+}
+
+// Route of mmdit_linear_fwd for bf16 activations.
+static int linear_route(const mmdit_linear& l, int M, int route) {
+  if (route != MMDIT_ROUTE_AUTO) return route;
+  if (M <= 16 && l.k_in % 128 == 0) return MMDIT_ROUTE_STREAM;
+  if (l.fmt != MMDIT_W_DENSE && M >= kExpandMinRows) return MMDIT_ROUTE_DECODE;
+  return MMDIT_ROUTE_TILED;
+}
+
+static int check_linear_call(const mmdit_linear* l, int32_t act_dtype, int32_t M, int32_t route, Geo& g) {
+  if (!l) return fail(MMDIT_ERR_NULL, "linear is NULL");
+  if (act_dtype != MMDIT_F32 && act_dtype != MMDIT_BF16) return fail(MMDIT_ERR_DTYPE, "act_dtype %d", act_dtype);
+  if (M < 0 || l->n_out < 1 || l->k_in < 1) return fail(MMDIT_ERR_SHAPE, "need M >= 0, n_out >= 1, k_in >= 1");
+  if (route < MMDIT_ROUTE_AUTO || route > MMDIT_ROUTE_STREAM) return fail(MMDIT_ERR_SHAPE, "route %d", route);
+  g = Geo{};
+  g.B = 1;
+  g.bf16 = act_dtype == MMDIT_BF16;
+  g.esz = g.bf16 ? 2 : 4;
+  g.L = M;
+  int r;
+  if ((r = check_linear(*l, l->n_out, l->k_in, g, "linear"))) return r;
+  if (!g.bf16 && route != MMDIT_ROUTE_AUTO && route != MMDIT_ROUTE_TILED)
+    return fail(MMDIT_ERR_UNSUPPORTED, "float32 layers run on the tiled route only");
+  if (g.bf16) {
+    const int rt = linear_route(*l, M, route);
+    if (rt == MMDIT_ROUTE_STREAM && (M > 16 || l->k_in % 128))
+      return fail(MMDIT_ERR_SHAPE, "the weight-streaming route needs M <= 16 and k_in a multiple of 128");
+    if (rt == MMDIT_ROUTE_DECODE && l->fmt == MMDIT_W_DENSE)
+      return fail(MMDIT_ERR_SHAPE, "the decoding route needs a quantised layer");
+  }
+  if ((int64_t)M * l->k_in >= (int64_t(1) << 31) || (int64_t)M * l->n_out >= (int64_t(1) << 31))
+    return fail(MMDIT_ERR_SHAPE, "M * width too large for 32-bit indexing");
+  return MMDIT_OK;
+}
+
+int mmdit_linear_workspace(const mmdit_linear* l, int32_t act_dtype, int32_t M, int32_t route, size_t* bytes) {
+  Geo g;
+  int r;
+  if (!bytes) return fail(MMDIT_ERR_NULL, "bytes is NULL");
+  if ((r = check_linear_call(l, act_dtype, M, route, g))) return r;
+  *bytes = g.bf16 && linear_route(*l, M, route) == MMDIT_ROUTE_DECODE ? align_up((size_t)l->n_out * l->k_in * 2) : 0;
+  return MMDIT_OK;
+}
+
+int mmdit_linear_fwd(const mmdit_linear* l, int32_t act_dtype, const void* x, int32_t M, void* y, int32_t y_f32,
+                     int32_t route, void* ws, size_t ws_bytes, void* hip_stream) {
+  Geo g;
+  int r;
+  if ((r = check_linear_call(l, act_dtype, M, route, g))) return r;
+  if (M == 0) return MMDIT_OK;
+  if (!x || !y) return fail(MMDIT_ERR_NULL, "NULL x or y");
+  if ((uintptr_t)x % 16 || (uintptr_t)y % 16) return fail(MMDIT_ERR_SHAPE, "x and y must be 16-byte aligned");
+  const hipStream_t st = (hipStream_t)hip_stream;
+  const bool yf = y_f32 || !g.bf16;
+  const int rt = g.bf16 ? linear_route(*l, M, route) : MMDIT_ROUTE_TILED;
+  size_t need = 0;
+  if ((r = mmdit_linear_workspace(l, act_dtype, M, route, &need))) return r;
+  if (need && (!ws || ws_bytes < need)) return fail(MMDIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  if (rt == MMDIT_ROUTE_STREAM) {
+    const double wb = l->fmt == MMDIT_W_DENSE ? 2.0 : l->fmt == MMDIT_W_Q4G64 ? 0.5 + 2.0 / 64
+                      : l->fmt == MMDIT_W_Q8G64 ? 1.0 + 2.0 / 64 : l->fmt == MMDIT_W_Q1G128 ? 0.125 + 2.0 / 128
+                      : 0.25 + 2.0 / 128;
+    ProfScope ps(PC_STREAM, (double)l->n_out * l->k_in * wb, st);
+    HIP_TRY(launch_linear_skinny(x, M, l->w, l->scales, l->bias, l->fmt, y, yf, l->n_out, l->k_in, st));
+    return MMDIT_OK;
+  }
+  Ctx c{st, g, 1e-6f, 1e-6f};
+  if (rt == MMDIT_ROUTE_DECODE) {
+    c.xw = ws;
+    c.xw_bytes = ws_bytes;
+  }
+  GemmProblem p = base_problem(*l);
+  p.A = x; p.lda = l->k_in; p.M = M;
+  p.out = y; p.ldo = l->n_out; p.out_f32 = yf;
+  return gemm(c, &p, 1, EPI_STORE);
+}
+
 int mmdit_pack_latents(const void* z, void* x, int32_t B, int32_t C, int32_t H, int32_t W,
                        int32_t elem_bytes, void* hip_stream) {
   if (!z || !x) return fail(MMDIT_ERR_NULL, "NULL buffer");
@@ -1008,7 +1126,7 @@ int mmdit_rope_table(const int32_t* ids, int32_t L, const int32_t* axes_dim, dou
 
 int mmdit_profile_begin(int32_t kernel_class, int32_t max_launches) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
-  if (kernel_class < PC_GEMM || kernel_class > PC_DEQUANT) return fail(MMDIT_ERR_SHAPE, "unknown kernel class %d", kernel_class);
+  if (kernel_class < PC_GEMM || kernel_class > PC_STREAM) return fail(MMDIT_ERR_SHAPE, "unknown kernel class %d", kernel_class);
   if (max_launches < 1 || max_launches > 1 << 20) return fail(MMDIT_ERR_SHAPE, "max_launches out of range");
   if (g_prof.active) return fail(MMDIT_ERR_UNSUPPORTED, "profiling already active");
   for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);

@@ -126,11 +126,14 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
+  // Scores arrive as exp2 arguments: Q carries scale * log2(e), and the
+  // score MFMAs of every tile after the first start from -m_run, so
+  // s = S c2 - m_run with m_run the running max (first tile: s = S c2).
   f32x16 s[2];
   bf16x8 pb[4];
   constexpr float kNegBig = -1e30f;
   float m_run = kNegBig, l_run = 0.f;
-  const float c2 = a.scale * 1.4426950408889634f;
+  float s_init = 0.f;  // -m_run once the first tile has set m_run
 
   // MFMA phase pieces. V^T fragments of dim blocks db0, db0+1 (8 reads) and
   // K fragments of dims 16*kk0 .. 16*kk0+63 (8 reads); MFMA groups of 8:
@@ -183,8 +186,8 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
     rd_k(ka, sk, 0);
     mm_v4(va, vb, 2);
     rd_k(kc, sk, 4);
-    s[0] = (f32x16){};
-    s[1] = (f32x16){};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[0][i] = s[1][i] = s_init;
     mm_k(ka, 0);
     mm_k(kc, 4);
     __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
@@ -200,8 +203,8 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
     bf16x8 ka[8], kc[8];
     rd_k(ka, sk, 0);
     rd_k(kc, sk, 4);
-    s[0] = (f32x16){};
-    s[1] = (f32x16){};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[0][i] = s[1][i] = s_init;
     mm_k(ka, 0);
     mm_k(kc, 4);
     __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
@@ -219,7 +222,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
     __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  // softmax of S(kt). Probabilities p = exp2(s c2 - m_run) go to bf16 for
+  // softmax of S(kt). Probabilities p = exp2(s) = exp2(S c2 - m_run) go to bf16 for
   // the PV product; their row sums stay float32. Fast path: m_run is kept
   // while every p stays at most kPMax. All p are non-negative, so a row sum
   // (both lanes of a query) at most kPMax bounds each of them, and no tile max
@@ -234,7 +237,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -m_run));
+        const float p = __builtin_amdgcn_exp2f(s[kb][r]);
         if (r & 1) ps1 += p; else ps0 += p;
         pb[kb * 2 + (r >> 3)][r & 7] = (bf16)p;
       }
@@ -264,16 +267,24 @@ __device__ __forceinline__ void attn_unit(const AttnArgs& a, char* smem, int uni
 #pragma unroll
       for (int r = 1; r < 15; r += 2) mx = fmaxf(mx, fmaxf(s[1][r], s[1][r + 1]));
       mx = fmaxf(mx, s[1][15]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
-      const float m_new = fmaxf(m_run, mx);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // s = S c2 - base with base = -s_init (0 on the first tile)
+      const float base = -s_init;
+      const float m_new = fmaxf(m_run, mx + base);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
       l_run *= alpha;
       m_run = m_new;
+      const float delta = m_new - base;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] -= delta;
       ps = probs();
     }
     l_run += ps;
+    s_init = -m_run;
     // keep the conversions in this phase (they would sink to their MFMAs)
 #pragma unroll
     for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[i]));

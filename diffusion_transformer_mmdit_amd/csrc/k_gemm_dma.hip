@@ -332,7 +332,8 @@ __device__ __forceinline__ void qk_epilogue(const GemmProblem& P, char* smem, in
 #pragma unroll
     for (int c = 0; c < 64; ++c) ss += v[c] * v[c];
     ss += __shfl_xor(ss, 32);
-    const float rstd = 1.0f / sqrtf(ss * (1.0f / 128.0f) + eps);
+    // q rows carry the attention's score scale
+    const float rstd = (which ? 1.0f : P.qk_qscale) / sqrtf(ss * (1.0f / 128.0f) + eps);
     const int m = m0w + 32 * i + r;
     if (m < M) {
       const int b = m / rows;

@@ -65,70 +65,142 @@ __global__ __launch_bounds__(256) void k_adaln_ln(LnArgs a, int rows) {
   }
 }
 
-// One 256-thread block per row when h is a multiple of 1024: each thread
-// holds C = h / 1024 chunks of 4 (chunk i at column 4 (256 i + tid)); shift
-// and scale are requested together with x, before the reductions; the two
-// block reductions go through LDS.
-template <typename TX, typename TY, int C>
-__global__ __launch_bounds__(256) void k_adaln_ln_row(LnArgs a) {
-  __shared__ float red[2][4];
+// R rows per 256-thread block (h a multiple of 1024) when the R rows share
+// one modulation vector (same segment and batch): shift and scale are read
+// once per block instead of once per row (for h 3072 they are 24 KB of
+// float32 against 12 KB of x per row), the R rows' x are all requested
+// before the reductions, and the R rows' sums share each block reduction.
+// Blocks whose rows do not share a modulation vector, and a last partial
+// block, run their rows one at a time.
+template <typename TX, typename TY, int C, int R>
+__global__ __launch_bounds__(256) void k_adaln_ln_rows(LnArgs a, int rows) {
+  __shared__ float red[2][R][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = blockIdx.x;
-  const int s = r < a.seg_rows[0] ? 0 : 1;
-  const int local = s == 0 ? r : r - a.seg_rows[0];
-  const TX* x = reinterpret_cast<const TX*>(seg_row(a.seg[s], local, sizeof(TX)));
-  const int b = local / a.seg[s].rows_per_batch;
-  const float* mod = a.mod[s] + (int64_t)b * a.mod_bstride;
-  float v[C][4], sh[C][4], sc[C][4];
-#pragma unroll
-  for (int i = 0; i < C; ++i) load4(x + (i * 256 + tid) * 4, v[i]);
-#pragma unroll
-  for (int i = 0; i < C; ++i) {
-    load4(mod + a.shift_off + (i * 256 + tid) * 4, sh[i]);
-    load4(mod + a.scale_off + (i * 256 + tid) * 4, sc[i]);
-  }
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < C; ++i) sum += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
-  sum = wave_sum(sum);
-  if (lane == 0) red[0][wave] = sum;
-  __syncthreads();
+  const int r0 = blockIdx.x * R;
+  auto where = [&](int r, int& s, int& local, int& b) {
+    s = r < a.seg_rows[0] ? 0 : 1;
+    local = s == 0 ? r : r - a.seg_rows[0];
+    b = local / a.seg[s].rows_per_batch;
+  };
+  int s0, l0, b0, s1, l1, b1;
+  where(r0, s0, l0, b0);
+  where(r0 + R - 1 < rows ? r0 + R - 1 : rows - 1, s1, l1, b1);
   const float inv_h = 1.0f / (float)(C * 1024);
-  const float mean = ((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) * inv_h;
-  float sq = 0.f;
+  if (r0 + R <= rows && s0 == s1 && b0 == b1) {
+    const float* mod = a.mod[s0] + (int64_t)b0 * a.mod_bstride;
+    float v[R][C][4], sh[C][4], sc[C][4];
 #pragma unroll
-  for (int i = 0; i < C; ++i)
+    for (int q = 0; q < R; ++q) {
+      const TX* x = reinterpret_cast<const TX*>(seg_row(a.seg[s0], l0 + q, sizeof(TX)));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float d = v[i][j] - mean;
-      sq += d * d;
+      for (int i = 0; i < C; ++i) load4(x + (i * 256 + tid) * 4, v[q][i]);
     }
-  sq = wave_sum(sq);
-  if (lane == 0) red[1][wave] = sq;
-  __syncthreads();
-  const float var = ((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) * inv_h;
-  const float rstd = 1.0f / sqrtf(var + a.eps);
-  TY* y = reinterpret_cast<TY*>(a.y) + (int64_t)r * a.h;
 #pragma unroll
-  for (int i = 0; i < C; ++i) {
-    float o[4];
+    for (int i = 0; i < C; ++i) {
+      load4(mod + a.shift_off + (i * 256 + tid) * 4, sh[i]);
+      load4(mod + a.scale_off + (i * 256 + tid) * 4, sc[i]);
+    }
+    float mean[R], rstd[R];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = (1.0f + sc[i][j]) * ((v[i][j] - mean) * rstd) + sh[i][j];
-    store4(y + (i * 256 + tid) * 4, o);
+    for (int q = 0; q < R; ++q) {
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < C; ++i) sum += (v[q][i][0] + v[q][i][1]) + (v[q][i][2] + v[q][i][3]);
+      sum = wave_sum(sum);
+      if (lane == 0) red[0][q][wave] = sum;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      mean[q] = ((red[0][q][0] + red[0][q][1]) + (red[0][q][2] + red[0][q][3])) * inv_h;
+      float sq = 0.f;
+#pragma unroll
+      for (int i = 0; i < C; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float d = v[q][i][j] - mean[q];
+          sq += d * d;
+        }
+      sq = wave_sum(sq);
+      if (lane == 0) red[1][q][wave] = sq;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const float var = ((red[1][q][0] + red[1][q][1]) + (red[1][q][2] + red[1][q][3])) * inv_h;
+      rstd[q] = 1.0f / sqrtf(var + a.eps);
+      TY* y = reinterpret_cast<TY*>(a.y) + (int64_t)(r0 + q) * a.h;
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        float o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = (1.0f + sc[i][j]) * ((v[q][i][j] - mean[q]) * rstd[q]) + sh[i][j];
+        store4(y + (i * 256 + tid) * 4, o);
+      }
+    }
+    return;
+  }
+  // rows one at a time (block-uniform loop)
+  for (int q = 0; q < R; ++q) {
+    const int r = r0 + q;
+    if (r >= rows) break;
+    int s, local, b;
+    where(r, s, local, b);
+    const TX* x = reinterpret_cast<const TX*>(seg_row(a.seg[s], local, sizeof(TX)));
+    const float* mod = a.mod[s] + (int64_t)b * a.mod_bstride;
+    float v[C][4];
+#pragma unroll
+    for (int i = 0; i < C; ++i) load4(x + (i * 256 + tid) * 4, v[i]);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < C; ++i) sum += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+    sum = wave_sum(sum);
+    if (lane == 0) red[0][0][wave] = sum;
+    __syncthreads();
+    const float mean = ((red[0][0][0] + red[0][0][1]) + (red[0][0][2] + red[0][0][3])) * inv_h;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < C; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float d = v[i][j] - mean;
+        sq += d * d;
+      }
+    sq = wave_sum(sq);
+    if (lane == 0) red[1][0][wave] = sq;
+    __syncthreads();
+    const float var = ((red[1][0][0] + red[1][0][1]) + (red[1][0][2] + red[1][0][3])) * inv_h;
+    const float rstd = 1.0f / sqrtf(var + a.eps);
+    TY* y = reinterpret_cast<TY*>(a.y) + (int64_t)r * a.h;
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      float sh[4], sc[4], o[4];
+      load4(mod + a.shift_off + (i * 256 + tid) * 4, sh);
+      load4(mod + a.scale_off + (i * 256 + tid) * 4, sc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = (1.0f + sc[j]) * ((v[i][j] - mean) * rstd) + sh[j];
+      store4(y + (i * 256 + tid) * 4, o);
+    }
+    __syncthreads();  // red is reused by the next row
   }
 }
 
+#ifndef MMDIT_LN_ROWS
+#define MMDIT_LN_ROWS 4
+#endif
+
 template <int C>
 static void launch_ln_row(const LnArgs& a, int rows, bool x_f32, bool y_bf16, hipStream_t s) {
-  dim3 grid(rows), block(256);
+  constexpr int R = MMDIT_LN_ROWS;
+  dim3 grid((rows + R - 1) / R), block(256);
   if (x_f32 && y_bf16)
-    hipLaunchKernelGGL((k_adaln_ln_row<float, bf16, C>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_adaln_ln_rows<float, bf16, C, R>), grid, block, 0, s, a, rows);
   else if (x_f32)
-    hipLaunchKernelGGL((k_adaln_ln_row<float, float, C>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_adaln_ln_rows<float, float, C, R>), grid, block, 0, s, a, rows);
   else if (y_bf16)
-    hipLaunchKernelGGL((k_adaln_ln_row<bf16, bf16, C>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_adaln_ln_rows<bf16, bf16, C, R>), grid, block, 0, s, a, rows);
   else
-    hipLaunchKernelGGL((k_adaln_ln_row<bf16, float, C>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_adaln_ln_rows<bf16, float, C, R>), grid, block, 0, s, a, rows);
 }
 
 template <int NC>
@@ -367,6 +439,8 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
     const int t = t0 + p * 16 + (tid >> 4);
     float y[8];
     qk_rotate(xq[p], seg_of[p] ? gq[1] : gq[0], cs[p], a.eps, valid[p], y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] *= a.qscale;
     if (t < a.Lpad) store8(Q + (int64_t)t * 128 + d0, y);
     qk_rotate(xk[p], seg_of[p] ? gk[1] : gk[0], cs[p], a.eps, valid[p], y);
     if (t < a.Lpad) store8(K + (int64_t)t * 128 + d0, y);

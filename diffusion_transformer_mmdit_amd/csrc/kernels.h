@@ -92,6 +92,7 @@ struct QkNormArgs {
   void* V;
   int32_t B, H, L, Lpad;
   float eps;
+  float qscale;  // Q is written times qscale (the bf16 attention's score scale)
 };
 hipError_t launch_qk_norm_rope(const QkNormArgs& a, bool bf16, bool v_trans, hipStream_t s);
 // bf16 only, after the fused QKV epilogue: zeroes rows t in [L, Lpad) of Q
@@ -194,6 +195,7 @@ struct GemmProblem {
   const float* rope;  // [L, 64, 2] cos, sin
   int32_t qk_h, qk_rows, qk_tok0, qk_Lpad;
   float qk_eps;
+  float qk_qscale;  // Q is written times qk_qscale
 };
 
 // Up to two problems with the same epilogue in one launch (text and image
@@ -208,6 +210,13 @@ hipError_t launch_gemm_f32(const GemmProblem* p, int nprob, int epi, hipStream_t
 // into dense bf16 [N, K] at `out` (16-byte aligned): the same bf16 values the
 // GEMM kernels stage when they dequantise a tile.
 hipError_t launch_dequant(const void* w, const void* scales, int fmt, int N, int K, void* out, hipStream_t s);
+
+// y [M, N] (float32 when y_f32, else bf16) = x [M, K] (bf16, row stride K)
+// W^T + bias for M <= 16 rows, weights in format fmt (0 dense bf16, 1-4
+// quantised, layouts as the GEMMs read them), decoded in registers;
+// K % 128 == 0; x, W 16-byte aligned.
+hipError_t launch_linear_skinny(const void* x, int M, const void* W, const void* scales, const void* bias, int fmt,
+                                void* y, bool y_f32, int N, int K, hipStream_t s);
 
 // ---- joint attention ------------------------------------------------------------
 // O rows: token t of batch b goes to seg[0] row (b, t) if t < seg_len0 else
@@ -226,7 +235,8 @@ struct AttnArgs {
   RowSeg out[2];
   int32_t seg_len0;
   int32_t B, H, L, Lpad;
-  float scale;  // 1/sqrt(d)
+  float scale;  // 1/sqrt(d) (float32 path; the bf16 path takes Q already
+                // multiplied by scale * log2(e), see kAttnQScale)
   // bf16 path: scratch for the partial results of split units (at least
   // kAttnPartBytes, 16-byte aligned), or null to run every unit whole.
   // full_units and workers are set by the launcher.
@@ -243,6 +253,10 @@ struct AttnArgs {
 // kernel combines the pieces of each unit.
 constexpr int kAttnWaves = 8;
 constexpr int kAttnTailWorkers = 256;
+// The bf16 attention reads Q multiplied by 1/sqrt(128) * log2(e), applied
+// where Q is written (the QK RMSNorm + RoPE epilogue or kernel), so that the
+// score MFMA yields exp2 arguments directly.
+constexpr float kAttnQScale = 0.08838834764831845f * 1.4426950408889634f;
 // one record per piece: O [256][128] float32, then m [256], l [256]
 constexpr size_t kAttnRecFloats = (size_t)32 * kAttnWaves * 130;
 constexpr size_t kAttnPartBytes = 2 * (size_t)kAttnTailWorkers * kAttnRecFloats * 4;

@@ -381,17 +381,63 @@ int mmdit_quantise(const float* w, int32_t n_out, int32_t k_in, int32_t bits,
 int mmdit_dequantise(const void* w, const void* scales, int32_t fmt, int32_t n_out, int32_t k_in,
                      void* out, void* hip_stream);
 
+/* ---- single operations ------------------------------------------------ */
+
+/* Device, async. adaLN-modulated LayerNorm of `rows` rows (mflux-rs cards
+ * "Dual-Stream MMDiT" / "Single-Stream Blocks": LayerNorm modulated by shift
+ * and scale from the conditioning vector; stable-diffusion.rs README: fused
+ * layer_norm): y[r, :] = (1 + scale) * LN(x[r, :]) + shift, LN without
+ * affine, biased variance, statistics in float32. x [rows, hidden]: float32
+ * when x_f32 (or act_dtype is F32), else bf16; y [rows, hidden] in act_dtype;
+ * shift_scale: device float32 [2, hidden], shift then scale, shared by all
+ * rows. hidden a multiple of 256 in [256, 4096]; pointers 16-byte aligned.
+ * The same kernel as the blocks' modulated LayerNorm. Errors:
+ * MMDIT_ERR_NULL, MMDIT_ERR_DTYPE, MMDIT_ERR_SHAPE, MMDIT_ERR_HIP. */
+int mmdit_adaln_layernorm(const void* x, int32_t x_f32, void* y, int32_t act_dtype, int32_t rows, int32_t hidden,
+                          const float* shift_scale, float eps, void* hip_stream);
+
+/* Routes of mmdit_linear_fwd (bf16 activations). AUTO: STREAM for M <= 16
+ * (k_in a multiple of 128), else DECODE for quantised weights from 1024
+ * rows, else TILED. TILED: the tiled MFMA GEMMs, quantised weight tiles
+ * dequantised as they are staged (stable-diffusion.rs README: dequantised
+ * inside the matmul a tile at a time). DECODE: the quantised layer decoded
+ * once into the workspace as bf16 (the values mmdit_dequantise gives), then
+ * the dense tiled GEMM. STREAM: the weight-streaming kernel for M <= 16:
+ * every weight read once, codes decoded in registers (HBM-bound). */
+typedef enum { MMDIT_ROUTE_AUTO = 0, MMDIT_ROUTE_TILED = 1, MMDIT_ROUTE_DECODE = 2, MMDIT_ROUTE_STREAM = 3 } mmdit_route;
+
+/* Host. Workspace bytes of mmdit_linear_fwd: 2 * n_out * k_in (rounded up)
+ * when the route decodes, else 0. */
+int mmdit_linear_workspace(const mmdit_linear* l, int32_t act_dtype, int32_t M, int32_t route, size_t* bytes);
+
+/* Device, async. One linear layer y = x W^T + b of the step (any projection,
+ * weights in any mmdit_wfmt): x [M, k_in] in act_dtype (row stride k_in),
+ * y [M, n_out] float32 when y_f32 (or act_dtype is F32), else bf16; both
+ * device, 16-byte aligned. route: mmdit_route (float32 activations: AUTO or
+ * TILED only). ws: device workspace of mmdit_linear_workspace() bytes (may
+ * be NULL when that is 0). Results are the same bf16-operand, float32-
+ * accumulated products the blocks compute, whatever the route. Errors:
+ * MMDIT_ERR_NULL, MMDIT_ERR_DTYPE (format / dtype), MMDIT_ERR_SHAPE (sizes,
+ * a route the shape does not allow, alignment), MMDIT_ERR_WORKSPACE,
+ * MMDIT_ERR_UNSUPPORTED, MMDIT_ERR_HIP. */
+int mmdit_linear_fwd(const mmdit_linear* l, int32_t act_dtype, const void* x, int32_t M, void* y, int32_t y_f32,
+                     int32_t route, void* ws, size_t ws_bytes, void* hip_stream);
+
 /* Kernel timing for benchmarks. While enabled, each launch of the selected
  * kernel class is bracketed by HIP events recorded on the launch stream.
  * classes: 1 = GEMMs (all projections), 2 = joint attention,
  * 3 = adaLN LayerNorm, 4 = QK RMSNorm + RoPE, 5 = modulation / conditioning
  * GEMV, 6 = single-block linear1 GEMM (split GELU epilogue), 7 = GEMMs with
  * the gated-residual epilogue (out-projection, fc2, linear2), 8 = decoding of
- * quantised weights to bf16 ahead of a launch.
+ * quantised weights to bf16 ahead of a launch, 9 = dual-block QKV GEMM (QK
+ * RMSNorm + RoPE epilogue), 10 = dual-block fc1 GEMM (GELU epilogue),
+ * 11 = weight-streaming linear (mmdit_linear_fwd, STREAM route; work = weight
+ * bytes).
  * mmdit_profile_begin creates up to max_launches event pairs (host call, no
  * device allocation). mmdit_profile_end waits for the recorded events and
  * returns the summed kernel time, the launch count and the summed algorithmic
- * FLOPs (classes 1, 2, 6, 7) or bytes (classes 3-5, 8) of those launches.
+ * FLOPs (classes 1, 2, 6, 7, 9, 10) or bytes (classes 3-5, 8, 11) of those
+ * launches.
  * Thread-safe; a launch whose call is still in progress when
  * mmdit_profile_end runs on another thread is not counted. */
 int mmdit_profile_begin(int32_t kernel_class, int32_t max_launches);

@@ -325,3 +325,36 @@ def test_resid_field_is_checked(lib):
     c32 = bd.make_config(I.CFG4)
     c16 = bd.make_config(I.CFG4, resid=bd.RESID_BF16)
     assert bd.mmdit_step_workspace(c32) - bd.mmdit_step_workspace(c16) >= I.CFG4.seq_len * 3072 * 2
+
+
+def test_linear_entry_point_errors_before_launch(lib):
+    # argument errors of mmdit_linear_fwd / mmdit_linear_workspace return
+    # before any device work (dummy device pointers are never touched)
+    dummy = C.c_void_p(4096)
+    lin = bd.mmdit_linear(w=4096, scales=4096, bias=None, fmt=bd.W_Q4G64, n_out=328, k_in=384)
+    n = C.c_size_t()
+    assert lib.mmdit_linear_workspace(C.byref(lin), bd.BF16, 300, bd.ROUTE_DECODE, C.byref(n)) == 0
+    assert n.value >= 328 * 384 * 2
+    assert lib.mmdit_linear_workspace(C.byref(lin), bd.BF16, 300, bd.ROUTE_TILED, C.byref(n)) == 0 and n.value == 0
+    assert lib.mmdit_linear_workspace(C.byref(lin), bd.BF16, 5, bd.ROUTE_AUTO, C.byref(n)) == 0 and n.value == 0
+    # the streaming route needs M <= 16
+    assert lib.mmdit_linear_fwd(C.byref(lin), bd.BF16, dummy, 17, dummy, 1, bd.ROUTE_STREAM, None, 0, None) == 2
+    # the decoding route needs its workspace
+    assert lib.mmdit_linear_fwd(C.byref(lin), bd.BF16, dummy, 300, dummy, 1, bd.ROUTE_DECODE, None, 0, None) == 4
+    # quantised weights need bf16 activations; unknown route
+    assert lib.mmdit_linear_fwd(C.byref(lin), bd.F32, dummy, 8, dummy, 1, bd.ROUTE_AUTO, None, 0, None) == 3
+    assert lib.mmdit_linear_fwd(C.byref(lin), bd.BF16, dummy, 8, dummy, 1, 7, None, 0, None) == 2
+    dense = bd.mmdit_linear(w=4096, scales=None, bias=None, fmt=bd.W_DENSE, n_out=328, k_in=384)
+    assert lib.mmdit_linear_fwd(C.byref(dense), bd.BF16, dummy, 300, dummy, 1, bd.ROUTE_DECODE, dummy, 1 << 20,
+                                None) == 2
+    # M = 0 is a no-op, NULL weights an error
+    assert lib.mmdit_linear_fwd(C.byref(dense), bd.BF16, None, 0, None, 1, bd.ROUTE_AUTO, None, 0, None) == 0
+    assert lib.mmdit_linear_fwd(None, bd.BF16, dummy, 4, dummy, 1, bd.ROUTE_AUTO, None, 0, None) == 1
+
+
+def test_adaln_layernorm_errors_before_launch(lib):
+    dummy = C.c_void_p(4096)
+    assert lib.mmdit_adaln_layernorm(dummy, 1, dummy, bd.BF16, 10, 300, dummy, C.c_float(1e-6), None) == 2
+    assert lib.mmdit_adaln_layernorm(dummy, 1, dummy, 5, 10, 256, dummy, C.c_float(1e-6), None) == 3
+    assert lib.mmdit_adaln_layernorm(None, 1, dummy, bd.BF16, 10, 256, dummy, C.c_float(1e-6), None) == 1
+    assert lib.mmdit_adaln_layernorm(None, 1, None, bd.BF16, 0, 256, None, C.c_float(1e-6), None) == 0
