@@ -82,7 +82,7 @@ class mmdit_step_cache(C.Structure):
 class mmdit_step_opts(C.Structure):
     _fields_ = [("ctx_packed", C.c_void_p), ("ctx_len", C.c_int32), ("has_guidance", C.c_int32),
                 ("guidance", C.c_double), ("cache", C.POINTER(mmdit_step_cache)), ("cache_threshold", C.c_double),
-                ("dequant", C.c_int32)]
+                ("dequant", C.c_int32), ("cache_on_device", C.c_int32)]
 
 
 # Every function the header declares, with its ctypes signature.
@@ -92,6 +92,7 @@ _SIGS = {
     "mmdit_single_block_workspace": (C.c_int, [C.POINTER(mmdit_dims), C.POINTER(C.c_size_t)]),
     "mmdit_step_workspace": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(C.c_size_t)]),
     "mmdit_step_cache_bytes": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(C.c_size_t)]),
+    "mmdit_step_cache_read": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(mmdit_step_cache), _P]),
     "mmdit_step_workspace_ex": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(mmdit_model_w),
                                           C.POINTER(mmdit_step_opts), C.POINTER(C.c_size_t)]),
     "mmdit_double_block_fwd": (C.c_int, [C.POINTER(mmdit_dims), C.POINTER(mmdit_double_w), _P, _P, _P, _P,
@@ -360,10 +361,14 @@ def mmdit_step_cache_bytes(cfg: mmdit_config) -> int:
 
 class StepCache:
     """Step-cache state of one generation: the device buffer (a torch uint8
-    tensor) and the mmdit_step_cache struct the library updates."""
+    tensor) and the mmdit_step_cache struct the library updates. on_device:
+    the decision is taken by a kernel (graph-capturable); read() copies it
+    back into ran_blocks / rel / acc."""
 
-    def __init__(self, cfg: mmdit_config, device="cuda"):
+    def __init__(self, cfg: mmdit_config, device="cuda", on_device: bool = False):
         import torch
+        self.cfg = cfg
+        self.on_device = on_device
         self.buf = torch.empty(mmdit_step_cache_bytes(cfg), dtype=torch.uint8, device=device)
         self.c = mmdit_step_cache()
         self.c.buf = self.buf.data_ptr()
@@ -383,6 +388,12 @@ class StepCache:
     def rel(self) -> float:
         return self.c.rel
 
+    def read(self, stream=None):
+        """mmdit_step_cache_read: waits for the stream, then fills ran_blocks,
+        acc and rel from the device state."""
+        _check(lib().mmdit_step_cache_read(C.byref(self.cfg), C.byref(self.c), _stream(stream)),
+               "mmdit_step_cache_read")
+
 
 def mmdit_step_ex(cfg, w: mmdit_model_w, x_packed, v_out, txt_emb, y, ids, sigma: float, sigma_next: float, ws,
                   ctx_packed=None, ctx_len: int = 0, guidance: Optional[float] = None, stream=None,
@@ -396,6 +407,7 @@ def mmdit_step_ex(cfg, w: mmdit_model_w, x_packed, v_out, txt_emb, y, ids, sigma
     if cache is not None:
         o.cache = C.pointer(cache.c)
         o.cache_threshold = float(cache_threshold)
+        o.cache_on_device = 1 if cache.on_device else 0
     _check(lib().mmdit_step_ex(C.byref(cfg), C.byref(w), _ptr(x_packed), _ptr(v_out), _ptr(txt_emb), _ptr(y),
                                _ptr(ids), float(sigma), float(sigma_next), C.byref(o), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream)),

@@ -298,6 +298,9 @@ struct Ctx {
   float ln_eps, rms_eps;
   void* xw = nullptr;  // decoded-weight scratch (null: quantised layers stay fused)
   size_t xw_bytes = 0;
+  // step-cache guard passed to every launch (null: unguarded): the launches
+  // do nothing when the device-side cache decision reuses the residual
+  const int* skip = nullptr;
 };
 
 char* ptr(void* base, size_t off) { return reinterpret_cast<char*>(base) + off; }
@@ -325,7 +328,7 @@ int expand_quantised(const Ctx& c, GemmProblem* p, int np) {
       const double wb = p[i].fmt == MMDIT_W_Q4G64 ? 0.5 : p[i].fmt == MMDIT_W_Q8G64 ? 1.0
                         : p[i].fmt == MMDIT_W_Q1G128 ? 0.125 : 0.25;
       ProfScope ps(PC_DEQUANT, (double)p[i].N * p[i].K * (wb + 2.0), c.s);
-      HIP_TRY(launch_dequant(p[i].W, p[i].scales, p[i].fmt, p[i].N, p[i].K, d, c.s));
+      HIP_TRY(launch_dequant(p[i].W, p[i].scales, p[i].fmt, p[i].N, p[i].K, d, c.s, c.skip));
     }
     src[i] = p[i].W;
     dst[i] = d;
@@ -337,6 +340,7 @@ int expand_quantised(const Ctx& c, GemmProblem* p, int np) {
 }
 
 int gemm(const Ctx& c, GemmProblem* p, int np, int epi) {
+  for (int i = 0; i < np; ++i) p[i].skip = c.skip;
   if (int r = expand_quantised(c, p, np)) return r;
   double flops = 0;
   for (int i = 0; i < np; ++i) flops += 2.0 * p[i].M * (double)p[i].N * p[i].K;
@@ -359,6 +363,7 @@ int gemv(const Ctx& c, const mmdit_linear& l, const void* x, bool x_f32, int x_b
   a.N = l.n_out; a.K = l.k_in; a.B = c.g.B;
   a.x_bstride = x_bstride; a.y_bstride = y_bstride;
   a.silu_in = silu; a.accumulate = accumulate;
+  a.skip = c.skip;
   ProfScope ps(PC_GEMV, (double)l.n_out * l.k_in * c.g.esz, c.s);
   HIP_TRY(launch_gemv(a, c.g.bf16, x_f32 || !c.g.bf16, c.s));
   return MMDIT_OK;
@@ -403,6 +408,7 @@ int run_ln(const Ctx& c, const Part* parts, int np, int mod_bstride, int shift_o
   }
   a.mod_bstride = mod_bstride; a.shift_off = shift_off; a.scale_off = scale_off;
   a.y = y; a.h = g.h; a.eps = c.ln_eps;
+  a.skip = c.skip;
   if (rows == 0) return MMDIT_OK;
   ProfScope ps(PC_LN, (double)rows * g.h * ((res_f32 ? 4 : g.esz) + g.esz), c.s);
   HIP_TRY(launch_adaln_ln(a, rows, res_f32 || !g.bf16, g.bf16, c.s));
@@ -448,6 +454,7 @@ int run_qk_attn(const Ctx& c, const Part* parts, int np, void* qkv, const void* 
   q.Q = ptr(ws, w.q); q.K = ptr(ws, w.k); q.V = ptr(ws, w.v);
   q.B = g.B; q.H = g.H; q.L = g.L; q.Lpad = g.Lpad; q.eps = c.rms_eps;
   q.qscale = g.bf16 ? kAttnQScale : 1.0f;
+  q.skip = c.skip;
   if (qk_fused) {  // Q, K and V^T are written; only the pad rows remain
     if (g.Lpad > g.L) HIP_TRY(launch_qkv_pad_zero(q, c.s));
   } else {
@@ -459,6 +466,7 @@ int run_qk_attn(const Ctx& c, const Part* parts, int np, void* qkv, const void* 
   at.seg_len0 = q.seg_len0;
   at.B = g.B; at.H = g.H; at.L = g.L; at.Lpad = g.Lpad;
   at.scale = 1.0f / sqrtf(128.0f);
+  at.skip = c.skip;
   {
     ProfScope ps(PC_ATTN, 4.0 * g.B * g.H * (double)g.L * g.L * 128, c.s);
     HIP_TRY(g.bf16 ? launch_attention_bf16(at, c.s) : launch_attention_f32(at, c.s));
@@ -705,9 +713,9 @@ int mmdit_step_workspace_ex(const mmdit_config* cfg, const mmdit_model_w* w, con
 }
 
 // Step-cache buffer: a_prev [B Li h], residual [B Li h] (float32), per-row
-// partial sums [B Li 2].
+// partial sums [B Li 2], the device-side decision state (CacheState).
 struct CacheLay {
-  size_t prev, resid, part, total;
+  size_t prev, resid, part, state, total;
 };
 static CacheLay plan_cache(const Geo& g) {
   CacheLay c;
@@ -715,7 +723,8 @@ static CacheLay plan_cache(const Geo& g) {
   c.prev = 0;
   c.resid = align_up(n * 4);
   c.part = align_up(c.resid + n * 4);
-  c.total = align_up(c.part + (size_t)g.B * g.Li * 2 * 4);
+  c.state = align_up(c.part + (size_t)g.B * g.Li * 2 * 4);
+  c.total = align_up(c.state + sizeof(CacheState));
   return c;
 }
 
@@ -725,6 +734,25 @@ int mmdit_step_cache_bytes(const mmdit_config* cfg, size_t* bytes) {
   if (!bytes) return fail(MMDIT_ERR_NULL, "bytes is NULL");
   if ((r = check_config(cfg, g))) return r;
   *bytes = plan_cache(g).total;
+  return MMDIT_OK;
+}
+
+int mmdit_step_cache_read(const mmdit_config* cfg, mmdit_step_cache* cache, void* hip_stream) {
+  Geo g;
+  int r;
+  if (!cache || !cache->buf) return fail(MMDIT_ERR_NULL, "cache or cache->buf is NULL");
+  if ((r = check_config(cfg, g))) return r;
+  const CacheLay cl = plan_cache(g);
+  if (cache->bytes < cl.total)
+    return fail(MMDIT_ERR_WORKSPACE, "cache buffer %zu bytes, need %zu", cache->bytes, cl.total);
+  if (!cache->valid) return fail(MMDIT_ERR_SHAPE, "no step of this generation has run (cache->valid == 0)");
+  CacheState st;
+  const hipStream_t s = (hipStream_t)hip_stream;
+  HIP_TRY(hipMemcpyAsync(&st, ptr(cache->buf, cl.state), sizeof st, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  cache->ran_blocks = st.ran_blocks;
+  cache->acc = st.acc;
+  cache->rel = st.rel;
   return MMDIT_OK;
 }
 
@@ -764,6 +792,9 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
     if (cache->bytes < plan_cache(g).total)
       return fail(MMDIT_ERR_WORKSPACE, "cache buffer %zu bytes, need %zu", cache->bytes, plan_cache(g).total);
   }
+  if (opts->cache_on_device != 0 && opts->cache_on_device != 1)
+    return fail(MMDIT_ERR_SHAPE, "cache_on_device %d must be 0 or 1", opts->cache_on_device);
+  const bool dev_cache = cache && opts->cache_on_device == 1;
   if (g.Lt > 0 && !txt_emb) return fail(MMDIT_ERR_NULL, "txt_emb is NULL with txt_len > 0");
   if ((cfg->n_double > 0 && !w->dbl) || (cfg->n_single > 0 && !w->sgl)) return fail(MMDIT_ERR_NULL, "block weight arrays are NULL");
   if (!std::isfinite(sigma) || !std::isfinite(sigma_next)) return fail(MMDIT_ERR_SHAPE, "sigma values must be finite");
@@ -829,6 +860,7 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   auto flush = [&]() -> int {
     if (ga.nseg == 0) return MMDIT_OK;
     ProfScope ps(PC_GEMV, gemv_bytes, c.s);
+    ga.skip = c.skip;
     HIP_TRY(launch_gemv_multi(ga, g.bf16, c.s));
     ga.nseg = 0;
     gemv_bytes = 0;
@@ -844,6 +876,9 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   if ((r = add(w->final_mod, mods + lay.mod_final, 2 * h))) return r;
   if (cfg->n_double > 0 && (r = add(w->dbl[0].img.mod, mods + lay.mod_dual + (size_t)B * 6 * h, 6 * h))) return r;
   if (cache && (r = flush())) return r;
+  // the RoPE table depends on the ids only; built before a cached step's
+  // decision so that the guarded launches below are the blocks' alone
+  if ((r = rope(c, &cfg->dims, ids, table))) return r;
 
   // image input projection into the f32 residual
   const void* xa = x_packed;
@@ -890,7 +925,14 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
     ca.eps = c.ln_eps;
     ca.first = cache->valid ? 0 : 1;
     HIP_TRY(launch_cache_delta(ca, c.s));
-    if (cache->valid) {
+    if (dev_cache) {
+      // decided on the device: every launch up to the residual store is
+      // guarded by the decision's skip flag (graph-capturable, no wait)
+      CacheState* st = (CacheState*)ptr(cache->buf, cl.state);
+      HIP_TRY(launch_cache_decide(part, B * g.Li, ca.first, opts->cache_threshold, st, c.s));
+      HIP_TRY(launch_cache_apply((float*)ximg, resid, nimg, &st->skip, c.s));
+      c.skip = &st->skip;
+    } else if (cache->valid) {
       std::vector<float> hp((size_t)2 * B * g.Li);
       HIP_TRY(hipMemcpyAsync(hp.data(), part, hp.size() * sizeof(float), hipMemcpyDeviceToHost, c.s));
       HIP_TRY(hipStreamSynchronize(c.s));
@@ -904,8 +946,10 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
       run_blocks = !(acc < opts->cache_threshold);
       if (run_blocks) acc = 0.0;
     }
-    if (run_blocks) HIP_TRY(launch_axpby(resid, (const float*)ximg, 0.f, 1.f, nimg, c.s));  // resid <- img0
-    else HIP_TRY(launch_axpby((float*)ximg, resid, 1.f, 1.f, nimg, c.s));             // img0 + residual
+    if (!dev_cache) {
+      if (run_blocks) HIP_TRY(launch_axpby(resid, (const float*)ximg, 0.f, 1.f, nimg, c.s));  // resid <- img0
+      else HIP_TRY(launch_axpby((float*)ximg, resid, 1.f, 1.f, nimg, c.s));             // img0 + residual
+    }
   }
 
   Part parts[2];
@@ -921,7 +965,6 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
     for (int i = 0; i < cfg->n_single; ++i)
       if ((r = add(w->sgl[i].mod, mods + lay.mod_single + (size_t)i * B * 3 * h, 3 * h))) return r;
     if ((r = flush())) return r;
-    if ((r = rope(c, &cfg->dims, ids, table))) return r;
     if (g.Lt > 0) {
       GemmProblem gt = base_problem(w->txt_in);
       gt.A = txt_emb; gt.lda = cfg->txt_in_dim; gt.M = B * g.Lt;
@@ -945,7 +988,9 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
         if ((r = run_single(c, w->sgl[i], &parts[1], 1, !rb, table, ws, lay.blk))) return r;
       }
     }
-    if (cache) HIP_TRY(launch_axpby(resid, (const float*)ximg, -1.f, 1.f, nimg, c.s));  // resid <- img - img0
+    if (dev_cache) HIP_TRY(launch_cache_store(resid, (const float*)ximg, nimg, c.skip, c.s));  // img - img0
+    else if (cache) HIP_TRY(launch_axpby(resid, (const float*)ximg, -1.f, 1.f, nimg, c.s));  // resid <- img - img0
+    c.skip = nullptr;
   }
   // final layer on the generated image rows, Euler update fused into the epilogue
   Part fin = parts[1];
@@ -961,7 +1006,10 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   f.dsigma = (float)(sigma_next - sigma);
   f.v_out = (float*)v_out;
   if ((r = gemm(c, &f, 1, EPI_EULER))) return r;
-  if (cache) {
+  if (dev_cache) {
+    cache->valid = 1;
+    cache->ran_blocks = -1;  // on the device until mmdit_step_cache_read
+  } else if (cache) {
     cache->valid = 1;
     cache->ran_blocks = run_blocks ? 1 : 0;
     cache->acc = acc;

@@ -16,6 +16,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// A launch guarded by a step-cache flag does nothing when the flag (written
+// on the device by the cache decision of an earlier kernel on the stream) is
+// nonzero; a null guard always runs. Uniform across the grid, so a block
+// returns whole, before any barrier.
+__device__ __forceinline__ bool guard_skip(const int* g) { return g != nullptr && *g != 0; }
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 

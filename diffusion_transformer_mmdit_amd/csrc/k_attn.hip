@@ -406,6 +406,7 @@ __device__ __forceinline__ int64_t attn_share_begin(int w, int64_t T, int worker
 }
 
 __global__ __launch_bounds__(64 * kAttnWaves, 2) void k_attn_bf16(AttnArgs a) {
+  if (guard_skip(a.skip)) return;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int nt = (a.L + kAttnK - 1) / kAttnK;
   if (!a.part || (int)blockIdx.x < a.full_units) {
@@ -437,6 +438,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, 2) void k_attn_bf16(AttnArgs a) {
 constexpr int kAttnMaxPieces = 8;
 
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  if (guard_skip(a.skip)) return;
   constexpr int QU = 32 * kAttnWaves;  // queries per unit
   const int nt = (a.L + kAttnK - 1) / kAttnK;
   const int tail = attn_qblocks(a) * a.H * a.B - a.full_units;
@@ -512,6 +514,7 @@ hipError_t launch_attention_bf16(const AttnArgs& in, hipStream_t s) {
 constexpr int kF32QPerBlock = 16;
 
 __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
+  if (guard_skip(a.skip)) return;
   __shared__ float qs[4][128];
   __shared__ float ps[4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;

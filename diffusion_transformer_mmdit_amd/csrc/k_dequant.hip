@@ -62,7 +62,8 @@ __device__ __forceinline__ void decode_run(const char* __restrict__ w, const bf1
 
 template <int FMT>
 __global__ __launch_bounds__(256) void k_dequant(const char* __restrict__ w, const bf16* __restrict__ scales,
-                                                 bf16* __restrict__ out, int K, int64_t runs) {
+                                                 bf16* __restrict__ out, int K, int64_t runs, const int* skip) {
+  if (guard_skip(skip)) return;
   __shared__ bf16x8 stage[256 * 4];
   const int64_t t0 = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63);  // the wavefront's first run
   const int64_t t = t0 + (threadIdx.x & 63);
@@ -74,7 +75,8 @@ __global__ __launch_bounds__(256) void k_dequant(const char* __restrict__ w, con
   decode_run<FMT>(w, scales, out, K, rk, t, stage + (threadIdx.x & ~63) * 4);
 }
 
-hipError_t launch_dequant(const void* w, const void* scales, int fmt, int N, int K, void* out, hipStream_t s) {
+hipError_t launch_dequant(const void* w, const void* scales, int fmt, int N, int K, void* out, hipStream_t s,
+                          const int* skip) {
   const int group = fmt == 3 || fmt == 4 ? 128 : 64;
   if (N < 0 || K <= 0 || K % group != 0 || fmt < 1 || fmt > 4) return hipErrorInvalidValue;
   const int64_t runs = (int64_t)N * (K / 32);
@@ -84,10 +86,10 @@ hipError_t launch_dequant(const void* w, const void* scales, int fmt, int N, int
   const bf16* sp = reinterpret_cast<const bf16*>(scales);
   bf16* op = reinterpret_cast<bf16*>(out);
   switch (fmt) {
-    case 1: hipLaunchKernelGGL(k_dequant<1>, grid, dim3(256), 0, s, wp, sp, op, K, runs); break;
-    case 2: hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, s, wp, sp, op, K, runs); break;
-    case 3: hipLaunchKernelGGL(k_dequant<3>, grid, dim3(256), 0, s, wp, sp, op, K, runs); break;
-    default: hipLaunchKernelGGL(k_dequant<4>, grid, dim3(256), 0, s, wp, sp, op, K, runs); break;
+    case 1: hipLaunchKernelGGL(k_dequant<1>, grid, dim3(256), 0, s, wp, sp, op, K, runs, skip); break;
+    case 2: hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, s, wp, sp, op, K, runs, skip); break;
+    case 3: hipLaunchKernelGGL(k_dequant<3>, grid, dim3(256), 0, s, wp, sp, op, K, runs, skip); break;
+    default: hipLaunchKernelGGL(k_dequant<4>, grid, dim3(256), 0, s, wp, sp, op, K, runs, skip); break;
   }
   return hipGetLastError();
 }

@@ -23,6 +23,7 @@ constexpr int kLDK = kBK + 8;
 
 template <int BM, int BN, int WM, int WN, int EPI, int FMT>
 __global__ __launch_bounds__(256) void k_gemm_bf16(GemmBatch gb) {
+  if (guard_skip(gb.p[0].skip)) return;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int A_CH = BM * 8 / 256;                                  // 16-byte A chunks per thread

@@ -439,6 +439,7 @@ __device__ __forceinline__ void v_epilogue(const GemmProblem& P, char* smem, int
 // 32 weights.
 template <int EPI, int BK, int S, int CPOL, int FMT, int DS, int W>
 __global__ __launch_bounds__(64 * W, 1) void k_gemm_dma(GemmBatch gb) {
+  if (guard_skip(gb.p[0].skip)) return;
   constexpr int NT = 64 * W;                       // threads
   constexpr int WN = W / 2;                        // wavefront columns (2 rows of wavefronts)
   constexpr int TN = kDBN / WN;                    // columns of a wavefront tile (128 rows)

@@ -11,6 +11,7 @@ constexpr int kF32K = 16;
 
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_f32(GemmBatch gb) {
+  if (guard_skip(gb.p[0].skip)) return;
   __shared__ float As[kF32K][kF32T + 4];
   __shared__ float Bs[kF32K][kF32T + 4];
   int prob, tm, tn;

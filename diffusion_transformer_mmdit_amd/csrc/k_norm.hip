@@ -24,6 +24,7 @@ __device__ __forceinline__ const char* seg_row(const RowSeg& s, int local, int e
 // constant so the loads are issued back to back).
 template <typename TX, typename TY, int NC>
 __global__ __launch_bounds__(256) void k_adaln_ln(LnArgs a, int rows) {
+  if (guard_skip(a.skip)) return;
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
@@ -74,6 +75,7 @@ __global__ __launch_bounds__(256) void k_adaln_ln(LnArgs a, int rows) {
 // block, run their rows one at a time.
 template <typename TX, typename TY, int C, int R>
 __global__ __launch_bounds__(256) void k_adaln_ln_rows(LnArgs a, int rows) {
+  if (guard_skip(a.skip)) return;
   __shared__ float red[2][R][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = blockIdx.x * R;
@@ -360,6 +362,95 @@ hipError_t launch_axpby(float* y, const float* x, float alpha, float beta, int64
   return hipGetLastError();
 }
 
+// ------------------------------------------------- device-side cache decision --
+// One 256-thread block: thread t sums rows t, t + 256, ... in order (float64),
+// then a fixed-order tree over the threads; thread 0 applies the rule.
+__global__ __launch_bounds__(256) void k_cache_decide(const float* __restrict__ part, int rows, int first,
+                                                      double threshold, CacheState* st) {
+  __shared__ double red[2][256];
+  double num = 0.0, den = 0.0;
+  for (int r = threadIdx.x; r < rows; r += 256) {
+    num += (double)part[2 * (int64_t)r];
+    den += (double)part[2 * (int64_t)r + 1];
+  }
+  red[0][threadIdx.x] = num;
+  red[1][threadIdx.x] = den;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + w];
+      red[1][threadIdx.x] += red[1][threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x != 0) return;
+  CacheState o;
+  o.pad = 0;
+  if (first) {
+    o.skip = 0;
+    o.acc = 0.0;
+    o.rel = 0.0;
+    o.steps = 1;
+  } else {
+    num = red[0][0];
+    den = red[1][0];
+    const double rel = den > 0.0 ? num / den : (num > 0.0 ? __builtin_inf() : 0.0);
+    double acc = st->acc + rel;
+    const bool run = !(acc < threshold);
+    if (run) acc = 0.0;
+    o.skip = run ? 0 : 1;
+    o.acc = acc;
+    o.rel = rel;
+    o.steps = st->steps + 1;
+  }
+  o.ran_blocks = 1 - o.skip;
+  *st = o;
+}
+
+hipError_t launch_cache_decide(const float* part, int rows, int first, double threshold, CacheState* st,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(k_cache_decide, dim3(1), dim3(256), 0, s, part, rows, first, threshold, st);
+  return hipGetLastError();
+}
+
+// mode 0: img += resid when *skip, else resid = img; mode 1: resid = img -
+// resid unless *skip. Four floats per thread, grid-stride.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_cache_apply(float4* __restrict__ img, float4* __restrict__ resid,
+                                                     int64_t n4, const int* skip) {
+  const bool sk = *skip != 0;
+  if (MODE == 1 && sk) return;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const float4 xv = img[i];
+    if (MODE == 0 && !sk) {
+      resid[i] = xv;
+    } else {
+      const float4 rv = resid[i];
+      if (MODE == 0) img[i] = make_float4(xv.x + rv.x, xv.y + rv.y, xv.z + rv.z, xv.w + rv.w);
+      else resid[i] = make_float4(xv.x - rv.x, xv.y - rv.y, xv.z - rv.z, xv.w - rv.w);
+    }
+  }
+}
+
+template <int MODE>
+static hipError_t launch_cache_apply_mode(float* img, float* resid, int64_t n, const int* skip, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  const int64_t want = (n4 + 255) / 256;
+  const int grid = (int)(want < 2048 ? want : 2048);
+  hipLaunchKernelGGL(k_cache_apply<MODE>, dim3(grid), dim3(256), 0, s, reinterpret_cast<float4*>(img),
+                     reinterpret_cast<float4*>(resid), n4, skip);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_apply(float* img, float* resid, int64_t n, const int* skip, hipStream_t s) {
+  return launch_cache_apply_mode<0>(img, resid, n, skip, s);
+}
+
+hipError_t launch_cache_store(float* resid, const float* img, int64_t n, const int* skip, hipStream_t s) {
+  return launch_cache_apply_mode<1>(const_cast<float*>(img), resid, n, skip, s);
+}
+
 // ----------------------------------------------------------- QK RMSNorm + RoPE --
 // Block (64-token tile, head, batch), 256 threads. q and k: 16 lanes per
 // token, 8 dims per lane; RMS over the 128 dims of the head, times the
@@ -391,6 +482,7 @@ __device__ __forceinline__ void qk_rotate(const float (&x)[8], const float (&g)[
 
 template <typename T, bool VT>
 __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
+  if (guard_skip(a.skip)) return;
   const int t0 = blockIdx.x * kQkTile;
   const int hh = blockIdx.y;
   const int b = blockIdx.z;
@@ -482,6 +574,7 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormArgs a) {
 // One thread per (batch, head, pad row, 8 dims): Q and K rows t in [L, Lpad)
 // and V^T positions p in [L & ~15, Lpad) whose token vkey_pos(p) is >= L.
 __global__ void k_qkv_pad_zero(QkNormArgs a) {
+  if (guard_skip(a.skip)) return;
   const int L0 = a.L & ~15;
   const int npos = a.Lpad - L0;
   const int64_t n = (int64_t)a.B * a.H * npos * 16;
@@ -622,6 +715,7 @@ __device__ __forceinline__ void gemv_rows(const float* xs, const TW* W, const TW
 
 template <typename TW, typename TX>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
+  if (guard_skip(a.skip)) return;
   extern __shared__ float xs[];  // [B, K]
   gemv_stage_x<TX>(xs, a.x, a.B, a.K, a.x_bstride, a.silu_in);
   const int lane = threadIdx.x & 63;
@@ -634,6 +728,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 // block b serves the segment whose block range holds b.
 template <typename TW>
 __global__ __launch_bounds__(256) void k_gemv_multi(GemvMultiArgs a) {
+  if (guard_skip(a.skip)) return;
   extern __shared__ float xs[];  // [B, K]
   int sg = 0;
   for (int i = 1; i < a.nseg; ++i)
@@ -658,6 +753,7 @@ constexpr int kGemv4Rows = 4;
 
 template <int NCH, int BB>
 __global__ __launch_bounds__(256) void k_gemv_multi4(GemvMultiArgs a) {
+  if (guard_skip(a.skip)) return;
   extern __shared__ float xs[];  // [B, K]
   int sg = 0;
   for (int i = 1; i < a.nseg; ++i)

@@ -50,6 +50,7 @@ struct LnArgs {
   void* y;
   int32_t h;
   float eps;
+  const int* skip = nullptr;  // step-cache guard (see guard_skip), null: always run
 };
 // x_f32: residual rows are float32 (else the activation type);
 // y_bf16: output bf16 (else float32).
@@ -76,6 +77,27 @@ hipError_t launch_cache_delta(const CacheDeltaArgs& a, hipStream_t s);
 // alpha == 0 writes beta * x[i] without reading y.
 hipError_t launch_axpby(float* y, const float* x, float alpha, float beta, int64_t n, hipStream_t s);
 
+// Device-side cache decision, one block: num = sum part[2r], den = sum
+// part[2r + 1] over `rows` rows (float64, fixed order); rel = num / den (inf
+// when den == 0 < num, 0 when both are 0); acc = st->acc + rel; the step
+// reuses the residual (st->skip = 1) while acc < threshold, else runs the
+// blocks (st->skip = 0) and acc restarts at 0. first != 0: a generation's
+// first step (runs the blocks, acc = rel = 0).
+struct CacheState {
+  int32_t skip;        // 1: this step reuses the residual
+  int32_t ran_blocks;  // !skip
+  int32_t steps;       // steps decided since the generation started
+  int32_t pad;
+  double acc, rel;
+};
+hipError_t launch_cache_decide(const float* part, int rows, int first, double threshold, CacheState* st,
+                               hipStream_t s);
+// n floats (n % 4 == 0, 16-byte aligned): img += resid when *skip, else
+// resid = img (the residual base img0 of a step that runs the blocks).
+hipError_t launch_cache_apply(float* img, float* resid, int64_t n, const int* skip, hipStream_t s);
+// resid = img - resid unless *skip (the image-stream residual of the blocks).
+hipError_t launch_cache_store(float* resid, const float* img, int64_t n, const int* skip, hipStream_t s);
+
 // ---- QK RMSNorm + RoPE + attention layout ------------------------------------
 // Token t of batch b reads q|k|v from row (b, t) of seg[0] when t < seg_len0,
 // else row (b, t - seg_len0) of seg[1] (q at col 0, k at h, v at 2h).
@@ -93,6 +115,7 @@ struct QkNormArgs {
   int32_t B, H, L, Lpad;
   float eps;
   float qscale;  // Q is written times qscale (the bf16 attention's score scale)
+  const int* skip = nullptr;  // step-cache guard (see guard_skip), null: always run
 };
 hipError_t launch_qk_norm_rope(const QkNormArgs& a, bool bf16, bool v_trans, hipStream_t s);
 // bf16 only, after the fused QKV epilogue: zeroes rows t in [L, Lpad) of Q
@@ -114,6 +137,7 @@ struct GemvArgs {
   int32_t N, K, B;
   int32_t x_bstride, y_bstride;
   bool silu_in, accumulate;
+  const int* skip = nullptr;  // step-cache guard (see guard_skip), null: always run
 };
 hipError_t launch_gemv(const GemvArgs& a, bool w_bf16, bool x_f32, hipStream_t s);
 // Up to kGemvMaxSeg GEMVs sharing one float32 input (SiLU applied), B <= 4
@@ -132,6 +156,7 @@ struct GemvMultiArgs {
   int32_t K, B, x_bstride;
   int32_t nseg;
   GemvSeg seg[kGemvMaxSeg];
+  const int* skip = nullptr;  // step-cache guard (see guard_skip), null: always run
 };
 hipError_t launch_gemv_multi(const GemvMultiArgs& a, bool w_bf16, hipStream_t s);
 
@@ -196,6 +221,8 @@ struct GemmProblem {
   int32_t qk_h, qk_rows, qk_tok0, qk_Lpad;
   float qk_eps;
   float qk_qscale;  // Q is written times qk_qscale
+  // step-cache guard of the launch (read from the first problem), null: run
+  const int* skip = nullptr;
 };
 
 // Up to two problems with the same epilogue in one launch (text and image
@@ -209,7 +236,8 @@ hipError_t launch_gemm_f32(const GemmProblem* p, int nprob, int epi, hipStream_t
 // Quantised weights (fmt 1-4, layouts as the GEMM kernels read them) decoded
 // into dense bf16 [N, K] at `out` (16-byte aligned): the same bf16 values the
 // GEMM kernels stage when they dequantise a tile.
-hipError_t launch_dequant(const void* w, const void* scales, int fmt, int N, int K, void* out, hipStream_t s);
+hipError_t launch_dequant(const void* w, const void* scales, int fmt, int N, int K, void* out, hipStream_t s,
+                          const int* skip = nullptr);
 
 // y [M, N] (float32 when y_f32, else bf16) = x [M, K] (bf16, row stride K)
 // W^T + bias for M <= 16 rows, weights in format fmt (0 dense bf16, 1-4
@@ -242,6 +270,7 @@ struct AttnArgs {
   // full_units and workers are set by the launcher.
   float* part;
   int32_t full_units, workers;
+  const int* skip = nullptr;  // step-cache guard (see guard_skip), null: always run
 };
 // bf16 attention blocks: kAttnWaves wavefronts of 32 queries each, one
 // block per CU. A unit is 32 * kAttnWaves queries of one (batch, head)

@@ -242,22 +242,40 @@ int mmdit_step(const mmdit_config* cfg, const mmdit_model_w* w,
  * resets the sum to 0. A first step (valid == 0) always runs the blocks.
  *   cache: the generation's state (below), NULL for no caching.
  *   cache_threshold: >= 0; 0 runs the blocks on every step.
- * A cached step waits for its stream once (it reads rel back to decide), so
- * it cannot be captured into a HIP graph. Needs n_double >= 1. */
+ *   cache_on_device: 0 = the host decides: the step waits for its stream
+ *   once to read rel back, and fills ran_blocks, acc and rel before it
+ *   returns (not capturable into a HIP graph). 1 = a kernel decides: the
+ *   decision state (acc, rel, ran_blocks) stays in cache->buf, every launch
+ *   of the blocks is enqueued and does nothing when the step reuses the
+ *   residual, and the call never waits, so the step can be captured into a
+ *   HIP graph; read the state with mmdit_step_cache_read. A graph captured
+ *   with valid == 1 continues the generation on each replay; start a
+ *   generation with an ordinary call (valid == 0). The results are bit for
+ *   bit those of cache_on_device = 0.
+ * Needs n_double >= 1. */
 typedef struct {
   void* buf;          /* device memory of mmdit_step_cache_bytes(cfg) bytes, caller-owned;
                          the library keeps a_prev and the residual there (float32) */
   size_t bytes;       /* size of buf */
   int32_t valid;      /* in/out: 0 starts a generation; set to 1 by a successful step.
                          After an error return, set it to 0 before the next step. */
-  int32_t ran_blocks; /* out: 1 if the step ran the blocks, 0 if it reused the residual */
+  int32_t ran_blocks; /* out: 1 if the step ran the blocks, 0 if it reused the residual;
+                         -1 after a cache_on_device step (see mmdit_step_cache_read) */
   double acc;         /* in/out: summed rel since the last step that ran the blocks */
   double rel;         /* out: the step's rel (0 when it started a generation) */
 } mmdit_step_cache;
 
 /* Host. Bytes of mmdit_step_cache.buf for cfg (2 B img_len hidden floats for
- * a_prev and the residual, plus per-row partial sums). */
+ * a_prev and the residual, per-row partial sums and 32 bytes of decision
+ * state). */
 int mmdit_step_cache_bytes(const mmdit_config* cfg, size_t* bytes);
+
+/* Host, waits for hip_stream. After steps with cache_on_device = 1: copies
+ * the decision of the last step enqueued on hip_stream from cache->buf into
+ * cache->ran_blocks, acc and rel. Errors: MMDIT_ERR_NULL (cache or buf),
+ * MMDIT_ERR_WORKSPACE (cache->bytes too small), MMDIT_ERR_SHAPE (valid == 0:
+ * no step has run), MMDIT_ERR_HIP. */
+int mmdit_step_cache_read(const mmdit_config* cfg, mmdit_step_cache* cache, void* hip_stream);
 
 /* dequant (quantised layers only): 0 = automatic (decoded once per launch
  * into bf16 scratch from 1024 rows on, see the workspace functions), 1 =
@@ -270,6 +288,7 @@ typedef struct {
   mmdit_step_cache* cache;
   double cache_threshold;
   int32_t dequant;
+  int32_t cache_on_device; /* 0 or 1, see step caching above */
 } mmdit_step_opts;
 
 /* One denoising step with options (context tokens, guidance). Arguments as
@@ -278,7 +297,8 @@ typedef struct {
  * text, generated, then context rows. The workspace is
  * mmdit_step_workspace(cfg). Errors as for mmdit_step; MMDIT_ERR_SHAPE for
  * ctx_len out of range, a non-finite guidance, a negative or NaN
- * cache_threshold, caching without a dual block, or dequant not 0 or 1;
+ * cache_threshold, caching without a dual block, or dequant or
+ * cache_on_device not 0 or 1;
  * MMDIT_ERR_NULL for a NULL
  * ctx_packed with ctx_len > 0, a NULL cache->buf, or a guidance model called
  * without a guidance value (mmdit_step on such a model fails the same way);

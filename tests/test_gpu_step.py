@@ -219,8 +219,15 @@ def cached_oracle(s, g, dbl, sgl, inp, ids, sig, thr, Xc=None):
     return out
 
 
-def cached_gpu(s, g, dbl, sgl, inp, ids, sig, thr, Xc=None):
-    """mmdit_step_ex with a step cache over the schedule, same tuple per step."""
+def cached_gpu(s, g, dbl, sgl, inp, ids, sig, thr, Xc=None, mode="host"):
+    """mmdit_step_ex with a step cache over the schedule, same tuple per step.
+
+    mode "host": the host decides (the state is in the struct after each
+    call); "device": a kernel decides, read back with mmdit_step_cache_read;
+    "graph": the first step eager, the others captured into HIP graphs (one
+    per schedule position) and replayed, the whole generation twice, with
+    eager work and synchronisations between the replays: both passes must
+    agree bit for bit."""
     t = torch()
     dt = dtype_code(s.dtype)
     Lc = 0 if Xc is None else Xc.shape[1]
@@ -229,22 +236,62 @@ def cached_gpu(s, g, dbl, sgl, inp, ids, sig, thr, Xc=None):
     M = bd.ModelW(g, [bd.DoubleW(d, dt, "cuda") for d in dbl], [bd.SingleW(w, dt, "cuda") for w in sgl], dt, "cuda")
     mc = M.c()
     z = t.from_numpy(inp["z"]).cuda()
-    X = t.empty((s.batch, s.img_len, s.in_ch), dtype=t.float32, device="cuda")
-    bd.mmdit_pack_latents(z, X)
+    X0 = t.empty((s.batch, s.img_len, s.in_ch), dtype=t.float32, device="cuda")
+    bd.mmdit_pack_latents(z, X0)
+    X = X0.clone()
     v = t.empty_like(X)
     T, y, ids_d = up(inp["T"], s.dtype), up(inp["y"], s.dtype), up_i32(ids)
     xc = None if Xc is None else t.from_numpy(Xc).cuda()
     ws = workspace(bd.mmdit_step_workspace(cfg))
-    cache = bd.StepCache(cfg)
-    out = []
-    for i in range(len(sig) - 1):
-        print(f"cached step {i} B={s.batch} h={s.hidden} Lt={s.txt_len} Lg={s.img_len} Lc={Lc} {s.dtype} "
-              f"threshold {thr:.4g}", flush=True)
+    cache = bd.StepCache(cfg, on_device=mode != "host")
+
+    def step(i):
         bd.mmdit_step_ex(cfg, mc, X, v, T, y, ids_d, sig[i], sig[i + 1], ws, ctx_packed=xc, ctx_len=Lc,
                          cache=cache, cache_threshold=thr)
+
+    def record():
         sync()
-        out.append((down(X), down(v), cache.ran_blocks, cache.rel, cache.c.acc))
-    return out
+        if mode != "host":
+            cache.read()
+        return (down(X), down(v), cache.ran_blocks, cache.rel, cache.c.acc)
+
+    tag = f"B={s.batch} h={s.hidden} Lt={s.txt_len} Lg={s.img_len} Lc={Lc} {s.dtype} threshold {thr:.4g} {mode}"
+    if mode != "graph":
+        out = []
+        for i in range(len(sig) - 1):
+            print(f"cached step {i} {tag}", flush=True)
+            step(i)
+            out.append(record())
+        return out
+    print(f"cached step 0 (eager) {tag}", flush=True)
+    step(0)
+    sync()
+    graphs = []
+    cap = t.cuda.Stream()
+    cap.wait_stream(t.cuda.current_stream())
+    for i in range(1, len(sig) - 1):
+        print(f"capturing cached step {i}", flush=True)
+        gr = t.cuda.CUDAGraph()
+        with t.cuda.graph(gr, stream=cap):
+            step(i)
+        graphs.append(gr)
+    sync()
+    passes = []
+    for k in range(2):
+        X.copy_(X0)
+        v.fill_(float("nan"))
+        cache.reset()
+        print(f"pass {k}: cached step 0 (eager)", flush=True)
+        step(0)
+        out = [record()]
+        for i, gr in enumerate(graphs, 1):
+            print(f"pass {k}: replay of cached step {i}", flush=True)
+            gr.replay()
+            out.append(record())
+        passes.append(out)
+    for a, b in zip(*passes):
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2:] == b[2:]
+    return passes[1]
 
 
 def check_cached(s, cgh=0, cgw=0, n_steps=5, rel_tol=1e-4):
@@ -274,6 +321,17 @@ def check_cached(s, cgh=0, cgw=0, n_steps=5, rel_tol=1e-4):
         assert abs(a[4] - b[4]) <= rel_tol * max(b[4], 1e-30) or a[4] == b[4] == 0.0, (i, a[4], b[4])
         assert_parity(a[1], b[1], s.dtype, f"cached step {i} v (ran blocks {b[2]})")
         assert_parity(a[0], b[0], s.dtype, f"cached step {i} x_next")
+    # the decision taken on the device, eagerly and from HIP graphs: the same
+    # decisions, and the same kernels on the same data, so x and v bit for
+    # bit those of the host decision (rel and acc summed in another order)
+    for mode in ("device", "graph"):
+        dv = cached_gpu(s, g, dbl, sgl, inp, ids, sig, thr, Xc, mode=mode)
+        for i, (a, b) in enumerate(zip(dv, got)):
+            assert a[2] == b[2], (mode, i, a[2], b[2])
+            assert abs(a[3] - b[3]) <= 1e-9 * max(b[3], 1e-30), (mode, i, a[3], b[3])
+            assert abs(a[4] - b[4]) <= 1e-9 * max(b[4], 1e-30) or a[4] == b[4] == 0.0, (mode, i, a[4], b[4])
+            assert np.array_equal(a[1], b[1]), f"{mode} step {i}: v differs from the host decision's"
+            assert np.array_equal(a[0], b[0]), f"{mode} step {i}: x differs from the host decision's"
 
 
 def test_step_cache_f32_tiny_batch2():

@@ -217,6 +217,9 @@ def test_step_ex_errors_before_launch(lib):
     o = bd.mmdit_step_opts(has_guidance=1, guidance=3.5,
                            cache=C.pointer(bd.mmdit_step_cache(buf=fake, bytes=need - 1)), cache_threshold=0.1)
     assert call(C.byref(o)) == 4                                            # cache buffer too small
+    o = bd.mmdit_step_opts(has_guidance=1, guidance=3.5, cache=C.pointer(cache), cache_threshold=0.1,
+                           cache_on_device=2)
+    assert call(C.byref(o)) == 2                                            # unknown decision mode
     cfg0 = bd.make_config(dataclasses.replace(s, n_double=0))
     o = bd.mmdit_step_opts(has_guidance=1, guidance=3.5, cache=C.pointer(cache), cache_threshold=0.1)
     assert lib.mmdit_step_ex(C.byref(cfg0), C.byref(w), fake, None, fake, fake, fake, 1.0, 0.5, C.byref(o), fake,
@@ -227,8 +230,24 @@ def test_step_ex_errors_before_launch(lib):
 def test_step_cache_bytes(lib):
     s = I.CFG4
     n = bd.mmdit_step_cache_bytes(bd.make_config(s))
-    # a_prev and the residual in float32 plus two floats per image row
-    assert 2 * s.img_len * s.hidden * 4 + s.img_len * 8 <= n <= 2 * s.img_len * s.hidden * 4 + s.img_len * 8 + 1024
+    # a_prev and the residual in float32, two floats per image row, 32 bytes
+    # of decision state
+    lo = 2 * s.img_len * s.hidden * 4 + s.img_len * 8 + 32
+    assert lo <= n <= lo + 1024
+
+
+def test_step_cache_read_errors(lib):
+    # checked before the device copy: the buffer pointer is never used
+    cfg = bd.make_config(I.CFG4)
+    need = bd.mmdit_step_cache_bytes(cfg)
+    fake = 0x6000
+    assert lib.mmdit_step_cache_read(C.byref(cfg), None, None) == 1
+    c = bd.mmdit_step_cache(buf=None, bytes=need, valid=1)
+    assert lib.mmdit_step_cache_read(C.byref(cfg), C.byref(c), None) == 1     # NULL buffer
+    c = bd.mmdit_step_cache(buf=fake, bytes=need - 1, valid=1)
+    assert lib.mmdit_step_cache_read(C.byref(cfg), C.byref(c), None) == 4     # buffer too small
+    c = bd.mmdit_step_cache(buf=fake, bytes=need, valid=0)
+    assert lib.mmdit_step_cache_read(C.byref(cfg), C.byref(c), None) == 2     # no step has run
 
 
 def test_dequantise_argument_errors(lib):
