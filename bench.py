@@ -16,7 +16,8 @@ share; the HBM-bound kernels in the step and alone (cold and warm Infinity
 Cache); weight streaming of a quantised layer at 1 and 16 rows; HIP-graph
 replay; block TFLOP/s (4608 tokens) and the configuration-2 block (1280
 tokens); the bf16-residual, quantised, ternary, reference-image and guided
-variants; and the CPU oracle on a bounded sample.
+variants; the cached guided generation with the decision on the host, on the
+device, and replayed from HIP graphs; and the CPU oracle on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
