@@ -1125,6 +1125,11 @@ int mmdit_linear_fwd(const mmdit_linear* l, int32_t act_dtype, const void* x, in
   if ((r = mmdit_linear_workspace(l, act_dtype, M, route, &need))) return r;
   if (need && (!ws || ws_bytes < need)) return fail(MMDIT_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
   if (rt == MMDIT_ROUTE_STREAM) {
+    // the kernel reads 16-byte pieces of dense, 4-bit and 8-bit rows (8 and
+    // 4 bytes of ternary and 1-bit rows) and 4-byte pairs of 4/8-bit scales
+    const int wal = l->fmt == MMDIT_W_Q1G128 ? 4 : l->fmt == MMDIT_W_TQ2G128 ? 8 : 16;
+    if ((uintptr_t)l->w % wal || (l->scales && (uintptr_t)l->scales % 4))
+      return fail(MMDIT_ERR_SHAPE, "weight-streaming route: weights must be %d-byte and scales 4-byte aligned", wal);
     const double wb = l->fmt == MMDIT_W_DENSE ? 2.0 : l->fmt == MMDIT_W_Q4G64 ? 0.5 + 2.0 / 64
                       : l->fmt == MMDIT_W_Q8G64 ? 1.0 + 2.0 / 64 : l->fmt == MMDIT_W_Q1G128 ? 0.125 + 2.0 / 128
                       : 0.25 + 2.0 / 128;

@@ -435,8 +435,11 @@ int mmdit_linear_workspace(const mmdit_linear* l, int32_t act_dtype, int32_t M, 
  * y [M, n_out] float32 when y_f32 (or act_dtype is F32), else bf16; both
  * device, 16-byte aligned. route: mmdit_route (float32 activations: AUTO or
  * TILED only). ws: device workspace of mmdit_linear_workspace() bytes (may
- * be NULL when that is 0). Results are the same bf16-operand, float32-
- * accumulated products the blocks compute, whatever the route. Errors:
+ * be NULL when that is 0). Results are the bf16-operand, float32-accumulated
+ * products the blocks compute; the weight-streaming route multiplies each
+ * 4-bit group's float32 sum of q x by its scale instead of rounding s q to
+ * bf16 first. The weight-streaming route needs l->w 16-byte aligned (8 for
+ * ternary, 4 for 1-bit) and l->scales 4-byte aligned. Errors:
  * MMDIT_ERR_NULL, MMDIT_ERR_DTYPE (format / dtype), MMDIT_ERR_SHAPE (sizes,
  * a route the shape does not allow, alignment), MMDIT_ERR_WORKSPACE,
  * MMDIT_ERR_UNSUPPORTED, MMDIT_ERR_HIP. */

@@ -366,6 +366,11 @@ def test_linear_entry_point_errors_before_launch(lib):
     dense = bd.mmdit_linear(w=4096, scales=None, bias=None, fmt=bd.W_DENSE, n_out=328, k_in=384)
     assert lib.mmdit_linear_fwd(C.byref(dense), bd.BF16, dummy, 300, dummy, 1, bd.ROUTE_DECODE, dummy, 1 << 20,
                                 None) == 2
+    # the streaming route reads 16-byte pieces of 4-bit rows and 4-byte scale pairs
+    odd = bd.mmdit_linear(w=4096 + 8, scales=4096, bias=None, fmt=bd.W_Q4G64, n_out=328, k_in=384)
+    assert lib.mmdit_linear_fwd(C.byref(odd), bd.BF16, dummy, 4, dummy, 1, bd.ROUTE_STREAM, None, 0, None) == 2
+    odd = bd.mmdit_linear(w=4096, scales=4096 + 2, bias=None, fmt=bd.W_Q4G64, n_out=328, k_in=384)
+    assert lib.mmdit_linear_fwd(C.byref(odd), bd.BF16, dummy, 4, dummy, 1, bd.ROUTE_STREAM, None, 0, None) == 2
     # M = 0 is a no-op, NULL weights an error
     assert lib.mmdit_linear_fwd(C.byref(dense), bd.BF16, None, 0, None, 1, bd.ROUTE_AUTO, None, 0, None) == 0
     assert lib.mmdit_linear_fwd(None, bd.BF16, dummy, 4, dummy, 1, bd.ROUTE_AUTO, None, 0, None) == 1
