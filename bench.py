@@ -16,8 +16,10 @@ share; the HBM-bound kernels in the step and alone (cold and warm Infinity
 Cache); weight streaming of a quantised layer at 1 and 16 rows; HIP-graph
 replay; block TFLOP/s (4608 tokens) and the configuration-2 block (1280
 tokens); the bf16-residual, quantised, ternary, reference-image and guided
-variants; the cached guided generation with the decision on the host, on the
-device, and replayed from HIP graphs; and the CPU oracle on a bounded sample.
+variants; the 4-step loop and the guided generation with the modulation
+vectors of 4 timesteps computed in one pass; the cached guided generation
+with the decision on the host, on the device, and replayed from HIP graphs;
+and the CPU oracle on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -216,6 +218,24 @@ def main():
     loop4(0)
     loop_ms = timed(loop4, max(2, a.steps // 4))
     log(f"4-step loop: {loop_ms:.2f} ms")
+    # the same loop with the modulation vectors of its 4 timesteps computed in
+    # one pass over the modulation weights (mmdit_step_modulations), inside
+    # the timed region; the final latent must equal the plain loop's
+    mods4 = torch.empty(bd.mmdit_step_modulations_bytes(cfg, 4), dtype=torch.uint8, device=dev)
+    x_plain = X.clone()
+
+    def loop4_shared(_):
+        X.copy_(X0)
+        bd.mmdit_step_modulations(cfg, mc, y, sig[:4], mods4)
+        for j in range(4):
+            bd.mmdit_step_ex(cfg, mc, X, v, T, None, ids, sig[j], sig[j + 1], ws, mods=mods4, mods_count=4,
+                             mods_index=j)
+    loop4_shared(0)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(X, x_plain))
+    loop_shared_ms = timed(loop4_shared, max(2, a.steps // 4))
+    log(f"4-step loop, modulations shared: {loop_shared_ms:.2f} ms (final latent equal to the plain loop's: {same})")
+    del mods4, x_plain
     flops = step_flops(s)
 
     # every MFMA-bound kernel class of the step, timed with HIP events around
@@ -285,6 +305,7 @@ def main():
                       "global_batch": 1, "seq_len": s.seq_len, "image_tokens": s.img_len, "text_tokens": s.txt_len,
                       "parallelism": "single GPU"},
            "step_spread_ms": spread, "loop_4_steps_ms": round(loop_ms, 3),
+           "loop_4_steps_shared_modulations": {"ms": round(loop_shared_ms, 3), "final_latent_identical": same},
            "device": {"name": torch.cuda.get_device_name(0), "hip": torch.version.hip,
                       "torch": torch.__version__},
            "step_tflops": round(flops / ms / 1e9, 1),
@@ -592,6 +613,27 @@ def main():
         out["dev_generation"] = {"steps": nd, "guidance": 4.0, "seconds": round(dsec, 3),
                                  "ms_per_step": round(dsec * 1e3 / nd, 3)}
         log(f"dev generation: {nd} steps in {dsec:.2f} s ({dsec * 1e3 / nd:.2f} ms/step)")
+
+        # the same generation with the modulation vectors of each group of 4
+        # timesteps computed in one pass over the modulation weights
+        mods4 = torch.empty(bd.mmdit_step_modulations_bytes(cfg, 4), dtype=torch.uint8, device=dev)
+        Xm = X.clone()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i0 in range(0, nd, 4):
+            cnt = min(4, nd - i0)
+            bd.mmdit_step_modulations(cfg, mdc, y, sigd[i0:i0 + cnt], mods4, guidance=4.0)
+            for j in range(cnt):
+                bd.mmdit_step_ex(cfg, mdc, Xm, v, T, None, ids, sigd[i0 + j], sigd[i0 + j + 1], ws, mods=mods4,
+                                 mods_count=cnt, mods_index=j)
+        torch.cuda.synchronize()
+        msec = time.perf_counter() - t1
+        out["dev_generation_shared_modulations"] = {
+            "seconds": round(msec, 3), "ms_per_step": round(msec * 1e3 / nd, 3),
+            "final_latent_identical": bool(torch.equal(Xm, Xd))}
+        log(f"dev generation, modulations shared by groups of 4 steps: {msec:.2f} s, "
+            f"same latent {torch.equal(Xm, Xd)}")
+        del Xm, mods4
 
         # the same generation with step caching: steps whose summed change of
         # the first block's modulated input stays below the threshold reuse

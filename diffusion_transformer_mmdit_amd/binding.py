@@ -82,7 +82,8 @@ class mmdit_step_cache(C.Structure):
 class mmdit_step_opts(C.Structure):
     _fields_ = [("ctx_packed", C.c_void_p), ("ctx_len", C.c_int32), ("has_guidance", C.c_int32),
                 ("guidance", C.c_double), ("cache", C.POINTER(mmdit_step_cache)), ("cache_threshold", C.c_double),
-                ("dequant", C.c_int32), ("cache_on_device", C.c_int32)]
+                ("dequant", C.c_int32), ("cache_on_device", C.c_int32), ("mods", C.c_void_p),
+                ("mods_count", C.c_int32), ("mods_index", C.c_int32)]
 
 
 # Every function the header declares, with its ctypes signature.
@@ -93,6 +94,9 @@ _SIGS = {
     "mmdit_step_workspace": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(C.c_size_t)]),
     "mmdit_step_cache_bytes": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(C.c_size_t)]),
     "mmdit_step_cache_read": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(mmdit_step_cache), _P]),
+    "mmdit_step_modulations_bytes": (C.c_int, [C.POINTER(mmdit_config), C.c_int32, C.POINTER(C.c_size_t)]),
+    "mmdit_step_modulations": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(mmdit_model_w), _P, C.POINTER(C.c_double),
+                                         C.c_int32, C.POINTER(mmdit_step_opts), _P, C.c_size_t, _P]),
     "mmdit_step_workspace_ex": (C.c_int, [C.POINTER(mmdit_config), C.POINTER(mmdit_model_w),
                                           C.POINTER(mmdit_step_opts), C.POINTER(C.c_size_t)]),
     "mmdit_double_block_fwd": (C.c_int, [C.POINTER(mmdit_dims), C.POINTER(mmdit_double_w), _P, _P, _P, _P,
@@ -397,9 +401,13 @@ class StepCache:
 
 def mmdit_step_ex(cfg, w: mmdit_model_w, x_packed, v_out, txt_emb, y, ids, sigma: float, sigma_next: float, ws,
                   ctx_packed=None, ctx_len: int = 0, guidance: Optional[float] = None, stream=None,
-                  cache: Optional[StepCache] = None, cache_threshold: float = 0.0, dequant_in_gemm: bool = False):
+                  cache: Optional[StepCache] = None, cache_threshold: float = 0.0, dequant_in_gemm: bool = False,
+                  mods=None, mods_count: int = 0, mods_index: int = 0):
     o = mmdit_step_opts()
     o.dequant = 1 if dequant_in_gemm else 0
+    o.mods = _ptr(mods)
+    o.mods_count = int(mods_count)
+    o.mods_index = int(mods_index)
     o.ctx_packed = _ptr(ctx_packed)
     o.ctx_len = int(ctx_len)
     o.has_guidance = 0 if guidance is None else 1
@@ -412,6 +420,25 @@ def mmdit_step_ex(cfg, w: mmdit_model_w, x_packed, v_out, txt_emb, y, ids, sigma
                                _ptr(ids), float(sigma), float(sigma_next), C.byref(o), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream)),
            "mmdit_step_ex")
+
+
+def mmdit_step_modulations_bytes(cfg: mmdit_config, n_sigma: int) -> int:
+    n = C.c_size_t()
+    _check(lib().mmdit_step_modulations_bytes(C.byref(cfg), int(n_sigma), C.byref(n)), "mmdit_step_modulations_bytes")
+    return n.value
+
+
+def mmdit_step_modulations(cfg, w: mmdit_model_w, y, sigmas, mods, guidance: Optional[float] = None, stream=None):
+    """Modulation vectors for the timesteps `sigmas` in one pass over the
+    modulation weights; pass `mods` to mmdit_step_ex with mods_count =
+    len(sigmas) and mods_index = j for the step at sigmas[j]."""
+    sg = (C.c_double * len(sigmas))(*[float(v) for v in sigmas])
+    o = mmdit_step_opts()
+    o.has_guidance = 0 if guidance is None else 1
+    o.guidance = 0.0 if guidance is None else float(guidance)
+    _check(lib().mmdit_step_modulations(C.byref(cfg), C.byref(w), _ptr(y), sg, len(sigmas), C.byref(o), _ptr(mods),
+                                        mods.numel() * mods.element_size(), _stream(stream)),
+           "mmdit_step_modulations")
 
 
 NOALLOC_SCRATCH_BYTES = 256 << 20  # the library's scratch per GPU (mmdit_step_noalloc)

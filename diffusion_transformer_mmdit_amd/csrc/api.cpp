@@ -250,6 +250,22 @@ struct StepWs {
   size_t mod_dual, mod_single, mod_final;  // offsets inside mods (floats)
 };
 
+// Where the modulation vectors of a step sit. Each modulation matrix (dual
+// block i stream s, single block i, the final layer) holds its rows for n
+// timesteps of B batch rows each, [n B, width], timestep j first; a step
+// reads the rows of timestep j. Inside the step workspace n = 1, j = 0;
+// mmdit_step_modulations fills n timesteps at once.
+struct ModLay {
+  float* base;
+  size_t B, h, nd, ns, n, j;
+  float* dual(int i, int s) const { return base + (((size_t)i * 2 + s) * n + j) * B * 6 * h; }
+  float* single(int i) const { return base + nd * 2 * n * B * 6 * h + ((size_t)i * n + j) * B * 3 * h; }
+  float* fin() const { return base + nd * 2 * n * B * 6 * h + ns * n * B * 3 * h + j * B * 2 * h; }
+  static size_t floats(size_t B, size_t h, size_t nd, size_t ns, size_t n) {
+    return n * B * h * (nd * 12 + ns * 3 + 2);
+  }
+};
+
 // Residual bytes per element inside mmdit_step.
 int step_resid_esz(const Geo& g) { return g.resid == MMDIT_RESID_BF16 ? 2 : 4; }
 
@@ -737,6 +753,121 @@ int mmdit_step_cache_bytes(const mmdit_config* cfg, size_t* bytes) {
   return MMDIT_OK;
 }
 
+int mmdit_step_modulations_bytes(const mmdit_config* cfg, int32_t n_sigma, size_t* bytes) {
+  Geo g;
+  int r;
+  if (!bytes) return fail(MMDIT_ERR_NULL, "bytes is NULL");
+  if ((r = check_config(cfg, g))) return r;
+  if (n_sigma < 1 || (int64_t)n_sigma * g.B > kGemvMaxB)
+    return fail(MMDIT_ERR_SHAPE, "n_sigma %d times batch %d must be in [1, %d]", n_sigma, g.B, kGemvMaxB);
+  const size_t rows = (size_t)n_sigma * g.B;
+  // the modulation matrices, then scratch for the timestep embeddings, the
+  // conditioning MLPs' hidden rows, the conditioning vectors and the pooled
+  // text vectors repeated per timestep
+  *bytes = align_up(ModLay::floats(g.B, g.h, cfg->n_double, cfg->n_single, n_sigma) * 4) +
+           align_up(rows * cfg->temb_dim * 4) + 2 * align_up(rows * g.h * 4) +
+           align_up(rows * cfg->vec_in_dim * g.esz);
+  return MMDIT_OK;
+}
+
+int mmdit_step_modulations(const mmdit_config* cfg, const mmdit_model_w* w, const void* y, const double* sigmas,
+                           int32_t n_sigma, const mmdit_step_opts* opts, void* mods, size_t mods_bytes,
+                           void* hip_stream) {
+  Geo g;
+  int r;
+  size_t need = 0;
+  if ((r = mmdit_step_modulations_bytes(cfg, n_sigma, &need))) return r;
+  g = Geo{};
+  if ((r = check_config(cfg, g))) return r;
+  if (!w || !y || !sigmas || !mods) return fail(MMDIT_ERR_NULL, "NULL weights, y, sigmas or mods");
+  if ((uintptr_t)mods % 16) return fail(MMDIT_ERR_SHAPE, "mods must be 16-byte aligned");
+  if (mods_bytes < need) return fail(MMDIT_ERR_WORKSPACE, "mods buffer %zu bytes, need %zu", mods_bytes, need);
+  for (int j = 0; j < n_sigma; ++j)
+    if (!std::isfinite(sigmas[j])) return fail(MMDIT_ERR_SHAPE, "sigma values must be finite");
+  const mmdit_step_opts none{};
+  if (!opts) opts = &none;
+  const bool guided = w->guidance_in0.w != nullptr;
+  if (guided) {
+    if (!opts->has_guidance)
+      return fail(MMDIT_ERR_NULL, "the model has a guidance embedder: pass a guidance value");
+    if (!std::isfinite(opts->guidance)) return fail(MMDIT_ERR_SHAPE, "guidance must be finite");
+  }
+  if ((cfg->n_double > 0 && !w->dbl) || (cfg->n_single > 0 && !w->sgl)) return fail(MMDIT_ERR_NULL, "block weight arrays are NULL");
+  const int h = g.h, B = g.B;
+  if ((r = check_gemv(w->time_in0, h, cfg->temb_dim, "time_in0"))) return r;
+  if ((r = check_gemv(w->time_in1, h, h, "time_in1"))) return r;
+  if ((r = check_gemv(w->vec_in0, h, cfg->vec_in_dim, "vec_in0"))) return r;
+  if ((r = check_gemv(w->vec_in1, h, h, "vec_in1"))) return r;
+  if (guided) {
+    if ((r = check_gemv(w->guidance_in0, h, cfg->temb_dim, "guidance_in0"))) return r;
+    if ((r = check_gemv(w->guidance_in1, h, h, "guidance_in1"))) return r;
+  }
+  if ((r = check_gemv(w->final_mod, 2 * h, h, "final_mod"))) return r;
+  for (int i = 0; i < cfg->n_double; ++i) {
+    if ((r = check_gemv(w->dbl[i].txt.mod, 6 * h, h, "dbl.txt.mod"))) return fail(r, "dbl[%d]: %s", i, g_err.c_str());
+    if ((r = check_gemv(w->dbl[i].img.mod, 6 * h, h, "dbl.img.mod"))) return fail(r, "dbl[%d]: %s", i, g_err.c_str());
+  }
+  for (int i = 0; i < cfg->n_single; ++i)
+    if ((r = check_gemv(w->sgl[i].mod, 3 * h, h, "sgl.mod"))) return fail(r, "sgl[%d]: %s", i, g_err.c_str());
+
+  // rows j B + b: timestep j, batch row b
+  const int rows = n_sigma * B;
+  Geo gr = g;
+  gr.B = rows;
+  Ctx c{(hipStream_t)hip_stream, gr, cfg->dims.ln_eps, cfg->dims.rms_eps};
+  const ModLay ml{(float*)mods, (size_t)B, (size_t)h, (size_t)cfg->n_double, (size_t)cfg->n_single,
+                  (size_t)n_sigma, 0};
+  size_t at = align_up(ModLay::floats(B, h, cfg->n_double, cfg->n_single, n_sigma) * 4);
+  float* temb = (float*)ptr(mods, at);
+  at += align_up((size_t)rows * cfg->temb_dim * 4);
+  float* hid = (float*)ptr(mods, at);
+  at += align_up((size_t)rows * h * 4);
+  float* vec = (float*)ptr(mods, at);
+  at += align_up((size_t)rows * h * 4);
+  void* yrep = ptr(mods, at);
+  // conditioning vectors, as in the step, one row per (timestep, batch row)
+  for (int j = 0; j < n_sigma; ++j)
+    HIP_TRY(launch_timestep_embedding(temb + (size_t)j * B * cfg->temb_dim, B, cfg->temb_dim, sigmas[j], c.s));
+  if ((r = gemv(c, w->time_in0, temb, true, cfg->temb_dim, hid, h, false, false))) return r;
+  if ((r = gemv(c, w->time_in1, hid, true, h, vec, h, true, false))) return r;
+  if (guided) {
+    HIP_TRY(launch_timestep_embedding(temb, rows, cfg->temb_dim, opts->guidance, c.s));
+    if ((r = gemv(c, w->guidance_in0, temb, true, cfg->temb_dim, hid, h, false, false))) return r;
+    if ((r = gemv(c, w->guidance_in1, hid, true, h, vec, h, true, true))) return r;
+  }
+  for (int j = 0; j < n_sigma; ++j)  // the pooled vectors, once per timestep
+    HIP_TRY(launch_convert(y, !g.bf16, ptr(yrep, (size_t)j * B * cfg->vec_in_dim * g.esz), !g.bf16,
+                           (int64_t)B * cfg->vec_in_dim, c.s));
+  if ((r = gemv(c, w->vec_in0, yrep, false, cfg->vec_in_dim, hid, h, false, false))) return r;
+  if ((r = gemv(c, w->vec_in1, hid, true, h, vec, h, true, true))) return r;
+  // every modulation matrix, all timesteps in one pass over its weights
+  GemvMultiArgs ga{};
+  ga.x = vec; ga.K = h; ga.B = rows; ga.x_bstride = h;
+  double gemv_bytes = 0;
+  auto flush = [&]() -> int {
+    if (ga.nseg == 0) return MMDIT_OK;
+    ProfScope ps(PC_GEMV, gemv_bytes, c.s);
+    HIP_TRY(launch_gemv_multi(ga, g.bf16, c.s));
+    ga.nseg = 0;
+    gemv_bytes = 0;
+    return MMDIT_OK;
+  };
+  auto add = [&](const mmdit_linear& l, float* out, int y_bstride) -> int {
+    GemvSeg& sg = ga.seg[ga.nseg++];
+    sg.W = l.w; sg.bias = l.bias; sg.y = out; sg.N = l.n_out; sg.y_bstride = y_bstride;
+    gemv_bytes += (double)l.n_out * l.k_in * g.esz;
+    return ga.nseg == kGemvMaxSeg ? flush() : MMDIT_OK;
+  };
+  if ((r = add(w->final_mod, ml.fin(), 2 * h))) return r;
+  for (int i = 0; i < cfg->n_double; ++i) {
+    if ((r = add(w->dbl[i].txt.mod, ml.dual(i, 0), 6 * h))) return r;
+    if ((r = add(w->dbl[i].img.mod, ml.dual(i, 1), 6 * h))) return r;
+  }
+  for (int i = 0; i < cfg->n_single; ++i)
+    if ((r = add(w->sgl[i].mod, ml.single(i), 3 * h))) return r;
+  return flush();
+}
+
 int mmdit_step_cache_read(const mmdit_config* cfg, mmdit_step_cache* cache, void* hip_stream) {
   Geo g;
   int r;
@@ -767,9 +898,9 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   Geo g;
   int r;
   if ((r = check_config(cfg, g))) return r;
-  if (!w || !x_packed || !y || !ids) return fail(MMDIT_ERR_NULL, "NULL weights, latent, y or ids");
   const mmdit_step_opts none{};
   if (!opts) opts = &none;
+  if (!w || !x_packed || !ids || (!y && !opts->mods)) return fail(MMDIT_ERR_NULL, "NULL weights, latent, y or ids");
   const void* ctx_packed = opts->ctx_packed;
   const int ctx_len = opts->ctx_len;
   if (ctx_len < 0 || ctx_len >= g.Li)
@@ -777,12 +908,17 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   if (ctx_len > 0 && !ctx_packed) return fail(MMDIT_ERR_NULL, "ctx_packed is NULL with ctx_len > 0");
   const int Lg = g.Li - ctx_len;  // generated image tokens per batch
   const bool guided = w->guidance_in0.w != nullptr;
-  if (guided) {
+  if (guided && !opts->mods) {  // given modulations already hold the guidance
     if (!opts->has_guidance)
       return fail(MMDIT_ERR_NULL, "the model has a guidance embedder: pass a guidance value (mmdit_step_ex)");
     if (!std::isfinite(opts->guidance)) return fail(MMDIT_ERR_SHAPE, "guidance must be finite");
   }
   if (opts->dequant != 0 && opts->dequant != 1) return fail(MMDIT_ERR_SHAPE, "dequant %d must be 0 or 1", opts->dequant);
+  if (opts->mods) {
+    if (opts->mods_count < 1 || opts->mods_index < 0 || opts->mods_index >= opts->mods_count)
+      return fail(MMDIT_ERR_SHAPE, "mods_index %d must be in [0, mods_count %d)", opts->mods_index, opts->mods_count);
+    if ((uintptr_t)opts->mods % 16) return fail(MMDIT_ERR_SHAPE, "mods must be 16-byte aligned");
+  }
   mmdit_step_cache* cache = opts->cache;
   if (cache) {
     if (std::isnan(opts->cache_threshold) || opts->cache_threshold < 0)
@@ -836,20 +972,26 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   float* vec = (float*)ptr(ws, lay.vec);
   float* temb = (float*)ptr(ws, lay.temb);
   float* hid = (float*)ptr(ws, lay.hid);
-  float* mods = (float*)ptr(ws, lay.mods);
   float* table = (float*)ptr(ws, lay.table);
+  // modulation vectors: computed below, or given (mmdit_step_modulations)
+  const bool given = opts->mods != nullptr;
+  const ModLay ml{given ? (float*)opts->mods : (float*)ptr(ws, lay.mods), (size_t)B, (size_t)h,
+                  (size_t)cfg->n_double, (size_t)cfg->n_single, given ? (size_t)opts->mods_count : 1,
+                  given ? (size_t)opts->mods_index : 0};
 
   // conditioning vector: L1(SiLU(L0(temb))) + V1(SiLU(V0(y)))
-  HIP_TRY(launch_timestep_embedding(temb, B, cfg->temb_dim, sigma, c.s));
-  if ((r = gemv(c, w->time_in0, temb, true, cfg->temb_dim, hid, h, false, false))) return r;
-  if ((r = gemv(c, w->time_in1, hid, true, h, vec, h, true, false))) return r;
-  if (guided) {  // + G1(SiLU(G0(temb(guidance))))
-    HIP_TRY(launch_timestep_embedding(temb, B, cfg->temb_dim, opts->guidance, c.s));
-    if ((r = gemv(c, w->guidance_in0, temb, true, cfg->temb_dim, hid, h, false, false))) return r;
-    if ((r = gemv(c, w->guidance_in1, hid, true, h, vec, h, true, true))) return r;
+  if (!given) {
+    HIP_TRY(launch_timestep_embedding(temb, B, cfg->temb_dim, sigma, c.s));
+    if ((r = gemv(c, w->time_in0, temb, true, cfg->temb_dim, hid, h, false, false))) return r;
+    if ((r = gemv(c, w->time_in1, hid, true, h, vec, h, true, false))) return r;
+    if (guided) {  // + G1(SiLU(G0(temb(guidance))))
+      HIP_TRY(launch_timestep_embedding(temb, B, cfg->temb_dim, opts->guidance, c.s));
+      if ((r = gemv(c, w->guidance_in0, temb, true, cfg->temb_dim, hid, h, false, false))) return r;
+      if ((r = gemv(c, w->guidance_in1, hid, true, h, vec, h, true, true))) return r;
+    }
+    if ((r = gemv(c, w->vec_in0, y, false, cfg->vec_in_dim, hid, h, false, false))) return r;
+    if ((r = gemv(c, w->vec_in1, hid, true, h, vec, h, true, true))) return r;
   }
-  if ((r = gemv(c, w->vec_in0, y, false, cfg->vec_in_dim, hid, h, false, false))) return r;
-  if ((r = gemv(c, w->vec_in1, hid, true, h, vec, h, true, true))) return r;
   // every block's modulation, all from SiLU(vec): batched into launches of
   // up to kGemvMaxSeg weight matrices. The final layer's and the first dual
   // block's image modulation come first: a step that reuses the cached
@@ -867,14 +1009,15 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
     return MMDIT_OK;
   };
   auto add = [&](const mmdit_linear& l, float* out, int y_bstride) -> int {
+    if (given) return MMDIT_OK;
     if (B > kGemvMaxB) return gemv(c, l, vec, true, h, out, y_bstride, true, false);
     GemvSeg& sg = ga.seg[ga.nseg++];
     sg.W = l.w; sg.bias = l.bias; sg.y = out; sg.N = l.n_out; sg.y_bstride = y_bstride;
     gemv_bytes += (double)l.n_out * l.k_in * g.esz;
     return ga.nseg == kGemvMaxSeg ? flush() : MMDIT_OK;
   };
-  if ((r = add(w->final_mod, mods + lay.mod_final, 2 * h))) return r;
-  if (cfg->n_double > 0 && (r = add(w->dbl[0].img.mod, mods + lay.mod_dual + (size_t)B * 6 * h, 6 * h))) return r;
+  if ((r = add(w->final_mod, ml.fin(), 2 * h))) return r;
+  if (cfg->n_double > 0 && (r = add(w->dbl[0].img.mod, ml.dual(0, 1), 6 * h))) return r;
   if (cache && (r = flush())) return r;
   // the RoPE table depends on the ids only; built before a cached step's
   // decision so that the guarded launches below are the blocks' alone
@@ -915,7 +1058,7 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
     float* part = (float*)ptr(cache->buf, cl.part);
     CacheDeltaArgs ca{};
     ca.x = (const float*)ximg;
-    ca.mod = mods + lay.mod_dual + (size_t)B * 6 * h;  // shift1 at 0, scale1 at h
+    ca.mod = ml.dual(0, 1);  // shift1 at 0, scale1 at h
     ca.mod_bstride = 6 * h;
     ca.rows_per_batch = g.Li;
     ca.prev = (float*)ptr(cache->buf, cl.prev);
@@ -958,12 +1101,11 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
               rows_of(x, (int64_t)B * g.Lt, g.Li, h, re), nullptr};
   if (run_blocks) {
     for (int i = 0; i < cfg->n_double; ++i) {
-      float* md = mods + lay.mod_dual + (size_t)i * 2 * B * 6 * h;
-      if ((r = add(w->dbl[i].txt.mod, md, 6 * h))) return r;
-      if (i > 0 && (r = add(w->dbl[i].img.mod, md + (size_t)B * 6 * h, 6 * h))) return r;
+      if ((r = add(w->dbl[i].txt.mod, ml.dual(i, 0), 6 * h))) return r;
+      if (i > 0 && (r = add(w->dbl[i].img.mod, ml.dual(i, 1), 6 * h))) return r;
     }
     for (int i = 0; i < cfg->n_single; ++i)
-      if ((r = add(w->sgl[i].mod, mods + lay.mod_single + (size_t)i * B * 3 * h, 3 * h))) return r;
+      if ((r = add(w->sgl[i].mod, ml.single(i), 3 * h))) return r;
     if ((r = flush())) return r;
     if (g.Lt > 0) {
       GemmProblem gt = base_problem(w->txt_in);
@@ -972,14 +1114,13 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
       if ((r = gemm(c, &gt, 1, EPI_STORE))) return r;
     }
     for (int i = 0; i < cfg->n_double; ++i) {
-      float* md = mods + lay.mod_dual + (size_t)i * 2 * B * 6 * h;
-      parts[0].mod = md;
-      parts[1].mod = md + (size_t)B * 6 * h;
+      parts[0].mod = ml.dual(i, 0);
+      parts[1].mod = ml.dual(i, 1);
       const mmdit_stream_w* sw[2] = {&w->dbl[i].txt, &w->dbl[i].img};
       if ((r = run_double(c, sw, parts, !rb, table, ws, lay.blk))) return r;
     }
     for (int i = 0; i < cfg->n_single; ++i) {
-      float* ms = mods + lay.mod_single + (size_t)i * B * 3 * h;
+      float* ms = ml.single(i);
       parts[0].mod = ms;
       parts[1].mod = ms;
       if (g.Lt > 0) {
@@ -996,7 +1137,7 @@ int mmdit::step_impl(const mmdit_config* cfg, const mmdit_model_w* w, void* x_pa
   Part fin = parts[1];
   fin.len = Lg;
   fin.x_in.rows_per_batch = Lg;  // batch stride stays Li rows
-  fin.mod = mods + lay.mod_final;
+  fin.mod = ml.fin();
   void* xn = ptr(ws, lay.blk.xn);
   if ((r = run_ln(c, &fin, 1, 2 * h, 0, h, !rb, xn))) return r;
   GemmProblem f = base_problem(w->final_lin);

@@ -750,6 +750,12 @@ __global__ __launch_bounds__(256) void k_gemv_multi(GemvMultiArgs a) {
 // quarters (lane ^ 16: one row), then a butterfly over 16 lanes; lane 16 q
 // ends with row q.
 constexpr int kGemv4Rows = 4;
+// With several batch rows, row groups of 4 x kGemv4Rows rows per block:
+// SiLU(x) is staged in LDS once per block and serves all of them (one group
+// per block staged it 4 times as often: at 4 batch rows, 48 KB of LDS
+// traffic per 16 weight rows). One batch row keeps one group per block.
+template <int BB>
+constexpr int gemv4_groups() { return BB > 1 ? 4 : 1; }
 
 template <int NCH, int BB>
 __global__ __launch_bounds__(256) void k_gemv_multi4(GemvMultiArgs a) {
@@ -759,58 +765,72 @@ __global__ __launch_bounds__(256) void k_gemv_multi4(GemvMultiArgs a) {
   for (int i = 1; i < a.nseg; ++i)
     if ((int)blockIdx.x >= a.seg[i].block0) sg = i;
   const GemvSeg& g = a.seg[sg];
-  const int lane = threadIdx.x & 63;
-  const int n0 = (((int)blockIdx.x - g.block0) * 4 + (threadIdx.x >> 6)) * kGemv4Rows;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K = NCH * 512, N = g.N;
-  constexpr int B = BB;
   const bf16* W = reinterpret_cast<const bf16*>(g.W);
+  const bf16* bias = reinterpret_cast<const bf16*>(g.bias);
   // x first: requesting the weights ahead of the staging barrier measured
   // slower (4.1 against 6.0 TB/s on 24 x 18432 x 3072)
-  gemv_stage_x<float>(xs, a.x, B, K, a.x_bstride, true);
-  bf16x8 w[kGemv4Rows][NCH];
+  gemv_stage_x<float>(xs, a.x, BB, K, a.x_bstride, true);
+  constexpr int RG = gemv4_groups<BB>();
+  for (int rg = 0; rg < RG; ++rg) {
+    const int n0 = ((((int)blockIdx.x - g.block0) * RG + rg) * 4 + wave) * kGemv4Rows;
+    if (n0 >= N) break;  // uniform over the wavefront; no barrier follows
+    bf16x8 w[kGemv4Rows][NCH];
 #pragma unroll
-  for (int r = 0; r < kGemv4Rows; ++r) {
-    const int n = n0 + r < N ? n0 + r : N - 1;  // rows past N re-read the last row; dropped below
+    for (int r = 0; r < kGemv4Rows; ++r) {
+      const int n = n0 + r < N ? n0 + r : N - 1;  // rows past N re-read the last row; dropped below
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) w[r][c] = *reinterpret_cast<const bf16x8*>(W + (int64_t)n * K + (lane + 64 * c) * 8);
-  }
-  float acc[kGemv4Rows][BB];
+      for (int c = 0; c < NCH; ++c) w[r][c] = *reinterpret_cast<const bf16x8*>(W + (int64_t)n * K + (lane + 64 * c) * 8);
+    }
+    float acc[kGemv4Rows][BB];
 #pragma unroll
-  for (int r = 0; r < kGemv4Rows; ++r)
+    for (int r = 0; r < kGemv4Rows; ++r)
 #pragma unroll
-    for (int bb = 0; bb < BB; ++bb) acc[r][bb] = 0.f;
+      for (int bb = 0; bb < BB; ++bb) acc[r][bb] = 0.f;
+    // each weight converted once, then multiplied by every batch row (per
+    // (row, batch row) the additions run over c, then i, whatever BB is)
 #pragma unroll
-  for (int bb = 0; bb < BB; ++bb) {
-    {
+    for (int c = 0; c < NCH; ++c) {
+      float xv[BB][8];
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
+      for (int bb = 0; bb < BB; ++bb) {
         const f32x4 x0 = *reinterpret_cast<const f32x4*>(xs + bb * K + (lane + 64 * c) * 8);
         const f32x4 x1 = *reinterpret_cast<const f32x4*>(xs + bb * K + (lane + 64 * c) * 8 + 4);
-        const float xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
 #pragma unroll
-        for (int r = 0; r < kGemv4Rows; ++r)
+        for (int i = 0; i < 4; ++i) {
+          xv[bb][i] = x0[i];
+          xv[bb][4 + i] = x1[i];
+        }
+      }
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[r][bb] += (float)w[r][c][i] * xv[i];
+      for (int r = 0; r < kGemv4Rows; ++r) {
+        float wf[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wf[i] = (float)w[r][c][i];
+#pragma unroll
+        for (int bb = 0; bb < BB; ++bb)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[r][bb] += wf[i] * xv[bb][i];
       }
     }
-  }
-  const bool hi32 = lane & 32, hi16 = lane & 16;
-  const bf16* bias = reinterpret_cast<const bf16*>(g.bias);
+    const bool hi32 = lane & 32, hi16 = lane & 16;
 #pragma unroll
-  for (int bb = 0; bb < BB; ++bb) {
-    // halves: lanes < 32 keep rows 0, 1; lanes >= 32 keep rows 2, 3
-    const float s0 = hi32 ? acc[0][bb] : acc[2][bb];
-    const float s1 = hi32 ? acc[1][bb] : acc[3][bb];
-    const float k0 = hi32 ? acc[2][bb] : acc[0][bb];
-    const float k1 = hi32 ? acc[3][bb] : acc[1][bb];
-    const float u0 = k0 + __shfl_xor(s0, 32);
-    const float u1 = k1 + __shfl_xor(s1, 32);
-    // quarters: lanes with bit 4 clear keep the first row of the pair
-    float v = (hi16 ? u1 : u0) + __shfl_xor(hi16 ? u0 : u1, 16);
+    for (int bb = 0; bb < BB; ++bb) {
+      // halves: lanes < 32 keep rows 0, 1; lanes >= 32 keep rows 2, 3
+      const float s0 = hi32 ? acc[0][bb] : acc[2][bb];
+      const float s1 = hi32 ? acc[1][bb] : acc[3][bb];
+      const float k0 = hi32 ? acc[2][bb] : acc[0][bb];
+      const float k1 = hi32 ? acc[3][bb] : acc[1][bb];
+      const float u0 = k0 + __shfl_xor(s0, 32);
+      const float u1 = k1 + __shfl_xor(s1, 32);
+      // quarters: lanes with bit 4 clear keep the first row of the pair
+      float v = (hi16 ? u1 : u0) + __shfl_xor(hi16 ? u0 : u1, 16);
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    const int n = n0 + 2 * (lane >> 5) + ((lane >> 4) & 1);
-    if ((lane & 15) == 0 && n < N) g.y[(int64_t)bb * g.y_bstride + n] = v + (bias ? (float)bias[n] : 0.f);
+      for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+      const int n = n0 + 2 * (lane >> 5) + ((lane >> 4) & 1);
+      if ((lane & 15) == 0 && n < N) g.y[(int64_t)bb * g.y_bstride + n] = v + (bias ? (float)bias[n] : 0.f);
+    }
   }
 }
 
@@ -841,7 +861,7 @@ hipError_t launch_gemv_multi(const GemvMultiArgs& a0, bool w_bf16, hipStream_t s
   GemvMultiArgs a = a0;
   int blocks = 0;
   if (w_bf16 && a.K % 512 == 0 && a.K <= 4096 && a.B >= 1 && a.B <= kGemvMaxB) {
-    const int rows_per_block = 4 * kGemv4Rows;
+    const int rows_per_block = 4 * kGemv4Rows * (a.B > 1 ? gemv4_groups<2>() : gemv4_groups<1>());
     for (int i = 0; i < a.nseg; ++i) {
       a.seg[i].block0 = blocks;
       blocks += (a.seg[i].N + rows_per_block - 1) / rows_per_block;

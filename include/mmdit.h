@@ -289,6 +289,15 @@ typedef struct {
   double cache_threshold;
   int32_t dequant;
   int32_t cache_on_device; /* 0 or 1, see step caching above */
+  /* Modulation vectors computed beforehand by mmdit_step_modulations (device,
+   * 16-byte aligned), or NULL to compute them in the step. mods_count: the
+   * n_sigma of that call; mods_index: which of its timesteps this step is
+   * (its sigma must be the one the step is called with; the library cannot
+   * check that). With mods set the step neither reads y nor needs a
+   * guidance value. */
+  const void* mods;
+  int32_t mods_count;
+  int32_t mods_index;
 } mmdit_step_opts;
 
 /* One denoising step with options (context tokens, guidance). Arguments as
@@ -297,8 +306,9 @@ typedef struct {
  * text, generated, then context rows. The workspace is
  * mmdit_step_workspace(cfg). Errors as for mmdit_step; MMDIT_ERR_SHAPE for
  * ctx_len out of range, a non-finite guidance, a negative or NaN
- * cache_threshold, caching without a dual block, or dequant or
- * cache_on_device not 0 or 1;
+ * cache_threshold, caching without a dual block, dequant or
+ * cache_on_device not 0 or 1, mods_index outside [0, mods_count) or mods
+ * misaligned;
  * MMDIT_ERR_NULL for a NULL
  * ctx_packed with ctx_len > 0, a NULL cache->buf, or a guidance model called
  * without a guidance value (mmdit_step on such a model fails the same way);
@@ -307,6 +317,32 @@ int mmdit_step_ex(const mmdit_config* cfg, const mmdit_model_w* w,
                   void* x_packed, void* v_out, const void* txt_emb, const void* y,
                   const int32_t* ids, double sigma, double sigma_next, const mmdit_step_opts* opts,
                   void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Host. Bytes of the buffer mmdit_step_modulations fills for n_sigma
+ * timesteps: n_sigma * batch * hidden * (12 n_double + 3 n_single + 2)
+ * floats of modulation vectors plus scratch for the conditioning vectors.
+ * Errors: MMDIT_ERR_NULL, config errors, MMDIT_ERR_SHAPE when n_sigma is
+ * below 1 or n_sigma * batch exceeds 4. */
+int mmdit_step_modulations_bytes(const mmdit_config* cfg, int32_t n_sigma, size_t* bytes);
+
+/* Device, async. The conditioning vectors and every modulation vector of the
+ * step (each block's adaLN shift / scale / gate chunks and the final layer's)
+ * for the n_sigma timesteps sigmas[0 .. n_sigma) (host array) at once: each
+ * modulation weight matrix is read once for all of them instead of once per
+ * step (these weights are 6.5 GB at h 3072, the step's largest HBM stream;
+ * they depend on the step only through the conditioning vector, mflux-rs
+ * page, Dual-Stream MMDiT and Single-Stream Blocks cards). y [B, vec_in_dim]
+ * as for mmdit_step; opts: only has_guidance / guidance are read (required
+ * when the model has a guidance embedder). mods: device buffer of
+ * mmdit_step_modulations_bytes(cfg, n_sigma) bytes, 16-byte aligned, passed
+ * to the steps as opts->mods with mods_count = n_sigma and mods_index = j for
+ * the step at sigmas[j]. The results are bit for bit those a step computes
+ * for itself. Errors: MMDIT_ERR_NULL, MMDIT_ERR_SHAPE (n_sigma, alignment,
+ * non-finite sigma or guidance), MMDIT_ERR_WORKSPACE (mods_bytes too small),
+ * MMDIT_ERR_DTYPE, MMDIT_ERR_HIP; nothing is launched on an argument error. */
+int mmdit_step_modulations(const mmdit_config* cfg, const mmdit_model_w* w, const void* y, const double* sigmas,
+                           int32_t n_sigma, const mmdit_step_opts* opts, void* mods, size_t mods_bytes,
+                           void* hip_stream);
 
 /* Host. The workspace mmdit_step_ex needs for these weights and options
  * (opts may be NULL): without room for decoded weights when no layer is

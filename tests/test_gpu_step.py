@@ -441,3 +441,53 @@ def test_step_quantised_final_layer(bits):
                          s.heads, s.axes_dim, s.theta)
     assert_parity(down(v), vr, "bf16", f"{bits}-bit final layer: v")
     assert_parity(down(X), Xr, "bf16", f"{bits}-bit final layer: x_next")
+
+
+# ------------------------------------------- modulations of several steps ---
+def check_shared_modulations(s: I.Shape, n_sigma: int, guidance=None):
+    """Every step of a schedule run with the modulation vectors that
+    mmdit_step_modulations computed for n_sigma timesteps in one pass gives
+    the plain step's x and v bit for bit (the same GEMVs per row), and the
+    plain step matches the oracle."""
+    t = torch()
+    g, dbl, sgl = model_numpy(s)
+    if guidance is not None:
+        g = dict(g, **I.guidance_weights(s))
+    inp = I.step_inputs(s)
+    ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
+    sig = oracle.schedule(n_sigma, s.img_len)
+    dt = dtype_code(s.dtype)
+    cfg = bd.make_config(s)
+    M = bd.ModelW(g, [bd.DoubleW(d, dt, "cuda") for d in dbl], [bd.SingleW(w, dt, "cuda") for w in sgl], dt, "cuda")
+    mc = M.c()
+    z = t.from_numpy(inp["z"]).cuda()
+    X0 = t.empty((s.batch, s.img_len, s.in_ch), dtype=t.float32, device="cuda")
+    bd.mmdit_pack_latents(z, X0)
+    T, y, ids_d = up(inp["T"], s.dtype), up(inp["y"], s.dtype), up_i32(ids)
+    ws = workspace(bd.mmdit_step_workspace(cfg))
+    mods = t.empty(bd.mmdit_step_modulations_bytes(cfg, n_sigma), dtype=t.uint8, device="cuda")
+    print(f"modulations of {n_sigma} steps, B={s.batch} h={s.hidden} {s.dtype} guidance={guidance}", flush=True)
+    bd.mmdit_step_modulations(cfg, mc, y, sig[:n_sigma], mods, guidance=guidance)
+    Xp, Xs = X0.clone(), X0.clone()
+    vp, vs = t.empty_like(X0), t.empty_like(X0)
+    for j in range(n_sigma):
+        bd.mmdit_step_ex(cfg, mc, Xp, vp, T, y, ids_d, sig[j], sig[j + 1], ws, guidance=guidance)
+        # the shared-modulation step reads neither y nor the guidance value
+        bd.mmdit_step_ex(cfg, mc, Xs, vs, T, None, ids_d, sig[j], sig[j + 1], ws, mods=mods, mods_count=n_sigma,
+                         mods_index=j)
+        sync()
+        assert np.array_equal(down(vp), down(vs)), f"step {j}: v differs"
+        assert np.array_equal(down(Xp), down(Xs)), f"step {j}: x differs"
+        if j == 0:
+            Xr, vr = oracle.step(g, dbl, sgl, oracle.pack_latents(inp["z"]), inp["T"], inp["y"], ids, sig[0], sig[1],
+                                 s.heads, s.axes_dim, s.theta, guidance=guidance)
+            assert_parity(down(vs), vr, s.dtype, "first step with shared modulations: v")
+
+
+def test_shared_modulations_f32_batch2():
+    check_shared_modulations(dataclasses.replace(TINY_F32, batch=2, txt_len=11, grid_h=6, grid_w=5, cfg_id=62), 2)
+
+
+def test_shared_modulations_bf16_guided_four_steps():
+    s = dataclasses.replace(I.CFG4, n_double=2, n_single=2, txt_len=64, grid_h=16, grid_w=16, cfg_id=63)
+    check_shared_modulations(s, 4, guidance=3.5)

@@ -382,3 +382,36 @@ def test_adaln_layernorm_errors_before_launch(lib):
     assert lib.mmdit_adaln_layernorm(dummy, 1, dummy, 5, 10, 256, dummy, C.c_float(1e-6), None) == 3
     assert lib.mmdit_adaln_layernorm(None, 1, dummy, bd.BF16, 10, 256, dummy, C.c_float(1e-6), None) == 1
     assert lib.mmdit_adaln_layernorm(None, 1, None, bd.BF16, 0, 256, None, C.c_float(1e-6), None) == 0
+
+
+def test_step_modulations_errors_before_launch(lib):
+    # argument errors return before any device work (dummy pointers unused)
+    s = I.Shape(hidden=256, heads=2, mlp_hidden=512, txt_len=16, grid_h=8, grid_w=8, dtype="f32", cfg_id=64,
+                n_double=1, n_single=1, txt_in_dim=256, vec_in_dim=256)
+    cfg = bd.make_config(s)
+    n = C.c_size_t()
+    assert lib.mmdit_step_modulations_bytes(C.byref(cfg), 0, C.byref(n)) == 2
+    assert lib.mmdit_step_modulations_bytes(C.byref(cfg), 5, C.byref(n)) == 2          # at most 4 rows
+    assert lib.mmdit_step_modulations_bytes(C.byref(cfg), 4, C.byref(n)) == 0
+    # 4 timesteps of (12 + 3 + 2) h floats each, plus the conditioning scratch
+    assert n.value >= 4 * 17 * 256 * 4
+    cfg2 = bd.make_config(dataclasses.replace(s, batch=2))
+    assert lib.mmdit_step_modulations_bytes(C.byref(cfg2), 3, C.byref(n)) == 2         # 3 x 2 rows
+    need = bd.mmdit_step_modulations_bytes(cfg, 2)
+    w = bd.mmdit_model_w()
+    fake = 0x6000
+    sg = (C.c_double * 2)(1.0, 0.5)
+    call = lambda mods, nbytes, sig=sg, y=fake: lib.mmdit_step_modulations(  # noqa: E731
+        C.byref(cfg), C.byref(w), y, sig, 2, None, mods, nbytes, None)
+    assert call(fake, need, y=None) == 1                                                # NULL y
+    assert call(None, need) == 1                                                        # NULL buffer
+    assert call(fake + 8, need) == 2                                                    # misaligned buffer
+    assert call(fake, need - 1) == 4                                                    # buffer too small
+    assert call(fake, need, sig=(C.c_double * 2)(1.0, float("nan"))) == 2              # non-finite sigma
+    # a step given modulations checks which timestep it is
+    o = bd.mmdit_step_opts(mods=fake, mods_count=2, mods_index=2)
+    assert lib.mmdit_step_ex(C.byref(cfg), C.byref(w), fake, None, fake, None, fake, 1.0, 0.5, C.byref(o), fake,
+                             1 << 40, None) == 2
+    o = bd.mmdit_step_opts(mods=fake + 4, mods_count=2, mods_index=1)
+    assert lib.mmdit_step_ex(C.byref(cfg), C.byref(w), fake, None, fake, None, fake, 1.0, 0.5, C.byref(o), fake,
+                             1 << 40, None) == 2
