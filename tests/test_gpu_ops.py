@@ -118,3 +118,32 @@ def test_adaln_layernorm(h, x_f32):
     sync()
     ref = oracle.modulate(x, mod[0][None, :], mod[1][None, :])
     assert_parity(down(y), ref, "bf16", f"adaLN LayerNorm h {h} x_f32 {x_f32}")
+
+
+@pytest.mark.parametrize("fmt", list(BITS))
+@pytest.mark.parametrize("shape", [(3072, 15360), (21504, 3072)], ids=["linear2", "linear1"])
+def test_linear_weight_streaming_model_shapes(fmt, shape):
+    # the weight-streaming route at the model's own layer shapes (N, K):
+    # single-block linear2 (3072 x 15360, 15 k blocks per wavefront) and
+    # linear1 (21504 x 3072, 3 per wavefront), one row and 16 rows
+    t = torch()
+    n, k = shape
+    w = I.round_bf16(I.normal((n, k), (84, n, k), std=0.02))
+    b = I.round_bf16(I.normal((n,), (84, n, 1), std=0.02))
+    bits = BITS[fmt]
+    lin = bd.Linear.from_numpy(w, b, bd.BF16, "cuda", bits)
+    if bits in (4, 8):
+        q, sc = oracle.quantise(w, bits)
+        wo = oracle.dequantise(q, sc)
+    elif bits in (1, 2):
+        c, sc = oracle.quantise_g128(w, bits)
+        wo = oracle.dequantise_g128(c, sc, bits)
+    else:
+        wo = w
+    for M in (1, 16):
+        x = I.round_bf16(I.normal((M, k), (85, n, M)))
+        y = t.empty((M, n), dtype=t.float32, device="cuda")
+        print(f"linear stream {fmt} {n}x{k} M={M}", flush=True)
+        bd.mmdit_linear_fwd(lin, up(x, "bf16"), y, route=bd.ROUTE_STREAM)
+        sync()
+        assert_parity(down(y), oracle.linear(x, wo, b), "bf16", f"stream {fmt} {n}x{k} M={M}")
