@@ -771,7 +771,16 @@ __global__ __launch_bounds__(256) void k_gemv_multi4(GemvMultiArgs a) {
   const bf16* bias = reinterpret_cast<const bf16*>(g.bias);
   // x first: requesting the weights ahead of the staging barrier measured
   // slower (4.1 against 6.0 TB/s on 24 x 18432 x 3072)
-  gemv_stage_x<float>(xs, a.x, BB, K, a.x_bstride, true);
+  // SiLU(x) staged as two halves per batch row: floats 0..3 of every
+  // 8-float chunk, then floats 4..7, so that a lane's two 16-byte reads of
+  // its chunk lane + 64 c are 16 bytes apart from its neighbours' (one
+  // 32-byte read per lane would put 8 lanes on each bank)
+  for (int i = threadIdx.x; i < BB * K; i += 256) {
+    const int bb = i / K, k = i - bb * K;
+    const float v = silu_f<true>(reinterpret_cast<const float*>(a.x)[(int64_t)bb * a.x_bstride + k]);
+    xs[bb * K + ((k >> 2) & 1) * (K / 2) + (k >> 3) * 4 + (k & 3)] = v;
+  }
+  __syncthreads();
   constexpr int RG = gemv4_groups<BB>();
   for (int rg = 0; rg < RG; ++rg) {
     const int n0 = ((((int)blockIdx.x - g.block0) * RG + rg) * 4 + wave) * kGemv4Rows;
@@ -795,8 +804,8 @@ __global__ __launch_bounds__(256) void k_gemv_multi4(GemvMultiArgs a) {
       float xv[BB][8];
 #pragma unroll
       for (int bb = 0; bb < BB; ++bb) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(xs + bb * K + (lane + 64 * c) * 8);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(xs + bb * K + (lane + 64 * c) * 8 + 4);
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(xs + bb * K + (lane + 64 * c) * 4);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(xs + bb * K + K / 2 + (lane + 64 * c) * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           xv[bb][i] = x0[i];
