@@ -491,3 +491,62 @@ def test_shared_modulations_f32_batch2():
 def test_shared_modulations_bf16_guided_four_steps():
     s = dataclasses.replace(I.CFG4, n_double=2, n_single=2, txt_len=64, grid_h=16, grid_w=16, cfg_id=63)
     check_shared_modulations(s, 4, guidance=3.5)
+
+
+def test_shared_modulations_with_context_and_device_cache():
+    # the options together: reference-image tokens, shared modulation
+    # vectors, and the step cache decided on the device; every step equals
+    # the plain cached step (modulations computed in the step, decision on
+    # the host) bit for bit, decisions included
+    t = torch()
+    s = dataclasses.replace(I.CFG4, n_double=1, n_single=1, txt_len=64, grid_h=12, grid_w=12, cfg_id=65)
+    cgh = cgw = 12
+    g, dbl, sgl = model_numpy(s)
+    inp = I.step_inputs(s)
+    Lc = cgh * cgw
+    Xc = np.random.default_rng(3000).standard_normal((s.batch, Lc, s.in_ch)).astype(np.float32)
+    ids = ctx_ids(s, cgh, cgw)
+    n = 4
+    sig = oracle.schedule(n, s.img_len)
+    dt = dtype_code(s.dtype)
+    cfg = bd.make_config(s)
+    cfg.dims.img_len = s.img_len + Lc
+    M = bd.ModelW(g, [bd.DoubleW(d, dt, "cuda") for d in dbl], [bd.SingleW(w, dt, "cuda") for w in sgl], dt, "cuda")
+    mc = M.c()
+    X0 = t.empty((s.batch, s.img_len, s.in_ch), dtype=t.float32, device="cuda")
+    bd.mmdit_pack_latents(t.from_numpy(inp["z"]).cuda(), X0)
+    T, y, ids_d = up(inp["T"], s.dtype), up(inp["y"], s.dtype), up_i32(ids)
+    xc = t.from_numpy(Xc).cuda()
+    ws = workspace(bd.mmdit_step_workspace(cfg))
+    mods = t.empty(bd.mmdit_step_modulations_bytes(cfg, n), dtype=t.uint8, device="cuda")
+    bd.mmdit_step_modulations(cfg, mc, y, sig[:n], mods)
+    # threshold between the second step's change and the sum of the second
+    # and third (read from a pass that never reruns the blocks), so the
+    # second step reuses the residual and the third runs the blocks
+    probe = bd.StepCache(cfg)
+    Xp, vp = X0.clone(), t.empty_like(X0)
+    rel = []
+    for j in range(3):
+        bd.mmdit_step_ex(cfg, mc, Xp, vp, T, y, ids_d, sig[j], sig[j + 1], ws, ctx_packed=xc, ctx_len=Lc,
+                         cache=probe, cache_threshold=float("inf"))
+        sync()
+        rel.append(probe.rel)
+    thr = rel[1] + 0.5 * rel[2]
+    ch, cd = bd.StepCache(cfg), bd.StepCache(cfg, on_device=True)
+    Xh, Xd = X0.clone(), X0.clone()
+    vh, vd = t.empty_like(X0), t.empty_like(X0)
+    runs = []
+    for j in range(n):
+        print(f"step {j}: plain host-cached step against shared modulations + device cache", flush=True)
+        bd.mmdit_step_ex(cfg, mc, Xh, vh, T, y, ids_d, sig[j], sig[j + 1], ws, ctx_packed=xc, ctx_len=Lc,
+                         cache=ch, cache_threshold=thr)
+        bd.mmdit_step_ex(cfg, mc, Xd, vd, T, None, ids_d, sig[j], sig[j + 1], ws, ctx_packed=xc, ctx_len=Lc,
+                         cache=cd, cache_threshold=thr, mods=mods, mods_count=n, mods_index=j)
+        sync()
+        cd.read()
+        assert cd.ran_blocks == ch.ran_blocks, (j, cd.ran_blocks, ch.ran_blocks)
+        runs.append(ch.ran_blocks)
+        assert np.array_equal(down(vh), down(vd)), f"step {j}: v differs"
+        assert np.array_equal(down(Xh), down(Xd)), f"step {j}: x differs"
+    print(f"blocks ran at steps: {runs}", flush=True)
+    assert runs[:3] == [True, False, True], runs
