@@ -182,8 +182,12 @@ int check_single(const mmdit_single_w& s, const Geo& g) {
 //   o   [rows, h] (dual) or cat [rows, h + m] (single), mlp [rows, m] (dual).
 //   attn  partial results of key-split attention units (bf16 path).
 //   xw  bf16 weights decoded from a quantised layer (only when expanding).
+// Laid out as o, xn, qkv, Q, K, V, mlp, attn, xw, so that the float32
+// partial sums of a split-K gated-residual GEMM fit in scratch that is dead
+// during it: [xn, mlp end) when the GEMM reads o (out-projection, linear2),
+// [o, V end) when it reads mlp (fc2).
 struct BlockWs {
-  size_t xn, qkv, q, k, v, o, mlp, attn, xw, xw_bytes, total;
+  size_t o, xn, qkv, q, k, v, mlp, attn, xw, xw_bytes, total;
 };
 
 // Quantised layers of launches with at least this many rows are decoded into
@@ -213,12 +217,12 @@ BlockWs plan_block(const Geo& g, size_t base, size_t xw_bytes) {
   const size_t rows = (size_t)g.B * g.L;
   const size_t qkvh = (size_t)g.B * g.H * g.Lpad * 128;
   size_t at = base;
+  w.o = at; at = align_up(at + rows * (size_t)(g.h + g.m) * g.esz);
   w.xn = at; at = align_up(at + rows * g.h * g.esz);
   w.qkv = at; at = align_up(at + rows * 3 * g.h * g.esz);
   w.q = at; at = align_up(at + qkvh * g.esz);
   w.k = at; at = align_up(at + qkvh * g.esz);
   w.v = at; at = align_up(at + qkvh * g.esz);
-  w.o = at; at = align_up(at + rows * (size_t)(g.h + g.m) * g.esz);
   w.mlp = at; at = align_up(at + rows * g.m * g.esz);
   w.attn = at; at = align_up(at + (g.bf16 ? kAttnPartBytes : 0));
   w.xw = at; w.xw_bytes = xw_bytes; at = align_up(at + xw_bytes);
@@ -314,6 +318,10 @@ struct Ctx {
   float ln_eps, rms_eps;
   void* xw = nullptr;  // decoded-weight scratch (null: quantised layers stay fused)
   size_t xw_bytes = 0;
+  // dead scratch for split-K partial sums of the next gated-residual launch
+  // (null: it runs whole)
+  float* part = nullptr;
+  size_t part_bytes = 0;
   // step-cache guard passed to every launch (null: unguarded): the launches
   // do nothing when the device-side cache decision reuses the residual
   const int* skip = nullptr;
@@ -366,8 +374,19 @@ int gemm(const Ctx& c, GemmProblem* p, int np, int epi) {
                : epi == EPI_QKV                        ? PC_GEMM_QKV
                : epi == EPI_GELU                       ? PC_GEMM_FC1
                                                        : -1);
-  if (!c.g.bf16) HIP_TRY(launch_gemm_f32(p, np, epi, c.s));
-  else if (gemm_dma_eligible(p, np, epi)) HIP_TRY(launch_gemm_dma(p, np, epi, c.s));
+  if (!c.g.bf16) {
+    HIP_TRY(launch_gemm_f32(p, np, epi, c.s));
+    return MMDIT_OK;
+  }
+  if (gemm_dma_eligible(p, np, epi)) {
+    HIP_TRY(launch_gemm_dma(p, np, epi, c.s));
+    return MMDIT_OK;
+  }
+  int ways = c.part && (uintptr_t)c.part % 16 == 0 ? gemm_splitk_ways(p, np, epi) : 1;
+  size_t mn = 0;
+  for (int i = 0; i < np; ++i) mn += (size_t)p[i].M * p[i].N;
+  while (ways > 1 && (size_t)ways * mn * 4 > c.part_bytes) --ways;
+  if (ways > 1) HIP_TRY(launch_gemm_dma_splitk(p, np, epi, ways, c.part, c.s));
   else HIP_TRY(launch_gemm_bf16(p, np, epi, c.s));
   return MMDIT_OK;
 }
@@ -382,6 +401,29 @@ int gemv(const Ctx& c, const mmdit_linear& l, const void* x, bool x_f32, int x_b
   a.skip = c.skip;
   ProfScope ps(PC_GEMV, (double)l.n_out * l.k_in * c.g.esz, c.s);
   HIP_TRY(launch_gemv(a, c.g.bf16, x_f32 || !c.g.bf16, c.s));
+  return MMDIT_OK;
+}
+
+// The modulation GEMVs of one block call, SiLU(vec) times each matrix: one
+// launch over all matrices when the batch fits one pass of the multi-GEMV.
+int mod_gemvs(const Ctx& c, const mmdit_linear* const* l, float* const* y, int n, const void* vec) {
+  const Geo& g = c.g;
+  if (g.B > kGemvMaxB) {
+    for (int i = 0; i < n; ++i)
+      if (int r = gemv(c, *l[i], vec, false, g.h, y[i], l[i]->n_out, true, false)) return r;
+    return MMDIT_OK;
+  }
+  GemvMultiArgs ga{};
+  ga.x = vec; ga.K = g.h; ga.B = g.B; ga.x_bstride = g.h; ga.x_bf16 = g.bf16;
+  ga.skip = c.skip;
+  double bytes = 0;
+  for (int i = 0; i < n; ++i) {
+    GemvSeg& sg = ga.seg[ga.nseg++];
+    sg.W = l[i]->w; sg.bias = l[i]->bias; sg.y = y[i]; sg.N = l[i]->n_out; sg.y_bstride = l[i]->n_out;
+    bytes += (double)l[i]->n_out * l[i]->k_in * g.esz;
+  }
+  ProfScope ps(PC_GEMV, bytes, c.s);
+  HIP_TRY(launch_gemv_multi(ga, g.bf16, c.s));
   return MMDIT_OK;
 }
 
@@ -497,6 +539,17 @@ GemmProblem base_problem(const mmdit_linear& l) {
   return p;
 }
 
+// The context of a gated-residual launch whose split-K partial sums may use
+// the dead block scratch [from, to) (bf16 path).
+Ctx with_part(const Ctx& c, void* ws, size_t from, size_t to) {
+  Ctx r = c;
+  if (c.g.bf16 && to > from) {
+    r.part = (float*)ptr(ws, from);
+    r.part_bytes = to - from;
+  }
+  return r;
+}
+
 // Dual-stream block; parts[0] text, parts[1] image; sw[p] the stream weights.
 int run_double(const Ctx& c, const mmdit_stream_w* const sw[2], const Part* parts, bool res_f32,
                const float* table, void* ws, const BlockWs& w) {
@@ -533,7 +586,7 @@ int run_double(const Ctx& c, const mmdit_stream_w* const sw[2], const Part* part
     gp[p].res_in = parts[p].x_in; gp[p].res_out = parts[p].x_out; gp[p].res_f32 = res_f32;
     gp[p].gate = parts[p].mod + 2 * h; gp[p].gate_bstride = 6 * h;
   }
-  if ((r = gemm(c, gp, 2, EPI_GATE_RES))) return r;
+  if ((r = gemm(with_part(c, ws, w.xn, w.attn), gp, 2, EPI_GATE_RES))) return r;
   // adaLN LayerNorm 2 on the updated residual
   Part p2[2] = {parts[0], parts[1]};
   for (int p = 0; p < 2; ++p) p2[p].x_in = parts[p].x_out;
@@ -554,7 +607,7 @@ int run_double(const Ctx& c, const mmdit_stream_w* const sw[2], const Part* part
     gp[p].res_in = parts[p].x_out; gp[p].res_out = parts[p].x_out; gp[p].res_f32 = res_f32;
     gp[p].gate = parts[p].mod + 5 * h; gp[p].gate_bstride = 6 * h;
   }
-  return gemm(c, gp, 2, EPI_GATE_RES);
+  return gemm(with_part(c, ws, w.o, w.mlp), gp, 2, EPI_GATE_RES);
 }
 
 // Single-stream block over np parts sharing the weights.
@@ -589,7 +642,7 @@ int run_single(const Ctx& c, const mmdit_single_w& sw, const Part* parts, int np
     gp[p].res_in = parts[p].x_in; gp[p].res_out = parts[p].x_out; gp[p].res_f32 = res_f32;
     gp[p].gate = parts[p].mod + 2 * h; gp[p].gate_bstride = 3 * h;
   }
-  return gemm(c, gp, np, EPI_GATE_RES);
+  return gemm(with_part(c, ws, w.xn, w.attn), gp, np, EPI_GATE_RES);
 }
 
 int rope(const Ctx& c, const mmdit_dims* d, const int32_t* ids, float* table) {
@@ -642,8 +695,11 @@ int mmdit_double_block_fwd(const mmdit_dims* dims, const mmdit_double_w* w, cons
   float* mod_txt = mod;
   float* mod_img = mod + (size_t)g.B * 6 * g.h;
   if ((r = rope(c, dims, ids, table))) return r;
-  if ((r = gemv(c, w->txt.mod, vec, false, g.h, mod_txt, 6 * g.h, true, false))) return r;
-  if ((r = gemv(c, w->img.mod, vec, false, g.h, mod_img, 6 * g.h, true, false))) return r;
+  {
+    const mmdit_linear* ml[2] = {&w->txt.mod, &w->img.mod};
+    float* const my[2] = {mod_txt, mod_img};
+    if ((r = mod_gemvs(c, ml, my, 2, vec))) return r;
+  }
   Part parts[2];
   void* tin = const_cast<void*>(txt_in ? txt_in : img_in);
   void* tout = txt_out ? txt_out : img_out;
@@ -673,7 +729,11 @@ int mmdit_single_block_fwd(const mmdit_dims* dims, const mmdit_single_w* w, cons
   float* table = (float*)ptr(ws, lay.table);
   float* mod = (float*)ptr(ws, lay.mod);
   if ((r = rope(c, dims, ids, table))) return r;
-  if ((r = gemv(c, w->mod, vec, false, g.h, mod, 3 * g.h, true, false))) return r;
+  {
+    const mmdit_linear* ml[1] = {&w->mod};
+    float* const my[1] = {mod};
+    if ((r = mod_gemvs(c, ml, my, 1, vec))) return r;
+  }
   const bool rf = g.resid == MMDIT_RESID_F32;
   const int re = rf ? 4 : g.esz;
   Part part = {g.L, 0, rows_of(const_cast<void*>(x_in), 0, g.L, g.h, re), rows_of(x_out, 0, g.L, g.h, re), mod};

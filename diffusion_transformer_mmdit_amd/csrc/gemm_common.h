@@ -10,6 +10,7 @@ struct GemmBatch {
   GemmProblem p[2];
   int32_t tiles_m[2], tiles_n[2];
   int32_t tile_start[3];
+  int32_t ksplit = 1;  // k-ranges per tile (direct-to-LDS split-K)
 };
 
 template <typename TA>

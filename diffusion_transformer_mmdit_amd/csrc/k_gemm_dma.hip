@@ -58,6 +58,18 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Work unit of this workgroup: tile (prob, tm, tn) and k-range ks. Units are
+// numbered k-range first (unit = ks * tiles + tile), so after the XCD remap
+// of tile_of the units of one XCD share a k-range and neighbouring tiles.
+__device__ __forceinline__ void unit_of(const GemmBatch& gb, int& prob, int& tm, int& tn, int& ks) {
+  const int nb = gridDim.x;
+  int bid = blockIdx.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int tiles = gb.tile_start[2];
+  ks = bid / tiles;
+  tile_coords(gb, bid - ks * tiles, prob, tm, tn);
+}
+
 // Chunk order inside an LDS row of BK bf16 (16-byte chunks): chunk c of row r
 // sits at position c ^ swz(r). Chosen so the 16-byte fragment reads of
 // consecutive rows (same c) hit distinct banks for 32 and for 64 banks.
@@ -111,7 +123,8 @@ typedef __attribute__((address_space(1))) bf16x8 gbf16x8;
 // output); for the gated residual, the residual is float32.
 template <int EPI, int TN, bool FULL, bool ALT>
 __device__ __forceinline__ void dma_epilogue_impl(const GemmProblem& P, float* stg, int m0w, int n0w, int lane,
-                                                  const f32x16 (&acc)[4][TN / 32], const float (&bias)[4]) {
+                                                  const f32x16 (&acc)[4][TN / 32], const float (&bias)[4],
+                                                  int ks) {
   constexpr int NJF = TN / 32;          // 32-column blocks of the wavefront tile
   constexpr int LPR = TN / 4;           // lanes per row in the read-back phase
   constexpr int RPI = 64 / LPR;         // rows per read-back instruction
@@ -154,6 +167,11 @@ __device__ __forceinline__ void dma_epilogue_impl(const GemmProblem& P, float* s
     }
     ld = ld_o * esz;
     ldi = ld_i * esz;
+  } else if constexpr (EPI == EPI_PARTIAL) {
+    // float32 rows of k-range ks: part[ks][m][n], row stride N
+    obase = (gchar*)pin(reinterpret_cast<char*>(P.part));
+    ld = (int64_t)N * 4;
+    obase += ((int64_t)ks * M * N + (int64_t)m0w * N + n) * 4;
   } else {
     obase = (gchar*)pin(reinterpret_cast<char*>(to2 ? P.out2 : P.out));
     ld = pin(to2 ? P.ldo2 : P.ldo) * 2;
@@ -229,6 +247,10 @@ __device__ __forceinline__ void dma_epilogue_impl(const GemmProblem& P, float* s
         for (int t = 0; t < GR; ++t) {
           const int r = 32 * i + RPI * (GR * h + t) + rs;
           if (!FULL && (m0w + r >= M || !n_ok)) continue;
+          if constexpr (EPI == EPI_PARTIAL) {
+            *(gf32x4*)(obase + r * ld) = a[t];
+            continue;
+          }
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = a[t][e] + bias[e];
@@ -255,7 +277,8 @@ __device__ __forceinline__ void dma_epilogue_impl(const GemmProblem& P, float* s
 // Column counts and row strides are multiples of 4 (checked before launch):
 // a lane's 4 columns are all in range or all out of range. `bias` holds the
 // lane's 4 columns' bias (loaded by the caller ahead of time). Outputs are
-// bf16 (plain) or bf16 / float32 (gated residual).
+// bf16 (plain) or bf16 / float32 (gated residual), or the float32 partial
+// sums of k-range `side` (EPI_PARTIAL, no bias).
 template <int EPI, int TN>
 __device__ __forceinline__ void dma_epilogue(const GemmProblem& P, char* smem, int m0w, int n0w, int wave,
                                              int lane, const f32x16 (&acc)[4][TN / 32], int side,
@@ -270,11 +293,11 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& P, char* smem, i
   if constexpr (EPI == EPI_SPLIT) alt = side == 1;
   if constexpr (EPI == EPI_GATE_RES) alt = P.res_f32;
   if (full) {
-    if (alt) dma_epilogue_impl<EPI, TN, true, true>(P, stg, m0w, n0w, lane, acc, bias);
-    else dma_epilogue_impl<EPI, TN, true, false>(P, stg, m0w, n0w, lane, acc, bias);
+    if (alt) dma_epilogue_impl<EPI, TN, true, true>(P, stg, m0w, n0w, lane, acc, bias, side);
+    else dma_epilogue_impl<EPI, TN, true, false>(P, stg, m0w, n0w, lane, acc, bias, side);
   } else {
-    if (alt) dma_epilogue_impl<EPI, TN, false, true>(P, stg, m0w, n0w, lane, acc, bias);
-    else dma_epilogue_impl<EPI, TN, false, false>(P, stg, m0w, n0w, lane, acc, bias);
+    if (alt) dma_epilogue_impl<EPI, TN, false, true>(P, stg, m0w, n0w, lane, acc, bias, side);
+    else dma_epilogue_impl<EPI, TN, false, false>(P, stg, m0w, n0w, lane, acc, bias, side);
   }
 }
 
@@ -460,9 +483,10 @@ __global__ __launch_bounds__(64 * W, 1) void k_gemm_dma(GemmBatch gb) {
   static_assert(FMT == 0 || BK == 64, "quantised weights need 64-wide k-tiles (one scale group)");
   static_assert(!SUB || PCS >= 1, "one sub-byte piece per thread at least");
   static_assert(S * STAGE >= W * 32 * (TN + 4) * 4, "epilogue staging must fit in the operand stages");
+  static_assert(EPI != EPI_PARTIAL || FMT == 0, "split-K runs on dense weights");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  int prob, tm, tn;
-  tile_of(gb, prob, tm, tn);
+  int prob, tm, tn, ks;
+  unit_of(gb, prob, tm, tn, ks);
   const GemmProblem& P = gb.p[prob];
   const int M = P.M, N = P.N, K = P.K;
   const int m0 = tm * kDBM, n0 = tn * kDBN;
@@ -478,6 +502,15 @@ __global__ __launch_bounds__(64 * W, 1) void k_gemm_dma(GemmBatch gb) {
   // (w*NJ + j)*64 + i of the tile.
   const char* abase = reinterpret_cast<const char*>(P.A);
   const char* bbase = reinterpret_cast<const char*>(P.W);
+  // k-tiles of this unit: all of them, or range ks of ksplit near-equal ranges
+  int nk = K / BK;
+  if constexpr (EPI == EPI_PARTIAL) {
+    const int nsplit = gb.ksplit;
+    const int k0t = ks * nk / nsplit;
+    nk = (ks + 1) * nk / nsplit - k0t;
+    abase += (size_t)k0t * BK * 2;
+    bbase += (size_t)k0t * BK * 2;
+  }
   uint32_t aoffg[NJ], boffg[FMT == 0 ? NJ : 1];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -631,7 +664,7 @@ __global__ __launch_bounds__(64 * W, 1) void k_gemm_dma(GemmBatch gb) {
   // bias of this lane's epilogue columns (requested now, used at the end)
   float ebias[4] = {0.f, 0.f, 0.f, 0.f};
   {
-    const bf16* bp = reinterpret_cast<const bf16*>(P.bias);
+    const bf16* bp = EPI == EPI_PARTIAL ? nullptr : reinterpret_cast<const bf16*>(P.bias);
     const int n = n0 + wn0 + 4 * (lane % (TN / 4));
     if (bp && n < N) {
       const bf16x4 v = *reinterpret_cast<const bf16x4*>(bp + n);
@@ -640,7 +673,6 @@ __global__ __launch_bounds__(64 * W, 1) void k_gemm_dma(GemmBatch gb) {
     }
   }
 
-  const int nk = K / BK;
   constexpr int DSP = FMT == 0 ? DS : 1;
   constexpr int PER = (G + DSP - 1) / DSP;  // requests per substep
   // Dense operands, 2 stages: the loop issues every request unconditionally
@@ -775,7 +807,7 @@ __global__ __launch_bounds__(64 * W, 1) void k_gemm_dma(GemmBatch gb) {
       dma_epilogue<EPI_SPLIT, TN>(P, smem, m0 + wm0, n0 + wn0, wave, lane, acc, split_side_of(P, n0, kDBN), ebias);
     }
   } else {
-    const int side = EPI == EPI_SPLIT ? split_side_of(P, n0, kDBN) : 0;
+    const int side = EPI == EPI_SPLIT ? split_side_of(P, n0, kDBN) : EPI == EPI_PARTIAL ? ks : 0;
     dma_epilogue<EPI, TN>(P, smem, m0 + wm0, n0 + wn0, wave, lane, acc, side, ebias);
   }
 }
@@ -826,15 +858,24 @@ static hipError_t launch_dma_epi(const GemmProblem* p, int nprob, hipStream_t s)
 
 static bool aligned(const void* p, int bytes) { return ((uintptr_t)p % bytes) == 0; }
 
-// True when the DMA kernel applies: no Euler epilogue, one weight format per
-// launch, K a multiple of the k-tile, rows of A 16-byte aligned, N >= 128,
-// column counts, row strides and base pointers of every output (and of bias,
-// gate and residual) aligned for 4-column vector access, a tile-aligned split
-// column (split epilogue), and enough 256 x 256 tiles to occupy most of the
-// 256 CUs.
-bool gemm_dma_eligible(const GemmProblem* p, int nprob, int epi) {
+int64_t gemm_dma_tiles(int M, int N) { return (int64_t)((M + kDBM - 1) / kDBM) * ((N + kDBN - 1) / kDBN); }
+
+// Launches with fewer 256 x 256 tiles than this leave too many of the 256 CUs
+// idle for the direct-to-LDS kernel (one tile per CU); they run on the
+// 128 / 64-row tiles of the register-staged kernel, or split along k.
+#ifndef MMDIT_DMA_MIN_TILES
+#define MMDIT_DMA_MIN_TILES 128
+#endif
+constexpr int64_t kDmaMinTiles = MMDIT_DMA_MIN_TILES;
+
+// True when the DMA kernel can run the launch: no Euler epilogue, one weight
+// format per launch, K a multiple of the k-tile, rows of A 16-byte aligned,
+// N >= 128, column counts, row strides and base pointers of every output
+// (and of bias, gate and residual) aligned for 4-column vector access, and a
+// tile-aligned split column (split epilogue). Sets the launch's tile count.
+static bool dma_shape_ok(const GemmProblem* p, int nprob, int epi, int64_t& tiles) {
   if (epi == EPI_EULER) return false;
-  int64_t tiles = 0;
+  tiles = 0;
   int fmt = -1;
   for (int i = 0; i < nprob; ++i) {
     const GemmProblem& q = p[i];
@@ -861,9 +902,87 @@ bool gemm_dma_eligible(const GemmProblem* p, int nprob, int epi) {
       if ((epi == EPI_SPLIT || epi == EPI_SPLIT_QKV) && (q.split_n % kDBN != 0 || q.ldo2 % 4 || !aligned(q.out2, 8)))
         return false;
     }
-    tiles += (int64_t)((q.M + kDBM - 1) / kDBM) * ((q.N + kDBN - 1) / kDBN);
+    tiles += gemm_dma_tiles(q.M, q.N);
   }
-  return tiles >= 200;
+  return true;
+}
+
+// The DMA kernel takes the launch whole when its shape allows and it has
+// enough tiles to occupy most of the CUs.
+bool gemm_dma_eligible(const GemmProblem* p, int nprob, int epi) {
+  int64_t tiles = 0;
+  return dma_shape_ok(p, nprob, epi, tiles) && tiles >= kDmaMinTiles;
+}
+
+// Split-K: k-ranges of at least kSplitMinKTiles k-tiles, at most kMaxSplit
+// ranges, and no more units than one per CU.
+constexpr int kMaxSplit = 4, kSplitMinKTiles = 8, kSplitUnits = 256;
+
+int splitk_ways(int64_t tiles, int K) {
+  if (tiles <= 0 || tiles >= kDmaMinTiles) return 1;
+  int64_t w = kSplitUnits / tiles;
+  if (w > kMaxSplit) w = kMaxSplit;
+  const int64_t byk = (int64_t)(K / kDBK) / kSplitMinKTiles;
+  if (w > byk) w = byk;
+  return w >= 2 ? (int)w : 1;
+}
+
+int gemm_splitk_ways(const GemmProblem* p, int nprob, int epi) {
+  int64_t tiles = 0;
+  if (epi != EPI_GATE_RES || !dma_shape_ok(p, nprob, epi, tiles)) return 1;
+  int K = 0;
+  for (int i = 0; i < nprob; ++i) {
+    if (p[i].M == 0) continue;
+    if (p[i].fmt != 0) return 1;  // dense weights only
+    K = K == 0 || p[i].K < K ? p[i].K : K;
+  }
+  return splitk_ways(tiles, K);
+}
+
+// Split-K completion of the gated residual: v = bias + the k-ranges' partial
+// sums added in range order, res_out = res_in + gate[b, n] * v. One thread
+// per 4 consecutive columns of a row (column counts, strides and pointers
+// are 4-column aligned, as the DMA kernel requires).
+__global__ __launch_bounds__(256) void k_splitk_gate_res(GemmBatch gb) {
+  if (guard_skip(gb.p[0].skip)) return;
+  const int64_t q0 = (int64_t)gb.p[0].M * (gb.p[0].N / 4);
+  const int64_t q1 = (int64_t)gb.p[1].M * (gb.p[1].N / 4);
+  int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= q0 + q1) return;
+  const int prob = q < q0 ? 0 : 1;
+  if (prob) q -= q0;
+  const GemmProblem& P = gb.p[prob];
+  const int nq = P.N / 4;
+  const int m = (int)(q / nq), n = (int)(q - (int64_t)m * nq) * 4;
+  const int64_t mn = (int64_t)P.M * P.N;
+  const float* src = P.part + (int64_t)m * P.N + n;
+  f32x4 v = *reinterpret_cast<const f32x4*>(src);
+  for (int k = 1; k < gb.ksplit; ++k) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(src + k * mn);
+    v = v + w;
+  }
+  if (P.bias) {
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(P.bias) + n);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += (float)b[e];
+  }
+  const int b = m / P.res_out.rows_per_batch;
+  const f32x4 g = *reinterpret_cast<const f32x4*>(P.gate + (int64_t)b * P.gate_bstride + n);
+  const int64_t oi = seg_offset<bf16>(P.res_in, m) + n;
+  const int64_t oo = seg_offset<bf16>(P.res_out, m) + n;
+  if (P.res_f32) {
+    const f32x4 r = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(P.res_in.base) + oi);
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = r[e] + g[e] * v[e];
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(P.res_out.base) + oo) = o;
+  } else {
+    const bf16x4 r = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(P.res_in.base) + oi);
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (bf16)((float)r[e] + g[e] * v[e]);
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(P.res_out.base) + oo) = o;
+  }
 }
 
 // Quantised weights run with eight wavefronts (two per SIMD): each
@@ -895,6 +1014,41 @@ hipError_t launch_gemm_dma(const GemmProblem* p, int nprob, int epi, hipStream_t
     case EPI_SPLIT_QKV: return launch_dma_epi<EPI_SPLIT_QKV>(p, nprob, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gemm_dma_splitk(const GemmProblem* p, int nprob, int epi, int ways, float* part, hipStream_t s) {
+  if (epi != EPI_GATE_RES || ways < 2 || nprob < 1 || nprob > 2) return hipErrorInvalidValue;
+  GemmBatch gb{};
+  int tiles = 0;
+  int64_t quads = 0;
+  size_t at = 0;
+  for (int i = 0; i < 2; ++i) {
+    if (i < nprob) {
+      gb.p[i] = p[i];
+      gb.p[i].part = part + at;
+      at += (size_t)ways * p[i].M * p[i].N;
+      gb.tiles_m[i] = (p[i].M + kDBM - 1) / kDBM;
+      gb.tiles_n[i] = (p[i].N + kDBN - 1) / kDBN;
+      tiles += gb.tiles_m[i] * gb.tiles_n[i];
+      quads += (int64_t)p[i].M * (p[i].N / 4);
+    } else {
+      gb.tiles_m[i] = 1;
+      gb.tiles_n[i] = 1;
+    }
+    gb.tile_start[i + 1] = tiles;
+  }
+  gb.ksplit = ways;
+  if (tiles == 0) return hipSuccess;
+  constexpr int BK = MMDIT_DMA_BK, S = MMDIT_DMA_STAGES;
+  const size_t lds = (size_t)S * 2 * kDBM * BK * 2;
+  static std::atomic<uint64_t> lds_set{0};
+  const void* kfn = (const void*)k_gemm_dma<EPI_PARTIAL, BK, S, MMDIT_DMA_CPOL, 0, MMDIT_DMA_SPREAD, MMDIT_DMA_WAVES>;
+  const hipError_t e = ensure_lds_limit(kfn, (int)lds, lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gemm_dma<EPI_PARTIAL, BK, S, MMDIT_DMA_CPOL, 0, MMDIT_DMA_SPREAD, MMDIT_DMA_WAVES>),
+                     dim3(tiles * ways), dim3(64 * MMDIT_DMA_WAVES), lds, s, gb);
+  hipLaunchKernelGGL(k_splitk_gate_res, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s, gb);
+  return hipGetLastError();
 }
 
 }  // namespace mmdit

@@ -724,7 +724,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
                 a.y_bstride, a.accumulate, n0, lane);
 }
 
-// Several GEMVs over the same input in one launch (float32 x, SiLU applied):
+// Several GEMVs over the same input in one launch (float32 or bf16 x, SiLU applied):
 // block b serves the segment whose block range holds b.
 template <typename TW>
 __global__ __launch_bounds__(256) void k_gemv_multi(GemvMultiArgs a) {
@@ -734,7 +734,8 @@ __global__ __launch_bounds__(256) void k_gemv_multi(GemvMultiArgs a) {
   for (int i = 1; i < a.nseg; ++i)
     if ((int)blockIdx.x >= a.seg[i].block0) sg = i;
   const GemvSeg& g = a.seg[sg];
-  gemv_stage_x<float>(xs, a.x, a.B, a.K, a.x_bstride, true);
+  if (a.x_bf16) gemv_stage_x<bf16>(xs, a.x, a.B, a.K, a.x_bstride, true);
+  else gemv_stage_x<float>(xs, a.x, a.B, a.K, a.x_bstride, true);
   const int lane = threadIdx.x & 63;
   const int n0 = (((int)blockIdx.x - g.block0) * 4 + (threadIdx.x >> 6)) * kGemvRowsPerWave;
   gemv_rows<TW>(xs, reinterpret_cast<const TW*>(g.W), reinterpret_cast<const TW*>(g.bias), g.y, g.N, a.K, a.B,
@@ -777,7 +778,9 @@ __global__ __launch_bounds__(256) void k_gemv_multi4(GemvMultiArgs a) {
   // 32-byte read per lane would put 8 lanes on each bank)
   for (int i = threadIdx.x; i < BB * K; i += 256) {
     const int bb = i / K, k = i - bb * K;
-    const float v = silu_f<true>(reinterpret_cast<const float*>(a.x)[(int64_t)bb * a.x_bstride + k]);
+    const int64_t xi = (int64_t)bb * a.x_bstride + k;
+    const float v = silu_f<true>(a.x_bf16 ? (float)reinterpret_cast<const bf16*>(a.x)[xi]
+                                          : reinterpret_cast<const float*>(a.x)[xi]);
     xs[bb * K + ((k >> 2) & 1) * (K / 2) + (k >> 3) * 4 + (k & 3)] = v;
   }
   __syncthreads();

@@ -152,9 +152,10 @@ struct GemvSeg {
   int32_t block0;  // set by the launcher
 };
 struct GemvMultiArgs {
-  const void* x;  // float32 [B, x_bstride]
+  const void* x;  // [B, x_bstride], float32 (bf16 when x_bf16)
   int32_t K, B, x_bstride;
   int32_t nseg;
+  bool x_bf16 = false;
   GemvSeg seg[kGemvMaxSeg];
   const int* skip = nullptr;  // step-cache guard (see guard_skip), null: always run
 };
@@ -184,6 +185,9 @@ enum Epi : int {
   // instead of `out` (256x256 direct-to-LDS kernel, dense bf16 weights only)
   EPI_QKV = 5,
   EPI_SPLIT_QKV = 6,
+  // internal to split-K: the float32 sums over one k-range go to part
+  // [ksplit, M, N]; a second kernel applies the real epilogue
+  EPI_PARTIAL = 7,
 };
 
 struct GemmProblem {
@@ -221,6 +225,8 @@ struct GemmProblem {
   int32_t qk_h, qk_rows, qk_tok0, qk_Lpad;
   float qk_eps;
   float qk_qscale;  // Q is written times qk_qscale
+  // split-K partial sums [ksplit, M, N] float32 (set by the split-K launcher)
+  float* part = nullptr;
   // step-cache guard of the launch (read from the first problem), null: run
   const int* skip = nullptr;
 };
@@ -231,6 +237,17 @@ hipError_t launch_gemm_bf16(const GemmProblem* p, int nprob, int epi, hipStream_
 // Dense bf16 with direct-to-LDS staging, 256x256 tiles (large problems).
 bool gemm_dma_eligible(const GemmProblem* p, int nprob, int epi);
 hipError_t launch_gemm_dma(const GemmProblem* p, int nprob, int epi, hipStream_t s);
+// Split-K on the direct-to-LDS kernel for gated-residual launches with too
+// few 256x256 tiles to fill the chip: each tile's k-tiles are cut into
+// `ways` ranges, one workgroup per (range, tile) writes float32 partial sums,
+// and a second kernel adds them in range order and applies the epilogue.
+// gemm_splitk_ways: the number of ranges for this launch (1: no split);
+// splitk_ways: the same rule from the launch's tile count and k depth.
+int splitk_ways(int64_t tiles, int K);
+int64_t gemm_dma_tiles(int M, int N);
+int gemm_splitk_ways(const GemmProblem* p, int nprob, int epi);
+// part: float32 scratch of ways * sum(M N) values, 16-byte aligned
+hipError_t launch_gemm_dma_splitk(const GemmProblem* p, int nprob, int epi, int ways, float* part, hipStream_t s);
 // float32 operands and accumulation (VALU), dense weights only.
 hipError_t launch_gemm_f32(const GemmProblem* p, int nprob, int epi, hipStream_t s);
 // Quantised weights (fmt 1-4, layouts as the GEMM kernels read them) decoded
