@@ -122,6 +122,41 @@ def cpu_baseline(s):
                        f"{len(os.sched_getaffinity(0))} cores")}
 
 
+def time_config2(dev, g, steps):
+    """One dual block at 512x512 (256 text + 1024 image tokens, h 3072), two
+    weight sets alternating (680 MB each), timed back to back."""
+    import torch
+
+    from diffusion_transformer_mmdit_amd import binding as bd
+    from diffusion_transformer_mmdit_amd import inputs as I
+    from diffusion_transformer_mmdit_amd import random_init as RI
+    s2 = I.CFG2
+    dims2 = bd.make_dims(s2)
+    d2 = [RI.double_block(s2, 300 + i, dev) for i in range(2)]
+    d2c = [d.c() for d in d2]
+    img2 = torch.randn((1, s2.img_len, s2.hidden), generator=g, device=dev).to(torch.bfloat16)
+    txt2 = torch.randn((1, s2.txt_len, s2.hidden), generator=g, device=dev).to(torch.bfloat16)
+    vec2 = torch.randn((1, s2.hidden), generator=g, device=dev).to(torch.bfloat16)
+    ids2 = torch.from_numpy(bd.mmdit_make_ids(s2.grid_h, s2.grid_w, s2.txt_len)).to(dev)
+    ws2 = torch.empty(bd.mmdit_double_block_workspace(dims2), dtype=torch.uint8, device=dev)
+    io2, to2 = torch.empty_like(img2), torch.empty_like(txt2)
+    f2 = lambda i: bd.mmdit_double_block_fwd(dims2, d2c[i % 2], img2, txt2, io2, to2, vec2, ids2, ws2)  # noqa
+    for i in range(4):
+        f2(i)
+    n = max(4 * steps, 16)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for i in range(n):
+        f2(i)
+    torch.cuda.synchronize()
+    c2ms = (time.perf_counter() - t) * 1e3 / n
+    bf2 = block_flops(s2)
+    log(f"config-2 dual block (1280 tokens): {c2ms:.4f} ms ({bf2 / c2ms / 1e9:.0f} TFLOP/s)")
+    return {"ms": round(c2ms, 4), "tflops": round(bf2 / c2ms / 1e9, 1),
+            "frac": round(bf2 / c2ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "block_fwd_per_s": round(1e3 / c2ms, 1), "flops": bf2, "tokens": s2.seq_len}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +168,8 @@ def main():
                     help="step-cache threshold of the cached 50-step generation")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (calibrates HBM byte counters)")
+    ap.add_argument("--config2-only", action="store_true",
+                    help="time only the 1280-token dual block and print its figures as the JSON line")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): the library has no multi-GPU path",
@@ -158,6 +195,11 @@ def main():
         torch.cuda.synchronize()
         log(f"copy probe: {a.copy_probe_mib} MiB read + {a.copy_probe_mib} MiB written")
         del src, dst
+    if a.config2_only:
+        r = time_config2(dev, torch.Generator(device=dev).manual_seed(7), a.steps)
+        print(json.dumps({"metric": "dual_block_ms_1280_tokens", "value": r["ms"], "unit": "ms",
+                          "higher_is_better": False, "dtype": "bf16", "data": "synthetic", "config2": r}))
+        return
     s = I.CFG4
     log(f"building random-init model: {s.n_double}+{s.n_single} blocks, h {s.hidden}, bf16")
     t0 = time.perf_counter()
@@ -369,28 +411,7 @@ def main():
             f"({bf / sms / 1e9:.0f} TFLOP/s)")
         del dbl, sgl, dblc, sglc, wsb
 
-        # configuration 2: one dual block at 512x512 (256 text + 1024 image
-        # tokens), two weight sets alternating (680 MB each)
-        s2 = I.CFG2
-        dims2 = bd.make_dims(s2)
-        d2 = [RI.double_block(s2, 300 + i, dev) for i in range(2)]
-        d2c = [d.c() for d in d2]
-        img2 = torch.randn((1, s2.img_len, s2.hidden), generator=g, device=dev).to(torch.bfloat16)
-        txt2 = torch.randn((1, s2.txt_len, s2.hidden), generator=g, device=dev).to(torch.bfloat16)
-        ids2 = torch.from_numpy(bd.mmdit_make_ids(s2.grid_h, s2.grid_w, s2.txt_len)).to(dev)
-        ws2 = torch.empty(bd.mmdit_double_block_workspace(dims2), dtype=torch.uint8, device=dev)
-        io2, to2 = torch.empty_like(img2), torch.empty_like(txt2)
-        f2 = lambda i: bd.mmdit_double_block_fwd(dims2, d2c[i % 2], img2, txt2, io2, to2, vec, ids2, ws2)  # noqa
-        for i in range(4):
-            f2(i)
-        c2ms = timed(f2, max(4 * a.steps, 16))
-        bf2 = block_flops(s2)
-        out["config2_dual_block"] = {"ms": round(c2ms, 4), "tflops": round(bf2 / c2ms / 1e9, 1),
-                                     "frac": round(bf2 / c2ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-                                     "block_fwd_per_s": round(1e3 / c2ms, 1), "flops": bf2,
-                                     "tokens": s2.seq_len}
-        log(f"config-2 dual block (1280 tokens): {c2ms:.4f} ms ({bf2 / c2ms / 1e9:.0f} TFLOP/s)")
-        del d2, d2c, ws2
+        out["config2_dual_block"] = time_config2(dev, g, a.steps)
 
         # the step with its residual stream held in bf16 (dims.resid)
         cfg16 = bd.make_config(s, resid=bd.RESID_BF16)

@@ -487,3 +487,50 @@ def test_blocks_float32_residual_with_bf16_operands():
     bd.mmdit_single_block_fwd(dims, S_.c(), xin, out, vec, up_i32(ids), ws)
     sync()
     assert_parity(down(out), oracle_single(s, ws_, x, ids), "bf16", "f32-residual single")
+
+
+# Gated-residual GEMMs with fewer than 128 tiles of 256 x 256 are split along
+# k (float32 partial sums, then a reduce that applies bias, gate and
+# residual). Ways per launch (k-ranges) in these shapes:
+# - h 1536, m 3072, 77 + 600 tokens: out-projection 3 (1536 / 64 k-tiles
+#   allow no more), fc2 4, linear2 4;
+# - h 1024, m 4096, no text, 2 x 320 image tokens, float32 residual:
+#   out-projection 2, fc2 4, linear2 4 (the text problem is empty).
+SPLIT_K_CASES = {
+    "three_ways_ragged": (I.Shape(hidden=1536, heads=12, mlp_hidden=3072, txt_len=77, grid_h=24, grid_w=25,
+                                  dtype="bf16", cfg_id=81), False),
+    "two_ways_f32_residual_batch2": (I.Shape(hidden=1024, heads=8, mlp_hidden=4096, txt_len=0, grid_h=16,
+                                             grid_w=20, batch=2, dtype="bf16", cfg_id=82), True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SPLIT_K_CASES))
+def test_blocks_split_k_gated_residual(case):
+    t = torch()
+    s, f32_resid = SPLIT_K_CASES[case]
+    x = I.block_inputs(s)
+    ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
+    dims = bd.make_dims(s, resid=bd.RESID_F32) if f32_resid else bd.make_dims(s)
+    rd = "f32" if f32_resid else "bf16"
+    w = I.double_block_weights(s, 0)
+    W = bd.DoubleW(w, bd.BF16, "cuda")
+    img, txt = up(x["x_img"], rd), up(x["x_txt"], rd)
+    img_o, txt_o = t.empty_like(img), t.empty_like(txt)
+    vec = up(x["vec"], "bf16")
+    ws = workspace(bd.mmdit_double_block_workspace(dims))
+    print(f"split-k double block {case}", flush=True)
+    bd.mmdit_double_block_fwd(dims, W.c(), img, txt, img_o, txt_o, vec, up_i32(ids), ws)
+    sync()
+    rimg, rtxt = oracle_double(s, w, x, ids)
+    assert_parity(down(img_o), rimg, "bf16", f"split-k {case} img")
+    if s.txt_len:
+        assert_parity(down(txt_o), rtxt, "bf16", f"split-k {case} txt")
+    ws_ = I.single_block_weights(s, 0)
+    S_ = bd.SingleW(ws_, bd.BF16, "cuda")
+    xin = up(x["x"], rd)
+    out = t.empty_like(xin)
+    wss = workspace(bd.mmdit_single_block_workspace(dims))
+    print(f"split-k single block {case}", flush=True)
+    bd.mmdit_single_block_fwd(dims, S_.c(), xin, out, vec, up_i32(ids), wss)
+    sync()
+    assert_parity(down(out), oracle_single(s, ws_, x, ids), "bf16", f"split-k {case} single")
