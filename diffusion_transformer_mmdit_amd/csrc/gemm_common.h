@@ -126,14 +126,16 @@ __device__ __forceinline__ void deq_tq2_32(uint32_t w0, uint32_t w1, uint32_t s1
   }
 }
 
-// GELU-tanh for the bf16 kernels: exp2 and reciprocal on the hardware
-// transcendental units (results are rounded to bf16 afterwards).
+// GELU-tanh for the bf16 kernels (results are rounded to bf16 afterwards).
+// With u = sqrt(2/pi) (x + 0.044715 x^3), 0.5 x (1 + tanh u) = x / (1 +
+// exp(-2u)); exp(-2u) = exp2(x (a + b x^2)) with a = -2 sqrt(2/pi) log2(e),
+// b = 0.044715 a. Five VALU operations plus exp2 and a reciprocal on the
+// transcendental unit; no 1 - r cancellation for negative x.
 __device__ __forceinline__ float gelu_fast(float x) {
-  const float k0 = 0.7978845608028654f, k1 = 0.044715f;
-  const float u = k0 * x * fmaf(k1, x * x, 1.0f);
-  const float e = __builtin_amdgcn_exp2f(u * 2.8853900817779268f);  // exp(2u)
-  const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
-  return 0.5f * x * (1.0f + t);
+  constexpr float a = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+  constexpr float b = 0.044715f * a;
+  const float e = __builtin_amdgcn_exp2f(x * fmaf(b, x * x, a));
+  return x * __builtin_amdgcn_rcpf(e + 1.0f);
 }
 
 // Epilogue of one 32x32 MFMA accumulator block held by a lane: 16 rows

@@ -17,6 +17,8 @@
 // 64 banks). The swizzle is applied on the load side: lane i of a DMA
 // instruction writes slot i, so it fetches the global chunk destined for that
 // slot.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace mmdit {
@@ -177,6 +179,50 @@ __device__ __forceinline__ void dma_epilogue_impl(const GemmProblem& P, float* s
     ld = pin(to2 ? P.ldo2 : P.ldo) * 2;
     obase += ((int64_t)m0w * (ld / 2) + n - (to2 ? pin(P.split_n) : 0)) * 2;
   }
+  if constexpr (EPI == EPI_GATE_RES && FULL) {
+    // Residual rows requested one group ahead: the loads of group k + 1 are
+    // in flight while group k is combined and stored (GR rows per lane and
+    // group, RPL / GR groups per 32-row chunk).
+    constexpr int GPC = RPL / GR, NG = 4 * GPC;
+    typedef typename std::conditional<f32r, f32x4, bf16x4>::type RT;
+    typedef __attribute__((address_space(1))) const RT gcRT;
+    RT rbuf[2][GR];
+    auto row_of = [&](int k, int t) { return 32 * (k / GPC) + RPI * (GR * (k % GPC) + t) + rs; };
+#pragma unroll
+    for (int t = 0; t < GR; ++t) rbuf[0][t] = *(gcRT*)(ibase + row_of(0, t) * ldi);
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      const int i = k / GPC, h = k % GPC;
+      if (h == 0) {
+#pragma unroll
+        for (int j = 0; j < NJF; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<f32x4*>(stg + (lane & 31) * LD + 32 * j + 8 * g + 4 * (lane >> 5)) =
+                (f32x4){acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+      }
+      f32x4 a[GR];
+#pragma unroll
+      for (int t = 0; t < GR; ++t) a[t] = *reinterpret_cast<const f32x4*>(stg + (RPI * (GR * h + t) + rs) * LD + 4 * c4);
+      if (k + 1 < NG) {
+#pragma unroll
+        for (int t = 0; t < GR; ++t) rbuf[(k + 1) & 1][t] = *(gcRT*)(ibase + row_of(k + 1, t) * ldi);
+      }
+#pragma unroll
+      for (int t = 0; t < GR; ++t) {
+        const RT rv = rbuf[k & 1][t];
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (float)rv[e] + gate1[e] * (a[t][e] + bias[e]);
+        gchar* dstp = obase + row_of(k, t) * ld;
+        if constexpr (f32r)
+          *(gf32x4*)dstp = (f32x4){o[0], o[1], o[2], o[3]};
+        else
+          *(gbf16x4*)dstp = (bf16x4){(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     // stage rows 32i .. 32i+31: lane owns row lane%32 of each group
@@ -308,14 +354,26 @@ __device__ __forceinline__ void dma_epilogue(const GemmProblem& P, char* smem, i
 // staged through LDS as in dma_epilogue_impl; lane (r = lane % 32, hf =
 // lane / 32) then takes dims 64 hf .. 64 hf + 63 of chunk row r, so a row's
 // sum of squares is the lane's 64 terms plus its partner's (lane ^ 32), and
-// every rotation pair lies in one lane. Rows go to Q (K) [B, H, Lpad, 128]
-// as 16-byte stores.
+// every rotation pair lies in one lane. Rows go to Q (K) [B, H, Lpad, 128].
+//
+// When the chunk's 32 rows are consecutive tokens of one batch (every chunk
+// but a ragged last one or one that straddles a batch), their angles are one
+// contiguous 16 KB block of the table and their output rows one contiguous
+// 8 KB block of Q (K): the angles arrive by whole-wavefront 1 KB loads
+// (requested one chunk ahead) and are handed to the lanes of their rows
+// through the chunk's LDS slice, and the bf16 results go back through the
+// slice so that each store writes 4 whole rows. Other chunks load each row's
+// angles and store each row's halves lane by lane. A wavefront touches only
+// its own LDS slice, and its LDS operations complete in program order.
 template <int TN>
 __device__ __forceinline__ void qk_epilogue(const GemmProblem& P, char* smem, int m0w, int n0w, int wave,
                                             int lane, const f32x16 (&acc)[4][TN / 32]) {
   static_assert(TN == 128, "one head per wavefront tile");
-  constexpr int LD = TN + 4;
+  constexpr int LD = TN + 4;   // float32 row stride of the slice (angles use 128 of it)
+  constexpr int LDB = 136;     // bf16 row stride of the staged output rows
   float* stg = reinterpret_cast<float*>(smem) + wave * (32 * LD);
+  // output rows: a second slice per wavefront, after the four float32 slices
+  bf16* stgb = reinterpret_cast<bf16*>(smem + 4 * 32 * LD * 4) + wave * (32 * LDB);
   const int M = pin(P.M);
   const int qk_h = pin(P.qk_h);
   const int which = n0w >= qk_h ? 1 : 0;  // 0 q, 1 k
@@ -325,11 +383,38 @@ __device__ __forceinline__ void qk_epilogue(const GemmProblem& P, char* smem, in
   const float eps = P.qk_eps;
   const int r = lane & 31, hf = lane >> 5;
   gchar* dst = (gchar*)pin(reinterpret_cast<char*>(which ? P.qk_K : P.qk_Q));
-  const bf16* gsc = reinterpret_cast<const bf16*>(which ? P.kn : P.qn) + 64 * hf;
-  const bf16* bp = reinterpret_cast<const bf16*>(P.bias);
-  const float* rope = P.rope;
+  gcchar* gsc = (gcchar*)(reinterpret_cast<const char*>(which ? P.kn : P.qn) + 128 * hf);
+  gcchar* bp = (gcchar*)pin(reinterpret_cast<const char*>(P.bias));
+  gcchar* rope = (gcchar*)pin(reinterpret_cast<const char*>(P.rope));
+  // the lane's 64 norm weights and biases serve all four chunks
+  bf16x8 g8[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) g8[q] = *(const __attribute__((address_space(1))) bf16x8*)(gsc + 16 * q);
+  bf16x4 b4[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) b4[q] = bp ? *(gcbf16x4*)(bp + (n0w + 64 * hf + 4 * q) * 2) : bf16x4{};
+  // chunk i: first row mc, batch bF, first token tF; fast when its 32 rows
+  // are in range and in one batch (then tokens tF .. tF + 31)
+  auto chunk = [&](int i, int& bF, int& tF) {
+    const int mc = m0w + 32 * i;
+    bF = mc / rows;
+    tF = tok0 + (mc - bF * rows);
+    return mc + 32 <= M && (mc + 31) / rows == bF;
+  };
+  f32x4 tbl[16];  // angles of a fast chunk as loaded: floats 256 q + 4 lane .. + 3 of its block
+  auto load_block = [&](int tF) {
+    gcchar* tb = rope + (int64_t)tF * 512;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) tbl[q] = *(gcf32x4*)(tb + q * 1024 + lane * 16);
+  };
+  {
+    int b0, t0;
+    if (chunk(0, b0, t0)) load_block(t0);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    int bF, tF;
+    const bool fast = chunk(i, bF, tF);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -341,15 +426,7 @@ __device__ __forceinline__ void qk_epilogue(const GemmProblem& P, char* smem, in
     for (int q = 0; q < 16; ++q) {
       const f32x4 x = *reinterpret_cast<const f32x4*>(stg + r * LD + 64 * hf + 4 * q);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
-    }
-    if (bp) {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const bf16x4 b4 = *reinterpret_cast<const bf16x4*>(bp + n0w + 64 * hf + 4 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * q + e] += (float)b4[e];
-      }
+      for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e] + (float)b4[q][e];
     }
     float ss = 0.f;
 #pragma unroll
@@ -357,30 +434,60 @@ __device__ __forceinline__ void qk_epilogue(const GemmProblem& P, char* smem, in
     ss += __shfl_xor(ss, 32);
     // q rows carry the attention's score scale
     const float rstd = (which ? 1.0f : P.qk_qscale) / sqrtf(ss * (1.0f / 128.0f) + eps);
-    const int m = m0w + 32 * i + r;
-    if (m < M) {
-      const int b = m / rows;
-      const int t = tok0 + (m - b * rows);
-      const float* tb = rope + ((int64_t)t * 64 + 32 * hf) * 2;
-      gchar* out = dst + ((((int64_t)b * H + hh) * Lpad + t) * 128 + 64 * hf) * 2;
+    int m = m0w + 32 * i + r;
+    const bool ok = m < M;
+    m = ok ? m : M - 1;  // rows past the end read a valid row's angles and store nothing
+    const int b = m / rows;
+    const int t = tok0 + (m - b * rows);
+    asm volatile("" ::: "memory");  // the chunk's reads of the slice stay ahead of the angle writes
+    if (fast) {
+      // angles of row 2q + lane / 32 (floats 4 (lane % 32) ..) into the slice
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const f32x4 c0 = *reinterpret_cast<const f32x4*>(tb + 8 * q);
-        const f32x4 c1 = *reinterpret_cast<const f32x4*>(tb + 8 * q + 4);
-        const bf16x8 g8 = *reinterpret_cast<const bf16x8*>(gsc + 8 * q);
-        const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-        bf16x8 o;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float y0 = v[8 * q + 2 * u] * rstd * (float)g8[2 * u];
-          const float y1 = v[8 * q + 2 * u + 1] * rstd * (float)g8[2 * u + 1];
-          const float c = cs[2 * u], sn = cs[2 * u + 1];
-          o[2 * u] = (bf16)(c * y0 - sn * y1);
-          o[2 * u + 1] = (bf16)(sn * y0 + c * y1);
-        }
-        *(gbf16x8*)(out + 16 * q) = o;
+      for (int q = 0; q < 16; ++q) *reinterpret_cast<f32x4*>(stg + (2 * q + hf) * LD + 4 * r) = tbl[q];
+      if (i + 1 < 4) {
+        int bn, tn;
+        if (chunk(i + 1, bn, tn)) load_block(tn);
       }
     }
+    asm volatile("" ::: "memory");
+    const float* arow = stg + r * LD + 64 * hf;
+    gcchar* tb = rope + ((int64_t)t * 128 + 64 * hf) * 4;
+    gchar* orow = dst + ((((int64_t)b * H + hh) * Lpad + t) * 128 + 64 * hf) * 2;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      f32x4 ca, cb;
+      if (fast) {
+        ca = *reinterpret_cast<const f32x4*>(arow + 8 * q);
+        cb = *reinterpret_cast<const f32x4*>(arow + 8 * q + 4);
+      } else {
+        ca = *(gcf32x4*)(tb + 32 * q);
+        cb = *(gcf32x4*)(tb + 32 * q + 16);
+      }
+      const float cs[8] = {ca[0], ca[1], ca[2], ca[3], cb[0], cb[1], cb[2], cb[3]};
+      bf16x8 o;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float y0 = v[8 * q + 2 * u] * rstd * (float)g8[q][2 * u];
+        const float y1 = v[8 * q + 2 * u + 1] * rstd * (float)g8[q][2 * u + 1];
+        const float c = cs[2 * u], sn = cs[2 * u + 1];
+        o[2 * u] = (bf16)(c * y0 - sn * y1);
+        o[2 * u + 1] = (bf16)(sn * y0 + c * y1);
+      }
+      if (fast) *reinterpret_cast<bf16x8*>(stgb + r * LDB + 64 * hf + 8 * q) = o;
+      else if (ok) *(gbf16x8*)(orow + 16 * q) = o;
+    }
+    asm volatile("" ::: "memory");
+    if (fast) {
+      // rows through the output slice: store k writes rows 4k .. 4k + 3 whole
+      gchar* out = dst + (((int64_t)bF * H + hh) * Lpad + tF) * 256;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int rr = 4 * k + (lane >> 4);
+        const bf16x8 w = *reinterpret_cast<const bf16x8*>(stgb + rr * LDB + 8 * (lane & 15));
+        *(gbf16x8*)(out + rr * 256 + 16 * (lane & 15)) = w;
+      }
+    }
+    asm volatile("" ::: "memory");  // the slices' reads stay ahead of the next chunk's writes
   }
 }
 
@@ -483,6 +590,8 @@ __global__ __launch_bounds__(64 * W, 1) void k_gemm_dma(GemmBatch gb) {
   static_assert(FMT == 0 || BK == 64, "quantised weights need 64-wide k-tiles (one scale group)");
   static_assert(!SUB || PCS >= 1, "one sub-byte piece per thread at least");
   static_assert(S * STAGE >= W * 32 * (TN + 4) * 4, "epilogue staging must fit in the operand stages");
+  static_assert(EPI != EPI_QKV && EPI != EPI_SPLIT_QKV || S * STAGE >= W * 32 * ((TN + 4) * 4 + 136 * 2),
+                "QK epilogue output slices must fit in the operand stages");
   static_assert(EPI != EPI_PARTIAL || FMT == 0, "split-K runs on dense weights");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int prob, tm, tn, ks;
