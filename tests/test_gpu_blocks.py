@@ -534,3 +534,20 @@ def test_blocks_split_k_gated_residual(case):
     bd.mmdit_single_block_fwd(dims, S_.c(), xin, out, vec, up_i32(ids), wss)
     sync()
     assert_parity(down(out), oracle_single(s, ws_, x, ids), "bf16", f"split-k {case} single")
+
+
+def test_blocks_full_width_between_128_and_200_tiles():
+    # h 3072, no text, 20 x 32 image tokens (640 rows): fc1 has 144 tiles of
+    # 256 x 256 and takes the direct-to-LDS kernel with the GELU epilogue in
+    # one partial round; QKV has 108 (register-staged kernel, separate QK
+    # pass); the out-projection, fc2 and linear2 (36 tiles each) are split
+    # along k in 4 ranges; linear1 has 252 (fused QK and split GELU)
+    s = I.Shape(txt_len=0, grid_h=20, grid_w=32, dtype="bf16", cfg_id=83)
+    x = I.block_inputs(s)
+    ids = oracle.make_ids(s.grid_h, s.grid_w, s.txt_len)
+    w = I.double_block_weights(s, 0)
+    img, _ = run_double(s, w, x, ids)
+    rimg, _ = oracle_double(s, w, x, ids)
+    assert_parity(img, rimg, "bf16", "640-row dual img")
+    ws_ = I.single_block_weights(s, 0)
+    assert_parity(run_single(s, ws_, x, ids), oracle_single(s, ws_, x, ids), "bf16", "640-row single")
